@@ -1,0 +1,1095 @@
+// SpectralQuant hot path on gfx950 (MI355X): table upload, sq_compress,
+// sq_scores, sq_attend, sq_dequantize.
+//
+// The method (SpectralQuant README, "Overview" and "Repository Structure";
+// ossradar.top summary, core capabilities): rotate each K/V vector into the
+// calibrated eigenbasis, quantise every rotated coordinate with its region's
+// Lloyd-Max codebook at its water-filled width, add a 1-bit QJL sketch of the
+// residual on the d_eff signal coordinates of keys only, pack bit-dense; at
+// decode time rotate the query once and score directly from the codes, and
+// dequantise values for the softmax-weighted sum.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace sq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float((uint32_t)u << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even (finite inputs)
+__host__ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  __builtin_memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t half_bits_rne(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Make this wave's earlier LDS writes visible to its other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ upload
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static sq_status hip_fail(const char *what, hipError_t e) {
+  return fail(SQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void release_tables(sq_calib *c) {
+  if (c->dev_blob) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (c->device >= 0 && cur != c->device) (void)hipSetDevice(c->device);
+    (void)hipFree(c->dev_blob);
+    if (c->device >= 0 && cur != c->device && cur >= 0) (void)hipSetDevice(cur);
+  }
+  c->dev_blob = nullptr;
+  c->dev_heads = nullptr;
+  c->dev_bytes = 0;
+  c->device = -1;
+}
+
+sq_status upload_tables(sq_calib *c, void *stream) {
+  const int nh = (int)c->heads.size();
+  // host image of the blob: [DevHead x nh] then per-head sections
+  std::vector<DevHead> desc(nh);
+  size_t off = align256(sizeof(DevHead) * nh);
+  for (int h = 0; h < nh; ++h) {
+    const HeadCal &hc = c->heads[h];
+    const int d = hc.d;
+    DevHead &D = desc[h];
+    std::memset(&D, 0, sizeof(D));
+    D.d = d;
+    D.d_eff = hc.d_eff;
+    D.m = hc.m;
+    D.W = hc.W;
+    D.code_bits = hc.code_bits;
+    D.n_thr = hc.n_thr;
+    D.n_cent = hc.n_cent;
+    D.has_gamma = hc.m > 0;
+    D.qjl_scale = hc.m > 0 ? (float)(std::sqrt(M_PI / 2.0) / hc.m) : 0.0f;
+    D.n_cent_sig = hc.d_eff < d ? hc.cent_base[hc.d_eff] : hc.n_cent;
+    D.off_R = off;       off = align256(off + sizeof(float) * d * d);
+    D.off_Rfrag = off;   off = align256(off + sizeof(uint16_t) * 3 * d * d);
+    D.off_coord = off;   off = align256(off + sizeof(DevCoord) * d);
+    D.off_thr = off;     off = align256(off + sizeof(float) * std::max(1, hc.n_thr));
+    D.off_cent = off;    off = align256(off + sizeof(float) * std::max(1, hc.n_cent));
+    D.off_S = off;       off = align256(off + sizeof(float) * std::max(1, hc.m * hc.d_eff));
+  }
+  std::vector<uint8_t> img(off, 0);
+  std::memcpy(img.data(), desc.data(), sizeof(DevHead) * nh);
+  for (int h = 0; h < nh; ++h) {
+    const HeadCal &hc = c->heads[h];
+    const DevHead &D = desc[h];
+    const int d = hc.d;
+    float *R = (float *)(img.data() + D.off_R);
+    for (int k = 0; k < d * d; ++k) R[k] = (float)hc.R[k];
+    // bf16 x3 split of R (hi + mid + lo reproduces R to ~2^-24 relative), laid
+    // out as MFMA 32x32x16 A operands: fragment (s, mb, ks), lane l, element e
+    // holds R_s[mb*32 + l%32][ks*16 + 8*(l/32) + e].
+    uint16_t *F = (uint16_t *)(img.data() + D.off_Rfrag);
+    const int MB = d / 32, KS = d / 16;
+    for (int mb = 0; mb < MB; ++mb)
+      for (int ks = 0; ks < KS; ++ks)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e) {
+            const int row = mb * 32 + (l & 31), col = ks * 16 + 8 * (l >> 5) + e;
+            double v = hc.R[(size_t)row * d + col];
+            uint16_t parts[3];
+            for (int s = 0; s < 3; ++s) {
+              parts[s] = f32_to_bf16_rne((float)v);
+              float back;
+              uint32_t u = (uint32_t)parts[s] << 16;
+              std::memcpy(&back, &u, 4);
+              v -= (double)back;
+            }
+            for (int s = 0; s < 3; ++s)
+              F[((((size_t)s * MB + mb) * KS + ks) * 64 + l) * 8 + e] = parts[s];
+          }
+    DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
+    for (int i = 0; i < d; ++i)
+      Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
+    if (hc.n_thr) std::memcpy(img.data() + D.off_thr, hc.thr.data(), sizeof(float) * hc.n_thr);
+    if (hc.n_cent) std::memcpy(img.data() + D.off_cent, hc.cent.data(), sizeof(float) * hc.n_cent);
+    if (hc.m) std::memcpy(img.data() + D.off_S, hc.S.data(), sizeof(float) * hc.m * hc.d_eff);
+  }
+  release_tables(c);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  void *p = nullptr;
+  e = hipMalloc(&p, off);
+  if (e != hipSuccess) return fail(SQ_ERR_ALLOC, std::string("hipMalloc tables: ") + hipGetErrorString(e));
+  hipStream_t s = (hipStream_t)stream;
+  e = hipMemcpyAsync(p, img.data(), off, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail("table upload", e);
+  }
+  c->dev_blob = p;
+  c->dev_heads = (DevHead *)p;
+  c->host_desc = desc;
+  c->dev_bytes = off;
+  c->device = dev;
+  return SQ_OK;
+}
+
+// ------------------------------------------------------------------ compress
+//
+// One wavefront compresses a tile of 64 tokens of one head; a workgroup holds
+// up to 4 such waves and shares the head's threshold and signal-centroid
+// tables in LDS.
+//   rotate:   y^T[coord][token] = R x^T as MFMA 32x32x16 bf16 tiles.  R is
+//             split into three bf16 terms (Henry, Tang & Heinecke, ARITH 2019:
+//             bf16x3), bf16 inputs are exact, so each product is exact in the
+//             fp32 accumulator.  fp32 inputs are split into three terms as well
+//             and the six leading cross products are accumulated.
+//   quantise: the 32x32 accumulator block goes through LDS so that each lane
+//             holds one token; lanes walk the block's coordinates in order
+//             (uniform width, uniform bit position) and binary-search the
+//             coordinate's thresholds in LDS.
+//   QJL:      signal-coordinate residuals are kept in LDS; z_j = [(S r)_j >= 0]
+//             with S read through the scalar cache.
+//   pack:     a running two-word bit window per lane; each completed word is
+//             stored at once, 64 lanes -> one coalesced 256-byte store.
+
+struct CompressArgs {
+  const DevHead *heads;
+  const uint8_t *blob;
+  const void *x;
+  uint32_t *packed;
+  int64_t xs_b, xs_h, xs_t;
+  int64_t ps_b, ps_h;
+  int64_t n_tokens;
+  int first_head, cbs;
+  int n_tiles;          // ceil(T / 64)
+  int lds_cent_off;     // floats: start of the signal-centroid table
+  int lds_wave_off;     // floats: start of the per-wave areas
+  int lds_wave_floats;  // floats per wave
+  int rstride;          // residual row stride (odd)
+};
+
+template <bool F32>
+__device__ __forceinline__ void split3(const float *v, uint4 &p0, uint4 &p1, uint4 &p2) {
+  uint16_t a[8], b[8], c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = v[e];
+    a[e] = f32_to_bf16_rne(x);
+    x -= __uint_as_float((uint32_t)a[e] << 16);
+    b[e] = f32_to_bf16_rne(x);
+    x -= __uint_as_float((uint32_t)b[e] << 16);
+    c[e] = f32_to_bf16_rne(x);
+  }
+  p0 = make_uint4(a[0] | (a[1] << 16), a[2] | (a[3] << 16), a[4] | (a[5] << 16), a[6] | (a[7] << 16));
+  p1 = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+  p2 = make_uint4(c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16));
+}
+
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Running bit window of one record (per lane); positions are wave-uniform.
+struct BitWriter {
+  uint32_t lo, hi;
+  int fill, wcur;
+  uint32_t *dst;   // &slot[tile*W*64 + lane]
+  bool valid;
+  __device__ __forceinline__ void store_word() {
+    dst[(int64_t)wcur * 64] = valid ? lo : 0u;
+    ++wcur;
+    lo = hi;
+    hi = 0;
+    fill -= 32;
+  }
+  __device__ __forceinline__ void put(uint32_t v, int b) {
+    lo |= v << fill;
+    if (fill + b > 32) hi = v >> (32 - fill);
+    fill += b;
+    if (fill >= 32) store_word();
+  }
+};
+
+template <int D, bool F32>
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int ch = a.first_head + b * a.cbs + h;
+  const DevHead *hd = a.heads + ch;
+  const int d_eff = hd->d_eff, m = hd->m, W = hd->W;
+  const int n_thr = hd->n_thr, n_cent_sig = m > 0 ? hd->n_cent_sig : 0;
+
+  float *s_thr = smem;
+  float *s_cent = smem + a.lds_cent_off;
+  {
+    const float *g_thr = (const float *)(a.blob + hd->off_thr);
+    for (int k = threadIdx.x; k < n_thr; k += blockDim.x) s_thr[k] = g_thr[k];
+    const float *g_cent = (const float *)(a.blob + hd->off_cent);
+    for (int k = threadIdx.x; k < n_cent_sig; k += blockDim.x) s_cent[k] = g_cent[k];
+  }
+  __syncthreads();
+
+  const int tile = blockIdx.x * nwaves + wave;
+  if (tile >= a.n_tiles) return;  // no block-level barrier after this point
+  float *yb = smem + a.lds_wave_off + wave * a.lds_wave_floats;  // [64][33]
+  float *rb = yb + 64 * 33;                                      // [64][rstride]
+  const int t0 = tile * 64;
+  const int64_t T = a.n_tokens;
+  const int64_t xbase = (int64_t)b * a.xs_b + (int64_t)h * a.xs_h;
+  constexpr int KS = D / 16, MB = D / 32;
+  const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag);
+  const DevCoord *coords = (const DevCoord *)(a.blob + hd->off_coord);
+
+  // B operands: x^T fragments, lane l -> token nb*32 + l%32, k = ks*16 + 8*(l/32) + e
+  uint4 xf[F32 ? 1 : 2][F32 ? 1 : KS];
+  if constexpr (!F32) {
+    const uint16_t *xp = (const uint16_t *)a.x + xbase;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t t = t0 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        xf[nb][ks] = t < T ? *(const uint4 *)(xp + t * a.xs_t + ks * 16 + 8 * (lane >> 5))
+                           : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  BitWriter bw;
+  bw.lo = bw.hi = 0;
+  bw.fill = 0;
+  bw.wcur = 0;
+  bw.dst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
+  bw.valid = (t0 + lane) < T;
+  float g2 = 0.0f;
+
+  for (int mb = 0; mb < MB; ++mb) {
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc0[v] = acc1[v] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 r0 = Rf[((0 * MB + mb) * KS + ks) * 64 + lane];
+      const uint4 r1 = Rf[((1 * MB + mb) * KS + ks) * 64 + lane];
+      const uint4 r2 = Rf[((2 * MB + mb) * KS + ks) * 64 + lane];
+      if constexpr (!F32) {
+        acc0 = mfma32(r0, xf[0][ks], acc0);
+        acc1 = mfma32(r0, xf[1][ks], acc1);
+        acc0 = mfma32(r1, xf[0][ks], acc0);
+        acc1 = mfma32(r1, xf[1][ks], acc1);
+        acc0 = mfma32(r2, xf[0][ks], acc0);
+        acc1 = mfma32(r2, xf[1][ks], acc1);
+      } else {
+        const float *xp = (const float *)a.x + xbase;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int64_t t = t0 + nb * 32 + (lane & 31);
+          float v[8];
+          if (t < T) {
+            const float4 *src = (const float4 *)(xp + t * a.xs_t + ks * 16 + 8 * (lane >> 5));
+            const float4 u0 = src[0], u1 = src[1];
+            v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+            v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+          }
+          uint4 x0, x1, x2;
+          split3<true>(v, x0, x1, x2);
+          f32x16 &acc = nb == 0 ? acc0 : acc1;
+          acc = mfma32(r0, x0, acc);
+          acc = mfma32(r0, x1, acc);
+          acc = mfma32(r1, x0, acc);
+          acc = mfma32(r0, x2, acc);
+          acc = mfma32(r2, x0, acc);
+          acc = mfma32(r1, x1, acc);
+        }
+      }
+    }
+    // accumulator (row = coord, col = token) -> LDS yb[token][coord]
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      yb[(lane & 31) * 33 + row] = acc0[v];
+      yb[(32 + (lane & 31)) * 33 + row] = acc1[v];
+    }
+    wave_lds_sync();
+    for (int cl = 0; cl < 32; ++cl) {
+      const int i = mb * 32 + cl;
+      const DevCoord cd = coords[i];
+      if (cd.width == 0) {
+        if (i < d_eff && m > 0) {
+          const float y = yb[lane * 33 + cl];
+          g2 += y * y;
+          rb[lane * a.rstride + i] = y;
+        }
+        continue;
+      }
+      const float y = yb[lane * 33 + cl];
+      const float *th = s_thr + cd.thr_base - 1;
+      int code = 0;
+      for (int k = cd.width - 1; k >= 0; --k) {
+        const int cand = code + (1 << k);
+        code = th[cand] < y ? cand : code;
+      }
+      bw.put((uint32_t)code, cd.width);
+      if (i < d_eff && m > 0) {
+        const float r = y - s_cent[cd.cent_base + code];
+        g2 += r * r;
+        rb[lane * a.rstride + i] = r;
+      }
+    }
+    wave_lds_sync();
+  }
+
+  uint32_t ghalf = 0;
+  if (m > 0) {
+    const float *S = (const float *)(a.blob + hd->off_S);
+    const float *rr = rb + lane * a.rstride;
+    for (int j = 0; j < m; ++j) {
+      float dot = 0.0f;
+      for (int i = 0; i < d_eff; ++i) dot = fmaf(S[j * d_eff + i], rr[i], dot);
+      bw.put(dot >= 0.0f ? 1u : 0u, 1);
+    }
+    ghalf = half_bits_rne(sqrtf(g2)) << 16;
+  }
+  while (bw.wcur < W) {
+    if (bw.wcur == W - 1) bw.lo |= ghalf;
+    bw.store_word();
+  }
+}
+
+// ------------------------------------------------------------------ scores
+//
+// A workgroup serves one (batch, KV head) and a contiguous run of 64-token
+// tiles.  Prologue: q~ = R q for the group's query heads and w = S q~[:d_eff]
+// (both to LDS), and the head's centroid table to LDS.  Main loop: lane =
+// token; the tile's record words are staged in LDS (lane-private rows), the
+// lane walks the coordinates in order with a two-word window, looks up the
+// centroid and accumulates q~_i * C_i[code] for every query head of the group
+// (one LDS broadcast read fetches q~_i for all of them), then adds the QJL
+// term sqrt(pi/2)/m * gamma * sum_j w_j (2 z_j - 1).
+
+struct ScoresArgs {
+  const DevHead *heads;
+  const uint8_t *blob;
+  const void *q;
+  const uint32_t *kpacked;
+  float *scores;
+  int64_t ps_b, ps_h;
+  int64_t n_tokens;
+  int first_head, cbs;
+  int n_q_heads, n_kv_heads;
+  int q_f32;
+  int n_tiles, tiles_per_block;
+  int lds_cent_off, lds_w_off, lds_rec_off;  // floats
+  int max_W;
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
+  extern __shared__ float smem[];
+  constexpr int GP = G <= 4 ? 4 : 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  const int ch = a.first_head + b * a.cbs + hkv;
+  const DevHead *hd = a.heads + ch;
+  const int d = hd->d, d_eff = hd->d_eff, m = hd->m, W = hd->W, n_cent = hd->n_cent;
+  const float *R = (const float *)(a.blob + hd->off_R);
+
+  float *qt = smem;                       // [d][GP]   q~
+  float *wq = smem + a.lds_w_off;         // [m][GP]   S q~
+  float *cent = smem + a.lds_cent_off;    // [n_cent]
+  uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off) + wave * a.max_W * 64;
+
+  // raw queries to the centroid area first (it is loaded afterwards)
+  float *qraw = cent;
+  const int64_t qbase = ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * d;
+  for (int k = threadIdx.x; k < G * d; k += blockDim.x)
+    qraw[k] = a.q_f32 ? ((const float *)a.q)[qbase + k]
+                      : bf16_to_f32(((const uint16_t *)a.q)[qbase + k]);
+  __syncthreads();
+  for (int k = threadIdx.x; k < GP * d; k += blockDim.x) {
+    const int g = k / d, i = k % d;
+    float acc = 0.0f;
+    if (g < G) {
+      const float *Ri = R + (size_t)i * d;
+      const float *qg = qraw + g * d;
+      for (int j = 0; j < d; ++j) acc = fmaf(Ri[j], qg[j], acc);
+    }
+    qt[i * GP + g] = acc;
+  }
+  __syncthreads();
+  if (m > 0) {
+    const float *S = (const float *)(a.blob + hd->off_S);
+    for (int k = threadIdx.x; k < m * GP; k += blockDim.x) {
+      const int j = k / GP, g = k % GP;
+      float acc = 0.0f;
+      for (int i = 0; i < d_eff; ++i) acc = fmaf(S[j * d_eff + i], qt[i * GP + g], acc);
+      wq[j * GP + g] = acc;
+    }
+  }
+  {
+    const float *gc = (const float *)(a.blob + hd->off_cent);
+    for (int k = threadIdx.x; k < n_cent; k += blockDim.x) cent[k] = gc[k];
+  }
+  __syncthreads();
+
+  const DevCoord *coords = (const DevCoord *)(a.blob + hd->off_coord);
+  const uint32_t *slot = a.kpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
+  const int tile_begin = blockIdx.x * a.tiles_per_block;
+  const int tile_end = min(a.n_tiles, tile_begin + a.tiles_per_block);
+  for (int tile = tile_begin + wave; tile < tile_end; tile += nwaves) {
+    const uint32_t *src = slot + (int64_t)tile * W * 64 + lane;
+    for (int w = 0; w < W; ++w) rec[w * 64 + lane] = src[w * 64];
+    rec[W * 64 + lane] = 0u;
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+    int cur = -1;
+    uint32_t lo = 0, hi = 0;
+    for (int i = 0; i < d; ++i) {
+      const DevCoord cd = coords[i];
+      if (cd.width == 0) continue;
+      const int w = cd.bit_off >> 5;
+      if (w != cur) {
+        lo = rec[w * 64 + lane];
+        hi = rec[(w + 1) * 64 + lane];
+        cur = w;
+      }
+      const uint32_t field = __builtin_amdgcn_alignbit(hi, lo, cd.bit_off & 31) & ((1u << cd.width) - 1u);
+      const float c = cent[cd.cent_base + field];
+      float qv[GP];
+      {
+        const float4 q0 = *(const float4 *)(qt + i * GP);
+        qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w;
+        if constexpr (GP > 4) {
+          const float4 q1 = *(const float4 *)(qt + i * GP + 4);
+          qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g] = fmaf(qv[g], c, acc[g]);
+    }
+    if (m > 0) {
+      float qa[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) qa[g] = 0.0f;
+      for (int j = 0; j < m; ++j) {
+        const int pos = hd->code_bits + j;
+        const uint32_t bit = (rec[(pos >> 5) * 64 + lane] >> (pos & 31)) & 1u;
+        const float sgn = bit ? 1.0f : -1.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) qa[g] = fmaf(sgn, wq[j * GP + g], qa[g]);
+      }
+      const float gm = half_bits_to_f32(rec[(W - 1) * 64 + lane] >> 16) * hd->qjl_scale;
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g] = fmaf(gm, qa[g], acc[g]);
+    }
+    const int64_t t = (int64_t)tile * 64 + lane;
+    if (t < a.n_tokens) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        a.scores[((int64_t)b * a.n_q_heads + (int64_t)hkv * G + g) * a.n_tokens + t] = acc[g];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attend
+//
+// Split-T softmax-weighted value sum in the rotated value space.  Kernel 1:
+// one workgroup per (batch, KV head, chunk of ATT_CHUNK tokens) computes, for
+// each query head of the group, the chunk max of scale*s, sum exp(scale*s -
+// max) and the partial sum over tokens of p_t * C_v[code] (thread = (token
+// slot, coordinate); records staged transposed in LDS).  Kernel 2: one
+// workgroup per (batch, query head) combines the chunks in order (no atomics,
+// deterministic) and un-rotates once: o = R_v^T o_rot / L.
+
+static constexpr int ATT_CHUNK = 1024;
+
+struct AttendArgs {
+  const DevHead *heads;
+  const uint8_t *blob;
+  const float *scores;
+  const uint32_t *vpacked;
+  float *ws;
+  float *out;
+  int64_t ps_b, ps_h;
+  int64_t n_tokens;
+  float scale;
+  int first_head, cbs;
+  int n_q_heads, n_kv_heads;
+  int n_chunks;
+  int lds_rec_off, lds_p_off, lds_red_off;  // floats
+  int max_W;
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
+  extern __shared__ float smem[];
+  constexpr int GP = G <= 4 ? 4 : 8;
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int ch = a.first_head + b * a.cbs + hkv;
+  const DevHead *hd = a.heads + ch;
+  const int d = hd->d, W = hd->W, n_cent = hd->n_cent;
+  const int64_t tb = (int64_t)chunk * ATT_CHUNK;
+  const int64_t te = min(a.n_tokens, tb + ATT_CHUNK);
+  float *cent = smem;                                  // [n_cent]
+  uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off);  // [64][W+1]
+  float *ps = smem + a.lds_p_off;                      // [64][GP]
+  float *red = smem + a.lds_red_off;                   // reduction scratch
+  {
+    const float *gc = (const float *)(a.blob + hd->off_cent);
+    for (int k = tid; k < n_cent; k += blockDim.x) cent[k] = gc[k];
+  }
+  // chunk max of scale * s per query head
+  const float *srow = a.scores + ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * a.n_tokens;
+  float mx[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = -INFINITY;
+    for (int64_t t = tb + tid; t < te; t += blockDim.x) v = fmaxf(v, a.scale * srow[g * a.n_tokens + t]);
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if ((tid & 63) == 0) red[(tid >> 6) * GP + g] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = red[g];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v = fmaxf(v, red[w * GP + g]);
+    mx[g] = v;
+  }
+  __syncthreads();
+
+  // thread -> (token slot, coordinate)
+  const int nslots = blockDim.x / d;
+  const int ci = tid % d, slotid = tid / d;
+  const DevCoord cd = ((const DevCoord *)(a.blob + hd->off_coord))[ci];
+  const uint32_t mask = cd.width ? ((1u << cd.width) - 1u) : 0u;
+  const int cw = cd.bit_off >> 5, cs = cd.bit_off & 31;
+  float acc[G];
+  float lsum[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = lsum[g] = 0.0f;
+  const uint32_t *slot = a.vpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
+  for (int64_t t0 = tb; t0 < te; t0 += 64) {
+    const int64_t tile = t0 / 64;
+    const uint32_t *src = slot + tile * W * 64;
+    for (int k = tid; k < W * 64; k += blockDim.x) rec[(k & 63) * (W + 1) + (k >> 6)] = src[k];
+    for (int k = tid; k < 64; k += blockDim.x) rec[k * (W + 1) + W] = 0u;
+    for (int k = tid; k < 64 * G; k += blockDim.x) {
+      const int tt = k % 64, g = k / 64;
+      const int64_t t = t0 + tt;
+      float p = 0.0f;
+      if (t < te) p = expf(a.scale * srow[g * a.n_tokens + t] - mx[g]);
+      ps[tt * GP + g] = p;
+    }
+    __syncthreads();
+    if (slotid < nslots) {
+      for (int tt = slotid; tt < 64; tt += nslots) {
+        if (t0 + tt >= te) break;
+        const uint32_t lo = rec[tt * (W + 1) + cw], hi = rec[tt * (W + 1) + cw + 1];
+        const uint32_t field = __builtin_amdgcn_alignbit(hi, lo, cs) & mask;
+        const float c = cd.width ? cent[cd.cent_base + field] : 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = fmaf(ps[tt * GP + g], c, acc[g]);
+      }
+    }
+    if (tid < 64) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) lsum[g] += ps[tid * GP + g];
+    }
+    __syncthreads();
+  }
+  // reduce acc over slots in order; reduce lsum over the first wave
+  for (int g = 0; g < G; ++g) {
+    if (slotid < nslots) red[(slotid * G + g) * d + ci] = acc[g];
+  }
+  __syncthreads();
+  float *dst = a.ws + (((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * a.n_chunks + chunk) * (d + 2);
+  if (tid < d) {
+    for (int g = 0; g < G; ++g) {
+      float s = 0.0f;
+      for (int sl = 0; sl < nslots; ++sl) s += red[(sl * G + g) * d + tid];
+      dst[(int64_t)g * a.n_chunks * (d + 2) + 2 + tid] = s;
+    }
+  }
+  if (tid < 64) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float v = lsum[g];
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (tid == 0) {
+        dst[(int64_t)g * a.n_chunks * (d + 2) + 0] = mx[g];
+        dst[(int64_t)g * a.n_chunks * (d + 2) + 1] = v;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
+  extern __shared__ float smem[];
+  const int tid = threadIdx.x;
+  const int bq = blockIdx.x;
+  const int b = bq / a.n_q_heads, hq = bq % a.n_q_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int ch = a.first_head + b * a.cbs + hq / G;
+  const DevHead *hd = a.heads + ch;
+  const int d = hd->d;
+  float *out = a.out + (int64_t)bq * d;
+  if (a.n_tokens == 0) {
+    for (int j = tid; j < d; j += blockDim.x) out[j] = 0.0f;
+    return;
+  }
+  const float *part = a.ws + (int64_t)bq * a.n_chunks * (d + 2);
+  float *wts = smem;              // [n_chunks]
+  float *orot = smem + a.n_chunks;  // [d]
+  float M = -INFINITY;
+  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, part[(int64_t)c * (d + 2)]);
+  float L = 0.0f;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const float e = expf(part[(int64_t)c * (d + 2)] - M);
+    L += e * part[(int64_t)c * (d + 2) + 1];
+    if (tid == 0) wts[c] = e;
+  }
+  __syncthreads();
+  for (int i = tid; i < d; i += blockDim.x) {
+    float s = 0.0f;
+    for (int c = 0; c < a.n_chunks; ++c) s = fmaf(wts[c], part[(int64_t)c * (d + 2) + 2 + i], s);
+    orot[i] = s / L;
+  }
+  __syncthreads();
+  const float *R = (const float *)(a.blob + hd->off_R);
+  for (int j = tid; j < d; j += blockDim.x) {
+    float s = 0.0f;
+    for (int i = 0; i < d; ++i) s = fmaf(R[(size_t)i * d + j], orot[i], s);
+    out[j] = s;
+  }
+}
+
+// ------------------------------------------------------------------ dequantize
+// Diagnostic: one workgroup per (batch, head, 16 tokens).  Thread = (token,
+// coordinate) decodes C_i[code] (+ the QJL correction on signal coordinates),
+// then x~ = R^T y^ per token.
+
+struct DequantArgs {
+  const DevHead *heads;
+  const uint8_t *blob;
+  const uint32_t *packed;
+  float *out;
+  int64_t ps_b, ps_h;
+  int64_t n_tokens;
+  int first_head, cbs, n_heads;
+};
+
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  __shared__ float yb[16 * 257];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int ch = a.first_head + b * a.cbs + h;
+  const DevHead *hd = a.heads + ch;
+  const int d = hd->d, W = hd->W, m = hd->m, d_eff = hd->d_eff;
+  const uint32_t *slot = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h;
+  const DevCoord *coords = (const DevCoord *)(a.blob + hd->off_coord);
+  const float *cent = (const float *)(a.blob + hd->off_cent);
+  const float *S = (const float *)(a.blob + hd->off_S);
+  const float *R = (const float *)(a.blob + hd->off_R);
+  const int64_t tbase = (int64_t)blockIdx.x * 16;
+  auto word = [&](int64_t t, int w) -> uint32_t {
+    return w < W ? slot[((t / 64) * W + w) * 64 + t % 64] : 0u;
+  };
+  for (int k = tid; k < 16 * d; k += blockDim.x) {
+    const int tt = k / d, i = k % d;
+    const int64_t t = tbase + tt;
+    float v = 0.0f;
+    if (t < a.n_tokens) {
+      const DevCoord cd = coords[i];
+      if (cd.width) {
+        const uint32_t f = __builtin_amdgcn_alignbit(word(t, (cd.bit_off >> 5) + 1), word(t, cd.bit_off >> 5),
+                                                    cd.bit_off & 31) & ((1u << cd.width) - 1u);
+        v = cent[cd.cent_base + f];
+      }
+      if (m > 0 && i < d_eff) {
+        float s = 0.0f;
+        for (int j = 0; j < m; ++j) {
+          const int pos = hd->code_bits + j;
+          const float sgn = ((word(t, pos >> 5) >> (pos & 31)) & 1u) ? 1.0f : -1.0f;
+          s = fmaf(sgn, S[j * d_eff + i], s);
+        }
+        v += hd->qjl_scale * half_bits_to_f32(word(t, W - 1) >> 16) * s;
+      }
+    }
+    yb[tt * 257 + i] = v;
+  }
+  __syncthreads();
+  for (int k = tid; k < 16 * d; k += blockDim.x) {
+    const int tt = k / d, j = k % d;
+    const int64_t t = tbase + tt;
+    if (t >= a.n_tokens) continue;
+    float s = 0.0f;
+    for (int i = 0; i < d; ++i) s = fmaf(R[(size_t)i * d + j], yb[tt * 257 + i], s);
+    a.out[(((int64_t)b * a.n_heads + h) * a.n_tokens + t) * d + j] = s;
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+static int device_lds_limit() {
+  int dev = 0, v = 65536;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  return v;
+}
+
+static sq_status check_handle(const sq_calib *c, const char *fn) {
+  if (!c) return fail(SQ_ERR_ARG, std::string(fn) + ": handle is NULL");
+  if (!c->dev_blob) return fail(SQ_ERR_STATE, std::string(fn) + ": calibration not uploaded (call sq_calib_upload)");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev != c->device)
+    return fail(SQ_ERR_STATE, std::string(fn) + ": calibration was uploaded to another device");
+  return SQ_OK;
+}
+
+// calibration heads used: first_head + b*cbs + h for b < batch, h < n_heads
+static sq_status check_heads(const sq_calib *c, int first_head, int n_heads, int batch, int cbs,
+                             const char *fn) {
+  const int64_t nh = (int64_t)c->heads.size();
+  if (n_heads <= 0 || batch < 0 || cbs < 0 || first_head < 0)
+    return fail(SQ_ERR_ARG, std::string(fn) + ": bad head range (need n_heads > 0, batch, cbs, first_head >= 0)");
+  const int64_t last = (int64_t)first_head + (int64_t)std::max(0, batch - 1) * cbs + n_heads - 1;
+  if (last >= nh) return fail(SQ_ERR_ARG, std::string(fn) + ": calibration head index out of range");
+  const int d = c->heads[first_head].d;
+  for (int64_t k = first_head; k <= last; ++k)
+    if (c->heads[k].d != d) return fail(SQ_ERR_ARG, std::string(fn) + ": heads of different head_dim");
+  return SQ_OK;
+}
+
+static sq_status check_slots(const sq_calib *c, int64_t n_tokens, int n_heads, int batch, int64_t ps_b,
+                             int64_t ps_h, const char *fn) {
+  const int64_t need = ((n_tokens + 63) / 64) * 64 * (int64_t)c->W_max;
+  if (ps_h < need) return fail(SQ_ERR_ARG, std::string(fn) + ": ps_head smaller than sq_packed_head_words");
+  if (batch > 1 && ps_b < ps_h * n_heads) return fail(SQ_ERR_ARG, std::string(fn) + ": ps_batch overlaps head slots");
+  return SQ_OK;
+}
+
+static sq_status launched(const char *fn) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(fn, e);
+  clear_error();
+  return SQ_OK;
+}
+
+}  // namespace sq
+
+using namespace sq;
+
+extern "C" sq_status sq_calib_upload(sq_calib *c, sq_stream stream) {
+  if (!c) return fail(SQ_ERR_ARG, "sq_calib_upload: handle is NULL");
+  sq_status st = upload_tables(c, stream);
+  if (st == SQ_OK) clear_error();
+  return st;
+}
+
+template <int D, bool F32>
+static void launch_compress(dim3 grid, dim3 block, size_t lds, hipStream_t s, const CompressArgs &a) {
+  hipLaunchKernelGGL((compress_kernel<D, F32>), grid, block, lds, s, a);
+}
+
+extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
+                                 int calib_batch_stride, const void *x, sq_dtype dt,
+                                 int64_t n_tokens, int64_t xs_batch, int64_t xs_head,
+                                 int64_t xs_token, uint32_t *packed, int64_t ps_batch,
+                                 int64_t ps_head, sq_stream stream) {
+  const char *fn = "sq_compress";
+  sq_status st = check_handle(c, fn);
+  if (st != SQ_OK) return st;
+  st = check_heads(c, first_head, n_heads, batch, calib_batch_stride, fn);
+  if (st != SQ_OK) return st;
+  if (n_tokens < 0) return fail(SQ_ERR_ARG, "sq_compress: n_tokens < 0");
+  if (dt != SQ_F32 && dt != SQ_BF16) return fail(SQ_ERR_ARG, "sq_compress: bad dtype");
+  if (n_tokens == 0 || batch == 0) { clear_error(); return SQ_OK; }
+  if (!x || !packed) return fail(SQ_ERR_ARG, "sq_compress: NULL pointer");
+  st = check_slots(c, n_tokens, n_heads, batch, ps_batch, ps_head, fn);
+  if (st != SQ_OK) return st;
+  const int esz = dt == SQ_F32 ? 4 : 2;
+  if (((uintptr_t)x % 16) || (xs_token * esz) % 16 || (xs_head * esz) % 16 || (xs_batch * esz) % 16)
+    return fail(SQ_ERR_ARG, "sq_compress: x and its strides must be 16-byte aligned");
+  if (xs_token < c->heads[first_head].d) return fail(SQ_ERR_ARG, "sq_compress: xs_token < head_dim");
+  if (n_tokens > ((int64_t)1 << 36) / 64) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many tokens");
+  const int d = c->heads[first_head].d;
+  // LDS: thresholds, signal centroids, per-wave [64][33] + [64][rstride]
+  int max_thr = 1, max_csig = 0, max_deff = 1;
+  for (int bb = 0; bb < std::max(1, batch); ++bb) {
+    for (int h = 0; h < n_heads; ++h) {
+      const HeadCal &hc = c->heads[first_head + bb * calib_batch_stride + h];
+      max_thr = std::max(max_thr, hc.n_thr);
+      if (hc.m > 0) {
+        max_csig = std::max(max_csig, c->host_desc[first_head + bb * calib_batch_stride + h].n_cent_sig);
+        max_deff = std::max(max_deff, hc.d_eff);
+      }
+    }
+    if (calib_batch_stride == 0) break;  // every batch entry uses the same heads
+  }
+  CompressArgs a{};
+  a.rstride = (max_deff % 2 == 0) ? max_deff + 1 : max_deff + 2;
+  a.lds_cent_off = (max_thr + 3) & ~3;
+  a.lds_wave_off = a.lds_cent_off + ((max_csig + 3) & ~3);
+  a.lds_wave_floats = 64 * 33 + 64 * a.rstride;
+  const int limit = device_lds_limit();
+  int nw = 4;
+  while (nw > 1 && (size_t)(a.lds_wave_off + nw * a.lds_wave_floats) * 4 > (size_t)limit) nw >>= 1;
+  const size_t lds = (size_t)(a.lds_wave_off + nw * a.lds_wave_floats) * 4;
+  if (lds > (size_t)limit)
+    return fail(SQ_ERR_UNSUPPORTED, "sq_compress: calibration tables exceed the LDS of one workgroup");
+  a.heads = c->dev_heads;
+  a.blob = (const uint8_t *)c->dev_blob;
+  a.x = x;
+  a.packed = packed;
+  a.xs_b = xs_batch; a.xs_h = xs_head; a.xs_t = xs_token;
+  a.ps_b = ps_batch; a.ps_h = ps_head;
+  a.n_tokens = n_tokens;
+  a.first_head = first_head;
+  a.cbs = calib_batch_stride;
+  a.n_tiles = (int)((n_tokens + 63) / 64);
+  dim3 grid((a.n_tiles + nw - 1) / nw, n_heads, batch), block(64 * nw);
+  if (grid.y > 65535 || grid.z > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many heads or batch entries");
+  hipStream_t s = (hipStream_t)stream;
+  const bool f32 = dt == SQ_F32;
+  switch (d) {
+    case 32:  f32 ? launch_compress<32, true>(grid, block, lds, s, a) : launch_compress<32, false>(grid, block, lds, s, a); break;
+    case 64:  f32 ? launch_compress<64, true>(grid, block, lds, s, a) : launch_compress<64, false>(grid, block, lds, s, a); break;
+    case 128: f32 ? launch_compress<128, true>(grid, block, lds, s, a) : launch_compress<128, false>(grid, block, lds, s, a); break;
+    case 256: f32 ? launch_compress<256, true>(grid, block, lds, s, a) : launch_compress<256, false>(grid, block, lds, s, a); break;
+    default: return fail(SQ_ERR_UNSUPPORTED, "sq_compress: head_dim");
+  }
+  return launched(fn);
+}
+
+template <int G>
+static void launch_scores(dim3 grid, dim3 block, size_t lds, hipStream_t s, const ScoresArgs &a) {
+  hipLaunchKernelGGL((scores_kernel<G>), grid, block, lds, s, a);
+}
+
+extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_batch_stride, int batch,
+                               int n_q_heads, int n_kv_heads, const void *q, sq_dtype qdt,
+                               const uint32_t *kpacked, int64_t ps_batch, int64_t ps_head,
+                               int64_t n_tokens, float *scores, sq_stream stream) {
+  const char *fn = "sq_scores";
+  sq_status st = check_handle(kc, fn);
+  if (st != SQ_OK) return st;
+  if (n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads)
+    return fail(SQ_ERR_ARG, "sq_scores: n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = n_q_heads / n_kv_heads;
+  if (G > 8) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: query group larger than 8");
+  st = check_heads(kc, first_head, n_kv_heads, batch, calib_batch_stride, fn);
+  if (st != SQ_OK) return st;
+  if (n_tokens < 0) return fail(SQ_ERR_ARG, "sq_scores: n_tokens < 0");
+  if (qdt != SQ_F32 && qdt != SQ_BF16) return fail(SQ_ERR_ARG, "sq_scores: bad dtype");
+  if (n_tokens == 0 || batch == 0) { clear_error(); return SQ_OK; }
+  if (!q || !kpacked || !scores) return fail(SQ_ERR_ARG, "sq_scores: NULL pointer");
+  st = check_slots(kc, n_tokens, n_kv_heads, batch, ps_batch, ps_head, fn);
+  if (st != SQ_OK) return st;
+  const int d = kc->heads[first_head].d;
+  int max_cent = 1, max_m = 0;
+  for (int bb = 0; bb < std::max(1, batch); ++bb) {
+    for (int h = 0; h < n_kv_heads; ++h) {
+      const HeadCal &hc = kc->heads[first_head + bb * calib_batch_stride + h];
+      max_cent = std::max(max_cent, hc.n_cent);
+      max_m = std::max(max_m, hc.m);
+    }
+    if (calib_batch_stride == 0) break;
+  }
+  const int GP = G <= 4 ? 4 : 8;
+  ScoresArgs a{};
+  a.lds_w_off = d * GP;
+  a.lds_cent_off = a.lds_w_off + std::max(1, max_m) * GP;
+  a.lds_rec_off = a.lds_cent_off + std::max(max_cent, G * d);
+  a.lds_rec_off = (a.lds_rec_off + 3) & ~3;
+  a.max_W = kc->W_max + 1;
+  const int nw = 4;
+  const size_t lds = (size_t)(a.lds_rec_off + nw * a.max_W * 64) * 4;
+  if (lds > (size_t)device_lds_limit()) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: tables exceed LDS");
+  a.heads = kc->dev_heads;
+  a.blob = (const uint8_t *)kc->dev_blob;
+  a.q = q;
+  a.kpacked = kpacked;
+  a.scores = scores;
+  a.ps_b = ps_batch; a.ps_h = ps_head;
+  a.n_tokens = n_tokens;
+  a.first_head = first_head;
+  a.cbs = calib_batch_stride;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.q_f32 = qdt == SQ_F32;
+  a.n_tiles = (int)((n_tokens + 63) / 64);
+  // enough workgroups to fill the chip: aim at >= 2048 in total
+  const int64_t pairs = (int64_t)batch * n_kv_heads;
+  int blocks_t = (int)std::min<int64_t>(a.n_tiles, std::max<int64_t>(1, (2048 + pairs - 1) / pairs));
+  a.tiles_per_block = (a.n_tiles + blocks_t - 1) / blocks_t;
+  blocks_t = (a.n_tiles + a.tiles_per_block - 1) / a.tiles_per_block;
+  dim3 grid(blocks_t, n_kv_heads, batch), block(64 * nw);
+  if (grid.z > 65535 || grid.y > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: grid too large");
+  hipStream_t s = (hipStream_t)stream;
+  switch (G) {
+    case 1: launch_scores<1>(grid, block, lds, s, a); break;
+    case 2: launch_scores<2>(grid, block, lds, s, a); break;
+    case 3: launch_scores<3>(grid, block, lds, s, a); break;
+    case 4: launch_scores<4>(grid, block, lds, s, a); break;
+    case 5: launch_scores<5>(grid, block, lds, s, a); break;
+    case 6: launch_scores<6>(grid, block, lds, s, a); break;
+    case 7: launch_scores<7>(grid, block, lds, s, a); break;
+    case 8: launch_scores<8>(grid, block, lds, s, a); break;
+  }
+  return launched(fn);
+}
+
+extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_tokens, int head_dim) {
+  if (batch <= 0 || n_q_heads <= 0 || n_tokens <= 0 || head_dim <= 0) return 0;
+  const int64_t nch = (n_tokens + ATT_CHUNK - 1) / ATT_CHUNK;
+  return (size_t)batch * n_q_heads * nch * (head_dim + 2) * sizeof(float);
+}
+
+template <int G>
+static void launch_attend(dim3 grid, dim3 block, size_t lds, hipStream_t s, const AttendArgs &a) {
+  hipLaunchKernelGGL((attend_partial_kernel<G>), grid, block, lds, s, a);
+}
+
+extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride, int batch,
+                               int n_q_heads, int n_kv_heads, const float *scores, float scale,
+                               const uint32_t *vpacked, int64_t ps_batch, int64_t ps_head,
+                               int64_t n_tokens, void *workspace, size_t ws_bytes, float *out,
+                               sq_stream stream) {
+  const char *fn = "sq_attend";
+  sq_status st = check_handle(vc, fn);
+  if (st != SQ_OK) return st;
+  if (n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads)
+    return fail(SQ_ERR_ARG, "sq_attend: n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = n_q_heads / n_kv_heads;
+  if (G > 8) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: query group larger than 8");
+  st = check_heads(vc, first_head, n_kv_heads, batch, calib_batch_stride, fn);
+  if (st != SQ_OK) return st;
+  if (n_tokens < 0) return fail(SQ_ERR_ARG, "sq_attend: n_tokens < 0");
+  if (batch == 0) { clear_error(); return SQ_OK; }
+  if (!out) return fail(SQ_ERR_ARG, "sq_attend: out is NULL");
+  const int d = vc->heads[first_head].d;
+  AttendArgs a{};
+  a.heads = vc->dev_heads;
+  a.blob = (const uint8_t *)vc->dev_blob;
+  a.scores = scores;
+  a.vpacked = vpacked;
+  a.out = out;
+  a.ps_b = ps_batch; a.ps_h = ps_head;
+  a.n_tokens = n_tokens;
+  a.scale = scale;
+  a.first_head = first_head;
+  a.cbs = calib_batch_stride;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  if (n_tokens == 0) {
+    a.n_chunks = 0;
+    hipLaunchKernelGGL(attend_combine_kernel, dim3(batch * n_q_heads), dim3(256), 0, s, a);
+    return launched(fn);
+  }
+  if (!scores || !vpacked || !workspace) return fail(SQ_ERR_ARG, "sq_attend: NULL pointer");
+  st = check_slots(vc, n_tokens, n_kv_heads, batch, ps_batch, ps_head, fn);
+  if (st != SQ_OK) return st;
+  if (ws_bytes < sq_attend_workspace_bytes(batch, n_q_heads, n_tokens, d))
+    return fail(SQ_ERR_ARG, "sq_attend: workspace too small");
+  a.ws = (float *)workspace;
+  a.n_chunks = (int)((n_tokens + ATT_CHUNK - 1) / ATT_CHUNK);
+  int max_cent = 1;
+  for (int bb = 0; bb < std::max(1, batch); ++bb) {
+    for (int h = 0; h < n_kv_heads; ++h)
+      max_cent = std::max(max_cent, vc->heads[first_head + bb * calib_batch_stride + h].n_cent);
+    if (calib_batch_stride == 0) break;
+  }
+  const int GP = G <= 4 ? 4 : 8;
+  a.max_W = vc->W_max;
+  a.lds_rec_off = (max_cent + 3) & ~3;
+  a.lds_p_off = a.lds_rec_off + ((64 * (a.max_W + 1) + 3) & ~3);
+  a.lds_red_off = a.lds_p_off + 64 * GP;
+  const int red_floats = std::max(4 * GP, (256 / d) * G * d);
+  const size_t lds = (size_t)(a.lds_red_off + red_floats) * 4;
+  if (lds > (size_t)device_lds_limit()) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: tables exceed LDS");
+  dim3 grid(a.n_chunks, n_kv_heads, batch), block(256);
+  if (grid.z > 65535 || grid.y > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: grid too large");
+  switch (G) {
+    case 1: launch_attend<1>(grid, block, lds, s, a); break;
+    case 2: launch_attend<2>(grid, block, lds, s, a); break;
+    case 3: launch_attend<3>(grid, block, lds, s, a); break;
+    case 4: launch_attend<4>(grid, block, lds, s, a); break;
+    case 5: launch_attend<5>(grid, block, lds, s, a); break;
+    case 6: launch_attend<6>(grid, block, lds, s, a); break;
+    case 7: launch_attend<7>(grid, block, lds, s, a); break;
+    case 8: launch_attend<8>(grid, block, lds, s, a); break;
+  }
+  sq_status s1 = launched(fn);
+  if (s1 != SQ_OK) return s1;
+  const size_t lds2 = (size_t)(a.n_chunks + d) * 4;
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(batch * n_q_heads), dim3(256), lds2, s, a);
+  return launched(fn);
+}
+
+extern "C" sq_status sq_dequantize(const sq_calib *c, int first_head, int n_heads, int batch,
+                                   int calib_batch_stride, const uint32_t *packed, int64_t ps_batch,
+                                   int64_t ps_head, int64_t n_tokens, float *out, sq_stream stream) {
+  const char *fn = "sq_dequantize";
+  sq_status st = check_handle(c, fn);
+  if (st != SQ_OK) return st;
+  st = check_heads(c, first_head, n_heads, batch, calib_batch_stride, fn);
+  if (st != SQ_OK) return st;
+  if (n_tokens < 0) return fail(SQ_ERR_ARG, "sq_dequantize: n_tokens < 0");
+  if (n_tokens == 0 || batch == 0) { clear_error(); return SQ_OK; }
+  if (!packed || !out) return fail(SQ_ERR_ARG, "sq_dequantize: NULL pointer");
+  st = check_slots(c, n_tokens, n_heads, batch, ps_batch, ps_head, fn);
+  if (st != SQ_OK) return st;
+  DequantArgs a{};
+  a.heads = c->dev_heads;
+  a.blob = (const uint8_t *)c->dev_blob;
+  a.packed = packed;
+  a.out = out;
+  a.ps_b = ps_batch; a.ps_h = ps_head;
+  a.n_tokens = n_tokens;
+  a.first_head = first_head;
+  a.cbs = calib_batch_stride;
+  a.n_heads = n_heads;
+  dim3 grid((unsigned)((n_tokens + 15) / 16), n_heads, batch), block(256);
+  hipLaunchKernelGGL(dequant_kernel, grid, block, 0, (hipStream_t)stream, a);
+  return launched(fn);
+}

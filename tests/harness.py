@@ -1,0 +1,124 @@
+"""Shared test machinery: build matching calibrations on both sides, compare
+GPU outputs with the oracle under the acceptance rules.
+
+Acceptance (the SpectralQuant build's parity bar):
+  * codes bit-exact wherever the oracle's rotated coordinate is farther than
+    1e-4 * sigma_i from every threshold; inside that band only +-1 flips;
+  * QJL bits exact unless |(S r)_j| <= 1e-3 ||S_j|| ||r|| or a signal code flipped;
+  * gamma within one half-precision ulp (or any value when a signal code flipped);
+  * dequantised vectors, scores and attention outputs within 1e-3 relative with a
+    floor: |gpu - ref| <= 1e-3 * (|ref| + floor).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+import workloads as wl
+
+BAND = 1e-4
+QJL_BAND = 1e-3
+RTOL = 1e-3
+
+
+def calib_inputs(cfg, heads, which, seed=wl.DEFAULT_SEED, n_tokens=None):
+    """heads: list of (layer, kv_head).  Returns (samples [H][n][d], gauss or None)."""
+    X = np.stack([wl.calibration_set(cfg, l, h, which, seed, n_tokens) for l, h in heads])
+    if which == "k" and cfg.qjl_bits > 0:
+        G = np.stack([wl.qjl_gaussian(cfg, l, h, "k", seed) for l, h in heads])
+    else:
+        G = None
+    return X.astype(np.float32), G
+
+
+def calibrate_both(sq, cfg, heads, which, budget, seed=wl.DEFAULT_SEED, n_tokens=None):
+    """Library calibration (handle) and oracle calibrations of the same heads;
+    asserts the integer parts agree exactly."""
+    X, G = calib_inputs(cfg, heads, which, seed, n_tokens)
+    qb = cfg.qjl_bits if which == "k" else 0
+    cal = sq.sq_calibrate(X, budget, qb, G)
+    ors = []
+    for k in range(len(heads)):
+        oc = oracle.calibrate(X[k], budget, qb, G[k] if G is not None else None)
+        inf = cal.info(k)
+        ex = cal.export(k)
+        assert inf.d_eff == oc.d_eff and inf.m == oc.m and inf.record_words == oc.W
+        assert np.array_equal(ex["widths"], oc.widths)
+        ors.append(oc)
+    return cal, ors
+
+
+def data_block(cfg, heads, which, T, seed=wl.DEFAULT_SEED):
+    return np.stack([wl.kv_block(cfg, l, h, which, T, "data", seed) for l, h in heads])
+
+
+def words_of(packed_slot: np.ndarray, W: int, T: int) -> np.ndarray:
+    """[T, W] record words of one head's slot."""
+    Tp = -(-T // 64) * 64
+    return (packed_slot[:Tp * W].reshape(Tp // 64, W, 64).transpose(0, 2, 1)
+            .reshape(Tp, W)[:T])
+
+
+def compare_compress(oc, gpu_slot: np.ndarray, x: np.ndarray, T: int):
+    """Check one head's GPU records against the oracle.  Returns a dict of
+    counts; raises AssertionError on a violation."""
+    res = oracle.compress(oc, x)
+    band = oracle.band_mask(oc, res.y, BAND)
+    qband = oracle.qjl_band_mask(oc, res, QJL_BAND)
+    ref = oracle.pack(oc.widths, oc.m, res.codes, res.z, res.gamma)
+    W = oc.W
+    gw = words_of(gpu_slot, W, T).astype(np.uint64)
+    rw = words_of(ref, W, T).astype(np.uint64)
+    Tp = -(-T // 64) * 64
+    # pad tokens must be zero
+    pad = (gpu_slot[:Tp * W].reshape(Tp // 64, W, 64).transpose(0, 2, 1).reshape(Tp, W)[T:])
+    assert np.all(pad == 0), "pad tokens not zero"
+    gc, gz, gg = oracle.unpack(oc.widths, oc.m, gpu_slot, T)
+    diff = gc != res.codes
+    assert not np.any(diff & ~band), f"{int((diff & ~band).sum())} code mismatches outside the band"
+    assert np.all(np.abs(gc - res.codes)[diff] <= 1), "in-band flip larger than one code"
+    n_flip = int(diff.sum())
+    tok_flip = diff.any(axis=1)
+    sig_flip = diff[:, :oc.d_eff].any(axis=1) if oc.m > 0 else np.zeros(T, bool)
+    out = dict(tokens=T, coords=int(T * oc.head_dim), band=int(band.sum()), flips=n_flip,
+               flip_tokens=int(tok_flip.sum()))
+    if oc.m > 0:
+        zd = gz != res.z
+        bad = zd & ~qband & ~sig_flip[:, None]
+        assert not np.any(bad), f"{int(bad.sum())} QJL bit mismatches outside the band"
+        gu = gg.view(np.uint16).astype(np.int64)
+        ru = res.gamma.view(np.uint16).astype(np.int64)
+        gbad = (np.abs(gu - ru) > 1) & ~sig_flip
+        assert not np.any(gbad), f"{int(gbad.sum())} gamma values off by more than one ulp"
+        out["qjl_flips"] = int(zd.sum())
+        out["gamma_ulp"] = int((gu != ru).sum())
+    # tokens with no excused difference must match bit for bit (gamma aside)
+    clean = ~tok_flip
+    if oc.m > 0:
+        clean &= ~(gz != res.z).any(axis=1)
+        mask = np.full(W, 0xFFFFFFFF, np.uint64)
+        mask[W - 1] = 0x0000FFFF
+        assert np.array_equal(gw[clean] & mask, rw[clean] & mask)
+    else:
+        assert np.array_equal(gw[clean], rw[clean])
+    return out, res
+
+
+def assert_close_floor(gpu, ref, floor, what, rtol=RTOL):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(gpu - ref)
+    lim = rtol * (np.abs(ref) + floor)
+    bad = err > lim
+    assert not np.any(bad), (f"{what}: {int(bad.sum())}/{bad.size} outside tolerance; "
+                             f"worst err/lim {float(np.max(err / lim)):.3g}")
+    return float(np.max(err / lim)) if err.size else 0.0
+
+
+def score_floor(oc, q: np.ndarray, xt: np.ndarray) -> np.ndarray:
+    """[G, T] floor ||q~|| ||x~_t|| / sqrt(d)."""
+    qn = np.linalg.norm(q, axis=1)
+    xn = np.linalg.norm(xt, axis=1)
+    return qn[:, None] * xn[None, :] / math.sqrt(oc.head_dim)

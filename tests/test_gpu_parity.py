@@ -1,0 +1,228 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Each test prints its case before touching the GPU.  Sizes are those the
+oracle finishes in seconds while still spanning several 64-token tiles and a
+ragged tail; the full-size decode configuration is covered by sampled checks in
+test_gpu_fullsize.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import harness as H
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def sq(torch_dev):
+    import compression_sq_compress_amd as m
+    return m
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(torch, arr, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to("cuda")
+    return t.to(dtype)
+
+
+def _compress_gpu(torch, sq, cal, x_np, dtype, T):
+    """x_np [B][H][T][d] -> packed uint32 numpy [B][H][slot]."""
+    x = _to_dev(torch, x_np, dtype)
+    B, Hh = x.shape[0], x.shape[1]
+    slot = cal.packed_head_words(T)
+    packed = torch.full((B, Hh, slot), -1, dtype=torch.int32, device="cuda")
+    sq.sq_compress(cal, x, packed)
+    torch.cuda.synchronize()
+    return packed.cpu().numpy().view(np.uint32)
+
+
+CASES = [
+    # name, config, heads, T, budget
+    ("tiny", "tiny", [(l, h) for l in range(3) for h in range(4)], 256, 3.0),
+    ("llama8b", "llama8b", [(0, h) for h in range(8)], 2048, 3.0),
+    ("llama8b-ragged", "llama8b", [(0, h) for h in range(2)], 1000, 3.0),
+    ("qwen14b-2.5b", "qwen14b", [(l, h) for l in (0, 47) for h in range(8)], 512, 2.5),
+    ("qwen14b-3.5b", "qwen14b", [(l, h) for l in (1,) for h in range(8)], 1024, 3.5),
+    ("gemma9b", "gemma9b", [(l, h) for l in (0,) for h in range(4)], 700, 3.0),
+]
+
+
+@pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_compress_matches_oracle(torch_dev, sq, name, cfgname, heads, T, budget, which):
+    torch = torch_dev
+    cfg = wl.CONFIGS[cfgname]
+    _case(f"compress {name} {which} T={T} budget={budget}")
+    cal, ors = H.calibrate_both(sq, cfg, heads, which, budget, n_tokens=T)
+    cal.upload()
+    x = H.data_block(cfg, heads, which, T)                 # [H][T][d]
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    packed = _compress_gpu(torch, sq, cal, x[None], dt, T)[0]
+    tot = dict(coords=0, band=0, flips=0)
+    for k in range(len(heads)):
+        stats, _ = H.compare_compress(ors[k], packed[k], x[k], T)
+        for key in tot:
+            tot[key] += stats[key]
+    print(f"  coords={tot['coords']} in-band={tot['band']} flips={tot['flips']} "
+          f"flip-rate={tot['flips'] / tot['coords']:.2e}", flush=True)
+    assert tot["flips"] <= max(4, tot["band"])
+
+
+@pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES[:4], ids=[c[0] for c in CASES[:4]])
+def test_scores_attend_dequant_on_oracle_records(torch_dev, sq, name, cfgname, heads, T, budget):
+    """sq_scores / sq_attend / sq_dequantize fed with ORACLE-packed records and
+    oracle scores, compared with the oracle on the same inputs."""
+    torch = torch_dev
+    cfg = wl.CONFIGS[cfgname]
+    _case(f"read-side {name} T={T}")
+    nkv = len(heads)
+    G = cfg.q_heads // cfg.kv_heads
+    kcal, kors = H.calibrate_both(sq, cfg, heads, "k", budget, n_tokens=T)
+    vcal, vors = H.calibrate_both(sq, cfg, heads, "v", budget, n_tokens=T)
+    kcal.upload()
+    vcal.upload()
+    xk = H.data_block(cfg, heads, "k", T)
+    xv = H.data_block(cfg, heads, "v", T)
+    slot_k = kcal.packed_head_words(T)
+    slot_v = vcal.packed_head_words(T)
+    kp = np.zeros((1, nkv, slot_k), np.uint32)
+    vp = np.zeros((1, nkv, slot_v), np.uint32)
+    rk, rv = [], []
+    for k in range(nkv):
+        r = oracle.compress(kors[k], xk[k])
+        p = oracle.pack(kors[k].widths, kors[k].m, r.codes, r.z, r.gamma)
+        kp[0, k, :len(p)] = p
+        rk.append(r)
+        r = oracle.compress(vors[k], xv[k])
+        p = oracle.pack(vors[k].widths, vors[k].m, r.codes, r.z, r.gamma)
+        vp[0, k, :len(p)] = p
+        rv.append(r)
+    q = wl.queries(cfg, 1, nkv * G)                       # [1][Hq][d]
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    qd = _to_dev(torch, q, dt)
+    kpd = torch.from_numpy(kp.view(np.int32)).cuda()
+    vpd = torch.from_numpy(vp.view(np.int32)).cuda()
+    scores = torch.zeros((1, nkv * G, T), dtype=torch.float32, device="cuda")
+    sq.sq_scores(kcal, qd, kpd, T, scores, nkv)
+    # dequantize (keys, with QJL) on oracle records
+    deq = torch.zeros((1, nkv, T, cfg.head_dim), dtype=torch.float32, device="cuda")
+    sq.sq_dequantize(kcal, kpd, T, deq)
+    torch.cuda.synchronize()
+    s_gpu = scores.cpu().numpy()[0]
+    deq_gpu = deq.cpu().numpy()[0]
+    worst = 0.0
+    oscores = np.zeros((nkv * G, T))
+    for k in range(nkv):
+        oc, r = kors[k], rk[k]
+        xt = oracle.dequantize(oc, r.codes, r.z, r.gamma)
+        H.assert_close_floor(deq_gpu[k], xt, np.linalg.norm(xt, axis=1)[:, None] / math.sqrt(cfg.head_dim),
+                             f"dequantize head {k}")
+        qg = q[0, k * G:(k + 1) * G].astype(np.float64)
+        ref = oracle.scores_rotated(oc, qg, r.codes, r.z, r.gamma)
+        oscores[k * G:(k + 1) * G] = ref
+        worst = max(worst, H.assert_close_floor(s_gpu[k * G:(k + 1) * G], ref,
+                                                H.score_floor(oc, qg, xt), f"scores head {k}"))
+    print(f"  scores worst err/tol = {worst:.3g}", flush=True)
+    # attend on oracle scores (float32 copy) and oracle value records
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    s32 = oscores.astype(np.float32)
+    sd = torch.from_numpy(s32[None].copy()).cuda()
+    ws = torch.zeros(sq.sq_attend_workspace_bytes(1, nkv * G, T, cfg.head_dim) // 4 + 1,
+                     dtype=torch.float32, device="cuda")
+    out = torch.zeros((1, nkv * G, cfg.head_dim), dtype=torch.float32, device="cuda")
+    sq.sq_attend(vcal, sd, scale, vpd, T, ws, out, nkv)
+    torch.cuda.synchronize()
+    o_gpu = out.cpu().numpy()[0]
+    for k in range(nkv):
+        ref = oracle.attend(vors[k], s32[k * G:(k + 1) * G].astype(np.float64), scale, rv[k].codes)
+        floor = np.linalg.norm(ref, axis=1, keepdims=True) / math.sqrt(cfg.head_dim)
+        H.assert_close_floor(o_gpu[k * G:(k + 1) * G], ref, floor, f"attend head {k}")
+
+
+@pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_end_to_end(torch_dev, sq, name, cfgname, heads, T, budget):
+    """GPU compress -> GPU scores -> GPU attend against the all-oracle pipeline;
+    tokens whose key codes flipped inside the band are excluded from the score
+    comparison (and counted)."""
+    torch = torch_dev
+    cfg = wl.CONFIGS[cfgname]
+    _case(f"end-to-end {name} T={T}")
+    nkv = len(heads)
+    G = cfg.q_heads // cfg.kv_heads
+    kcal, kors = H.calibrate_both(sq, cfg, heads, "k", budget, n_tokens=T)
+    vcal, vors = H.calibrate_both(sq, cfg, heads, "v", budget, n_tokens=T)
+    kcal.upload()
+    vcal.upload()
+    xk = H.data_block(cfg, heads, "k", T)
+    xv = H.data_block(cfg, heads, "v", T)
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    xkd = _to_dev(torch, xk[None], dt)
+    xvd = _to_dev(torch, xv[None], dt)
+    kp = torch.zeros((1, nkv, kcal.packed_head_words(T)), dtype=torch.int32, device="cuda")
+    vp = torch.zeros((1, nkv, vcal.packed_head_words(T)), dtype=torch.int32, device="cuda")
+    sq.sq_compress(kcal, xkd, kp)
+    sq.sq_compress(vcal, xvd, vp)
+    q = wl.queries(cfg, 1, nkv * G)
+    qd = _to_dev(torch, q, dt)
+    scores = torch.zeros((1, nkv * G, T), dtype=torch.float32, device="cuda")
+    sq.sq_scores(kcal, qd, kp, T, scores, nkv)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    ws = torch.zeros(sq.sq_attend_workspace_bytes(1, nkv * G, T, cfg.head_dim) // 4 + 1,
+                     dtype=torch.float32, device="cuda")
+    out = torch.zeros((1, nkv * G, cfg.head_dim), dtype=torch.float32, device="cuda")
+    sq.sq_attend(vcal, scores, scale, vp, T, ws, out, nkv)
+    torch.cuda.synchronize()
+    s_gpu = scores.cpu().numpy()[0]
+    o_gpu = out.cpu().numpy()[0]
+    kp_np = kp.cpu().numpy().view(np.uint32)[0]
+    vp_np = vp.cpu().numpy().view(np.uint32)[0]
+    excluded = 0
+    for k in range(nkv):
+        oc = kors[k]
+        r = oracle.compress(oc, xk[k])
+        gc, gz, gg = oracle.unpack(oc.widths, oc.m, kp_np[k], T)
+        same = (gc == r.codes).all(axis=1) & (gz == r.z).all(axis=1)
+        excluded += int((~same).sum())
+        qg = q[0, k * G:(k + 1) * G].astype(np.float64)
+        ref = oracle.scores_rotated(oc, qg, r.codes, r.z, r.gamma)
+        xt = oracle.dequantize(oc, r.codes, r.z, r.gamma)
+        fl = H.score_floor(oc, qg, xt)
+        H.assert_close_floor(s_gpu[k * G:(k + 1) * G][:, same], ref[:, same], fl[:, same],
+                             f"e2e scores head {k}")
+        rvv = oracle.compress(vors[k], xv[k])
+        vc, _, _ = oracle.unpack(vors[k].widths, 0, vp_np[k], T)
+        if same.all() and np.array_equal(vc, rvv.codes):
+            oref = oracle.attend(vors[k], ref, scale, rvv.codes)
+            floor = np.linalg.norm(oref, axis=1, keepdims=True) / math.sqrt(cfg.head_dim)
+            H.assert_close_floor(o_gpu[k * G:(k + 1) * G], oref, floor, f"e2e attend head {k}")
+    print(f"  tokens excluded for in-band key flips: {excluded}", flush=True)
+
+
+def test_compress_is_deterministic(torch_dev, sq):
+    torch = torch_dev
+    cfg = wl.CONFIGS["llama8b"]
+    heads = [(0, 0), (0, 1)]
+    _case("determinism llama8b k")
+    cal, _ = H.calibrate_both(sq, cfg, heads, "k", 3.0)
+    cal.upload()
+    x = H.data_block(cfg, heads, "k", 640)
+    a = _compress_gpu(torch, sq, cal, x[None], torch.bfloat16, 640)
+    b = _compress_gpu(torch, sq, cal, x[None], torch.bfloat16, 640)
+    assert np.array_equal(a, b)

@@ -1,0 +1,186 @@
+"""Host-side tests of libsq (no GPU): every declared symbol is exported, the
+host calibration matches the oracle, save/load round-trips, the host unpacker
+reads the oracle's record layout, and argument errors are reported."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+import compression_sq_compress_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "sq.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sq_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sq.lib()
+    names = _declared_symbols()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(sq.EXPORTS)
+
+
+def _heads(cfg, which, heads, n_tokens=None):
+    X = np.stack([wl.calibration_set(cfg, l, h, which, n_tokens=n_tokens) for l, h in heads])
+    G = (np.stack([wl.qjl_gaussian(cfg, l, h) for l, h in heads])
+         if which == "k" and cfg.qjl_bits else None)
+    return X.astype(np.float32), G
+
+
+@pytest.mark.parametrize("cfgname,which,heads,budget", [
+    ("tiny", "k", [(l, h) for l in range(3) for h in range(4)], 3.0),
+    ("tiny", "v", [(l, h) for l in range(3) for h in range(4)], 3.0),
+    ("llama8b", "k", [(0, h) for h in range(8)], 3.0),
+    ("llama8b", "v", [(0, h) for h in range(8)], 3.0),
+    ("qwen14b", "k", [(5, h) for h in range(4)], 2.5),
+    ("qwen14b", "v", [(6, h) for h in range(4)], 3.5),
+])
+def test_calibration_matches_oracle(cfgname, which, heads, budget):
+    cfg = wl.CONFIGS[cfgname]
+    X, G = _heads(cfg, which, heads)
+    qb = cfg.qjl_bits if which == "k" else 0
+    cal = sq.sq_calibrate(X, budget, qb, G)
+    assert cal.n_heads == len(heads)
+    for k in range(len(heads)):
+        oc = oracle.calibrate(X[k], budget, qb, G[k] if G is not None else None)
+        ex = cal.export(k)
+        inf = ex["info"]
+        assert inf.d_eff == oc.d_eff and inf.m == oc.m and inf.record_words == oc.W
+        assert inf.code_bits == int(oc.widths.sum())
+        np.testing.assert_array_equal(ex["widths"], oc.widths)
+        assert abs(inf.participation_ratio - oc.pr) <= 1e-10 * oc.pr
+        if math.isinf(oc.kappa):
+            assert math.isinf(inf.kappa)
+        else:
+            assert abs(inf.kappa - oc.kappa) <= 1e-8 * oc.kappa
+        np.testing.assert_allclose(ex["eigenvalues"], oc.lam, rtol=0, atol=1e-12 * oc.lam[0])
+        # eigenvectors of well-separated eigenvalues agree, same sign rule
+        gaps = np.abs(np.diff(oc.lam))
+        sep = np.minimum(np.r_[np.inf, gaps], np.r_[gaps, np.inf])
+        good = sep > 1e-3 * oc.lam[0]
+        np.testing.assert_allclose(ex["rotation"][good], oc.R[good], atol=1e-9)
+        thr = np.concatenate([t for t in oc.thresholds if len(t)] or [np.zeros(0)])
+        cen = np.concatenate([c for c in oc.centroids if len(c)] or [np.zeros(0)])
+        np.testing.assert_allclose(ex["thresholds"], thr, rtol=1e-6, atol=1e-6 * oc.sigma[0])
+        np.testing.assert_allclose(ex["centroids"], cen, rtol=1e-6, atol=1e-6 * oc.sigma[0])
+        if oc.m:
+            np.testing.assert_array_equal(ex["qjl"], oc.S.astype(np.float32))
+
+
+def test_calibration_thread_count_does_not_change_results():
+    cfg = wl.CONFIGS["llama8b"]
+    X, G = _heads(cfg, "k", [(0, h) for h in range(4)])
+    a = sq.sq_calibrate(X, 3.0, 1, G, n_threads=1)
+    b = sq.sq_calibrate(X, 3.0, 1, G, n_threads=4)
+    for k in range(4):
+        ea, eb = a.export(k), b.export(k)
+        for key in ("eigenvalues", "rotation", "widths", "thresholds", "centroids", "qjl"):
+            np.testing.assert_array_equal(ea[key], eb[key])
+
+
+def test_degenerate_calibrations_agree_on_integer_parts():
+    d = 32
+    zero = np.zeros((1, 40, d), np.float32)
+    cal = sq.sq_calibrate(zero, 3.0, 0, None)
+    oc = oracle.calibrate(zero[0], 3.0, 0, None)
+    assert cal.info(0).d_eff == oc.d_eff == 1
+    np.testing.assert_array_equal(cal.export(0)["widths"], oc.widths)
+    rank_def = wl.flat_data(16, d)[None].astype(np.float32)        # n < d
+    cal = sq.sq_calibrate(rank_def, 3.0, 0, None)
+    oc = oracle.calibrate(rank_def[0], 3.0, 0, None)
+    assert cal.info(0).d_eff == oc.d_eff
+    np.testing.assert_array_equal(cal.export(0)["widths"], oc.widths)
+
+
+def test_save_load_roundtrip(tmp_path):
+    cfg = wl.CONFIGS["tiny"]
+    X, G = _heads(cfg, "k", [(0, 0), (1, 2)])
+    cal = sq.sq_calibrate(X, 3.0, 1, G)
+    p = str(tmp_path / "c.sqcal")
+    cal.save(p)
+    cal2 = sq.Calibration.load(p)
+    assert cal2.n_heads == 2
+    for k in range(2):
+        a, b = cal.export(k), cal2.export(k)
+        for key in ("eigenvalues", "rotation", "widths", "thresholds", "centroids", "qjl"):
+            np.testing.assert_array_equal(a[key], b[key])
+        ia, ib = a["info"], b["info"]
+        assert (ia.d_eff, ia.m, ia.record_words, ia.n_thresholds) == (ib.d_eff, ib.m, ib.record_words, ib.n_thresholds)
+    assert cal.packed_head_words(100) == cal2.packed_head_words(100) == 128 * max(
+        cal.info(0).record_words, cal.info(1).record_words)
+    bad = tmp_path / "bad.sqcal"
+    bad.write_bytes(b"not a calibration file")
+    with pytest.raises(sq.SQError) as e:
+        sq.Calibration.load(str(bad))
+    assert e.value.status == 6
+    trunc = tmp_path / "trunc.sqcal"
+    trunc.write_bytes(open(p, "rb").read()[:200])
+    with pytest.raises(sq.SQError):
+        sq.Calibration.load(str(trunc))
+
+
+def test_host_unpack_reads_oracle_records():
+    cfg = wl.CONFIGS["llama8b"]
+    X, G = _heads(cfg, "k", [(0, 1)])
+    cal = sq.sq_calibrate(X, 3.0, 1, G)
+    oc = oracle.calibrate(X[0], 3.0, 1, G[0])
+    x = wl.kv_block(cfg, 0, 1, "k", 333, "data")
+    r = oracle.compress(oc, x)
+    p = oracle.pack(oc.widths, oc.m, r.codes, r.z, r.gamma)
+    codes, z, gamma = sq.sq_unpack(cal, 0, p, 333)
+    np.testing.assert_array_equal(codes, r.codes)
+    np.testing.assert_array_equal(z, r.z)
+    np.testing.assert_array_equal(gamma, r.gamma.astype(np.float32))
+
+
+def test_error_paths():
+    d = 32
+    x = wl.flat_data(64, d)[None].astype(np.float32)
+    with pytest.raises(sq.SQError) as e:
+        sq.sq_calibrate(np.zeros((1, 10, 48), np.float32), 3.0, 0)
+    assert e.value.status == 2
+    with pytest.raises(sq.SQError) as e:
+        sq.sq_calibrate(x[:, :1], 3.0, 0)
+    assert e.value.status == 3
+    bad = x.copy()
+    bad[0, 3, 5] = np.nan
+    with pytest.raises(sq.SQError) as e:
+        sq.sq_calibrate(bad, 3.0, 0)
+    assert e.value.status == 3
+    with pytest.raises(sq.SQError) as e:
+        sq.sq_calibrate(x, 9.0, 0)
+    assert e.value.status == 1
+    with pytest.raises(sq.SQError) as e:
+        sq.sq_calibrate(x, 3.0, 1, None)
+    assert e.value.status == 1
+    cal = sq.sq_calibrate(x, 3.0, 0)
+    with pytest.raises(sq.SQError) as e:
+        cal.info(1)
+    assert e.value.status == 1
+    lib = sq.lib()
+    # device calls on a handle that was never uploaded: rejected before any HIP call
+    st = lib.sq_compress(cal.handle, 0, 1, 1, 0, None, 1, 64, 0, 0, d, None, 0, 64, None)
+    assert st == 7 and b"upload" in lib.sq_last_error()
+    st = lib.sq_scores(None, 0, 0, 1, 4, 1, None, 1, None, 0, 0, 64, None, None)
+    assert st == 1
+    o = sq.CalibOpts()
+    assert lib.sq_calib_default_opts(None, 32) == 1
+    assert lib.sq_calib_default_opts(C.byref(o), 32) == 0 and o.max_bits == 8
+    assert lib.sq_packed_head_words(None, 10) == -1
+
+
+def test_workspace_size_formula():
+    assert sq.sq_attend_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * 32 * 130 * 4
+    assert sq.sq_attend_workspace_bytes(1, 4, 1, 32) == 4 * 1 * 34 * 4
+    assert sq.sq_attend_workspace_bytes(1, 4, 0, 32) == 0
