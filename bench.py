@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the SpectralQuant hot path on one MI355X.
+
+Workload (the decode configuration): 64 sequences x 32768 tokens, 8 KV heads
+(32 query heads, groups of 4), head_dim 128, bf16 keys/values with the
+Llama-shaped spectra, 3 bits per coordinate, keys with 1 QJL bit per signal
+dimension.  One step = the whole hot path over that batch:
+    sq_compress(K) + sq_compress(V)          (33.5 M vectors)
+  + sq_scores (bf16 queries)                 (fp32 scores [64][32][32768])
+  + sq_attend (softmax + value sum)          (fp32 out [64][32][128])
+Inputs are resident in HBM before the timed region; calibration (host, one
+time) is outside it.  ``value`` is KV vectors compressed per second of the
+whole step; per-kernel rates, the roofline of the dominant kernel and the CPU
+oracle on a bounded sample of the same workload are reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=None, help="override sequences (default 64)")
+    ap.add_argument("--tokens", type=int, default=None, help="override tokens (default 32768)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, kcal_in, vcal_in, sample_tokens):
+    """Time the CPU oracle, as it stands, on a bounded sample of the workload:
+    sequence 0, all 8 KV heads, the first ``sample_tokens`` tokens; compress K
+    and V (rotate, quantise, QJL, pack), score the 4 query heads of each group,
+    softmax + value sum.  Returns KV vectors per second."""
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    Xk, Gk = kcal_in
+    Xv = vcal_in
+    kors = [oracle.calibrate(Xk[h], 3.0, 1, Gk[h]) for h in range(cfg.kv_heads)]
+    vors = [oracle.calibrate(Xv[h], 3.0, 0, None) for h in range(cfg.kv_heads)]
+    xs_k = [wl.kv_block(cfg, 0, h, "k", sample_tokens, "data") for h in range(cfg.kv_heads)]
+    xs_v = [wl.kv_block(cfg, 0, h, "v", sample_tokens, "data") for h in range(cfg.kv_heads)]
+    q = wl.queries(cfg, 1, cfg.q_heads)[0]
+    G = cfg.q_heads // cfg.kv_heads
+    t0 = time.perf_counter()
+    for h in range(cfg.kv_heads):
+        rk = oracle.compress(kors[h], xs_k[h])
+        oracle.pack(kors[h].widths, kors[h].m, rk.codes, rk.z, rk.gamma)
+        rv = oracle.compress(vors[h], xs_v[h])
+        oracle.pack(vors[h].widths, 0, rv.codes, rv.z, rv.gamma)
+        s = oracle.scores_rotated(kors[h], q[h * G:(h + 1) * G], rk.codes, rk.z, rk.gamma)
+        oracle.attend(vors[h], s, 1 / math.sqrt(cfg.head_dim), rv.codes)
+    dt = time.perf_counter() - t0
+    n_vec = 2 * cfg.kv_heads * sample_tokens
+    return dict(value=n_vec / dt, unit="KV vectors/s", cores=int(threads), kind="oracle",
+                sample=(f"sequence 0, {cfg.kv_heads} KV heads x {sample_tokens} tokens, K and V "
+                        f"compress+pack, scores for {cfg.q_heads} query heads, softmax+attend; "
+                        f"{n_vec} vectors in {dt:.2f} s"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode workload shards by KV head with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    import compression_sq_compress_amd as sq
+
+    cfg = wl.CONFIGS["decode"]
+    B = args.batch or cfg.batch
+    T = args.tokens or cfg.tokens[0]
+    Hkv, Hq, d = cfg.kv_heads, cfg.q_heads, cfg.head_dim
+    G = Hq // Hkv
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # one-time host calibration (512-token calibration set per KV head)
+    Xk = np.stack([wl.calibration_set(cfg, 0, h, "k") for h in range(Hkv)]).astype(np.float32)
+    Gk = np.stack([wl.qjl_gaussian(cfg, 0, h) for h in range(Hkv)])
+    Xv = np.stack([wl.calibration_set(cfg, 0, h, "v") for h in range(Hkv)]).astype(np.float32)
+    kcal = sq.sq_calibrate(Xk, 3.0, 1, Gk).upload()
+    vcal = sq.sq_calibrate(Xv, 3.0, 0, None).upload()
+    Wk = max(kcal.info(h).record_words for h in range(Hkv))
+    Wv = max(vcal.info(h).record_words for h in range(Hkv))
+
+    # synthetic inputs resident in HBM
+    K = wl.decode_kv_on_device(cfg, "k", n_batch=B, n_tokens=T)
+    V = wl.decode_kv_on_device(cfg, "v", n_batch=B, n_tokens=T)
+    q = torch.from_numpy(wl.queries(cfg, B, Hq)).to(dev).to(torch.bfloat16)
+    kp = torch.empty((B, Hkv, kcal.packed_head_words(T)), dtype=torch.int32, device=dev)
+    vp = torch.empty((B, Hkv, vcal.packed_head_words(T)), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(sq.sq_attend_workspace_bytes(B, Hq, T, d) // 4, dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        sq.sq_compress(kcal, K, kp)
+        if ev: ev[1].record()
+        sq.sq_compress(vcal, V, vp)
+        if ev: ev[2].record()
+        sq.sq_scores(kcal, q, kp, T, scores, Hkv)
+        if ev: ev[3].record()
+        sq.sq_attend(vcal, scores, scale, vp, T, ws, out, Hkv)
+        if ev: ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
+    ms_ck, ms_cv, ms_sc, ms_at = per.mean(axis=0)
+    ms_step = wall * 1e3 / args.steps
+
+    n_vec = B * Hkv * T
+    # algorithmic bytes: compress reads d bf16 and writes one record per vector
+    bytes_ck = n_vec * (2 * d + 4 * Wk)
+    bytes_cv = n_vec * (2 * d + 4 * Wv)
+    bytes_sc = n_vec * 4 * Wk + B * Hq * T * 4 + B * Hq * d * 2
+    bytes_at = n_vec * 4 * Wv + B * Hq * T * 4 + B * Hq * d * 4
+    gbps = lambda b, ms: b / (ms * 1e-3) / 1e9
+    comp_ms = ms_ck + ms_cv
+    comp_gbps = gbps(bytes_ck + bytes_cv, comp_ms)
+    flops_comp = 2 * n_vec * 2 * d * d   # algorithmic rotation flops (K and V)
+    res = {
+        "metric": "KV vectors compressed/s + compressed q·K score GB/s (hd128), % HBM roofline",
+        "value": 2 * n_vec / (ms_step * 1e-3),
+        "unit": "KV vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode: {B} seqs x {T} tokens, {Hq} q / {Hkv} KV heads, hd{d}, "
+                               f"bf16 K/V, 3 bits/coord, 1 QJL bit per key signal dim",
+                   "batch": B, "tokens": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "avg_bits": 3.0, "record_words_k": Wk, "record_words_v": Wv},
+        "kernels_ms": {"compress_k": ms_ck, "compress_v": ms_cv, "scores": ms_sc, "attend": ms_at},
+        "compress_vectors_per_s": 2 * n_vec / (comp_ms * 1e-3),
+        "compress_GBps": comp_gbps,
+        "compress_mfma_frac": flops_comp / (comp_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "score_GBps": gbps(bytes_sc, ms_sc),
+        "score_hbm_frac": gbps(bytes_sc, ms_sc) / HBM_PEAK_GBPS,
+        "attend_GBps": gbps(bytes_at, ms_at),
+        "attend_hbm_frac": gbps(bytes_at, ms_at) / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "compress_kernel<128,bf16> (K and V launches)",
+                     "achieved": comp_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": comp_gbps / HBM_PEAK_GBPS, "traffic": None},
+        "roofline_scores": {"bound": "hbm", "kernel": "scores_kernel<4>",
+                            "achieved": gbps(bytes_sc, ms_sc), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": gbps(bytes_sc, ms_sc) / HBM_PEAK_GBPS,
+                            "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, (Xk, Gk), Xv, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,12 +25,21 @@ struct DevHead {
   int64_t off_Rfrag;    // bf16 [3][d/32][d/16][64][8]: hi/mid/lo split of R in
                         // MFMA 32x32x16 A-operand order (see compress kernel)
   int64_t off_coord;    // DevCoord [d]
-  int64_t off_thr;      // float [n_thr]   thresholds * sigma_i, per coordinate ascending
+  int64_t off_thr;      // float [n_cent]  thresholds * sigma_i of coordinate i in
+                        // breadth-first (Eytzinger) order at [cent_base_i + 1,
+                        // cent_base_i + 2^b_i): node n has children 2n, 2n+1
   int64_t off_cent;     // float [n_cent]  centroids * sigma_i
   int64_t off_S;        // float [m][d_eff] QJL sketch
+  int64_t off_wstart;   // int32 [W]: first coordinate reaching into word k | count << 16
+  int64_t off_chunks;   // int32 [d/32][4 + d] per wave of the compress kernel:
+                        //   [0] number of chunks, [1] first bit | end bit << 16 of
+                        //   the wave's contiguous code range, [2] first | end of
+                        //   the shared record words this wave stores, [3] unused,
+                        //   then chunks (start | count << 10 | width << 20) of <= 8
+                        //   equal-width coordinates in coordinate order
 };
 
 static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
-static_assert(sizeof(DevHead) == 96, "DevHead layout");
+static_assert(sizeof(DevHead) == 112, "DevHead layout");
 
 }  // namespace sq

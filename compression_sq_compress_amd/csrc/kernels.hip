@@ -47,11 +47,21 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
-// Make this wave's earlier LDS writes visible to its other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Uniform table reads go through the constant address space so that they
+// become scalar loads: the compiler can then neither confuse them with the
+// kernel's own global stores nor make them wait for those stores.
+#define SQ_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ const SQ_CONST T *cptr(const void *p) {
+  return (const SQ_CONST T *)(uintptr_t)p;
+}
+__device__ __forceinline__ DevCoord load_coord(const SQ_CONST DevCoord *p) {
+  DevCoord r;
+  r.bit_off = p->bit_off;
+  r.width = p->width;
+  r.thr_base = p->thr_base;
+  r.cent_base = p->cent_base;
+  return r;
 }
 
 // ------------------------------------------------------------------ upload
@@ -99,9 +109,11 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.off_R = off;       off = align256(off + sizeof(float) * d * d);
     D.off_Rfrag = off;   off = align256(off + sizeof(uint16_t) * 3 * d * d);
     D.off_coord = off;   off = align256(off + sizeof(DevCoord) * d);
-    D.off_thr = off;     off = align256(off + sizeof(float) * std::max(1, hc.n_thr));
+    D.off_thr = off;     off = align256(off + sizeof(float) * std::max(1, hc.n_cent));
     D.off_cent = off;    off = align256(off + sizeof(float) * std::max(1, hc.n_cent));
     D.off_S = off;       off = align256(off + sizeof(float) * std::max(1, hc.m * hc.d_eff));
+    D.off_wstart = off;  off = align256(off + sizeof(int32_t) * std::max(1, hc.W));
+    D.off_chunks = off;  off = align256(off + sizeof(int32_t) * (d / 32) * (4 + d));
   }
   std::vector<uint8_t> img(off, 0);
   std::memcpy(img.data(), desc.data(), sizeof(DevHead) * nh);
@@ -136,9 +148,101 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
     for (int i = 0; i < d; ++i)
       Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
-    if (hc.n_thr) std::memcpy(img.data() + D.off_thr, hc.thr.data(), sizeof(float) * hc.n_thr);
+    // thresholds in breadth-first order: node n (depth k, position p = n - 2^k)
+    // of coordinate i holds sorted threshold (2p + 1) * 2^(b - 1 - k) - 1
+    {
+      float *E = (float *)(img.data() + D.off_thr);
+      for (int i = 0; i < d; ++i) {
+        const int b = hc.widths[i];
+        if (b == 0) continue;
+        E[hc.cent_base[i]] = 0.0f;  // node 0 is never read
+        for (int n = 1; n < (1 << b); ++n) {
+          int k = 0;
+          while ((2 << k) <= n) ++k;
+          const int pos = n - (1 << k);
+          E[hc.cent_base[i] + n] = hc.thr[hc.thr_base[i] + (2 * pos + 1) * (1 << (b - 1 - k)) - 1];
+        }
+      }
+    }
     if (hc.n_cent) std::memcpy(img.data() + D.off_cent, hc.cent.data(), sizeof(float) * hc.n_cent);
     if (hc.m) std::memcpy(img.data() + D.off_S, hc.S.data(), sizeof(float) * hc.m * hc.d_eff);
+    int32_t *ws = (int32_t *)(img.data() + D.off_wstart);
+    for (int k = 0; k < hc.W; ++k) {
+      int c = 0;  // first coordinate whose field ends after bit 32k
+      while (c < d && hc.bit_off[c] + hc.widths[c] <= 32 * k) ++c;
+      int e = c;  // one past the last coordinate that starts before bit 32(k+1)
+      while (e < d && hc.bit_off[e] < 32 * (k + 1)) ++e;
+      ws[k] = c | ((e - c) << 16);
+    }
+    // Work split of the compress kernel: d/32 waves, each owning a contiguous
+    // coordinate range chosen to balance the search depth (sum of width + 1);
+    // within a range, runs of equal width cut into chunks of <= 8.  A record
+    // word lying wholly inside one wave's code bits is stored by that wave;
+    // every other word is assembled in LDS and stored by the highest wave
+    // that touches it (the last wave also owns the QJL bits and gamma).
+    {
+      const int NW = d / 32;
+      int32_t *CH = (int32_t *)(img.data() + D.off_chunks);
+      int total = 0;
+      for (int i = 0; i < d; ++i) total += hc.widths[i] + 1;
+      std::vector<int> cut(NW + 1, d);
+      cut[0] = 0;
+      int acc = 0, w = 1;
+      for (int i = 0; i < d && w < NW; ++i) {
+        acc += hc.widths[i] + 1;
+        if (acc * NW >= total * w) cut[w++] = i + 1;
+      }
+      for (; w < NW; ++w) cut[w] = d;
+      for (int w2 = 1; w2 <= NW; ++w2) cut[w2] = std::max(cut[w2], cut[w2 - 1]);
+      std::vector<int> sbit(NW), ebit(NW);
+      for (int w2 = 0; w2 < NW; ++w2) {
+        sbit[w2] = cut[w2] < d ? hc.bit_off[cut[w2]] : hc.code_bits;
+        ebit[w2] = cut[w2 + 1] < d ? hc.bit_off[cut[w2 + 1]] : hc.code_bits;
+      }
+      ebit[NW - 1] = 32 * hc.W;  // the last wave also covers QJL bits and gamma
+      // words a wave stores straight from its bit window: wholly inside its
+      // code bits (for the last wave with QJL, below the QJL bits)
+      std::vector<int> dfirst(NW), dend(NW);
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const int ecode = (w2 == NW - 1 && hc.m > 0) ? hc.code_bits : ebit[w2];
+        dfirst[w2] = (sbit[w2] + 31) / 32;
+        dend[w2] = std::max(dfirst[w2], ecode / 32);
+        if (w2 == NW - 1 && hc.m == 0) dend[w2] = std::max(dfirst[w2], hc.W);
+      }
+      // every other word: OR-assembled in LDS, stored by the highest wave
+      // that touches it
+      std::vector<int> owner(hc.W, -1);
+      for (int k = 0; k < hc.W; ++k) {
+        bool direct = false;
+        for (int w2 = 0; w2 < NW; ++w2)
+          if (k >= dfirst[w2] && k < dend[w2]) direct = true;
+        if (direct) continue;
+        owner[k] = NW - 1;
+        for (int w2 = 0; w2 < NW; ++w2)
+          if (sbit[w2] < ebit[w2] && sbit[w2] < 32 * (k + 1) && ebit[w2] > 32 * k) owner[k] = w2;
+      }
+      for (int w2 = 0; w2 < NW; ++w2) {
+        int32_t *row = CH + w2 * (4 + d);
+        int n = 0;
+        for (int i = cut[w2]; i < cut[w2 + 1];) {
+          int j = i;
+          while (j < cut[w2 + 1] && j - i < 8 && hc.widths[j] == hc.widths[i]) ++j;
+          row[4 + n++] = i | ((j - i) << 10) | (hc.widths[i] << 20);
+          i = j;
+        }
+        row[0] = n;
+        row[1] = sbit[w2] | (ebit[w2] << 16);
+        int f = -1, e = -1;
+        for (int k = 0; k < hc.W; ++k)
+          if (owner[k] == w2) {
+            if (f < 0) f = k;
+            e = k + 1;
+          }
+        if (f < 0) f = e = 0;
+        row[2] = f | (e << 16);
+        row[3] = dfirst[w2] | (dend[w2] << 16);
+      }
+    }
   }
   release_tables(c);
   int dev = 0;
@@ -164,22 +268,25 @@ sq_status upload_tables(sq_calib *c, void *stream) {
 
 // ------------------------------------------------------------------ compress
 //
-// One wavefront compresses a tile of 64 tokens of one head; a workgroup holds
-// up to 4 such waves and shares the head's threshold and signal-centroid
-// tables in LDS.
-//   rotate:   y^T[coord][token] = R x^T as MFMA 32x32x16 bf16 tiles.  R is
-//             split into three bf16 terms (Henry, Tang & Heinecke, ARITH 2019:
-//             bf16x3), bf16 inputs are exact, so each product is exact in the
-//             fp32 accumulator.  fp32 inputs are split into three terms as well
-//             and the six leading cross products are accumulated.
-//   quantise: the 32x32 accumulator block goes through LDS so that each lane
-//             holds one token; lanes walk the block's coordinates in order
-//             (uniform width, uniform bit position) and binary-search the
-//             coordinate's thresholds in LDS.
-//   QJL:      signal-coordinate residuals are kept in LDS; z_j = [(S r)_j >= 0]
-//             with S read through the scalar cache.
-//   pack:     a running two-word bit window per lane; each completed word is
-//             stored at once, 64 lanes -> one coalesced 256-byte store.
+// A workgroup of D/32 waves serves one calibration head and walks many
+// 64-token tiles.  Wave w owns eigen-coordinates [32w, 32w+32):
+//   rotate:   y^T[coord][token] = R x^T with MFMA 32x32x16 bf16.  R is split
+//             into three bf16 terms (Henry, Tang & Heinecke, ARITH 2019:
+//             bf16x3) so every product is exact in the fp32 accumulator; for
+//             head_dim <= 128 the wave's 32 rows of the three terms stay in
+//             registers for the workgroup's whole life, for 256 they are read
+//             per tile from the L2.  fp32 inputs are split into three terms as
+//             well and the six leading cross products are accumulated.  The
+//             x tile (B operand) is shared through LDS.
+//   quantise: the accumulators go to an LDS y tile; lane = token walks the
+//             wave's 32 coordinates in groups of 8 whose binary searches over
+//             the thresholds (LDS) advance in lock-step; the code replaces y in
+//             the tile, signal coordinates also leave their residual.
+//   pack:     after a workgroup barrier each wave assembles a share of the W
+//             record words (lane = token) from the codes of every coordinate
+//             that reaches into the word, the QJL bits z_j = [(S r)_j >= 0]
+//             that fall in it and, in word W-1, gamma = |r| as IEEE half; one
+//             coalesced 256-byte store per word.
 
 struct CompressArgs {
   const DevHead *heads;
@@ -190,14 +297,18 @@ struct CompressArgs {
   int64_t ps_b, ps_h;
   int64_t n_tokens;
   int first_head, cbs;
-  int n_tiles;          // ceil(T / 64)
-  int lds_cent_off;     // floats: start of the signal-centroid table
-  int lds_wave_off;     // floats: start of the per-wave areas
-  int lds_wave_floats;  // floats per wave
-  int rstride;          // residual row stride (odd)
+  int n_tiles;          // ceil(T / 64) per (batch, head)
+  int items;            // tiles one head's workgroups share
+  int lds_cent_off;     // floats: signal-centroid table
+  int lds_x_off;        // floats: x tile
+  int lds_y_off;        // floats: y / code tile
+  int lds_r_off;        // floats: residual tile
+  int lds_b_off;        // floats: shared record-word buffer
+  int ys;               // y tile row stride (floats, odd)
+  int rs;               // residual row stride (floats, odd)
+  int bws;              // word buffer row stride (words, odd)
 };
 
-template <bool F32>
 __device__ __forceinline__ void split3(const float *v, uint4 &p0, uint4 &p1, uint4 &p2) {
   uint16_t a[8], b[8], c[8];
 #pragma unroll
@@ -219,115 +330,128 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Running bit window of one record (per lane); positions are wave-uniform.
-struct BitWriter {
-  uint32_t lo, hi;
-  int fill, wcur;
-  uint32_t *dst;   // &slot[tile*W*64 + lane]
-  bool valid;
-  __device__ __forceinline__ void store_word() {
-    dst[(int64_t)wcur * 64] = valid ? lo : 0u;
-    ++wcur;
-    lo = hi;
-    hi = 0;
-    fill -= 32;
-  }
-  __device__ __forceinline__ void put(uint32_t v, int b) {
-    lo |= v << fill;
-    if (fill + b > 32) hi = v >> (32 - fill);
-    fill += b;
-    if (fill >= 32) store_word();
-  }
-};
+// Wait for this wave's LDS operations and keep the compiler from moving LDS
+// accesses across this point (cross-lane exchange within one wave).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D, bool F32>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+__global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
   extern __shared__ float smem[];
+  constexpr int NW = D / 32, KS = D / 16, MB = D / 32, NT = 64 * NW;
+  constexpr bool RES = D <= 128;           // rotation rows resident in registers
+  constexpr int XS = F32 ? D + 4 : D + 8;  // x tile row stride (elements)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int ch = a.first_head + b * a.cbs + h;
-  const DevHead *hd = a.heads + ch;
-  const int d_eff = hd->d_eff, m = hd->m, W = hd->W;
-  const int n_thr = hd->n_thr, n_cent_sig = m > 0 ? hd->n_cent_sig : 0;
-
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
+  const int h = blockIdx.y, bz = blockIdx.z;
+  const int ch = a.first_head + bz * a.cbs + h;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
+  const int d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
+  const int n_thr = hd->n_cent, n_cent_sig = m > 0 ? hd->n_cent_sig : 0;
   float *s_thr = smem;
   float *s_cent = smem + a.lds_cent_off;
+  float *ytile = smem + a.lds_y_off;             // [64][ys]
+  int *ctile = (int *)ytile;                     // codes, in place of y
+  float *rtile = smem + a.lds_r_off;             // [64][rs]
+  uint32_t *bwords = (uint32_t *)(smem + a.lds_b_off);  // [64][bws] shared record words
   {
     const float *g_thr = (const float *)(a.blob + hd->off_thr);
-    for (int k = threadIdx.x; k < n_thr; k += blockDim.x) s_thr[k] = g_thr[k];
+    for (int k = threadIdx.x; k < n_thr; k += NT) s_thr[k] = g_thr[k];
     const float *g_cent = (const float *)(a.blob + hd->off_cent);
-    for (int k = threadIdx.x; k < n_cent_sig; k += blockDim.x) s_cent[k] = g_cent[k];
+    for (int k = threadIdx.x; k < n_cent_sig; k += NT) s_cent[k] = g_cent[k];
   }
-  __syncthreads();
-
-  const int tile = blockIdx.x * nwaves + wave;
-  if (tile >= a.n_tiles) return;  // no block-level barrier after this point
-  float *yb = smem + a.lds_wave_off + wave * a.lds_wave_floats;  // [64][33]
-  float *rb = yb + 64 * 33;                                      // [64][rstride]
-  const int t0 = tile * 64;
-  const int64_t T = a.n_tokens;
-  const int64_t xbase = (int64_t)b * a.xs_b + (int64_t)h * a.xs_h;
-  constexpr int KS = D / 16, MB = D / 32;
   const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag);
-  const DevCoord *coords = (const DevCoord *)(a.blob + hd->off_coord);
-
-  // B operands: x^T fragments, lane l -> token nb*32 + l%32, k = ks*16 + 8*(l/32) + e
-  uint4 xf[F32 ? 1 : 2][F32 ? 1 : KS];
-  if constexpr (!F32) {
-    const uint16_t *xp = (const uint16_t *)a.x + xbase;
+  uint4 rf[RES ? 3 : 1][RES ? KS : 1];
+  if constexpr (RES) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int64_t t = t0 + nb * 32 + (lane & 31);
+    for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        xf[nb][ks] = t < T ? *(const uint4 *)(xp + t * a.xs_t + ks * 16 + 8 * (lane >> 5))
-                           : make_uint4(0, 0, 0, 0);
-    }
+      for (int ks = 0; ks < KS; ++ks) rf[sp][ks] = Rf[((sp * MB + w) * KS + ks) * 64 + lane];
   }
+  const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
+  const SQ_CONST int32_t *wstart = cptr<int32_t>(a.blob + hd->off_wstart);
+  const SQ_CONST int32_t *chunks = cptr<int32_t>(a.blob + hd->off_chunks);
+  const SQ_CONST float *thr_g = cptr<float>(a.blob + hd->off_thr);
+  const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
+  const int64_t T = a.n_tokens;
+  // record words handled by this wave
+  const int wb = (w * W) / NW, we = ((w + 1) * W) / NW;
 
-  BitWriter bw;
-  bw.lo = bw.hi = 0;
-  bw.fill = 0;
-  bw.wcur = 0;
-  bw.dst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
-  bw.valid = (t0 + lane) < T;
-  float g2 = 0.0f;
+  // x tile chunks of 16 bytes: CPR per row, CH per thread; the next tile's
+  // chunks are prefetched into registers while the current tile is processed
+  constexpr int ESZ = F32 ? 4 : 2;
+  constexpr int CPR = D * ESZ / 16;
+  constexpr int CH = 64 * CPR / NT;
+  uint4 xr[CH];
+  auto load_x = [&](int item) {
+    const int bb = a.cbs ? bz : item / a.n_tiles;
+    const int tl = a.cbs ? item : item % a.n_tiles;
+    const char *xp = (const char *)a.x + ((int64_t)bb * a.xs_b + (int64_t)h * a.xs_h) * ESZ;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = threadIdx.x + q * NT;
+      const int tt = c / CPR, col = c % CPR;
+      const int64_t t = (int64_t)tl * 64 + tt;
+      xr[q] = t < T ? *(const uint4 *)(xp + t * a.xs_t * ESZ + col * 16) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (blockIdx.x < a.items) load_x(blockIdx.x);
 
-  for (int mb = 0; mb < MB; ++mb) {
+  for (int item = blockIdx.x; item < a.items; item += gridDim.x) {
+    const int b = a.cbs ? bz : item / a.n_tiles;
+    const int tile = a.cbs ? item : item % a.n_tiles;
+    const int64_t t0 = (int64_t)tile * 64;
+    // ---- prefetched x tile -> LDS, then start loading the next one
+    {
+      char *xt = (char *)(smem + a.lds_x_off);
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        const int c = threadIdx.x + q * NT;
+        *(uint4 *)(xt + (c / CPR) * XS * ESZ + (c % CPR) * 16) = xr[q];
+      }
+    }
+    __syncthreads();
+    if (item + (int)gridDim.x < a.items) load_x(item + gridDim.x);
+    for (int k = threadIdx.x; k < 64 * a.bws; k += NT) bwords[k] = 0u;
+    // ---- rotate this wave's 32 coordinates for the 64 tokens
     f32x16 acc0, acc1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc0[v] = acc1[v] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint4 r0 = Rf[((0 * MB + mb) * KS + ks) * 64 + lane];
-      const uint4 r1 = Rf[((1 * MB + mb) * KS + ks) * 64 + lane];
-      const uint4 r2 = Rf[((2 * MB + mb) * KS + ks) * 64 + lane];
-      if constexpr (!F32) {
-        acc0 = mfma32(r0, xf[0][ks], acc0);
-        acc1 = mfma32(r0, xf[1][ks], acc1);
-        acc0 = mfma32(r1, xf[0][ks], acc0);
-        acc1 = mfma32(r1, xf[1][ks], acc1);
-        acc0 = mfma32(r2, xf[0][ks], acc0);
-        acc1 = mfma32(r2, xf[1][ks], acc1);
+      uint4 r0, r1, r2;
+      if constexpr (RES) {
+        r0 = rf[0][ks]; r1 = rf[1][ks]; r2 = rf[2][ks];
       } else {
-        const float *xp = (const float *)a.x + xbase;
+        r0 = Rf[((0 * MB + w) * KS + ks) * 64 + lane];
+        r1 = Rf[((1 * MB + w) * KS + ks) * 64 + lane];
+        r2 = Rf[((2 * MB + w) * KS + ks) * 64 + lane];
+      }
+      const int koff = ks * 16 + 8 * (lane >> 5);
+      if constexpr (!F32) {
+        const uint16_t *xt = (const uint16_t *)(smem + a.lds_x_off);
+        const uint4 x0 = *(const uint4 *)(xt + (lane & 31) * XS + koff);
+        const uint4 x1 = *(const uint4 *)(xt + (32 + (lane & 31)) * XS + koff);
+        acc0 = mfma32(r0, x0, acc0);
+        acc1 = mfma32(r0, x1, acc1);
+        acc0 = mfma32(r1, x0, acc0);
+        acc1 = mfma32(r1, x1, acc1);
+        acc0 = mfma32(r2, x0, acc0);
+        acc1 = mfma32(r2, x1, acc1);
+      } else {
+        const float *xt = smem + a.lds_x_off;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const int64_t t = t0 + nb * 32 + (lane & 31);
+          const float *src = xt + (nb * 32 + (lane & 31)) * XS + koff;
           float v[8];
-          if (t < T) {
-            const float4 *src = (const float4 *)(xp + t * a.xs_t + ks * 16 + 8 * (lane >> 5));
-            const float4 u0 = src[0], u1 = src[1];
-            v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
-            v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-          }
+          const float4 u0 = *(const float4 *)src, u1 = *(const float4 *)(src + 4);
+          v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+          v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
           uint4 x0, x1, x2;
-          split3<true>(v, x0, x1, x2);
+          split3(v, x0, x1, x2);
           f32x16 &acc = nb == 0 ? acc0 : acc1;
           acc = mfma32(r0, x0, acc);
           acc = mfma32(r0, x1, acc);
@@ -338,56 +462,111 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         }
       }
     }
-    // accumulator (row = coord, col = token) -> LDS yb[token][coord]
+    // accumulator (row = coordinate, column = token) -> y tile [token][coordinate]
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      yb[(lane & 31) * 33 + row] = acc0[v];
-      yb[(32 + (lane & 31)) * 33 + row] = acc1[v];
+      const int row = 32 * w + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      ytile[(lane & 31) * a.ys + row] = acc0[v];
+      ytile[(32 + (lane & 31)) * a.ys + row] = acc1[v];
     }
-    wave_lds_sync();
-    for (int cl = 0; cl < 32; ++cl) {
-      const int i = mb * 32 + cl;
-      const DevCoord cd = coords[i];
-      if (cd.width == 0) {
-        if (i < d_eff && m > 0) {
-          const float y = yb[lane * 33 + cl];
-          g2 += y * y;
-          rb[lane * a.rstride + i] = y;
+    __syncthreads();
+    // ---- quantise + pack (lane = token).  The wave walks its contiguous
+    // coordinate range in chunks of <= 8 equal-width coordinates whose
+    // searches advance together through the breadth-first threshold trees
+    // (root compared from a scalar register, one batch of LDS reads per
+    // further level); codes are appended in coordinate order to a two-word
+    // bit window.  Words wholly inside the wave's code bits go straight to
+    // HBM, shared words are OR-ed into the LDS word buffer.
+    const SQ_CONST int32_t *cl = chunks + w * (4 + D);
+    const int nch = cl[0];
+    const int sbit = cl[1] & 0xFFFF;
+    const int dfirst = cl[3] & 0xFFFF, dend = cl[3] >> 16;
+    uint32_t *dst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
+    const bool valid = t0 + lane < T;
+    uint32_t *bwrow = bwords + lane * a.bws;
+    {
+      uint32_t lo = 0, hi = 0;
+      int fill = sbit & 31, kw = sbit >> 5;
+      auto flush = [&]() {
+        if (kw >= dfirst && kw < dend) dst[(int64_t)kw * 64] = valid ? lo : 0u;
+        else atomicOr(bwrow + kw, lo);
+        ++kw;
+        lo = hi;
+        hi = 0;
+        fill -= 32;
+      };
+      for (int q = 0; q < nch; ++q) {
+        const int e = cl[4 + q];
+        const int start = e & 1023, cnt = (e >> 10) & 1023, bw = e >> 20;
+        float y[8];
+        int node[8], tb[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int i = start + min(c, cnt - 1);
+          y[c] = ytile[lane * a.ys + i];
+          tb[c] = coords[i].cent_base;
+          node[c] = 1;
         }
-        continue;
+        if (bw > 0) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) node[c] = 2 + (thr_g[tb[c] + 1] < y[c] ? 1 : 0);
+          for (int k = 1; k < bw; ++k) {
+            float th[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) th[c] = s_thr[tb[c] + node[c]];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) node[c] = node[c] + node[c] + (th[c] < y[c] ? 1 : 0);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (c < cnt) {
+            const int i = start + c;
+            const uint32_t code = (uint32_t)(node[c] - (1 << bw));
+            if (i < d_eff && m > 0)
+              rtile[lane * a.rs + i] = y[c] - (bw ? s_cent[tb[c] + (int)code] : 0.0f);
+            if (bw) {
+              lo |= code << fill;
+              if (fill + bw > 32) hi = code >> (32 - fill);
+              fill += bw;
+              if (fill >= 32) flush();
+            }
+          }
+        }
       }
-      const float y = yb[lane * 33 + cl];
-      const float *th = s_thr + cd.thr_base - 1;
-      int code = 0;
-      for (int k = cd.width - 1; k >= 0; --k) {
-        const int cand = code + (1 << k);
-        code = th[cand] < y ? cand : code;
-      }
-      bw.put((uint32_t)code, cd.width);
-      if (i < d_eff && m > 0) {
-        const float r = y - s_cent[cd.cent_base + code];
-        g2 += r * r;
-        rb[lane * a.rstride + i] = r;
+      if (fill > 0) {  // last, partial word of the range
+        if (kw >= dfirst && kw < dend) dst[(int64_t)kw * 64] = valid ? lo : 0u;
+        else atomicOr(bwrow + kw, lo);
       }
     }
-    wave_lds_sync();
-  }
-
-  uint32_t ghalf = 0;
-  if (m > 0) {
-    const float *S = (const float *)(a.blob + hd->off_S);
-    const float *rr = rb + lane * a.rstride;
-    for (int j = 0; j < m; ++j) {
-      float dot = 0.0f;
-      for (int i = 0; i < d_eff; ++i) dot = fmaf(S[j * d_eff + i], rr[i], dot);
-      bw.put(dot >= 0.0f ? 1u : 0u, 1);
+    __syncthreads();
+    // ---- shared words owned by this wave (the last wave adds QJL bits and gamma)
+    {
+      const int of = cl[2] & 0xFFFF, oe = cl[2] >> 16;
+      const float *rrow = rtile + lane * a.rs;
+      for (int k = of; k < oe; ++k) {
+        if (k >= dfirst && k < dend) continue;
+        uint32_t word = bwrow[k];
+        if (m > 0) {
+          const int lo_bit = 32 * k, hi_bit = lo_bit + 32;
+          const int jb = max(0, lo_bit - code_bits), je = min(m, hi_bit - code_bits);
+          for (int j = jb; j < je; ++j) {
+            float dot = 0.0f;
+            for (int i = 0; i < d_eff; ++i) dot = fmaf(S[j * d_eff + i], rrow[i], dot);
+            word |= (dot >= 0.0f ? 1u : 0u) << (code_bits + j - lo_bit);
+          }
+          if (k == W - 1) {
+            float g2 = 0.0f;
+            for (int i = 0; i < d_eff; ++i) g2 = fmaf(rrow[i], rrow[i], g2);
+            word |= half_bits_rne(sqrtf(g2)) << 16;
+          }
+        }
+        dst[(int64_t)k * 64] = valid ? word : 0u;
+      }
     }
-    ghalf = half_bits_rne(sqrtf(g2)) << 16;
-  }
-  while (bw.wcur < W) {
-    if (bw.wcur == W - 1) bw.lo |= ghalf;
-    bw.store_word();
+    // The x tile was last read by the MFMAs, which every wave finished before
+    // the barrier above; the y/code tile is rewritten only after the barrier
+    // that follows the next x store.  No further barrier is needed here.
   }
 }
 
@@ -422,10 +601,11 @@ template <int G>
 __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
   extern __shared__ float smem[];
   constexpr int GP = G <= 4 ? 4 : 8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + hkv;
-  const DevHead *hd = a.heads + ch;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d, d_eff = hd->d_eff, m = hd->m, W = hd->W, n_cent = hd->n_cent;
   const float *R = (const float *)(a.blob + hd->off_R);
 
@@ -453,7 +633,7 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
   }
   __syncthreads();
   if (m > 0) {
-    const float *S = (const float *)(a.blob + hd->off_S);
+    const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
     for (int k = threadIdx.x; k < m * GP; k += blockDim.x) {
       const int j = k / GP, g = k % GP;
       float acc = 0.0f;
@@ -467,7 +647,7 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
   }
   __syncthreads();
 
-  const DevCoord *coords = (const DevCoord *)(a.blob + hd->off_coord);
+  const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
   const uint32_t *slot = a.kpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
   const int tile_begin = blockIdx.x * a.tiles_per_block;
   const int tile_end = min(a.n_tiles, tile_begin + a.tiles_per_block);
@@ -481,7 +661,7 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
     int cur = -1;
     uint32_t lo = 0, hi = 0;
     for (int i = 0; i < d; ++i) {
-      const DevCoord cd = coords[i];
+      const DevCoord cd = load_coord(coords + i);
       if (cd.width == 0) continue;
       const int w = cd.bit_off >> 5;
       if (w != cur) {
@@ -563,7 +743,7 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + hkv;
-  const DevHead *hd = a.heads + ch;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d, W = hd->W, n_cent = hd->n_cent;
   const int64_t tb = (int64_t)chunk * ATT_CHUNK;
   const int64_t te = min(a.n_tokens, tb + ATT_CHUNK);
@@ -667,7 +847,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
   const int b = bq / a.n_q_heads, hq = bq % a.n_q_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int ch = a.first_head + b * a.cbs + hq / G;
-  const DevHead *hd = a.heads + ch;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d;
   float *out = a.out + (int64_t)bq * d;
   if (a.n_tokens == 0) {
@@ -720,12 +900,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + h;
-  const DevHead *hd = a.heads + ch;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d, W = hd->W, m = hd->m, d_eff = hd->d_eff;
   const uint32_t *slot = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h;
-  const DevCoord *coords = (const DevCoord *)(a.blob + hd->off_coord);
+  const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
   const float *cent = (const float *)(a.blob + hd->off_cent);
-  const float *S = (const float *)(a.blob + hd->off_S);
+  const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
   const float *R = (const float *)(a.blob + hd->off_R);
   const int64_t tbase = (int64_t)blockIdx.x * 16;
   auto word = [&](int64_t t, int w) -> uint32_t {
@@ -736,7 +916,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     const int64_t t = tbase + tt;
     float v = 0.0f;
     if (t < a.n_tokens) {
-      const DevCoord cd = coords[i];
+      const DevCoord cd = load_coord(coords + i);
       if (cd.width) {
         const uint32_t f = __builtin_amdgcn_alignbit(word(t, (cd.bit_off >> 5) + 1), word(t, cd.bit_off >> 5),
                                                     cd.bit_off & 31) & ((1u << cd.width) - 1u);
@@ -826,8 +1006,15 @@ extern "C" sq_status sq_calib_upload(sq_calib *c, sq_stream stream) {
 }
 
 template <int D, bool F32>
-static void launch_compress(dim3 grid, dim3 block, size_t lds, hipStream_t s, const CompressArgs &a) {
-  hipLaunchKernelGGL((compress_kernel<D, F32>), grid, block, lds, s, a);
+static void launch_compress(dim3 grid, size_t lds, hipStream_t s, const CompressArgs &a) {
+  hipLaunchKernelGGL((compress_kernel<D, F32>), grid, dim3(2 * D), lds, s, a);
+}
+
+static int device_cu_count() {
+  int dev = 0, v = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  return v;
 }
 
 extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
@@ -849,32 +1036,35 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   const int esz = dt == SQ_F32 ? 4 : 2;
   if (((uintptr_t)x % 16) || (xs_token * esz) % 16 || (xs_head * esz) % 16 || (xs_batch * esz) % 16)
     return fail(SQ_ERR_ARG, "sq_compress: x and its strides must be 16-byte aligned");
-  if (xs_token < c->heads[first_head].d) return fail(SQ_ERR_ARG, "sq_compress: xs_token < head_dim");
-  if (n_tokens > ((int64_t)1 << 36) / 64) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many tokens");
   const int d = c->heads[first_head].d;
-  // LDS: thresholds, signal centroids, per-wave [64][33] + [64][rstride]
+  if (xs_token < d) return fail(SQ_ERR_ARG, "sq_compress: xs_token < head_dim");
+  if (n_tokens > ((int64_t)1 << 36)) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many tokens");
+  // LDS: thresholds | signal centroids | x tile | y/code tile | residual tile
   int max_thr = 1, max_csig = 0, max_deff = 1;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
     for (int h = 0; h < n_heads; ++h) {
-      const HeadCal &hc = c->heads[first_head + bb * calib_batch_stride + h];
-      max_thr = std::max(max_thr, hc.n_thr);
+      const int k = first_head + bb * calib_batch_stride + h;
+      const HeadCal &hc = c->heads[k];
+      max_thr = std::max(max_thr, hc.n_cent);
       if (hc.m > 0) {
-        max_csig = std::max(max_csig, c->host_desc[first_head + bb * calib_batch_stride + h].n_cent_sig);
+        max_csig = std::max(max_csig, c->host_desc[k].n_cent_sig);
         max_deff = std::max(max_deff, hc.d_eff);
       }
     }
     if (calib_batch_stride == 0) break;  // every batch entry uses the same heads
   }
   CompressArgs a{};
-  a.rstride = (max_deff % 2 == 0) ? max_deff + 1 : max_deff + 2;
+  a.ys = d + 1;
+  a.rs = (max_deff % 2 == 0) ? max_deff + 1 : max_deff + 2;
+  const int xs_floats = dt == SQ_F32 ? 64 * (d + 4) : 64 * (d + 8) / 2;
   a.lds_cent_off = (max_thr + 3) & ~3;
-  a.lds_wave_off = a.lds_cent_off + ((max_csig + 3) & ~3);
-  a.lds_wave_floats = 64 * 33 + 64 * a.rstride;
-  const int limit = device_lds_limit();
-  int nw = 4;
-  while (nw > 1 && (size_t)(a.lds_wave_off + nw * a.lds_wave_floats) * 4 > (size_t)limit) nw >>= 1;
-  const size_t lds = (size_t)(a.lds_wave_off + nw * a.lds_wave_floats) * 4;
-  if (lds > (size_t)limit)
+  a.lds_x_off = a.lds_cent_off + ((max_csig + 3) & ~3);
+  a.lds_y_off = a.lds_x_off + xs_floats;
+  a.lds_r_off = a.lds_y_off + 64 * a.ys;
+  a.bws = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
+  a.lds_b_off = a.lds_r_off + 64 * a.rs;
+  const size_t lds = (size_t)(a.lds_b_off + 64 * a.bws) * 4;
+  if (lds > (size_t)device_lds_limit())
     return fail(SQ_ERR_UNSUPPORTED, "sq_compress: calibration tables exceed the LDS of one workgroup");
   a.heads = c->dev_heads;
   a.blob = (const uint8_t *)c->dev_blob;
@@ -886,15 +1076,20 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   a.first_head = first_head;
   a.cbs = calib_batch_stride;
   a.n_tiles = (int)((n_tokens + 63) / 64);
-  dim3 grid((a.n_tiles + nw - 1) / nw, n_heads, batch), block(64 * nw);
+  const int gz = calib_batch_stride ? batch : 1;
+  a.items = calib_batch_stride ? a.n_tiles : (int)std::min<int64_t>((int64_t)batch * a.n_tiles, INT32_MAX);
+  // enough resident workgroups to keep every CU busy; each walks many tiles
+  const int64_t want = (int64_t)device_cu_count() * (d >= 256 ? 1 : 2) * 2;
+  int gx = (int)std::max<int64_t>(1, std::min<int64_t>(a.items, (want + (int64_t)n_heads * gz - 1) / ((int64_t)n_heads * gz)));
+  dim3 grid(gx, n_heads, gz);
   if (grid.y > 65535 || grid.z > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many heads or batch entries");
   hipStream_t s = (hipStream_t)stream;
   const bool f32 = dt == SQ_F32;
   switch (d) {
-    case 32:  f32 ? launch_compress<32, true>(grid, block, lds, s, a) : launch_compress<32, false>(grid, block, lds, s, a); break;
-    case 64:  f32 ? launch_compress<64, true>(grid, block, lds, s, a) : launch_compress<64, false>(grid, block, lds, s, a); break;
-    case 128: f32 ? launch_compress<128, true>(grid, block, lds, s, a) : launch_compress<128, false>(grid, block, lds, s, a); break;
-    case 256: f32 ? launch_compress<256, true>(grid, block, lds, s, a) : launch_compress<256, false>(grid, block, lds, s, a); break;
+    case 32:  f32 ? launch_compress<32, true>(grid, lds, s, a) : launch_compress<32, false>(grid, lds, s, a); break;
+    case 64:  f32 ? launch_compress<64, true>(grid, lds, s, a) : launch_compress<64, false>(grid, lds, s, a); break;
+    case 128: f32 ? launch_compress<128, true>(grid, lds, s, a) : launch_compress<128, false>(grid, lds, s, a); break;
+    case 256: f32 ? launch_compress<256, true>(grid, lds, s, a) : launch_compress<256, false>(grid, lds, s, a); break;
     default: return fail(SQ_ERR_UNSUPPORTED, "sq_compress: head_dim");
   }
   return launched(fn);
