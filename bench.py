@@ -181,7 +181,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "compress_kernel<128,bf16> (K and V launches)",
                      "achieved": comp_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": comp_gbps / HBM_PEAK_GBPS, "traffic": None},
-        "roofline_scores": {"bound": "hbm", "kernel": "scores_kernel<4>",
+        "roofline_scores": {"bound": "hbm", "kernel": "scores_kernel<4,4> (4x4x4 bf16 MFMA)",
                             "achieved": gbps(bytes_sc, ms_sc), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": gbps(bytes_sc, ms_sc) / HBM_PEAK_GBPS,
                             "traffic": None},

@@ -31,6 +31,9 @@ struct DevHead {
   int64_t off_cent;     // float [n_cent]  centroids * sigma_i
   int64_t off_S;        // float [m][d_eff] QJL sketch
   int64_t off_wstart;   // int32 [W]: first coordinate reaching into word k | count << 16
+  int64_t off_desc;     // uint32 [d]: bit offset | width << 12 | centroid base << 16
+  int64_t off_lutp;     // uint32 [n_cent]: each centroid as bf16 hi | bf16 lo << 16
+                        // (hi + lo reproduces the fp32 centroid to ~2^-17)
   int64_t off_chunks;   // int32 [d/32][4 + d] per wave of the compress kernel:
                         //   [0] number of chunks, [1] first bit | end bit << 16 of
                         //   the wave's contiguous code range, [2] first | end of
@@ -40,6 +43,6 @@ struct DevHead {
 };
 
 static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
-static_assert(sizeof(DevHead) == 112, "DevHead layout");
+static_assert(sizeof(DevHead) == 128, "DevHead layout");
 
 }  // namespace sq

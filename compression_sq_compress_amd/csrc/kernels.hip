@@ -113,6 +113,8 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.off_cent = off;    off = align256(off + sizeof(float) * std::max(1, hc.n_cent));
     D.off_S = off;       off = align256(off + sizeof(float) * std::max(1, hc.m * hc.d_eff));
     D.off_wstart = off;  off = align256(off + sizeof(int32_t) * std::max(1, hc.W));
+    D.off_desc = off;    off = align256(off + sizeof(uint32_t) * d);
+    D.off_lutp = off;    off = align256(off + sizeof(uint32_t) * std::max(1, hc.n_cent));
     D.off_chunks = off;  off = align256(off + sizeof(int32_t) * (d / 32) * (4 + d));
   }
   std::vector<uint8_t> img(off, 0);
@@ -146,8 +148,11 @@ sq_status upload_tables(sq_calib *c, void *stream) {
               F[((((size_t)s * MB + mb) * KS + ks) * 64 + l) * 8 + e] = parts[s];
           }
     DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
-    for (int i = 0; i < d; ++i)
+    uint32_t *Dd = (uint32_t *)(img.data() + D.off_desc);
+    for (int i = 0; i < d; ++i) {
       Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
+      Dd[i] = (uint32_t)hc.bit_off[i] | ((uint32_t)hc.widths[i] << 12) | ((uint32_t)hc.cent_base[i] << 16);
+    }
     // thresholds in breadth-first order: node n (depth k, position p = n - 2^k)
     // of coordinate i holds sorted threshold (2p + 1) * 2^(b - 1 - k) - 1
     {
@@ -165,6 +170,18 @@ sq_status upload_tables(sq_calib *c, void *stream) {
       }
     }
     if (hc.n_cent) std::memcpy(img.data() + D.off_cent, hc.cent.data(), sizeof(float) * hc.n_cent);
+    {
+      uint32_t *P = (uint32_t *)(img.data() + D.off_lutp);
+      for (int k = 0; k < hc.n_cent; ++k) {
+        const float v = hc.cent[k];
+        const uint16_t hi = f32_to_bf16_rne(v);
+        float vh;
+        uint32_t u = (uint32_t)hi << 16;
+        std::memcpy(&vh, &u, 4);
+        const uint16_t lo = f32_to_bf16_rne(v - vh);
+        P[k] = (uint32_t)hi | ((uint32_t)lo << 16);
+      }
+    }
     if (hc.m) std::memcpy(img.data() + D.off_S, hc.S.data(), sizeof(float) * hc.m * hc.d_eff);
     int32_t *ws = (int32_t *)(img.data() + D.off_wstart);
     for (int k = 0; k < hc.W; ++k) {
@@ -572,14 +589,22 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
 
 // ------------------------------------------------------------------ scores
 //
-// A workgroup serves one (batch, KV head) and a contiguous run of 64-token
-// tiles.  Prologue: q~ = R q for the group's query heads and w = S q~[:d_eff]
-// (both to LDS), and the head's centroid table to LDS.  Main loop: lane =
-// token; the tile's record words are staged in LDS (lane-private rows), the
-// lane walks the coordinates in order with a two-word window, looks up the
-// centroid and accumulates q~_i * C_i[code] for every query head of the group
-// (one LDS broadcast read fetches q~_i for all of them), then adds the QJL
-// term sqrt(pi/2)/m * gamma * sum_j w_j (2 z_j - 1).
+// A workgroup serves one (batch, KV head) and a run of 64-token tiles; each
+// of its 4 waves takes NT tiles per pass, lane = token.
+// Prologue: q~ = R q for the query heads of the group (fp32), w = S q~[:d_eff]
+// scaled by sqrt(pi/2)/m, and the MFMA A operands built from q~ (below); the
+// head's centroid table, as bf16 hi/lo pairs, goes to LDS.
+// Pass: the NT tiles' record words are staged in lane-private LDS rows.  The
+// lane walks the coordinates in order (wave-uniform bit positions, a two-word
+// window per tile), fetches the pair (hi, lo) of C_i[code] and feeds it to
+// v_mfma_f32_4x4x4_16b_bf16 as the B operand: in block b, lane 4b+n supplies
+// column n = its own token.  The A operand rows are the query heads: for a
+// coordinate pair (i, i+1) the k-slots are (hi_i, lo_i, hi_i+1, lo_i+1) x
+// (qhi_i, qhi_i, qhi_i+1, qhi_i+1); every four coordinates one more MFMA adds
+// (hi_i..hi_i+3) x (qlo_i..qlo_i+3).  So each token's score is accumulated
+// for 4 query heads per MFMA, exact to ~2^-16 relative per term, and lands
+// in the token's own lane (register m = head m), where the QJL term
+// gamma * sum_j w_j (2 z_j - 1) is added before one coalesced store per head.
 
 struct ScoresArgs {
   const DevHead *heads;
@@ -593,116 +618,217 @@ struct ScoresArgs {
   int n_q_heads, n_kv_heads;
   int q_f32;
   int n_tiles, tiles_per_block;
-  int lds_cent_off, lds_w_off, lds_rec_off;  // floats
-  int max_W;
+  int lds_lut_off, lds_aq_off, lds_w_off, lds_rec_off;  // floats
+  int rec_tile;                                         // words per staged tile
 };
 
-template <int G>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(uint2 a, uint2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_pair(uint16_t x) { return (uint32_t)x | ((uint32_t)x << 16); }
+
+template <int G, int NT>
 __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
   extern __shared__ float smem[];
-  constexpr int GP = G <= 4 ? 4 : 8;
-  const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+  constexpr int GR = (G + 3) / 4, GP = 4 * GR;
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + hkv;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d, d_eff = hd->d_eff, m = hd->m, W = hd->W, n_cent = hd->n_cent;
-  const float *R = (const float *)(a.blob + hd->off_R);
+  const int code_bits = hd->code_bits;
+  const int NP = d / 2, NQ = d / 4;
+  uint32_t *lut = (uint32_t *)(smem + a.lds_lut_off);
+  uint2 *aq = (uint2 *)(smem + a.lds_aq_off);
+  float *wq = smem + a.lds_w_off;
 
-  float *qt = smem;                       // [d][GP]   q~
-  float *wq = smem + a.lds_w_off;         // [m][GP]   S q~
-  float *cent = smem + a.lds_cent_off;    // [n_cent]
-  uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off) + wave * a.max_W * 64;
-
-  // raw queries to the centroid area first (it is loaded afterwards)
-  float *qraw = cent;
-  const int64_t qbase = ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * d;
-  for (int k = threadIdx.x; k < G * d; k += blockDim.x)
-    qraw[k] = a.q_f32 ? ((const float *)a.q)[qbase + k]
-                      : bf16_to_f32(((const uint16_t *)a.q)[qbase + k]);
-  __syncthreads();
-  for (int k = threadIdx.x; k < GP * d; k += blockDim.x) {
-    const int g = k / d, i = k % d;
-    float acc = 0.0f;
-    if (g < G) {
-      const float *Ri = R + (size_t)i * d;
-      const float *qg = qraw + g * d;
-      for (int j = 0; j < d; ++j) acc = fmaf(Ri[j], qg[j], acc);
-    }
-    qt[i * GP + g] = acc;
-  }
-  __syncthreads();
-  if (m > 0) {
-    const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
-    for (int k = threadIdx.x; k < m * GP; k += blockDim.x) {
-      const int j = k / GP, g = k % GP;
-      float acc = 0.0f;
-      for (int i = 0; i < d_eff; ++i) acc = fmaf(S[j * d_eff + i], qt[i * GP + g], acc);
-      wq[j * GP + g] = acc;
-    }
-  }
+  // ---- prologue (scratch aliases the record area)
   {
-    const float *gc = (const float *)(a.blob + hd->off_cent);
-    for (int k = threadIdx.x; k < n_cent; k += blockDim.x) cent[k] = gc[k];
-  }
-  __syncthreads();
-
-  const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
-  const uint32_t *slot = a.kpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
-  const int tile_begin = blockIdx.x * a.tiles_per_block;
-  const int tile_end = min(a.n_tiles, tile_begin + a.tiles_per_block);
-  for (int tile = tile_begin + wave; tile < tile_end; tile += nwaves) {
-    const uint32_t *src = slot + (int64_t)tile * W * 64 + lane;
-    for (int w = 0; w < W; ++w) rec[w * 64 + lane] = src[w * 64];
-    rec[W * 64 + lane] = 0u;
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-    int cur = -1;
-    uint32_t lo = 0, hi = 0;
-    for (int i = 0; i < d; ++i) {
-      const DevCoord cd = load_coord(coords + i);
-      if (cd.width == 0) continue;
-      const int w = cd.bit_off >> 5;
-      if (w != cur) {
-        lo = rec[w * 64 + lane];
-        hi = rec[(w + 1) * 64 + lane];
-        cur = w;
+    float *qraw = smem + a.lds_rec_off;  // [G][d]
+    float *qt = qraw + G * d;            // [GP][d]
+    const int64_t qbase = ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * d;
+    for (int k = threadIdx.x; k < G * d; k += blockDim.x)
+      qraw[k] = a.q_f32 ? ((const float *)a.q)[qbase + k]
+                        : bf16_to_f32(((const uint16_t *)a.q)[qbase + k]);
+    __syncthreads();
+    const float *R = (const float *)(a.blob + hd->off_R);
+    for (int k = threadIdx.x; k < GP * d; k += blockDim.x) {
+      const int g = k / d, i = k % d;
+      float acc = 0.0f;
+      if (g < G) {
+        const float *Ri = R + (size_t)i * d;
+        const float *qg = qraw + g * d;
+        for (int j = 0; j < d; ++j) acc = fmaf(Ri[j], qg[j], acc);
       }
-      const uint32_t field = __builtin_amdgcn_alignbit(hi, lo, cd.bit_off & 31) & ((1u << cd.width) - 1u);
-      const float c = cent[cd.cent_base + field];
-      float qv[GP];
-      {
-        const float4 q0 = *(const float4 *)(qt + i * GP);
-        qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w;
-        if constexpr (GP > 4) {
-          const float4 q1 = *(const float4 *)(qt + i * GP + 4);
-          qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
+      qt[g * d + i] = acc;
+    }
+    __syncthreads();
+    if (m > 0) {
+      const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
+      const float sc = hd->qjl_scale;
+      for (int k = threadIdx.x; k < m * GP; k += blockDim.x) {
+        const int j = k / GP, g = k % GP;
+        float acc = 0.0f;
+        for (int i = 0; i < d_eff; ++i) acc = fmaf(S[j * d_eff + i], qt[g * d + i], acc);
+        wq[k] = sc * acc;
+      }
+    }
+    for (int k = threadIdx.x; k < GR * (NP + NQ) * 4; k += blockDim.x) {
+      const int mm = k & 3, rest = k >> 2;
+      const int r = rest / (NP + NQ), e = rest % (NP + NQ);
+      const float *qh = qt + (4 * r + mm) * d;
+      uint2 v;
+      if (e < NP) {
+        v.x = bf16_pair(f32_to_bf16_rne(qh[2 * e]));
+        v.y = bf16_pair(f32_to_bf16_rne(qh[2 * e + 1]));
+      } else {
+        uint16_t lo[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float x = qh[4 * (e - NP) + t];
+          lo[t] = f32_to_bf16_rne(x - bf16_to_f32(f32_to_bf16_rne(x)));
+        }
+        v.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+        v.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+      }
+      aq[k] = v;
+    }
+    const uint32_t *gl = (const uint32_t *)(a.blob + hd->off_lutp);
+    for (int k = threadIdx.x; k < n_cent; k += blockDim.x) lut[k] = gl[k];
+    __syncthreads();
+  }
+
+  const uint32_t *slot = a.kpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
+  uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off) + wave * NT * a.rec_tile;
+  const int tb = blockIdx.x * a.tiles_per_block;
+  const int te = min(a.n_tiles, tb + a.tiles_per_block);
+  const uint2 *aqm = aq + (lane & 3);
+
+  for (int tp = tb + wave * NT; tp < te; tp += 4 * NT) {
+    const int ntl = min(NT, te - tp);
+    // ---- stage the records: direct global -> LDS loads (lane l's word lands
+    // in column l of row w), all issued before the first wait; row W is zero
+#pragma unroll
+    for (int tq = 0; tq < NT; ++tq) {
+      if (tq < ntl) {
+        const uint32_t *src = slot + (int64_t)(tp + tq) * W * 64 + lane;
+        uint32_t *dstr = rec + tq * a.rec_tile;
+        for (int w = 0; w < W; ++w)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + w * 64),
+                                           (__attribute__((address_space(3))) void *)(dstr + w * 64), 4, 0, 0);
+        dstr[W * 64 + lane] = 0u;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged words are in LDS
+    f32x4 acc[NT][GR];
+#pragma unroll
+    for (int tq = 0; tq < NT; ++tq)
+#pragma unroll
+      for (int r = 0; r < GR; ++r) acc[tq][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int cur = -1;
+    uint32_t wlo[NT], whi[NT];
+#pragma unroll
+    for (int tq = 0; tq < NT; ++tq) wlo[tq] = whi[tq] = 0u;
+    // coordinate descriptors, 16 at a time (one scalar load), next block prefetched
+    const SQ_CONST uint32_t *dsc = cptr<uint32_t>(a.blob + hd->off_desc);
+    uint32_t dnext[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) dnext[c] = dsc[c];
+    for (int q16 = 0; q16 < d / 16; ++q16) {
+      uint32_t dcur[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) dcur[c] = dnext[c];
+      if (q16 + 1 < d / 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) dnext[c] = dsc[16 * (q16 + 1) + c];
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int qd = 4 * q16 + qq;
+        uint32_t dv[4][NT];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t e = dcur[4 * qq + c];
+          const int bo = e & 0xFFF, wd = (e >> 12) & 0xF, cb = e >> 16;
+          if (wd == 0) {
+#pragma unroll
+            for (int tq = 0; tq < NT; ++tq) dv[c][tq] = 0u;
+            continue;
+          }
+          const int w = bo >> 5;
+          if (w != cur) {
+#pragma unroll
+            for (int tq = 0; tq < NT; ++tq) {
+              wlo[tq] = rec[tq * a.rec_tile + w * 64 + lane];
+              whi[tq] = rec[tq * a.rec_tile + (w + 1) * 64 + lane];
+            }
+            cur = w;
+          }
+          const uint32_t mask = (1u << wd) - 1u;
+#pragma unroll
+          for (int tq = 0; tq < NT; ++tq) {
+            const uint32_t f = __builtin_amdgcn_alignbit(whi[tq], wlo[tq], bo & 31) & mask;
+            dv[c][tq] = lut[cb + f];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < GR; ++r) {
+          const uint2 a0 = aqm[(r * (NP + NQ) + 2 * qd) * 4];
+          const uint2 a1 = aqm[(r * (NP + NQ) + 2 * qd + 1) * 4];
+          const uint2 ac = aqm[(r * (NP + NQ) + NP + qd) * 4];
+#pragma unroll
+          for (int tq = 0; tq < NT; ++tq) {
+            acc[tq][r] = mfma4(a0, make_uint2(dv[0][tq], dv[1][tq]), acc[tq][r]);
+            acc[tq][r] = mfma4(a1, make_uint2(dv[2][tq], dv[3][tq]), acc[tq][r]);
+            const uint2 bh = make_uint2(__builtin_amdgcn_perm(dv[1][tq], dv[0][tq], 0x05040100u),
+                                        __builtin_amdgcn_perm(dv[3][tq], dv[2][tq], 0x05040100u));
+            acc[tq][r] = mfma4(ac, bh, acc[tq][r]);
+          }
         }
       }
-#pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = fmaf(qv[g], c, acc[g]);
     }
-    if (m > 0) {
-      float qa[G];
+    // ---- QJL term and stores
 #pragma unroll
-      for (int g = 0; g < G; ++g) qa[g] = 0.0f;
-      for (int j = 0; j < m; ++j) {
-        const int pos = hd->code_bits + j;
-        const uint32_t bit = (rec[(pos >> 5) * 64 + lane] >> (pos & 31)) & 1u;
-        const float sgn = bit ? 1.0f : -1.0f;
+    for (int tq = 0; tq < NT; ++tq) {
+      if (tq >= ntl) continue;
+      const uint32_t *rr = rec + tq * a.rec_tile + lane;
+      float qa[GP];
 #pragma unroll
-        for (int g = 0; g < G; ++g) qa[g] = fmaf(sgn, wq[j * GP + g], qa[g]);
+      for (int g = 0; g < GP; ++g) qa[g] = 0.0f;
+      float gm = 0.0f;
+      if (m > 0) {
+        for (int j = 0; j < m; ++j) {
+          const int pos = code_bits + j;
+          const float sgn = ((rr[(pos >> 5) * 64] >> (pos & 31)) & 1u) ? 1.0f : -1.0f;
+#pragma unroll
+          for (int g = 0; g < GP; g += 4) {
+            const float4 wv = *(const float4 *)(wq + j * GP + g);
+            qa[g] = fmaf(sgn, wv.x, qa[g]);
+            qa[g + 1] = fmaf(sgn, wv.y, qa[g + 1]);
+            qa[g + 2] = fmaf(sgn, wv.z, qa[g + 2]);
+            qa[g + 3] = fmaf(sgn, wv.w, qa[g + 3]);
+          }
+        }
+        gm = half_bits_to_f32(rr[(W - 1) * 64] >> 16);
       }
-      const float gm = half_bits_to_f32(rec[(W - 1) * 64 + lane] >> 16) * hd->qjl_scale;
+      const int64_t t = (int64_t)(tp + tq) * 64 + lane;
+      if (t < a.n_tokens) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = fmaf(gm, qa[g], acc[g]);
-    }
-    const int64_t t = (int64_t)tile * 64 + lane;
-    if (t < a.n_tokens) {
+        for (int r = 0; r < GR; ++r)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-        a.scores[((int64_t)b * a.n_q_heads + (int64_t)hkv * G + g) * a.n_tokens + t] = acc[g];
+          for (int mm = 0; mm < 4; ++mm) {
+            const int g = 4 * r + mm;
+            if (g < G)
+              a.scores[((int64_t)b * a.n_q_heads + (int64_t)hkv * G + g) * a.n_tokens + t] =
+                  fmaf(gm, qa[g], acc[tq][r][mm]);
+          }
+      }
     }
   }
 }
@@ -1095,9 +1221,16 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   return launched(fn);
 }
 
+template <int G, int NT>
+static void launch_scores(dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
+  hipLaunchKernelGGL((scores_kernel<G, NT>), grid, dim3(256), lds, s, a);
+}
+
 template <int G>
-static void launch_scores(dim3 grid, dim3 block, size_t lds, hipStream_t s, const ScoresArgs &a) {
-  hipLaunchKernelGGL((scores_kernel<G>), grid, block, lds, s, a);
+static void launch_scores_nt(int nt, dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
+  if (nt == 4) launch_scores<G, 4>(grid, lds, s, a);
+  else if (nt == 2) launch_scores<G, 2>(grid, lds, s, a);
+  else launch_scores<G, 1>(grid, lds, s, a);
 }
 
 extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_batch_stride, int batch,
@@ -1119,6 +1252,7 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
   if (!q || !kpacked || !scores) return fail(SQ_ERR_ARG, "sq_scores: NULL pointer");
   st = check_slots(kc, n_tokens, n_kv_heads, batch, ps_batch, ps_head, fn);
   if (st != SQ_OK) return st;
+  if (n_tokens > ((int64_t)1 << 36)) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: too many tokens");
   const int d = kc->heads[first_head].d;
   int max_cent = 1, max_m = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
@@ -1129,16 +1263,22 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
     }
     if (calib_batch_stride == 0) break;
   }
-  const int GP = G <= 4 ? 4 : 8;
+  const int GR = (G + 3) / 4, GP = 4 * GR;
   ScoresArgs a{};
-  a.lds_w_off = d * GP;
-  a.lds_cent_off = a.lds_w_off + std::max(1, max_m) * GP;
-  a.lds_rec_off = a.lds_cent_off + std::max(max_cent, G * d);
-  a.lds_rec_off = (a.lds_rec_off + 3) & ~3;
-  a.max_W = kc->W_max + 1;
-  const int nw = 4;
-  const size_t lds = (size_t)(a.lds_rec_off + nw * a.max_W * 64) * 4;
-  if (lds > (size_t)device_lds_limit()) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: tables exceed LDS");
+  a.lds_lut_off = 0;
+  a.lds_aq_off = (max_cent + 3) & ~3;                       // 16-byte aligned
+  a.lds_w_off = a.lds_aq_off + 2 * GR * (d / 2 + d / 4) * 4;
+  a.lds_rec_off = a.lds_w_off + ((std::max(1, max_m) * GP + 3) & ~3);
+  a.rec_tile = (kc->W_max + 1) * 64;
+  const int scratch = (G + GP) * d;                          // prologue floats
+  const int limit = device_lds_limit();
+  int nt = 4;
+  auto lds_for = [&](int n) {
+    return (size_t)(a.lds_rec_off + std::max(scratch, 4 * n * a.rec_tile)) * 4;
+  };
+  while (nt > 1 && lds_for(nt) > (size_t)std::min(limit, 72 * 1024)) nt >>= 1;
+  const size_t lds = lds_for(nt);
+  if (lds > (size_t)limit) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: tables exceed LDS");
   a.heads = kc->dev_heads;
   a.blob = (const uint8_t *)kc->dev_blob;
   a.q = q;
@@ -1152,23 +1292,26 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
   a.n_kv_heads = n_kv_heads;
   a.q_f32 = qdt == SQ_F32;
   a.n_tiles = (int)((n_tokens + 63) / 64);
-  // enough workgroups to fill the chip: aim at >= 2048 in total
+  // workgroups: enough to fill the chip, each a multiple of one pass (4 waves x nt tiles)
   const int64_t pairs = (int64_t)batch * n_kv_heads;
-  int blocks_t = (int)std::min<int64_t>(a.n_tiles, std::max<int64_t>(1, (2048 + pairs - 1) / pairs));
+  const int64_t want = (int64_t)device_cu_count() * 8;
+  int blocks_t = (int)std::min<int64_t>((a.n_tiles + 4 * nt - 1) / (4 * nt),
+                                        std::max<int64_t>(1, (want + pairs - 1) / pairs));
   a.tiles_per_block = (a.n_tiles + blocks_t - 1) / blocks_t;
+  a.tiles_per_block = ((a.tiles_per_block + 4 * nt - 1) / (4 * nt)) * (4 * nt);
   blocks_t = (a.n_tiles + a.tiles_per_block - 1) / a.tiles_per_block;
-  dim3 grid(blocks_t, n_kv_heads, batch), block(64 * nw);
+  dim3 grid(blocks_t, n_kv_heads, batch);
   if (grid.z > 65535 || grid.y > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: grid too large");
   hipStream_t s = (hipStream_t)stream;
   switch (G) {
-    case 1: launch_scores<1>(grid, block, lds, s, a); break;
-    case 2: launch_scores<2>(grid, block, lds, s, a); break;
-    case 3: launch_scores<3>(grid, block, lds, s, a); break;
-    case 4: launch_scores<4>(grid, block, lds, s, a); break;
-    case 5: launch_scores<5>(grid, block, lds, s, a); break;
-    case 6: launch_scores<6>(grid, block, lds, s, a); break;
-    case 7: launch_scores<7>(grid, block, lds, s, a); break;
-    case 8: launch_scores<8>(grid, block, lds, s, a); break;
+    case 1: launch_scores_nt<1>(nt, grid, lds, s, a); break;
+    case 2: launch_scores_nt<2>(nt, grid, lds, s, a); break;
+    case 3: launch_scores_nt<3>(nt, grid, lds, s, a); break;
+    case 4: launch_scores_nt<4>(nt, grid, lds, s, a); break;
+    case 5: launch_scores_nt<5>(nt, grid, lds, s, a); break;
+    case 6: launch_scores_nt<6>(nt, grid, lds, s, a); break;
+    case 7: launch_scores_nt<7>(nt, grid, lds, s, a); break;
+    case 8: launch_scores_nt<8>(nt, grid, lds, s, a); break;
   }
   return launched(fn);
 }
