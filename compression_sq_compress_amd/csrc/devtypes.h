@@ -15,31 +15,38 @@ struct DevCoord {
   int32_t cent_base;
 };
 
+// Compress work plan.  The kernel's d/32 waves each own a contiguous range of
+// eigen-coordinates; a range is cut into chunks of <= 8 coordinates of equal
+// width.  Wave header w (16 words): [0] chunks, [1] first bit | end bit << 16
+// of the wave's code range, [2] first | end of the shared record words the
+// wave stores, [3] first | end of the words it stores straight from its bit
+// window, [4] index of its first chunk.  Chunk (16 words): [0..7] root
+// threshold of each slot (fp32 bits; +inf in unused slots), [8] tree base,
+// [9] first coordinate, [10] count, [11] width b, [12] number of signal
+// coordinates (residual needed), [13] signal-centroid base.  Slot c's
+// threshold tree holds node n (1 <= n < 2^b, children 2n, 2n+1) at tree base
+// + c * 2^b + n - 1, and its signal centroids at signal base + c * 2^b + code.
+constexpr int PLAN_WORDS = 16;
+
 struct DevHead {
   int32_t d, d_eff, m, W;
-  int32_t code_bits, n_thr, n_cent, has_gamma;
+  int32_t code_bits, n_tree, n_cent, has_gamma;
   float qjl_scale;      // sqrt(pi/2) / m  (0 when m == 0)
-  int32_t n_cent_sig;   // centroids of the signal coordinates (the first d_eff)
-  int32_t pad1, pad2;
+  int32_t n_csig;       // floats in the signal-centroid table of the plan
+  int32_t n_chunks, pad2;
   int64_t off_R;        // float [d][d], row i = eigenvector i (y = R x)
   int64_t off_Rfrag;    // bf16 [3][d/32][d/16][64][8]: hi/mid/lo split of R in
                         // MFMA 32x32x16 A-operand order (see compress kernel)
   int64_t off_coord;    // DevCoord [d]
-  int64_t off_thr;      // float [n_cent]  thresholds * sigma_i of coordinate i in
-                        // breadth-first (Eytzinger) order at [cent_base_i + 1,
-                        // cent_base_i + 2^b_i): node n has children 2n, 2n+1
+  int64_t off_tree;     // float [n_tree]  thresholds * sigma_i, per chunk of the
+                        // compress plan, breadth-first (see PLAN_WORDS)
   int64_t off_cent;     // float [n_cent]  centroids * sigma_i
   int64_t off_S;        // float [m][d_eff] QJL sketch
-  int64_t off_wstart;   // int32 [W]: first coordinate reaching into word k | count << 16
+  int64_t off_plan;     // uint32 [d/32 + n_chunks + 1][PLAN_WORDS] compress plan
   int64_t off_desc;     // uint32 [d]: bit offset | width << 12 | centroid base << 16
   int64_t off_lutp;     // uint32 [n_cent]: each centroid as bf16 hi | bf16 lo << 16
                         // (hi + lo reproduces the fp32 centroid to ~2^-17)
-  int64_t off_chunks;   // int32 [d/32][4 + d] per wave of the compress kernel:
-                        //   [0] number of chunks, [1] first bit | end bit << 16 of
-                        //   the wave's contiguous code range, [2] first | end of
-                        //   the shared record words this wave stores, [3] unused,
-                        //   then chunks (start | count << 10 | width << 20) of <= 8
-                        //   equal-width coordinates in coordinate order
+  int64_t off_csig;     // float [n_csig]  signal centroids * sigma_i per plan chunk
 };
 
 static_assert(sizeof(DevCoord) == 16, "DevCoord layout");

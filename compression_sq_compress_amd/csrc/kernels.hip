@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <vector>
 
@@ -86,13 +87,144 @@ void release_tables(sq_calib *c) {
   c->device = -1;
 }
 
+// Compress plan of one head (layout in devtypes.h): wave headers, chunks,
+// padded threshold trees and signal centroids.
+struct HostPlan {
+  std::vector<uint32_t> words;
+  std::vector<float> tree, csig;
+  int n_chunks = 0;
+};
+
+static uint32_t f32_bits(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  return u;
+}
+
+static HostPlan build_plan(const HeadCal &hc) {
+  const int d = hc.d, NW = d / 32;
+  HostPlan P;
+  // wave ranges balanced on the quantiser's cost (~3 ops per tree level + 4)
+  int total = 0;
+  for (int i = 0; i < d; ++i) total += 3 * hc.widths[i] + 4;
+  std::vector<int> cut(NW + 1, d);
+  cut[0] = 0;
+  {
+    int acc = 0, w = 1;
+    for (int i = 0; i < d && w < NW; ++i) {
+      acc += 3 * hc.widths[i] + 4;
+      if (acc * NW >= total * w) cut[w++] = i + 1;
+    }
+    for (; w < NW; ++w) cut[w] = d;
+    for (int w2 = 1; w2 <= NW; ++w2) cut[w2] = std::max(cut[w2], cut[w2 - 1]);
+  }
+  std::vector<int> sbit(NW), ebit(NW);
+  for (int w = 0; w < NW; ++w) {
+    sbit[w] = cut[w] < d ? hc.bit_off[cut[w]] : hc.code_bits;
+    ebit[w] = cut[w + 1] < d ? hc.bit_off[cut[w + 1]] : hc.code_bits;
+  }
+  ebit[NW - 1] = 32 * hc.W;  // the last wave also covers QJL bits and gamma
+  // words a wave stores straight from its bit window: wholly inside its code
+  // bits (for the last wave with QJL, below the QJL bits)
+  std::vector<int> dfirst(NW), dend(NW);
+  for (int w = 0; w < NW; ++w) {
+    const int ecode = (w == NW - 1 && hc.m > 0) ? hc.code_bits : ebit[w];
+    dfirst[w] = (sbit[w] + 31) / 32;
+    dend[w] = std::max(dfirst[w], ecode / 32);
+    if (w == NW - 1 && hc.m == 0) dend[w] = std::max(dfirst[w], hc.W);
+  }
+  // every other word is OR-assembled in LDS and stored by the highest wave
+  // that touches it
+  std::vector<int> owner(hc.W, -1);
+  for (int k = 0; k < hc.W; ++k) {
+    bool direct = false;
+    for (int w = 0; w < NW; ++w)
+      if (k >= dfirst[w] && k < dend[w]) direct = true;
+    if (direct) continue;
+    owner[k] = NW - 1;
+    for (int w = 0; w < NW; ++w)
+      if (sbit[w] < ebit[w] && sbit[w] < 32 * (k + 1) && ebit[w] > 32 * k) owner[k] = w;
+  }
+  struct Ch { int start, cnt, b; };
+  std::vector<std::vector<Ch>> wch(NW);
+  for (int w = 0; w < NW; ++w)
+    for (int i = cut[w]; i < cut[w + 1];) {
+      int j = i;
+      while (j < cut[w + 1] && j - i < 8 && hc.widths[j] == hc.widths[i]) ++j;
+      wch[w].push_back({i, j - i, hc.widths[i]});
+      i = j;
+    }
+  for (int w = 0; w < NW; ++w) P.n_chunks += (int)wch[w].size();
+  P.words.assign((size_t)(NW + P.n_chunks + 1) * PLAN_WORDS, 0u);
+  const float inf = std::numeric_limits<float>::infinity();
+  // thresholds are compared through the sign of (threshold - y): store +0, never -0
+  auto canon = [](float v) { return v == 0.0f ? 0.0f : v; };
+  int q = 0;
+  for (int w = 0; w < NW; ++w) {
+    uint32_t *H = P.words.data() + (size_t)w * PLAN_WORDS;
+    H[0] = (uint32_t)wch[w].size();
+    H[1] = (uint32_t)sbit[w] | ((uint32_t)ebit[w] << 16);
+    int f = -1, e = -1;
+    for (int k = 0; k < hc.W; ++k)
+      if (owner[k] == w) {
+        if (f < 0) f = k;
+        e = k + 1;
+      }
+    if (f < 0) f = e = 0;
+    H[2] = (uint32_t)f | ((uint32_t)e << 16);
+    H[3] = (uint32_t)dfirst[w] | ((uint32_t)dend[w] << 16);
+    H[4] = (uint32_t)q;
+    for (const Ch &ch : wch[w]) {
+      uint32_t *C = P.words.data() + (size_t)(NW + q) * PLAN_WORDS;
+      const int b = ch.b, L = 1 << b;
+      const int nsig = hc.m > 0 ? std::max(0, std::min(ch.cnt, hc.d_eff - ch.start)) : 0;
+      C[8] = (uint32_t)(b > 0 ? P.tree.size() : 0);
+      C[9] = (uint32_t)ch.start;
+      C[10] = (uint32_t)ch.cnt;
+      C[11] = (uint32_t)b;
+      C[12] = (uint32_t)nsig;
+      C[13] = (uint32_t)(nsig > 0 && b > 0 ? P.csig.size() : 0);
+      for (int c = 0; c < 8; ++c) C[c] = f32_bits(inf);
+      if (b > 0) {
+        const size_t tb = P.tree.size();
+        P.tree.resize(tb + 8 * (size_t)L, inf);
+        for (int c = 0; c < ch.cnt; ++c) {
+          const int i = ch.start + c;
+          // node n (depth k, position p = n - 2^k) holds sorted threshold
+          // (2p + 1) * 2^(b - 1 - k) - 1
+          for (int n = 1; n < L; ++n) {
+            int k = 0;
+            while ((2 << k) <= n) ++k;
+            const int pos = n - (1 << k);
+            P.tree[tb + (size_t)c * L + n - 1] =
+                canon(hc.thr[hc.thr_base[i] + (2 * pos + 1) * (1 << (b - 1 - k)) - 1]);
+          }
+          C[c] = f32_bits(P.tree[tb + (size_t)c * L]);
+        }
+        if (nsig > 0) {
+          const size_t cb = P.csig.size();
+          P.csig.resize(cb + 8 * (size_t)L, 0.0f);
+          for (int c = 0; c < nsig; ++c)
+            for (int k = 0; k < L; ++k)
+              P.csig[cb + (size_t)c * L + k] = hc.cent[hc.cent_base[ch.start + c] + k];
+        }
+      }
+      ++q;
+    }
+  }
+  return P;
+}
+
 sq_status upload_tables(sq_calib *c, void *stream) {
   const int nh = (int)c->heads.size();
+  std::vector<HostPlan> plans(nh);
+  for (int h = 0; h < nh; ++h) plans[h] = build_plan(c->heads[h]);
   // host image of the blob: [DevHead x nh] then per-head sections
   std::vector<DevHead> desc(nh);
   size_t off = align256(sizeof(DevHead) * nh);
   for (int h = 0; h < nh; ++h) {
     const HeadCal &hc = c->heads[h];
+    const HostPlan &P = plans[h];
     const int d = hc.d;
     DevHead &D = desc[h];
     std::memset(&D, 0, sizeof(D));
@@ -101,27 +233,29 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.m = hc.m;
     D.W = hc.W;
     D.code_bits = hc.code_bits;
-    D.n_thr = hc.n_thr;
+    D.n_tree = (int)P.tree.size();
     D.n_cent = hc.n_cent;
     D.has_gamma = hc.m > 0;
     D.qjl_scale = hc.m > 0 ? (float)(std::sqrt(M_PI / 2.0) / hc.m) : 0.0f;
-    D.n_cent_sig = hc.d_eff < d ? hc.cent_base[hc.d_eff] : hc.n_cent;
+    D.n_csig = (int)P.csig.size();
+    D.n_chunks = P.n_chunks;
     D.off_R = off;       off = align256(off + sizeof(float) * d * d);
     D.off_Rfrag = off;   off = align256(off + sizeof(uint16_t) * 3 * d * d);
     D.off_coord = off;   off = align256(off + sizeof(DevCoord) * d);
-    D.off_thr = off;     off = align256(off + sizeof(float) * std::max(1, hc.n_cent));
+    D.off_tree = off;    off = align256(off + sizeof(float) * std::max<size_t>(1, P.tree.size()));
     D.off_cent = off;    off = align256(off + sizeof(float) * std::max(1, hc.n_cent));
     D.off_S = off;       off = align256(off + sizeof(float) * std::max(1, hc.m * hc.d_eff));
-    D.off_wstart = off;  off = align256(off + sizeof(int32_t) * std::max(1, hc.W));
+    D.off_plan = off;    off = align256(off + sizeof(uint32_t) * P.words.size());
     D.off_desc = off;    off = align256(off + sizeof(uint32_t) * d);
     D.off_lutp = off;    off = align256(off + sizeof(uint32_t) * std::max(1, hc.n_cent));
-    D.off_chunks = off;  off = align256(off + sizeof(int32_t) * (d / 32) * (4 + d));
+    D.off_csig = off;    off = align256(off + sizeof(float) * std::max<size_t>(1, P.csig.size()));
   }
   std::vector<uint8_t> img(off, 0);
   std::memcpy(img.data(), desc.data(), sizeof(DevHead) * nh);
   for (int h = 0; h < nh; ++h) {
     const HeadCal &hc = c->heads[h];
     const DevHead &D = desc[h];
+    const HostPlan &P = plans[h];
     const int d = hc.d;
     float *R = (float *)(img.data() + D.off_R);
     for (int k = 0; k < d * d; ++k) R[k] = (float)hc.R[k];
@@ -153,25 +287,12 @@ sq_status upload_tables(sq_calib *c, void *stream) {
       Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
       Dd[i] = (uint32_t)hc.bit_off[i] | ((uint32_t)hc.widths[i] << 12) | ((uint32_t)hc.cent_base[i] << 16);
     }
-    // thresholds in breadth-first order: node n (depth k, position p = n - 2^k)
-    // of coordinate i holds sorted threshold (2p + 1) * 2^(b - 1 - k) - 1
-    {
-      float *E = (float *)(img.data() + D.off_thr);
-      for (int i = 0; i < d; ++i) {
-        const int b = hc.widths[i];
-        if (b == 0) continue;
-        E[hc.cent_base[i]] = 0.0f;  // node 0 is never read
-        for (int n = 1; n < (1 << b); ++n) {
-          int k = 0;
-          while ((2 << k) <= n) ++k;
-          const int pos = n - (1 << k);
-          E[hc.cent_base[i] + n] = hc.thr[hc.thr_base[i] + (2 * pos + 1) * (1 << (b - 1 - k)) - 1];
-        }
-      }
-    }
+    if (!P.tree.empty()) std::memcpy(img.data() + D.off_tree, P.tree.data(), sizeof(float) * P.tree.size());
+    if (!P.csig.empty()) std::memcpy(img.data() + D.off_csig, P.csig.data(), sizeof(float) * P.csig.size());
+    std::memcpy(img.data() + D.off_plan, P.words.data(), sizeof(uint32_t) * P.words.size());
     if (hc.n_cent) std::memcpy(img.data() + D.off_cent, hc.cent.data(), sizeof(float) * hc.n_cent);
     {
-      uint32_t *P = (uint32_t *)(img.data() + D.off_lutp);
+      uint32_t *Pp = (uint32_t *)(img.data() + D.off_lutp);
       for (int k = 0; k < hc.n_cent; ++k) {
         const float v = hc.cent[k];
         const uint16_t hi = f32_to_bf16_rne(v);
@@ -179,87 +300,10 @@ sq_status upload_tables(sq_calib *c, void *stream) {
         uint32_t u = (uint32_t)hi << 16;
         std::memcpy(&vh, &u, 4);
         const uint16_t lo = f32_to_bf16_rne(v - vh);
-        P[k] = (uint32_t)hi | ((uint32_t)lo << 16);
+        Pp[k] = (uint32_t)hi | ((uint32_t)lo << 16);
       }
     }
     if (hc.m) std::memcpy(img.data() + D.off_S, hc.S.data(), sizeof(float) * hc.m * hc.d_eff);
-    int32_t *ws = (int32_t *)(img.data() + D.off_wstart);
-    for (int k = 0; k < hc.W; ++k) {
-      int c = 0;  // first coordinate whose field ends after bit 32k
-      while (c < d && hc.bit_off[c] + hc.widths[c] <= 32 * k) ++c;
-      int e = c;  // one past the last coordinate that starts before bit 32(k+1)
-      while (e < d && hc.bit_off[e] < 32 * (k + 1)) ++e;
-      ws[k] = c | ((e - c) << 16);
-    }
-    // Work split of the compress kernel: d/32 waves, each owning a contiguous
-    // coordinate range chosen to balance the search depth (sum of width + 1);
-    // within a range, runs of equal width cut into chunks of <= 8.  A record
-    // word lying wholly inside one wave's code bits is stored by that wave;
-    // every other word is assembled in LDS and stored by the highest wave
-    // that touches it (the last wave also owns the QJL bits and gamma).
-    {
-      const int NW = d / 32;
-      int32_t *CH = (int32_t *)(img.data() + D.off_chunks);
-      int total = 0;
-      for (int i = 0; i < d; ++i) total += hc.widths[i] + 1;
-      std::vector<int> cut(NW + 1, d);
-      cut[0] = 0;
-      int acc = 0, w = 1;
-      for (int i = 0; i < d && w < NW; ++i) {
-        acc += hc.widths[i] + 1;
-        if (acc * NW >= total * w) cut[w++] = i + 1;
-      }
-      for (; w < NW; ++w) cut[w] = d;
-      for (int w2 = 1; w2 <= NW; ++w2) cut[w2] = std::max(cut[w2], cut[w2 - 1]);
-      std::vector<int> sbit(NW), ebit(NW);
-      for (int w2 = 0; w2 < NW; ++w2) {
-        sbit[w2] = cut[w2] < d ? hc.bit_off[cut[w2]] : hc.code_bits;
-        ebit[w2] = cut[w2 + 1] < d ? hc.bit_off[cut[w2 + 1]] : hc.code_bits;
-      }
-      ebit[NW - 1] = 32 * hc.W;  // the last wave also covers QJL bits and gamma
-      // words a wave stores straight from its bit window: wholly inside its
-      // code bits (for the last wave with QJL, below the QJL bits)
-      std::vector<int> dfirst(NW), dend(NW);
-      for (int w2 = 0; w2 < NW; ++w2) {
-        const int ecode = (w2 == NW - 1 && hc.m > 0) ? hc.code_bits : ebit[w2];
-        dfirst[w2] = (sbit[w2] + 31) / 32;
-        dend[w2] = std::max(dfirst[w2], ecode / 32);
-        if (w2 == NW - 1 && hc.m == 0) dend[w2] = std::max(dfirst[w2], hc.W);
-      }
-      // every other word: OR-assembled in LDS, stored by the highest wave
-      // that touches it
-      std::vector<int> owner(hc.W, -1);
-      for (int k = 0; k < hc.W; ++k) {
-        bool direct = false;
-        for (int w2 = 0; w2 < NW; ++w2)
-          if (k >= dfirst[w2] && k < dend[w2]) direct = true;
-        if (direct) continue;
-        owner[k] = NW - 1;
-        for (int w2 = 0; w2 < NW; ++w2)
-          if (sbit[w2] < ebit[w2] && sbit[w2] < 32 * (k + 1) && ebit[w2] > 32 * k) owner[k] = w2;
-      }
-      for (int w2 = 0; w2 < NW; ++w2) {
-        int32_t *row = CH + w2 * (4 + d);
-        int n = 0;
-        for (int i = cut[w2]; i < cut[w2 + 1];) {
-          int j = i;
-          while (j < cut[w2 + 1] && j - i < 8 && hc.widths[j] == hc.widths[i]) ++j;
-          row[4 + n++] = i | ((j - i) << 10) | (hc.widths[i] << 20);
-          i = j;
-        }
-        row[0] = n;
-        row[1] = sbit[w2] | (ebit[w2] << 16);
-        int f = -1, e = -1;
-        for (int k = 0; k < hc.W; ++k)
-          if (owner[k] == w2) {
-            if (f < 0) f = k;
-            e = k + 1;
-          }
-        if (f < 0) f = e = 0;
-        row[2] = f | (e << 16);
-        row[3] = dfirst[w2] | (dend[w2] << 16);
-      }
-    }
   }
   release_tables(c);
   int dev = 0;
@@ -316,13 +360,11 @@ struct CompressArgs {
   int first_head, cbs;
   int n_tiles;          // ceil(T / 64) per (batch, head)
   int items;            // tiles one head's workgroups share
-  int lds_cent_off;     // floats: signal-centroid table
+  int lds_csig_off;     // floats: signal-centroid table (after the trees)
   int lds_x_off;        // floats: x tile
-  int lds_y_off;        // floats: y / code tile
-  int lds_r_off;        // floats: residual tile
+  int lds_y_off;        // floats: y tile; residuals replace y in place
   int lds_b_off;        // floats: shared record-word buffer
   int ys;               // y tile row stride (floats, odd)
-  int rs;               // residual row stride (floats, odd)
   int bws;              // word buffer row stride (words, odd)
 };
 
@@ -355,7 +397,73 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, bool F32>
+// Bit window of one wave's record words while it appends code fields.
+struct PackWin {
+  uint32_t lo, hi;
+  int fill, kw;
+};
+
+// One chunk of <= 8 coordinates of equal width B (lane = token).  The
+// searches of the 8 slots advance together down their breadth-first trees:
+// the root comes from a scalar register, each further level is one table
+// read at a compile-time offset; the step is decided by the sign of
+// (threshold - y), so a tie goes to the lower cell and the code is
+// #{thresholds < y}.  NaN coordinates are mapped to -inf first (code 0).
+// Codes are appended to the window in coordinate order; residuals of signal
+// coordinates replace y in the tile.
+template <int B, bool TG>
+__device__ __forceinline__ void quant_chunk(const uint32_t (&cd)[PLAN_WORDS], float *yrow,
+                                            const float *trees, const float *csig, PackWin &pw,
+                                            uint32_t *dst, uint32_t *bwrow, int dfirst, int dend,
+                                            bool valid) {
+  constexpr int L = 1 << B;
+  const int start = (int)cd[9], cnt = (int)cd[10], nsig = (int)cd[12];
+  float y[8];
+  uint32_t code[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) y[c] = fmaxf(yrow[start + min(c, cnt - 1)], -INFINITY);
+  if constexpr (B > 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) code[c] = __float_as_uint(__uint_as_float(cd[c]) - y[c]) >> 31;
+    const float *tb = trees + cd[8];
+#pragma unroll
+    for (int l = 1; l < B; ++l) {
+      float th[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) th[c] = tb[c * L + (1 << l) - 1 + (int)code[c]];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        code[c] = __builtin_amdgcn_alignbit(code[c], __float_as_uint(th[c] - y[c]), 31);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c < cnt) {
+        pw.lo |= code[c] << pw.fill;
+        if (pw.fill + B > 32) pw.hi = code[c] >> (32 - pw.fill);
+        pw.fill += B;
+        if (pw.fill >= 32) {
+          if (pw.kw >= dfirst && pw.kw < dend) dst[(int64_t)pw.kw * 64] = valid ? pw.lo : 0u;
+          else atomicOr(bwrow + pw.kw, pw.lo);
+          ++pw.kw;
+          pw.lo = pw.hi;
+          pw.hi = 0;
+          pw.fill -= 32;
+        }
+      }
+    }
+  }
+  if (nsig > 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < nsig) {
+        float r = y[c];
+        if constexpr (B > 0) r -= csig[cd[13] + c * L + code[c]];
+        yrow[start + c] = r;
+      }
+  }
+}
+
+template <int D, bool F32, bool TG>
 __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
   extern __shared__ float smem[];
   constexpr int NW = D / 32, KS = D / 16, MB = D / 32, NT = 64 * NW;
@@ -367,18 +475,21 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
   const int ch = a.first_head + bz * a.cbs + h;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
-  const int n_thr = hd->n_cent, n_cent_sig = m > 0 ? hd->n_cent_sig : 0;
-  float *s_thr = smem;
-  float *s_cent = smem + a.lds_cent_off;
   float *ytile = smem + a.lds_y_off;             // [64][ys]
-  int *ctile = (int *)ytile;                     // codes, in place of y
-  float *rtile = smem + a.lds_r_off;             // [64][rs]
   uint32_t *bwords = (uint32_t *)(smem + a.lds_b_off);  // [64][bws] shared record words
+  const float *trees;
+  float *s_csig = smem + a.lds_csig_off;
   {
-    const float *g_thr = (const float *)(a.blob + hd->off_thr);
-    for (int k = threadIdx.x; k < n_thr; k += NT) s_thr[k] = g_thr[k];
-    const float *g_cent = (const float *)(a.blob + hd->off_cent);
-    for (int k = threadIdx.x; k < n_cent_sig; k += NT) s_cent[k] = g_cent[k];
+    const int n_tree = hd->n_tree, n_csig = hd->n_csig;
+    const float *g_tree = (const float *)(a.blob + hd->off_tree);
+    if constexpr (TG) {
+      trees = g_tree;
+    } else {
+      for (int k = threadIdx.x; k < n_tree; k += NT) smem[k] = g_tree[k];
+      trees = smem;
+    }
+    const float *g_csig = (const float *)(a.blob + hd->off_csig);
+    for (int k = threadIdx.x; k < n_csig; k += NT) s_csig[k] = g_csig[k];
   }
   const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag);
   uint4 rf[RES ? 3 : 1][RES ? KS : 1];
@@ -388,14 +499,15 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) rf[sp][ks] = Rf[((sp * MB + w) * KS + ks) * 64 + lane];
   }
-  const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
-  const SQ_CONST int32_t *wstart = cptr<int32_t>(a.blob + hd->off_wstart);
-  const SQ_CONST int32_t *chunks = cptr<int32_t>(a.blob + hd->off_chunks);
-  const SQ_CONST float *thr_g = cptr<float>(a.blob + hd->off_thr);
+  const SQ_CONST uint32_t *plan = cptr<uint32_t>(a.blob + hd->off_plan);
   const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
   const int64_t T = a.n_tokens;
-  // record words handled by this wave
-  const int wb = (w * W) / NW, we = ((w + 1) * W) / NW;
+  const SQ_CONST uint32_t *hdr = plan + w * PLAN_WORDS;
+  const int nch = (int)hdr[0];
+  const int sbit = (int)(hdr[1] & 0xFFFF);
+  const int own_f = (int)(hdr[2] & 0xFFFF), own_e = (int)(hdr[2] >> 16);
+  const int dfirst = (int)(hdr[3] & 0xFFFF), dend = (int)(hdr[3] >> 16);
+  const SQ_CONST uint32_t *chunks = plan + (NW + (int)hdr[4]) * PLAN_WORDS;
 
   // x tile chunks of 16 bytes: CPR per row, CH per thread; the next tile's
   // chunks are prefetched into registers while the current tile is processed
@@ -487,103 +599,66 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
       ytile[(32 + (lane & 31)) * a.ys + row] = acc1[v];
     }
     __syncthreads();
-    // ---- quantise + pack (lane = token).  The wave walks its contiguous
-    // coordinate range in chunks of <= 8 equal-width coordinates whose
-    // searches advance together through the breadth-first threshold trees
-    // (root compared from a scalar register, one batch of LDS reads per
-    // further level); codes are appended in coordinate order to a two-word
-    // bit window.  Words wholly inside the wave's code bits go straight to
-    // HBM, shared words are OR-ed into the LDS word buffer.
-    const SQ_CONST int32_t *cl = chunks + w * (4 + D);
-    const int nch = cl[0];
-    const int sbit = cl[1] & 0xFFFF;
-    const int dfirst = cl[3] & 0xFFFF, dend = cl[3] >> 16;
+    // ---- quantise + pack (lane = token), chunk by chunk through the plan.
+    // Words wholly inside the wave's code bits go straight to HBM, shared
+    // words are OR-ed into the LDS word buffer.
     uint32_t *dst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
     const bool valid = t0 + lane < T;
     uint32_t *bwrow = bwords + lane * a.bws;
+    float *yrow = ytile + lane * a.ys;
     {
-      uint32_t lo = 0, hi = 0;
-      int fill = sbit & 31, kw = sbit >> 5;
-      auto flush = [&]() {
-        if (kw >= dfirst && kw < dend) dst[(int64_t)kw * 64] = valid ? lo : 0u;
-        else atomicOr(bwrow + kw, lo);
-        ++kw;
-        lo = hi;
-        hi = 0;
-        fill -= 32;
-      };
+      PackWin pw{0u, 0u, sbit & 31, sbit >> 5};
+      uint32_t cur[PLAN_WORDS];
+#pragma unroll
+      for (int k = 0; k < PLAN_WORDS; ++k) cur[k] = chunks[k];
       for (int q = 0; q < nch; ++q) {
-        const int e = cl[4 + q];
-        const int start = e & 1023, cnt = (e >> 10) & 1023, bw = e >> 20;
-        float y[8];
-        int node[8], tb[8];
+        uint32_t nxt[PLAN_WORDS];  // the plan ends with a spare chunk
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int i = start + min(c, cnt - 1);
-          y[c] = ytile[lane * a.ys + i];
-          tb[c] = coords[i].cent_base;
-          node[c] = 1;
-        }
-        if (bw > 0) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) node[c] = 2 + (thr_g[tb[c] + 1] < y[c] ? 1 : 0);
-          for (int k = 1; k < bw; ++k) {
-            float th[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) th[c] = s_thr[tb[c] + node[c]];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) node[c] = node[c] + node[c] + (th[c] < y[c] ? 1 : 0);
-          }
+        for (int k = 0; k < PLAN_WORDS; ++k) nxt[k] = chunks[(q + 1) * PLAN_WORDS + k];
+        switch (cur[11]) {
+          case 0: quant_chunk<0, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 1: quant_chunk<1, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 2: quant_chunk<2, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 3: quant_chunk<3, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 4: quant_chunk<4, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 5: quant_chunk<5, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 6: quant_chunk<6, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 7: quant_chunk<7, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          default: quant_chunk<8, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          if (c < cnt) {
-            const int i = start + c;
-            const uint32_t code = (uint32_t)(node[c] - (1 << bw));
-            if (i < d_eff && m > 0)
-              rtile[lane * a.rs + i] = y[c] - (bw ? s_cent[tb[c] + (int)code] : 0.0f);
-            if (bw) {
-              lo |= code << fill;
-              if (fill + bw > 32) hi = code >> (32 - fill);
-              fill += bw;
-              if (fill >= 32) flush();
-            }
-          }
-        }
+        for (int k = 0; k < PLAN_WORDS; ++k) cur[k] = nxt[k];
       }
-      if (fill > 0) {  // last, partial word of the range
-        if (kw >= dfirst && kw < dend) dst[(int64_t)kw * 64] = valid ? lo : 0u;
-        else atomicOr(bwrow + kw, lo);
+      if (pw.fill > 0) {  // last, partial word of the range
+        if (pw.kw >= dfirst && pw.kw < dend) dst[(int64_t)pw.kw * 64] = valid ? pw.lo : 0u;
+        else atomicOr(bwrow + pw.kw, pw.lo);
       }
     }
     __syncthreads();
-    // ---- shared words owned by this wave (the last wave adds QJL bits and gamma)
-    {
-      const int of = cl[2] & 0xFFFF, oe = cl[2] >> 16;
-      const float *rrow = rtile + lane * a.rs;
-      for (int k = of; k < oe; ++k) {
-        if (k >= dfirst && k < dend) continue;
-        uint32_t word = bwrow[k];
-        if (m > 0) {
-          const int lo_bit = 32 * k, hi_bit = lo_bit + 32;
-          const int jb = max(0, lo_bit - code_bits), je = min(m, hi_bit - code_bits);
-          for (int j = jb; j < je; ++j) {
-            float dot = 0.0f;
-            for (int i = 0; i < d_eff; ++i) dot = fmaf(S[j * d_eff + i], rrow[i], dot);
-            word |= (dot >= 0.0f ? 1u : 0u) << (code_bits + j - lo_bit);
-          }
-          if (k == W - 1) {
-            float g2 = 0.0f;
-            for (int i = 0; i < d_eff; ++i) g2 = fmaf(rrow[i], rrow[i], g2);
-            word |= half_bits_rne(sqrtf(g2)) << 16;
-          }
+    // ---- shared words owned by this wave (the last wave adds QJL bits and
+    // gamma from the residuals, which replaced y of the signal coordinates)
+    for (int k = own_f; k < own_e; ++k) {
+      if (k >= dfirst && k < dend) continue;
+      uint32_t word = bwrow[k];
+      if (m > 0) {
+        const int lo_bit = 32 * k, hi_bit = lo_bit + 32;
+        const int jb = max(0, lo_bit - code_bits), je = min(m, hi_bit - code_bits);
+        for (int j = jb; j < je; ++j) {
+          float dot = 0.0f;
+          for (int i = 0; i < d_eff; ++i) dot = fmaf(S[j * d_eff + i], yrow[i], dot);
+          word |= (dot >= 0.0f ? 1u : 0u) << (code_bits + j - lo_bit);
         }
-        dst[(int64_t)k * 64] = valid ? word : 0u;
+        if (k == W - 1) {
+          float g2 = 0.0f;
+          for (int i = 0; i < d_eff; ++i) g2 = fmaf(yrow[i], yrow[i], g2);
+          word |= half_bits_rne(sqrtf(g2)) << 16;
+        }
       }
+      dst[(int64_t)k * 64] = valid ? word : 0u;
     }
     // The x tile was last read by the MFMAs, which every wave finished before
-    // the barrier above; the y/code tile is rewritten only after the barrier
-    // that follows the next x store.  No further barrier is needed here.
+    // the barrier above; the y tile and the word buffer are rewritten only
+    // after the barrier that follows the next x store.
   }
 }
 
@@ -632,7 +707,7 @@ __device__ __forceinline__ f32x4 mfma4(uint2 a, uint2 b, f32x4 c) {
 
 __device__ __forceinline__ uint32_t bf16_pair(uint16_t x) { return (uint32_t)x | ((uint32_t)x << 16); }
 
-template <int G, int NT>
+template <int G, int NT, bool LG>
 __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
   extern __shared__ float smem[];
   constexpr int GR = (G + 3) / 4, GP = 4 * GR;
@@ -699,10 +774,16 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
       }
       aq[k] = v;
     }
-    const uint32_t *gl = (const uint32_t *)(a.blob + hd->off_lutp);
-    for (int k = threadIdx.x; k < n_cent; k += blockDim.x) lut[k] = gl[k];
+    if constexpr (!LG) {
+      const uint32_t *gl = (const uint32_t *)(a.blob + hd->off_lutp);
+      for (int k = threadIdx.x; k < n_cent; k += blockDim.x) lut[k] = gl[k];
+    }
     __syncthreads();
   }
+  // centroid pairs: LDS copy, or (tables too large for LDS) the global table
+  const uint32_t *lutv;
+  if constexpr (LG) lutv = (const uint32_t *)(a.blob + hd->off_lutp);
+  else lutv = lut;
 
   const uint32_t *slot = a.kpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
   uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off) + wave * NT * a.rec_tile;
@@ -774,7 +855,7 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
 #pragma unroll
           for (int tq = 0; tq < NT; ++tq) {
             const uint32_t f = __builtin_amdgcn_alignbit(whi[tq], wlo[tq], bo & 31) & mask;
-            dv[c][tq] = lut[cb + f];
+            dv[c][tq] = lutv[cb + f];
           }
         }
 #pragma unroll
@@ -1131,9 +1212,15 @@ extern "C" sq_status sq_calib_upload(sq_calib *c, sq_stream stream) {
   return st;
 }
 
-template <int D, bool F32>
+template <int D, bool F32, bool TG>
 static void launch_compress(dim3 grid, size_t lds, hipStream_t s, const CompressArgs &a) {
-  hipLaunchKernelGGL((compress_kernel<D, F32>), grid, dim3(2 * D), lds, s, a);
+  hipLaunchKernelGGL((compress_kernel<D, F32, TG>), grid, dim3(2 * D), lds, s, a);
+}
+
+template <int D>
+static void launch_compress_d(bool f32, bool tg, dim3 grid, size_t lds, hipStream_t s, const CompressArgs &a) {
+  if (f32) tg ? launch_compress<D, true, true>(grid, lds, s, a) : launch_compress<D, true, false>(grid, lds, s, a);
+  else tg ? launch_compress<D, false, true>(grid, lds, s, a) : launch_compress<D, false, false>(grid, lds, s, a);
 }
 
 static int device_cu_count() {
@@ -1165,32 +1252,32 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   const int d = c->heads[first_head].d;
   if (xs_token < d) return fail(SQ_ERR_ARG, "sq_compress: xs_token < head_dim");
   if (n_tokens > ((int64_t)1 << 36)) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many tokens");
-  // LDS: thresholds | signal centroids | x tile | y/code tile | residual tile
-  int max_thr = 1, max_csig = 0, max_deff = 1;
+  // LDS: threshold trees | signal centroids | x tile | y tile | word buffer
+  int max_tree = 0, max_csig = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
     for (int h = 0; h < n_heads; ++h) {
       const int k = first_head + bb * calib_batch_stride + h;
-      const HeadCal &hc = c->heads[k];
-      max_thr = std::max(max_thr, hc.n_cent);
-      if (hc.m > 0) {
-        max_csig = std::max(max_csig, c->host_desc[k].n_cent_sig);
-        max_deff = std::max(max_deff, hc.d_eff);
-      }
+      max_tree = std::max(max_tree, c->host_desc[k].n_tree);
+      max_csig = std::max(max_csig, c->host_desc[k].n_csig);
     }
     if (calib_batch_stride == 0) break;  // every batch entry uses the same heads
   }
   CompressArgs a{};
   a.ys = d + 1;
-  a.rs = (max_deff % 2 == 0) ? max_deff + 1 : max_deff + 2;
-  const int xs_floats = dt == SQ_F32 ? 64 * (d + 4) : 64 * (d + 8) / 2;
-  a.lds_cent_off = (max_thr + 3) & ~3;
-  a.lds_x_off = a.lds_cent_off + ((max_csig + 3) & ~3);
-  a.lds_y_off = a.lds_x_off + xs_floats;
-  a.lds_r_off = a.lds_y_off + 64 * a.ys;
   a.bws = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
-  a.lds_b_off = a.lds_r_off + 64 * a.rs;
+  const int xs_floats = dt == SQ_F32 ? 64 * (d + 4) : 64 * (d + 8) / 2;
+  const int rest = ((max_csig + 3) & ~3) + xs_floats + 64 * a.ys + 64 * a.bws;
+  const size_t limit = (size_t)device_lds_limit();
+  const size_t lds_in = (size_t)(((max_tree + 3) & ~3) + rest) * 4, lds_out = (size_t)rest * 4;
+  // trees stay in LDS unless moving them out is what lets two workgroups share a CU
+  const bool tg = lds_in > limit || (lds_in > limit / 2 && lds_out <= limit / 2);
+  const int tree_floats = tg ? 0 : ((max_tree + 3) & ~3);
+  a.lds_csig_off = tree_floats;
+  a.lds_x_off = a.lds_csig_off + ((max_csig + 3) & ~3);
+  a.lds_y_off = a.lds_x_off + xs_floats;
+  a.lds_b_off = a.lds_y_off + 64 * a.ys;
   const size_t lds = (size_t)(a.lds_b_off + 64 * a.bws) * 4;
-  if (lds > (size_t)device_lds_limit())
+  if (lds > limit)
     return fail(SQ_ERR_UNSUPPORTED, "sq_compress: calibration tables exceed the LDS of one workgroup");
   a.heads = c->dev_heads;
   a.blob = (const uint8_t *)c->dev_blob;
@@ -1212,25 +1299,26 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   hipStream_t s = (hipStream_t)stream;
   const bool f32 = dt == SQ_F32;
   switch (d) {
-    case 32:  f32 ? launch_compress<32, true>(grid, lds, s, a) : launch_compress<32, false>(grid, lds, s, a); break;
-    case 64:  f32 ? launch_compress<64, true>(grid, lds, s, a) : launch_compress<64, false>(grid, lds, s, a); break;
-    case 128: f32 ? launch_compress<128, true>(grid, lds, s, a) : launch_compress<128, false>(grid, lds, s, a); break;
-    case 256: f32 ? launch_compress<256, true>(grid, lds, s, a) : launch_compress<256, false>(grid, lds, s, a); break;
+    case 32:  launch_compress_d<32>(f32, tg, grid, lds, s, a); break;
+    case 64:  launch_compress_d<64>(f32, tg, grid, lds, s, a); break;
+    case 128: launch_compress_d<128>(f32, tg, grid, lds, s, a); break;
+    case 256: launch_compress_d<256>(f32, tg, grid, lds, s, a); break;
     default: return fail(SQ_ERR_UNSUPPORTED, "sq_compress: head_dim");
   }
   return launched(fn);
 }
 
-template <int G, int NT>
+template <int G, int NT, bool LG>
 static void launch_scores(dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
-  hipLaunchKernelGGL((scores_kernel<G, NT>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((scores_kernel<G, NT, LG>), grid, dim3(256), lds, s, a);
 }
 
 template <int G>
-static void launch_scores_nt(int nt, dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
-  if (nt == 4) launch_scores<G, 4>(grid, lds, s, a);
-  else if (nt == 2) launch_scores<G, 2>(grid, lds, s, a);
-  else launch_scores<G, 1>(grid, lds, s, a);
+static void launch_scores_nt(int nt, bool lg, dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
+  if (lg) launch_scores<G, 4, true>(grid, lds, s, a);
+  else if (nt == 4) launch_scores<G, 4, false>(grid, lds, s, a);
+  else if (nt == 2) launch_scores<G, 2, false>(grid, lds, s, a);
+  else launch_scores<G, 1, false>(grid, lds, s, a);
 }
 
 extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_batch_stride, int batch,
@@ -1265,19 +1353,26 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
   }
   const int GR = (G + 3) / 4, GP = 4 * GR;
   ScoresArgs a{};
-  a.lds_lut_off = 0;
-  a.lds_aq_off = (max_cent + 3) & ~3;                       // 16-byte aligned
-  a.lds_w_off = a.lds_aq_off + 2 * GR * (d / 2 + d / 4) * 4;
-  a.lds_rec_off = a.lds_w_off + ((std::max(1, max_m) * GP + 3) & ~3);
-  a.rec_tile = (kc->W_max + 1) * 64;
-  const int scratch = (G + GP) * d;                          // prologue floats
   const int limit = device_lds_limit();
+  const int scratch = (G + GP) * d;                          // prologue floats
   int nt = 4;
-  auto lds_for = [&](int n) {
+  bool lg = false;
+  // LDS: centroid pairs | MFMA A operands | QJL weights | record tiles
+  auto layout = [&](bool lut_in_lds, int n) {
+    a.lds_lut_off = 0;
+    a.lds_aq_off = lut_in_lds ? ((max_cent + 3) & ~3) : 0;  // 16-byte aligned
+    a.lds_w_off = a.lds_aq_off + 2 * GR * (d / 2 + d / 4) * 4;
+    a.lds_rec_off = a.lds_w_off + ((std::max(1, max_m) * GP + 3) & ~3);
+    a.rec_tile = (kc->W_max + 1) * 64;
     return (size_t)(a.lds_rec_off + std::max(scratch, 4 * n * a.rec_tile)) * 4;
   };
-  while (nt > 1 && lds_for(nt) > (size_t)std::min(limit, 72 * 1024)) nt >>= 1;
-  const size_t lds = lds_for(nt);
+  size_t lds = layout(true, nt);
+  while (nt > 1 && lds > (size_t)std::min(limit, 72 * 1024)) lds = layout(true, nt >>= 1);
+  if (lds > (size_t)limit) {  // centroid table too large: read it from the L1/L2
+    lg = true;
+    nt = 4;
+    lds = layout(false, nt);
+  }
   if (lds > (size_t)limit) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: tables exceed LDS");
   a.heads = kc->dev_heads;
   a.blob = (const uint8_t *)kc->dev_blob;
@@ -1304,14 +1399,14 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
   if (grid.z > 65535 || grid.y > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: grid too large");
   hipStream_t s = (hipStream_t)stream;
   switch (G) {
-    case 1: launch_scores_nt<1>(nt, grid, lds, s, a); break;
-    case 2: launch_scores_nt<2>(nt, grid, lds, s, a); break;
-    case 3: launch_scores_nt<3>(nt, grid, lds, s, a); break;
-    case 4: launch_scores_nt<4>(nt, grid, lds, s, a); break;
-    case 5: launch_scores_nt<5>(nt, grid, lds, s, a); break;
-    case 6: launch_scores_nt<6>(nt, grid, lds, s, a); break;
-    case 7: launch_scores_nt<7>(nt, grid, lds, s, a); break;
-    case 8: launch_scores_nt<8>(nt, grid, lds, s, a); break;
+    case 1: launch_scores_nt<1>(nt, lg, grid, lds, s, a); break;
+    case 2: launch_scores_nt<2>(nt, lg, grid, lds, s, a); break;
+    case 3: launch_scores_nt<3>(nt, lg, grid, lds, s, a); break;
+    case 4: launch_scores_nt<4>(nt, lg, grid, lds, s, a); break;
+    case 5: launch_scores_nt<5>(nt, lg, grid, lds, s, a); break;
+    case 6: launch_scores_nt<6>(nt, lg, grid, lds, s, a); break;
+    case 7: launch_scores_nt<7>(nt, lg, grid, lds, s, a); break;
+    case 8: launch_scores_nt<8>(nt, lg, grid, lds, s, a); break;
   }
   return launched(fn);
 }
