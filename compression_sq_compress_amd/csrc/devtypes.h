@@ -15,17 +15,18 @@ struct DevCoord {
   int32_t cent_base;
 };
 
-// Compress work plan.  The kernel's d/32 waves each own a contiguous range of
-// eigen-coordinates; a range is cut into chunks of <= 8 coordinates of equal
-// width.  Wave header w (16 words): [0] chunks, [1] first bit | end bit << 16
-// of the wave's code range, [2] first | end of the shared record words the
-// wave stores, [3] first | end of the words it stores straight from its bit
-// window, [4] index of its first chunk.  Chunk (16 words): [0..7] root
-// threshold of each slot (fp32 bits; +inf in unused slots), [8] tree base,
-// [9] first coordinate, [10] count, [11] width b, [12] number of signal
-// coordinates (residual needed), [13] signal-centroid base.  Slot c's
-// threshold tree holds node n (1 <= n < 2^b, children 2n, 2n+1) at tree base
-// + c * 2^b + n - 1, and its signal centroids at signal base + c * 2^b + code.
+// Compress work plan.  The kernel's d/16 waves each own a contiguous range of
+// eigen-coordinates; a range is cut into chunks of 1, 2, 4 or 8 coordinates
+// of equal width (runs of zero-width coordinates outside the signal range
+// need no chunk).  Wave header w (16 words): [0] chunks, [1] first bit | end
+// bit << 16 of the wave's code range, [2] first | end of the shared record
+// words the wave stores, [3] first | end of the words it stores straight from
+// its bit window, [4] index of its first chunk.  Chunk (16 words): [0..7]
+// root threshold of each coordinate (fp32 bits), [8] tree base, [9] first
+// coordinate, [10] count n, [11] width b, [12] number of signal coordinates
+// (residual needed), [13] signal-centroid base, [14] log2 n.  Coordinate c's
+// threshold tree holds node k (1 <= k < 2^b, children 2k, 2k+1) at tree base
+// + c * 2^b + k - 1, and its signal centroids at signal base + c * 2^b + code.
 constexpr int PLAN_WORDS = 16;
 
 struct DevHead {
@@ -35,14 +36,14 @@ struct DevHead {
   int32_t n_csig;       // floats in the signal-centroid table of the plan
   int32_t n_chunks, pad2;
   int64_t off_R;        // float [d][d], row i = eigenvector i (y = R x)
-  int64_t off_Rfrag;    // bf16 [3][d/32][d/16][64][8]: hi/mid/lo split of R in
-                        // MFMA 32x32x16 A-operand order (see compress kernel)
+  int64_t off_Rfrag;    // bf16 [3][d/16][d/32][64][8]: hi/mid/lo split of R in
+                        // MFMA 16x16x32 A-operand order (see compress kernel)
   int64_t off_coord;    // DevCoord [d]
   int64_t off_tree;     // float [n_tree]  thresholds * sigma_i, per chunk of the
                         // compress plan, breadth-first (see PLAN_WORDS)
   int64_t off_cent;     // float [n_cent]  centroids * sigma_i
   int64_t off_S;        // float [m][d_eff] QJL sketch
-  int64_t off_plan;     // uint32 [d/32 + n_chunks + 1][PLAN_WORDS] compress plan
+  int64_t off_plan;     // uint32 [d/16 + n_chunks + 1][PLAN_WORDS] compress plan
   int64_t off_desc;     // uint32 [d]: bit offset | width << 12 | centroid base << 16
   int64_t off_lutp;     // uint32 [n_cent]: each centroid as bf16 hi | bf16 lo << 16
                         // (hi + lo reproduces the fp32 centroid to ~2^-17)

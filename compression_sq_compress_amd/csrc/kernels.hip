@@ -23,7 +23,7 @@
 namespace sq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ helpers
 
@@ -102,7 +102,7 @@ static uint32_t f32_bits(float v) {
 }
 
 static HostPlan build_plan(const HeadCal &hc) {
-  const int d = hc.d, NW = d / 32;
+  const int d = hc.d, NW = d / 16;
   HostPlan P;
   // wave ranges balanced on the quantiser's cost (~3 ops per tree level + 4)
   int total = 0;
@@ -150,8 +150,15 @@ static HostPlan build_plan(const HeadCal &hc) {
   for (int w = 0; w < NW; ++w)
     for (int i = cut[w]; i < cut[w + 1];) {
       int j = i;
-      while (j < cut[w + 1] && j - i < 8 && hc.widths[j] == hc.widths[i]) ++j;
-      wch[w].push_back({i, j - i, hc.widths[i]});
+      while (j < cut[w + 1] && hc.widths[j] == hc.widths[i]) ++j;
+      // a run of equal width: chunks of 8, then the binary remainder
+      for (int k = i; k < j;) {
+        int n = 8;
+        while (n > j - k) n >>= 1;
+        const bool sig = hc.m > 0 && k < hc.d_eff;
+        if (hc.widths[i] > 0 || sig) wch[w].push_back({k, n, hc.widths[i]});
+        k += n;
+      }
       i = j;
     }
   for (int w = 0; w < NW; ++w) P.n_chunks += (int)wch[w].size();
@@ -184,10 +191,11 @@ static HostPlan build_plan(const HeadCal &hc) {
       C[11] = (uint32_t)b;
       C[12] = (uint32_t)nsig;
       C[13] = (uint32_t)(nsig > 0 && b > 0 ? P.csig.size() : 0);
+      C[14] = (uint32_t)(ch.cnt == 8 ? 3 : ch.cnt == 4 ? 2 : ch.cnt == 2 ? 1 : 0);
       for (int c = 0; c < 8; ++c) C[c] = f32_bits(inf);
       if (b > 0) {
         const size_t tb = P.tree.size();
-        P.tree.resize(tb + 8 * (size_t)L, inf);
+        P.tree.resize(tb + (size_t)ch.cnt * L, inf);
         for (int c = 0; c < ch.cnt; ++c) {
           const int i = ch.start + c;
           // node n (depth k, position p = n - 2^k) holds sorted threshold
@@ -203,7 +211,7 @@ static HostPlan build_plan(const HeadCal &hc) {
         }
         if (nsig > 0) {
           const size_t cb = P.csig.size();
-          P.csig.resize(cb + 8 * (size_t)L, 0.0f);
+          P.csig.resize(cb + (size_t)ch.cnt * L, 0.0f);
           for (int c = 0; c < nsig; ++c)
             for (int k = 0; k < L; ++k)
               P.csig[cb + (size_t)c * L + k] = hc.cent[hc.cent_base[ch.start + c] + k];
@@ -260,15 +268,15 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     float *R = (float *)(img.data() + D.off_R);
     for (int k = 0; k < d * d; ++k) R[k] = (float)hc.R[k];
     // bf16 x3 split of R (hi + mid + lo reproduces R to ~2^-24 relative), laid
-    // out as MFMA 32x32x16 A operands: fragment (s, mb, ks), lane l, element e
-    // holds R_s[mb*32 + l%32][ks*16 + 8*(l/32) + e].
+    // out as MFMA 16x16x32 A operands: fragment (s, mb, kb), lane l, element e
+    // holds R_s[mb*16 + l%16][kb*32 + 8*(l/16) + e].
     uint16_t *F = (uint16_t *)(img.data() + D.off_Rfrag);
-    const int MB = d / 32, KS = d / 16;
+    const int MB = d / 16, KB = d / 32;
     for (int mb = 0; mb < MB; ++mb)
-      for (int ks = 0; ks < KS; ++ks)
+      for (int kb = 0; kb < KB; ++kb)
         for (int l = 0; l < 64; ++l)
           for (int e = 0; e < 8; ++e) {
-            const int row = mb * 32 + (l & 31), col = ks * 16 + 8 * (l >> 5) + e;
+            const int row = mb * 16 + (l & 15), col = kb * 32 + 8 * (l >> 4) + e;
             double v = hc.R[(size_t)row * d + col];
             uint16_t parts[3];
             for (int s = 0; s < 3; ++s) {
@@ -279,7 +287,7 @@ sq_status upload_tables(sq_calib *c, void *stream) {
               v -= (double)back;
             }
             for (int s = 0; s < 3; ++s)
-              F[((((size_t)s * MB + mb) * KS + ks) * 64 + l) * 8 + e] = parts[s];
+              F[((((size_t)s * MB + mb) * KB + kb) * 64 + l) * 8 + e] = parts[s];
           }
     DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
     uint32_t *Dd = (uint32_t *)(img.data() + D.off_desc);
@@ -329,25 +337,27 @@ sq_status upload_tables(sq_calib *c, void *stream) {
 
 // ------------------------------------------------------------------ compress
 //
-// A workgroup of D/32 waves serves one calibration head and walks many
-// 64-token tiles.  Wave w owns eigen-coordinates [32w, 32w+32):
-//   rotate:   y^T[coord][token] = R x^T with MFMA 32x32x16 bf16.  R is split
-//             into three bf16 terms (Henry, Tang & Heinecke, ARITH 2019:
-//             bf16x3) so every product is exact in the fp32 accumulator; for
-//             head_dim <= 128 the wave's 32 rows of the three terms stay in
-//             registers for the workgroup's whole life, for 256 they are read
-//             per tile from the L2.  fp32 inputs are split into three terms as
-//             well and the six leading cross products are accumulated.  The
-//             x tile (B operand) is shared through LDS.
-//   quantise: the accumulators go to an LDS y tile; lane = token walks the
-//             wave's 32 coordinates in groups of 8 whose binary searches over
-//             the thresholds (LDS) advance in lock-step; the code replaces y in
-//             the tile, signal coordinates also leave their residual.
-//   pack:     after a workgroup barrier each wave assembles a share of the W
-//             record words (lane = token) from the codes of every coordinate
-//             that reaches into the word, the QJL bits z_j = [(S r)_j >= 0]
-//             that fall in it and, in word W-1, gamma = |r| as IEEE half; one
-//             coalesced 256-byte store per word.
+// A workgroup of D/16 waves serves one calibration head and walks many
+// 64-token tiles.
+//   rotate:   wave w computes y^T[coord][token] = R x^T for eigen-coordinates
+//             [16w, 16w+16) with MFMA 16x16x32 bf16.  R is split into three
+//             bf16 terms (Henry, Tang & Heinecke, ARITH 2019: bf16x3) so every
+//             product is exact in the fp32 accumulator; for head_dim <= 128 the
+//             wave's 16 rows of the three terms stay in registers for the
+//             workgroup's whole life, for 256 they are read per tile from the
+//             L2.  fp32 inputs are split into three terms as well and the six
+//             leading cross products are accumulated.  The x tile (B operand)
+//             is shared through LDS; the accumulators go to an LDS y tile.
+//   quantise: each wave owns a contiguous coordinate range (balanced on the
+//             search cost, not tied to its MFMA rows) cut into chunks of 1, 2,
+//             4 or 8 equal-width coordinates; lane = token, the chunk's binary
+//             searches advance in lock-step (see quant_chunk) and its codes are
+//             appended to a bit window that emits the record words.
+//   pack:     words wholly inside one wave's code bits are stored from its
+//             window; words shared between ranges are OR-ed together in LDS
+//             and, after a barrier, stored by one wave, the last one adding
+//             the QJL bits z_j = [(S r)_j >= 0] and gamma = |r| as IEEE half
+//             in word W-1.  Every store is one coalesced 256-byte row.
 
 struct CompressArgs {
   const DevHead *heads;
@@ -361,6 +371,8 @@ struct CompressArgs {
   int n_tiles;          // ceil(T / 64) per (batch, head)
   int items;            // tiles one head's workgroups share
   int lds_csig_off;     // floats: signal-centroid table (after the trees)
+  int lds_plan_off;     // floats: the head's compress plan
+  int lds_s_off;        // floats: QJL sketch S [m][d_eff], or -1: read from the table blob
   int lds_x_off;        // floats: x tile
   int lds_y_off;        // floats: y tile; residuals replace y in place
   int lds_b_off;        // floats: shared record-word buffer
@@ -384,8 +396,8 @@ __device__ __forceinline__ void split3(const float *v, uint4 &p0, uint4 &p1, uin
   p2 = make_uint4(c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16));
 }
 
-__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
@@ -397,76 +409,121 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// Bit window of one wave's record words while it appends code fields.
+// Bit window of one wave's record words while it appends code fields:
+// bits [0, fill) of lo are filled; lo is word kw of the record.
 struct PackWin {
-  uint32_t lo, hi;
+  uint32_t lo;
   int fill, kw;
 };
 
-// One chunk of <= 8 coordinates of equal width B (lane = token).  The
-// searches of the 8 slots advance together down their breadth-first trees:
+// Emit the window's full word and move on to the next one.  A word wholly
+// inside the wave's code bits goes straight to HBM; a word shared with
+// another wave's range is OR-ed into the LDS word buffer.
+__device__ __forceinline__ void win_flush(PackWin &pw, uint32_t next, uint32_t *dst, uint32_t *bwrow,
+                                          int dfirst, int dend, bool valid) {
+  if (pw.kw >= dfirst && pw.kw < dend) dst[(int64_t)pw.kw * 64] = valid ? pw.lo : 0u;
+  else atomicOr(bwrow + pw.kw, pw.lo);
+  ++pw.kw;
+  pw.lo = next;
+  pw.fill -= 32;
+}
+
+// One chunk of NS (1, 2, 4 or 8) coordinates of equal width B (lane =
+// token).  The NS searches advance together down their breadth-first trees:
 // the root comes from a scalar register, each further level is one table
 // read at a compile-time offset; the step is decided by the sign of
 // (threshold - y), so a tie goes to the lower cell and the code is
 // #{thresholds < y}.  NaN coordinates are mapped to -inf first (code 0).
-// Codes are appended to the window in coordinate order; residuals of signal
+// The chunk's NS * B code bits are assembled at compile-time shifts into one
+// 64-bit value and appended to the window at once.  Residuals of signal
 // coordinates replace y in the tile.
-template <int B, bool TG>
-__device__ __forceinline__ void quant_chunk(const uint32_t (&cd)[PLAN_WORDS], float *yrow,
-                                            const float *trees, const float *csig, PackWin &pw,
-                                            uint32_t *dst, uint32_t *bwrow, int dfirst, int dend,
-                                            bool valid) {
+struct ChunkArgs {
+  float root[8];  // per coordinate (wave-uniform values)
+  int tbase, start, nsig, cbase;
+};
+
+template <int B, int NS, bool TG>
+__device__ __forceinline__ void quant_chunk(const ChunkArgs &cd, float *yrow, const float *trees,
+                                            const float *csig, PackWin &pw, uint32_t *dst,
+                                            uint32_t *bwrow, int dfirst, int dend, bool valid) {
   constexpr int L = 1 << B;
-  const int start = (int)cd[9], cnt = (int)cd[10], nsig = (int)cd[12];
-  float y[8];
-  uint32_t code[8];
+  const int start = cd.start, nsig = cd.nsig;
+  float y[NS];
+  uint32_t code[NS];
+  const float *ys = yrow + start;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) y[c] = fmaxf(yrow[start + min(c, cnt - 1)], -INFINITY);
+  for (int c = 0; c < NS; ++c) y[c] = fmaxf(ys[c], -INFINITY);
   if constexpr (B > 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) code[c] = __float_as_uint(__uint_as_float(cd[c]) - y[c]) >> 31;
-    const float *tb = trees + cd[8];
+    for (int c = 0; c < NS; ++c) code[c] = __float_as_uint(cd.root[c] - y[c]) >> 31;
+    const float *tb = trees + cd.tbase;
 #pragma unroll
     for (int l = 1; l < B; ++l) {
-      float th[8];
+      float th[NS];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) th[c] = tb[c * L + (1 << l) - 1 + (int)code[c]];
+      for (int c = 0; c < NS; ++c) th[c] = tb[c * L + (1 << l) - 1 + (int)code[c]];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < NS; ++c)
         code[c] = __builtin_amdgcn_alignbit(code[c], __float_as_uint(th[c] - y[c]), 31);
     }
+    uint32_t v0 = 0u, v1 = 0u;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (c < cnt) {
-        pw.lo |= code[c] << pw.fill;
-        if (pw.fill + B > 32) pw.hi = code[c] >> (32 - pw.fill);
-        pw.fill += B;
-        if (pw.fill >= 32) {
-          if (pw.kw >= dfirst && pw.kw < dend) dst[(int64_t)pw.kw * 64] = valid ? pw.lo : 0u;
-          else atomicOr(bwrow + pw.kw, pw.lo);
-          ++pw.kw;
-          pw.lo = pw.hi;
-          pw.hi = 0;
-          pw.fill -= 32;
-        }
+    for (int c = 0; c < NS; ++c) {
+      const int sh = c * B;
+      if (sh < 32) {
+        v0 |= code[c] << sh;
+        if (sh + B > 32) v1 |= code[c] >> (32 - sh);
+      } else {
+        v1 |= code[c] << (sh - 32);
+      }
+    }
+    // append the NS * B bits of (v1:v0) at bit fill of the window; the
+    // double shifts keep every shift count below 32
+    const int f = pw.fill;
+    pw.lo |= v0 << f;
+    uint32_t w1 = (v0 >> 1) >> (31 - f);
+    uint32_t w2 = 0u;
+    if constexpr (NS * B > 32) {
+      w1 |= v1 << f;
+      w2 = (v1 >> 1) >> (31 - f);
+    }
+    pw.fill += NS * B;
+    if (pw.fill >= 32) {
+      win_flush(pw, w1, dst, bwrow, dfirst, dend, valid);
+      if constexpr (NS * B > 32) {
+        if (pw.fill >= 32) win_flush(pw, w2, dst, bwrow, dfirst, dend, valid);
       }
     }
   }
   if (nsig > 0) {
+    const float *cs = csig + cd.cbase;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < NS; ++c)
       if (c < nsig) {
         float r = y[c];
-        if constexpr (B > 0) r -= csig[cd[13] + c * L + code[c]];
+        if constexpr (B > 0) r -= cs[c * L + code[c]];
         yrow[start + c] = r;
       }
   }
 }
 
+template <int B, bool TG>
+__device__ __forceinline__ void quant_chunk_ns(int lg, const ChunkArgs &cd, float *yrow,
+                                               const float *trees, const float *csig, PackWin &pw,
+                                               uint32_t *dst, uint32_t *bwrow, int dfirst, int dend,
+                                               bool valid) {
+  switch (lg) {
+    case 0: quant_chunk<B, 1, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
+    case 1: quant_chunk<B, 2, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
+    case 2: quant_chunk<B, 4, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
+    default: quant_chunk<B, 8, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
+  }
+}
+
 template <int D, bool F32, bool TG>
-__global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
+__global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
   extern __shared__ float smem[];
-  constexpr int NW = D / 32, KS = D / 16, MB = D / 32, NT = 64 * NW;
+  constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
   constexpr bool RES = D <= 128;           // rotation rows resident in registers
   constexpr int XS = F32 ? D + 4 : D + 8;  // x tile row stride (elements)
   const int lane = threadIdx.x & 63;
@@ -490,24 +547,35 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
     }
     const float *g_csig = (const float *)(a.blob + hd->off_csig);
     for (int k = threadIdx.x; k < n_csig; k += NT) s_csig[k] = g_csig[k];
+    const uint32_t *g_plan = (const uint32_t *)(a.blob + hd->off_plan);
+    uint32_t *s_plan = (uint32_t *)(smem + a.lds_plan_off);
+    const int n_plan = (NW + hd->n_chunks + 1) * PLAN_WORDS;
+    for (int k = threadIdx.x; k < n_plan; k += NT) s_plan[k] = g_plan[k];
+    if (a.lds_s_off >= 0) {
+      const float *g_S = (const float *)(a.blob + hd->off_S);
+      for (int k = threadIdx.x; k < hd->m * hd->d_eff; k += NT) smem[a.lds_s_off + k] = g_S[k];
+    }
   }
   const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag);
-  uint4 rf[RES ? 3 : 1][RES ? KS : 1];
+  uint4 rf[RES ? 3 : 1][RES ? KB : 1];
   if constexpr (RES) {
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) rf[sp][ks] = Rf[((sp * MB + w) * KS + ks) * 64 + lane];
+      for (int kb = 0; kb < KB; ++kb) rf[sp][kb] = Rf[((sp * MB + w) * KB + kb) * 64 + lane];
   }
   const SQ_CONST uint32_t *plan = cptr<uint32_t>(a.blob + hd->off_plan);
-  const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
+  const float *S_lds = smem + max(0, a.lds_s_off);
+  const SQ_CONST float *S_glb = cptr<float>(a.blob + hd->off_S);
   const int64_t T = a.n_tokens;
   const SQ_CONST uint32_t *hdr = plan + w * PLAN_WORDS;
   const int nch = (int)hdr[0];
   const int sbit = (int)(hdr[1] & 0xFFFF);
   const int own_f = (int)(hdr[2] & 0xFFFF), own_e = (int)(hdr[2] >> 16);
   const int dfirst = (int)(hdr[3] & 0xFFFF), dend = (int)(hdr[3] >> 16);
-  const SQ_CONST uint32_t *chunks = plan + (NW + (int)hdr[4]) * PLAN_WORDS;
+  // chunk descriptors are read from the LDS copy of the plan: in-order LDS
+  // reads leave the compiler exact partial waits for the search reads
+  const uint4 *chunks = (const uint4 *)(smem + a.lds_plan_off) + (NW + (int)hdr[4]) * (PLAN_WORDS / 4);
 
   // x tile chunks of 16 bytes: CPR per row, CH per thread; the next tile's
   // chunks are prefetched into registers while the current tile is processed
@@ -545,59 +613,58 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
     __syncthreads();
     if (item + (int)gridDim.x < a.items) load_x(item + gridDim.x);
     for (int k = threadIdx.x; k < 64 * a.bws; k += NT) bwords[k] = 0u;
-    // ---- rotate this wave's 32 coordinates for the 64 tokens
-    f32x16 acc0, acc1;
+    // ---- rotate this wave's 16 coordinates for the 64 tokens (4 blocks of 16)
+    f32x4 acc[4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc0[v] = acc1[v] = 0.0f;
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int kb = 0; kb < KB; ++kb) {
       uint4 r0, r1, r2;
       if constexpr (RES) {
-        r0 = rf[0][ks]; r1 = rf[1][ks]; r2 = rf[2][ks];
+        r0 = rf[0][kb]; r1 = rf[1][kb]; r2 = rf[2][kb];
       } else {
-        r0 = Rf[((0 * MB + w) * KS + ks) * 64 + lane];
-        r1 = Rf[((1 * MB + w) * KS + ks) * 64 + lane];
-        r2 = Rf[((2 * MB + w) * KS + ks) * 64 + lane];
+        r0 = Rf[((0 * MB + w) * KB + kb) * 64 + lane];
+        r1 = Rf[((1 * MB + w) * KB + kb) * 64 + lane];
+        r2 = Rf[((2 * MB + w) * KB + kb) * 64 + lane];
       }
-      const int koff = ks * 16 + 8 * (lane >> 5);
+      const int koff = kb * 32 + 8 * (lane >> 4);
       if constexpr (!F32) {
         const uint16_t *xt = (const uint16_t *)(smem + a.lds_x_off);
-        const uint4 x0 = *(const uint4 *)(xt + (lane & 31) * XS + koff);
-        const uint4 x1 = *(const uint4 *)(xt + (32 + (lane & 31)) * XS + koff);
-        acc0 = mfma32(r0, x0, acc0);
-        acc1 = mfma32(r0, x1, acc1);
-        acc0 = mfma32(r1, x0, acc0);
-        acc1 = mfma32(r1, x1, acc1);
-        acc0 = mfma32(r2, x0, acc0);
-        acc1 = mfma32(r2, x1, acc1);
+        uint4 xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[j] = *(const uint4 *)(xt + (16 * j + (lane & 15)) * XS + koff);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r0, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r1, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r2, xv[j], acc[j]);
       } else {
         const float *xt = smem + a.lds_x_off;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const float *src = xt + (nb * 32 + (lane & 31)) * XS + koff;
+        for (int j = 0; j < 4; ++j) {
+          const float *src = xt + (16 * j + (lane & 15)) * XS + koff;
           float v[8];
           const float4 u0 = *(const float4 *)src, u1 = *(const float4 *)(src + 4);
           v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
           v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
           uint4 x0, x1, x2;
           split3(v, x0, x1, x2);
-          f32x16 &acc = nb == 0 ? acc0 : acc1;
-          acc = mfma32(r0, x0, acc);
-          acc = mfma32(r0, x1, acc);
-          acc = mfma32(r1, x0, acc);
-          acc = mfma32(r0, x2, acc);
-          acc = mfma32(r2, x0, acc);
-          acc = mfma32(r1, x1, acc);
+          acc[j] = mfma16(r0, x0, acc[j]);
+          acc[j] = mfma16(r0, x1, acc[j]);
+          acc[j] = mfma16(r1, x0, acc[j]);
+          acc[j] = mfma16(r0, x2, acc[j]);
+          acc[j] = mfma16(r2, x0, acc[j]);
+          acc[j] = mfma16(r1, x1, acc[j]);
         }
       }
     }
-    // accumulator (row = coordinate, column = token) -> y tile [token][coordinate]
+    // accumulators (row = coordinate, column = token) -> y tile [token][coordinate]
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = 32 * w + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      ytile[(lane & 31) * a.ys + row] = acc0[v];
-      ytile[(32 + (lane & 31)) * a.ys + row] = acc1[v];
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ytile[(16 * j + (lane & 15)) * a.ys + 16 * w + 4 * (lane >> 4) + r] = acc[j][r];
     __syncthreads();
     // ---- quantise + pack (lane = token), chunk by chunk through the plan.
     // Words wholly inside the wave's code bits go straight to HBM, shared
@@ -607,27 +674,36 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
     uint32_t *bwrow = bwords + lane * a.bws;
     float *yrow = ytile + lane * a.ys;
     {
-      PackWin pw{0u, 0u, sbit & 31, sbit >> 5};
-      uint32_t cur[PLAN_WORDS];
+      PackWin pw{0u, sbit & 31, sbit >> 5};
+      uint4 nx[4];
 #pragma unroll
-      for (int k = 0; k < PLAN_WORDS; ++k) cur[k] = chunks[k];
+      for (int k = 0; k < 4; ++k) nx[k] = chunks[k];
       for (int q = 0; q < nch; ++q) {
-        uint32_t nxt[PLAN_WORDS];  // the plan ends with a spare chunk
+        const uint4 c0 = nx[0], c1 = nx[1], c2 = nx[2], c3 = nx[3];
 #pragma unroll
-        for (int k = 0; k < PLAN_WORDS; ++k) nxt[k] = chunks[(q + 1) * PLAN_WORDS + k];
-        switch (cur[11]) {
-          case 0: quant_chunk<0, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 1: quant_chunk<1, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 2: quant_chunk<2, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 3: quant_chunk<3, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 4: quant_chunk<4, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 5: quant_chunk<5, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 6: quant_chunk<6, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 7: quant_chunk<7, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          default: quant_chunk<8, TG>(cur, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+        for (int k = 0; k < 4; ++k) nx[k] = chunks[(q + 1) * 4 + k];  // the plan ends with a spare chunk
+        ChunkArgs ca;
+        ca.root[0] = __uint_as_float(c0.x); ca.root[1] = __uint_as_float(c0.y);
+        ca.root[2] = __uint_as_float(c0.z); ca.root[3] = __uint_as_float(c0.w);
+        ca.root[4] = __uint_as_float(c1.x); ca.root[5] = __uint_as_float(c1.y);
+        ca.root[6] = __uint_as_float(c1.z); ca.root[7] = __uint_as_float(c1.w);
+        ca.tbase = __builtin_amdgcn_readfirstlane(c2.x);
+        ca.start = __builtin_amdgcn_readfirstlane(c2.y);
+        const int bw = __builtin_amdgcn_readfirstlane(c2.w);
+        ca.nsig = __builtin_amdgcn_readfirstlane(c3.x);
+        ca.cbase = __builtin_amdgcn_readfirstlane(c3.y);
+        const int lg = __builtin_amdgcn_readfirstlane(c3.z);  // log2 of the coordinate count
+        switch (bw) {
+          case 0: quant_chunk_ns<0, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 1: quant_chunk_ns<1, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 2: quant_chunk_ns<2, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 3: quant_chunk_ns<3, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 4: quant_chunk_ns<4, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 5: quant_chunk_ns<5, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 6: quant_chunk_ns<6, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          case 7: quant_chunk_ns<7, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
+          default: quant_chunk_ns<8, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
         }
-#pragma unroll
-        for (int k = 0; k < PLAN_WORDS; ++k) cur[k] = nxt[k];
       }
       if (pw.fill > 0) {  // last, partial word of the range
         if (pw.kw >= dfirst && pw.kw < dend) dst[(int64_t)pw.kw * 64] = valid ? pw.lo : 0u;
@@ -645,7 +721,11 @@ __global__ __launch_bounds__(D * 2) void compress_kernel(CompressArgs a) {
         const int jb = max(0, lo_bit - code_bits), je = min(m, hi_bit - code_bits);
         for (int j = jb; j < je; ++j) {
           float dot = 0.0f;
-          for (int i = 0; i < d_eff; ++i) dot = fmaf(S[j * d_eff + i], yrow[i], dot);
+          if (a.lds_s_off >= 0) {
+            for (int i = 0; i < d_eff; ++i) dot = fmaf(S_lds[j * d_eff + i], yrow[i], dot);
+          } else {
+            for (int i = 0; i < d_eff; ++i) dot = fmaf(S_glb[j * d_eff + i], yrow[i], dot);
+          }
           word |= (dot >= 0.0f ? 1u : 0u) << (code_bits + j - lo_bit);
         }
         if (k == W - 1) {
@@ -698,7 +778,6 @@ struct ScoresArgs {
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma4(uint2 a, uint2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a),
@@ -1214,7 +1293,7 @@ extern "C" sq_status sq_calib_upload(sq_calib *c, sq_stream stream) {
 
 template <int D, bool F32, bool TG>
 static void launch_compress(dim3 grid, size_t lds, hipStream_t s, const CompressArgs &a) {
-  hipLaunchKernelGGL((compress_kernel<D, F32, TG>), grid, dim3(2 * D), lds, s, a);
+  hipLaunchKernelGGL((compress_kernel<D, F32, TG>), grid, dim3(4 * D), lds, s, a);
 }
 
 template <int D>
@@ -1253,12 +1332,15 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   if (xs_token < d) return fail(SQ_ERR_ARG, "sq_compress: xs_token < head_dim");
   if (n_tokens > ((int64_t)1 << 36)) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many tokens");
   // LDS: threshold trees | signal centroids | x tile | y tile | word buffer
-  int max_tree = 0, max_csig = 0;
+  int max_tree = 0, max_csig = 0, max_plan = 0, max_s = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
     for (int h = 0; h < n_heads; ++h) {
       const int k = first_head + bb * calib_batch_stride + h;
-      max_tree = std::max(max_tree, c->host_desc[k].n_tree);
-      max_csig = std::max(max_csig, c->host_desc[k].n_csig);
+      const DevHead &hd = c->host_desc[k];
+      max_tree = std::max(max_tree, hd.n_tree);
+      max_csig = std::max(max_csig, hd.n_csig);
+      max_plan = std::max(max_plan, (hd.d / 16 + hd.n_chunks + 1) * PLAN_WORDS);
+      max_s = std::max(max_s, hd.m * hd.d_eff);
     }
     if (calib_batch_stride == 0) break;  // every batch entry uses the same heads
   }
@@ -1266,14 +1348,18 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   a.ys = d + 1;
   a.bws = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
   const int xs_floats = dt == SQ_F32 ? 64 * (d + 4) : 64 * (d + 8) / 2;
-  const int rest = ((max_csig + 3) & ~3) + xs_floats + 64 * a.ys + 64 * a.bws;
+  const bool s_in_lds = max_s <= 4096;  // a large sketch is read from the L1/L2 instead
+  const int s_floats = s_in_lds ? ((max_s + 3) & ~3) : 0;
+  const int rest = ((max_csig + 3) & ~3) + max_plan + s_floats + xs_floats + 64 * a.ys + 64 * a.bws;
   const size_t limit = (size_t)device_lds_limit();
   const size_t lds_in = (size_t)(((max_tree + 3) & ~3) + rest) * 4, lds_out = (size_t)rest * 4;
   // trees stay in LDS unless moving them out is what lets two workgroups share a CU
   const bool tg = lds_in > limit || (lds_in > limit / 2 && lds_out <= limit / 2);
   const int tree_floats = tg ? 0 : ((max_tree + 3) & ~3);
   a.lds_csig_off = tree_floats;
-  a.lds_x_off = a.lds_csig_off + ((max_csig + 3) & ~3);
+  a.lds_plan_off = a.lds_csig_off + ((max_csig + 3) & ~3);
+  a.lds_s_off = s_in_lds ? a.lds_plan_off + max_plan : -1;
+  a.lds_x_off = a.lds_plan_off + max_plan + s_floats;
   a.lds_y_off = a.lds_x_off + xs_floats;
   a.lds_b_off = a.lds_y_off + 64 * a.ys;
   const size_t lds = (size_t)(a.lds_b_off + 64 * a.bws) * 4;

@@ -5,7 +5,8 @@ Acceptance (the SpectralQuant build's parity bar):
   * codes bit-exact wherever the oracle's rotated coordinate is farther than
     1e-4 * sigma_i from every threshold; inside that band only +-1 flips;
   * QJL bits exact unless |(S r)_j| <= 1e-3 ||S_j|| ||r|| or a signal code flipped;
-  * gamma within one half-precision ulp (or any value when a signal code flipped);
+  * gamma within one half-precision ulp plus the rotation's forward error bound
+    sqrt(d_eff) (d + 1) 2^-24 |x| (any value when a signal code flipped);
   * dequantised vectors, scores and attention outputs within 1e-3 relative with a
     floor: |gpu - ref| <= 1e-3 * (|ref| + floor).
 """
@@ -90,8 +91,16 @@ def compare_compress(oc, gpu_slot: np.ndarray, x: np.ndarray, T: int):
         assert not np.any(bad), f"{int(bad.sum())} QJL bit mismatches outside the band"
         gu = gg.view(np.uint16).astype(np.int64)
         ru = res.gamma.view(np.uint16).astype(np.int64)
-        gbad = (np.abs(gu - ru) > 1) & ~sig_flip
-        assert not np.any(gbad), f"{int(gbad.sum())} gamma values off by more than one ulp"
+        # gamma = |r| inherits the rotation's absolute rounding error: each y_i
+        # of an fp32 dot product of d exact products is within (d + 1) u |x|
+        # (u = 2^-24; the +1 covers the bf16x3 representation of R), so |r|
+        # moves by at most sqrt(d_eff) times that, then one fp16 rounding.
+        g_ref = res.gamma.astype(np.float64)
+        ulp16 = np.exp2(np.floor(np.log2(np.maximum(g_ref, 2.0 ** -14))) - 10)
+        xn = np.linalg.norm(np.asarray(x, np.float64), axis=1)
+        tol = ulp16 + math.sqrt(oc.d_eff) * (oc.head_dim + 1) * 2.0 ** -24 * xn
+        gbad = (np.abs(gg.astype(np.float64) - g_ref) > tol) & ~sig_flip
+        assert not np.any(gbad), f"{int(gbad.sum())} gamma values outside one ulp + rotation error"
         out["qjl_flips"] = int(zd.sum())
         out["gamma_ulp"] = int((gu != ru).sum())
     # tokens with no excused difference must match bit for bit (gamma aside)
