@@ -101,22 +101,73 @@ static uint32_t f32_bits(float v) {
   return u;
 }
 
+// Does the compress kernel fold the QJL sketch into the quantiser of wave 0?
+// (Small sketches: the whole signal range then lies in wave 0's coordinates.)
+static bool qjl_inline(const HeadCal &hc) { return hc.m > 0 && hc.m <= 8 && hc.d_eff <= 8; }
+
+// Estimated cycles of one chunk of n coordinates of width b: each tree level
+// is one dependent LDS round trip, plus the issue of ~3b + 2 VALU per slot.
+static double chunk_cost(int b, int n) { return 300.0 * (b + 1) + 8.0 * n * (3 * b + 2) + 150.0; }
+
+// Cost of a run of n equal-width coordinates, cut into chunks of 8, 4, 2, 1.
+static double run_cost(int b, int n) {
+  double c = 0.0;
+  while (n > 0) {
+    int k = 8;
+    while (k > n) k >>= 1;
+    c += chunk_cost(b, k);
+    n -= k;
+  }
+  return c;
+}
+
 static HostPlan build_plan(const HeadCal &hc) {
   const int d = hc.d, NW = d / 16;
   HostPlan P;
-  // wave ranges balanced on the quantiser's cost (~3 ops per tree level + 4)
-  int total = 0;
-  for (int i = 0; i < d; ++i) total += 3 * hc.widths[i] + 4;
+  // Wave ranges: contiguous, minimising the largest estimated quantiser time
+  // (dynamic programme over cut points); with the QJL folded in, wave 0 must
+  // hold the whole signal range.
+  const bool qin = qjl_inline(hc);
+  std::vector<double> rc((size_t)(d + 1) * (d + 1), 0.0);  // rc[a*(d+1)+b]: cost of [a, b)
+  for (int a0 = 0; a0 < d; ++a0) {
+    double done = 0.0;
+    int rw = -1, rn = 0;
+    for (int b1 = a0 + 1; b1 <= d; ++b1) {
+      const int wd = hc.widths[b1 - 1];
+      if (wd != rw) {
+        if (rn && rw > 0) done += run_cost(rw, rn);
+        rw = wd;
+        rn = 0;
+      }
+      ++rn;
+      rc[(size_t)a0 * (d + 1) + b1] = done + (rw > 0 ? run_cost(rw, rn) : 0.0);
+    }
+  }
+  const double INF = 1e30;
+  if (qin) {
+    for (int b1 = 0; b1 < hc.d_eff; ++b1) rc[b1] = INF;   // wave 0 = [0, b1) needs b1 >= d_eff
+    for (int b1 = hc.d_eff; b1 <= d; ++b1) rc[b1] += 8.0 * hc.m * hc.d_eff + 500.0;
+  }
+  // f[k][b]: best max cost of covering [0, b) with k waves
+  std::vector<double> f((size_t)(NW + 1) * (d + 1), INF);
+  std::vector<int> arg((size_t)(NW + 1) * (d + 1), 0);
+  f[0] = 0.0;
+  for (int k = 1; k <= NW; ++k)
+    for (int b1 = 0; b1 <= d; ++b1)
+      for (int a0 = 0; a0 <= b1; ++a0) {
+        const double prev = f[(size_t)(k - 1) * (d + 1) + a0];
+        if (prev >= INF) continue;
+        const double c = std::max(prev, rc[(size_t)a0 * (d + 1) + b1]);
+        if (c < f[(size_t)k * (d + 1) + b1]) {
+          f[(size_t)k * (d + 1) + b1] = c;
+          arg[(size_t)k * (d + 1) + b1] = a0;
+        }
+      }
   std::vector<int> cut(NW + 1, d);
   cut[0] = 0;
-  {
-    int acc = 0, w = 1;
-    for (int i = 0; i < d && w < NW; ++i) {
-      acc += 3 * hc.widths[i] + 4;
-      if (acc * NW >= total * w) cut[w++] = i + 1;
-    }
-    for (; w < NW; ++w) cut[w] = d;
-    for (int w2 = 1; w2 <= NW; ++w2) cut[w2] = std::max(cut[w2], cut[w2 - 1]);
+  for (int k = NW, b1 = d; k >= 1; --k) {
+    cut[k] = b1;
+    b1 = arg[(size_t)k * (d + 1) + b1];
   }
   std::vector<int> sbit(NW), ebit(NW);
   for (int w = 0; w < NW; ++w) {
@@ -181,6 +232,12 @@ static HostPlan build_plan(const HeadCal &hc) {
     H[2] = (uint32_t)f | ((uint32_t)e << 16);
     H[3] = (uint32_t)dfirst[w] | ((uint32_t)dend[w] << 16);
     H[4] = (uint32_t)q;
+    if (qin && w == 0) {
+      int n_sig_chunks = 0;
+      for (const Ch &ch : wch[w])
+        if (ch.start < hc.d_eff) ++n_sig_chunks;
+      H[5] = (uint32_t)n_sig_chunks;
+    }
     for (const Ch &ch : wch[w]) {
       uint32_t *C = P.words.data() + (size_t)(NW + q) * PLAN_WORDS;
       const int b = ch.b, L = 1 << b;
@@ -373,10 +430,11 @@ struct CompressArgs {
   int lds_csig_off;     // floats: signal-centroid table (after the trees)
   int lds_plan_off;     // floats: the head's compress plan
   int lds_s_off;        // floats: QJL sketch S [m][d_eff], or -1: read from the table blob
+  int lds_sp_off;       // floats: S zero-padded to [8][8] (used when m, d_eff <= 8)
   int lds_x_off;        // floats: x tile
   int lds_y_off;        // floats: y tile; residuals replace y in place
   int lds_b_off;        // floats: shared record-word buffer
-  int ys;               // y tile row stride (floats, odd)
+  int ys;               // y tile row stride (floats, d + 3)
   int bws;              // word buffer row stride (words, odd)
 };
 
@@ -416,12 +474,12 @@ struct PackWin {
   int fill, kw;
 };
 
-// Emit the window's full word and move on to the next one.  A word wholly
-// inside the wave's code bits goes straight to HBM; a word shared with
-// another wave's range is OR-ed into the LDS word buffer.
-__device__ __forceinline__ void win_flush(PackWin &pw, uint32_t next, uint32_t *dst, uint32_t *bwrow,
-                                          int dfirst, int dend, bool valid) {
-  if (pw.kw >= dfirst && pw.kw < dend) dst[(int64_t)pw.kw * 64] = valid ? pw.lo : 0u;
+// Emit the window's full word into the LDS word buffer and move on to the
+// next one.  A word wholly inside the wave's code bits is written; a word
+// shared with another wave's range is OR-ed in.
+__device__ __forceinline__ void win_flush(PackWin &pw, uint32_t next, uint32_t *bwrow, int dfirst,
+                                          int dend) {
+  if (pw.kw >= dfirst && pw.kw < dend) bwrow[pw.kw] = pw.lo;
   else atomicOr(bwrow + pw.kw, pw.lo);
   ++pw.kw;
   pw.lo = next;
@@ -442,10 +500,17 @@ struct ChunkArgs {
   int tbase, start, nsig, cbase;
 };
 
-template <int B, int NS, bool TG>
+// Running QJL sums of the wave that holds the signal range: the dots
+// (S r)_j and |r|^2, from residuals still in registers.
+struct QjlAcc {
+  float dot[8];
+  float g2;
+};
+
+template <int B, int NS, bool TG, bool QJ>
 __device__ __forceinline__ void quant_chunk(const ChunkArgs &cd, float *yrow, const float *trees,
-                                            const float *csig, PackWin &pw, uint32_t *dst,
-                                            uint32_t *bwrow, int dfirst, int dend, bool valid) {
+                                            const float *csig, PackWin &pw, uint32_t *bwrow,
+                                            int dfirst, int dend, const float *sp, QjlAcc &qa) {
   constexpr int L = 1 << B;
   const int start = cd.start, nsig = cd.nsig;
   float y[NS];
@@ -489,9 +554,9 @@ __device__ __forceinline__ void quant_chunk(const ChunkArgs &cd, float *yrow, co
     }
     pw.fill += NS * B;
     if (pw.fill >= 32) {
-      win_flush(pw, w1, dst, bwrow, dfirst, dend, valid);
+      win_flush(pw, w1, bwrow, dfirst, dend);
       if constexpr (NS * B > 32) {
-        if (pw.fill >= 32) win_flush(pw, w2, dst, bwrow, dfirst, dend, valid);
+        if (pw.fill >= 32) win_flush(pw, w2, bwrow, dfirst, dend);
       }
     }
   }
@@ -502,26 +567,65 @@ __device__ __forceinline__ void quant_chunk(const ChunkArgs &cd, float *yrow, co
       if (c < nsig) {
         float r = y[c];
         if constexpr (B > 0) r -= cs[c * L + code[c]];
-        yrow[start + c] = r;
+        if constexpr (QJ) {  // signal coordinate start + c < 8: column of the padded sketch
+          qa.g2 = fmaf(r, r, qa.g2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qa.dot[j] = fmaf(sp[j * 8 + start + c], r, qa.dot[j]);
+        } else {
+          yrow[start + c] = r;
+        }
       }
   }
 }
 
-template <int B, bool TG>
+template <int B, bool TG, bool QJ>
 __device__ __forceinline__ void quant_chunk_ns(int lg, const ChunkArgs &cd, float *yrow,
                                                const float *trees, const float *csig, PackWin &pw,
-                                               uint32_t *dst, uint32_t *bwrow, int dfirst, int dend,
-                                               bool valid) {
+                                               uint32_t *bwrow, int dfirst, int dend,
+                                               const float *sp, QjlAcc &qa) {
   switch (lg) {
-    case 0: quant_chunk<B, 1, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
-    case 1: quant_chunk<B, 2, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
-    case 2: quant_chunk<B, 4, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
-    default: quant_chunk<B, 8, TG>(cd, yrow, trees, csig, pw, dst, bwrow, dfirst, dend, valid); break;
+    case 0: quant_chunk<B, 1, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 1: quant_chunk<B, 2, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 2: quant_chunk<B, 4, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    default: quant_chunk<B, 8, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
   }
 }
 
+// Decode one chunk descriptor (four 16-byte words from the LDS plan) and run
+// the chunk's quantiser for its width and size.
+template <bool TG, bool QJ>
+__device__ __forceinline__ void run_chunk(uint4 c0, uint4 c1, uint4 c2, uint4 c3, float *yrow,
+                                          const float *trees, const float *csig, PackWin &pw,
+                                          uint32_t *bwrow, int dfirst, int dend, const float *sp,
+                                          QjlAcc &qa) {
+  ChunkArgs ca;
+  ca.root[0] = __uint_as_float(c0.x); ca.root[1] = __uint_as_float(c0.y);
+  ca.root[2] = __uint_as_float(c0.z); ca.root[3] = __uint_as_float(c0.w);
+  ca.root[4] = __uint_as_float(c1.x); ca.root[5] = __uint_as_float(c1.y);
+  ca.root[6] = __uint_as_float(c1.z); ca.root[7] = __uint_as_float(c1.w);
+  ca.tbase = __builtin_amdgcn_readfirstlane(c2.x);
+  ca.start = __builtin_amdgcn_readfirstlane(c2.y);
+  const int bw = __builtin_amdgcn_readfirstlane(c2.w);
+  ca.nsig = __builtin_amdgcn_readfirstlane(c3.x);
+  ca.cbase = __builtin_amdgcn_readfirstlane(c3.y);
+  const int lg = __builtin_amdgcn_readfirstlane(c3.z);  // log2 of the coordinate count
+  switch (bw) {
+    case 0: quant_chunk_ns<0, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 1: quant_chunk_ns<1, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 2: quant_chunk_ns<2, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 3: quant_chunk_ns<3, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 4: quant_chunk_ns<4, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 5: quant_chunk_ns<5, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 6: quant_chunk_ns<6, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 7: quant_chunk_ns<7, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    default: quant_chunk_ns<8, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+  }
+}
+
+// At least 4 waves per SIMD (<= 128 VGPRs): two workgroups per CU for
+// head_dim 128, and what a 16-wave workgroup needs for 256.
 template <int D, bool F32, bool TG>
-__global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
+__global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
   extern __shared__ float smem[];
   constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
   constexpr bool RES = D <= 128;           // rotation rows resident in registers
@@ -551,9 +655,12 @@ __global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
     uint32_t *s_plan = (uint32_t *)(smem + a.lds_plan_off);
     const int n_plan = (NW + hd->n_chunks + 1) * PLAN_WORDS;
     for (int k = threadIdx.x; k < n_plan; k += NT) s_plan[k] = g_plan[k];
-    if (a.lds_s_off >= 0) {
-      const float *g_S = (const float *)(a.blob + hd->off_S);
+    const float *g_S = (const float *)(a.blob + hd->off_S);
+    if (a.lds_s_off >= 0)
       for (int k = threadIdx.x; k < hd->m * hd->d_eff; k += NT) smem[a.lds_s_off + k] = g_S[k];
+    if (threadIdx.x < 64) {
+      const int j = threadIdx.x >> 3, i = threadIdx.x & 7;
+      smem[a.lds_sp_off + threadIdx.x] = (j < hd->m && i < hd->d_eff) ? g_S[j * hd->d_eff + i] : 0.0f;
     }
   }
   const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag);
@@ -573,6 +680,7 @@ __global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
   const int sbit = (int)(hdr[1] & 0xFFFF);
   const int own_f = (int)(hdr[2] & 0xFFFF), own_e = (int)(hdr[2] >> 16);
   const int dfirst = (int)(hdr[3] & 0xFFFF), dend = (int)(hdr[3] >> 16);
+  const int nsc = (int)hdr[5];  // leading chunks with signal coordinates (small sketch, wave 0)
   // chunk descriptors are read from the LDS copy of the plan: in-order LDS
   // reads leave the compiler exact partial waits for the search reads
   const uint4 *chunks = (const uint4 *)(smem + a.lds_plan_off) + (NW + (int)hdr[4]) * (PLAN_WORDS / 4);
@@ -596,12 +704,30 @@ __global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
     }
   };
   if (blockIdx.x < a.items) load_x(blockIdx.x);
+  // The record words of a tile are assembled in the LDS word buffer and stored
+  // at the top of the next tile, before the next prefetch is issued: each
+  // wait for a prefetch then covers only memory operations issued a whole
+  // tile earlier.  A wave stores the words it finalises (its direct words and
+  // the shared words it owns) and zeroes the shared ones for the next tile.
+  for (int k = threadIdx.x; k < 64 * a.bws; k += NT) bwords[k] = 0u;
+  uint32_t *const bwrow = bwords + lane * a.bws;
+  uint32_t *pdst = nullptr;  // destination of the previous tile's records
+  bool pvalid = false;
+  auto store_prev = [&]() {
+    for (int k = dfirst; k < dend; ++k) pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
+    for (int k = own_f; k < own_e; ++k) {
+      if (k >= dfirst && k < dend) continue;
+      pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
+      bwrow[k] = 0u;
+    }
+  };
 
   for (int item = blockIdx.x; item < a.items; item += gridDim.x) {
     const int b = a.cbs ? bz : item / a.n_tiles;
     const int tile = a.cbs ? item : item % a.n_tiles;
     const int64_t t0 = (int64_t)tile * 64;
-    // ---- prefetched x tile -> LDS, then start loading the next one
+    // ---- prefetched x tile -> LDS, previous tile's records -> HBM, then
+    // start loading the next tile
     {
       char *xt = (char *)(smem + a.lds_x_off);
 #pragma unroll
@@ -610,9 +736,9 @@ __global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
         *(uint4 *)(xt + (c / CPR) * XS * ESZ + (c % CPR) * 16) = xr[q];
       }
     }
+    if (pdst) store_prev();
     __syncthreads();
     if (item + (int)gridDim.x < a.items) load_x(item + gridDim.x);
-    for (int k = threadIdx.x; k < 64 * a.bws; k += NT) bwords[k] = 0u;
     // ---- rotate this wave's 16 coordinates for the 64 tokens (4 blocks of 16)
     f32x4 acc[4];
 #pragma unroll
@@ -666,57 +792,55 @@ __global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
       for (int r = 0; r < 4; ++r)
         ytile[(16 * j + (lane & 15)) * a.ys + 16 * w + 4 * (lane >> 4) + r] = acc[j][r];
     __syncthreads();
-    // ---- quantise + pack (lane = token), chunk by chunk through the plan.
-    // Words wholly inside the wave's code bits go straight to HBM, shared
-    // words are OR-ed into the LDS word buffer.
-    uint32_t *dst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
-    const bool valid = t0 + lane < T;
-    uint32_t *bwrow = bwords + lane * a.bws;
+    // ---- quantise + pack (lane = token), chunk by chunk through the plan,
+    // into the LDS word buffer.  With a small sketch (m, d_eff <= 8) wave 0
+    // holds the whole signal range and adds the QJL bits and gamma itself.
     float *yrow = ytile + lane * a.ys;
+    const bool qin = m > 0 && m <= 8 && d_eff <= 8 && w == 0;
+    const float *sp = smem + a.lds_sp_off;
     {
       PackWin pw{0u, sbit & 31, sbit >> 5};
+      int q = 0;
+      if (qin) {  // the leading signal chunks, then the QJL bits and gamma
+        QjlAcc qa;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qa.dot[j] = 0.0f;
+        qa.g2 = 0.0f;
+        for (; q < nsc; ++q)
+          run_chunk<TG, true>(chunks[q * 4], chunks[q * 4 + 1], chunks[q * 4 + 2], chunks[q * 4 + 3],
+                              yrow, trees, s_csig, pw, bwrow, dfirst, dend, sp, qa);
+        uint32_t z = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z |= (j < m && qa.dot[j] >= 0.0f ? 1u : 0u) << j;
+        const int k0 = code_bits >> 5, sh = code_bits & 31;
+        atomicOr(bwrow + k0, z << sh);
+        if (sh + m > 32) atomicOr(bwrow + k0 + 1, z >> (32 - sh));
+        atomicOr(bwrow + W - 1, half_bits_rne(sqrtf(qa.g2)) << 16);
+      }
+      QjlAcc no_qjl;  // unused by the chunks below
       uint4 nx[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) nx[k] = chunks[k];
-      for (int q = 0; q < nch; ++q) {
+      for (int k = 0; k < 4; ++k) nx[k] = chunks[q * 4 + k];
+      for (; q < nch; ++q) {
         const uint4 c0 = nx[0], c1 = nx[1], c2 = nx[2], c3 = nx[3];
 #pragma unroll
         for (int k = 0; k < 4; ++k) nx[k] = chunks[(q + 1) * 4 + k];  // the plan ends with a spare chunk
-        ChunkArgs ca;
-        ca.root[0] = __uint_as_float(c0.x); ca.root[1] = __uint_as_float(c0.y);
-        ca.root[2] = __uint_as_float(c0.z); ca.root[3] = __uint_as_float(c0.w);
-        ca.root[4] = __uint_as_float(c1.x); ca.root[5] = __uint_as_float(c1.y);
-        ca.root[6] = __uint_as_float(c1.z); ca.root[7] = __uint_as_float(c1.w);
-        ca.tbase = __builtin_amdgcn_readfirstlane(c2.x);
-        ca.start = __builtin_amdgcn_readfirstlane(c2.y);
-        const int bw = __builtin_amdgcn_readfirstlane(c2.w);
-        ca.nsig = __builtin_amdgcn_readfirstlane(c3.x);
-        ca.cbase = __builtin_amdgcn_readfirstlane(c3.y);
-        const int lg = __builtin_amdgcn_readfirstlane(c3.z);  // log2 of the coordinate count
-        switch (bw) {
-          case 0: quant_chunk_ns<0, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 1: quant_chunk_ns<1, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 2: quant_chunk_ns<2, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 3: quant_chunk_ns<3, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 4: quant_chunk_ns<4, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 5: quant_chunk_ns<5, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 6: quant_chunk_ns<6, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          case 7: quant_chunk_ns<7, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-          default: quant_chunk_ns<8, TG>(lg, ca, yrow, trees, s_csig, pw, dst, bwrow, dfirst, dend, valid); break;
-        }
+        run_chunk<TG, false>(c0, c1, c2, c3, yrow, trees, s_csig, pw, bwrow, dfirst, dend, sp, no_qjl);
       }
       if (pw.fill > 0) {  // last, partial word of the range
-        if (pw.kw >= dfirst && pw.kw < dend) dst[(int64_t)pw.kw * 64] = valid ? pw.lo : 0u;
+        if (pw.kw >= dfirst && pw.kw < dend) bwrow[pw.kw] = pw.lo;
         else atomicOr(bwrow + pw.kw, pw.lo);
       }
     }
     __syncthreads();
-    // ---- shared words owned by this wave (the last wave adds QJL bits and
-    // gamma from the residuals, which replaced y of the signal coordinates)
-    for (int k = own_f; k < own_e; ++k) {
+    // ---- larger sketches: the last wave adds the QJL bits and gamma to the
+    // words it owns, from the residuals, which replaced y of the signal
+    // coordinates in the tile
+    const bool qslow = m > 0 && !(m <= 8 && d_eff <= 8);
+    for (int k = own_f; k < own_e && qslow && w == NW - 1; ++k) {
       if (k >= dfirst && k < dend) continue;
       uint32_t word = bwrow[k];
-      if (m > 0) {
+      {
         const int lo_bit = 32 * k, hi_bit = lo_bit + 32;
         const int jb = max(0, lo_bit - code_bits), je = min(m, hi_bit - code_bits);
         for (int j = jb; j < je; ++j) {
@@ -734,12 +858,15 @@ __global__ __launch_bounds__(D * 4) void compress_kernel(CompressArgs a) {
           word |= half_bits_rne(sqrtf(g2)) << 16;
         }
       }
-      dst[(int64_t)k * 64] = valid ? word : 0u;
+      bwrow[k] = word;
     }
+    pdst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
+    pvalid = t0 + lane < T;
     // The x tile was last read by the MFMAs, which every wave finished before
     // the barrier above; the y tile and the word buffer are rewritten only
     // after the barrier that follows the next x store.
   }
+  if (pdst) store_prev();
 }
 
 // ------------------------------------------------------------------ scores
@@ -1345,12 +1472,12 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
     if (calib_batch_stride == 0) break;  // every batch entry uses the same heads
   }
   CompressArgs a{};
-  a.ys = d + 1;
+  a.ys = d + 3;  // odd, and conflict-free for the MFMA-layout stores
   a.bws = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
   const int xs_floats = dt == SQ_F32 ? 64 * (d + 4) : 64 * (d + 8) / 2;
   const bool s_in_lds = max_s <= 4096;  // a large sketch is read from the L1/L2 instead
   const int s_floats = s_in_lds ? ((max_s + 3) & ~3) : 0;
-  const int rest = ((max_csig + 3) & ~3) + max_plan + s_floats + xs_floats + 64 * a.ys + 64 * a.bws;
+  const int rest = ((max_csig + 3) & ~3) + max_plan + s_floats + 64 + xs_floats + 64 * a.ys + 64 * a.bws;
   const size_t limit = (size_t)device_lds_limit();
   const size_t lds_in = (size_t)(((max_tree + 3) & ~3) + rest) * 4, lds_out = (size_t)rest * 4;
   // trees stay in LDS unless moving them out is what lets two workgroups share a CU
@@ -1359,7 +1486,8 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   a.lds_csig_off = tree_floats;
   a.lds_plan_off = a.lds_csig_off + ((max_csig + 3) & ~3);
   a.lds_s_off = s_in_lds ? a.lds_plan_off + max_plan : -1;
-  a.lds_x_off = a.lds_plan_off + max_plan + s_floats;
+  a.lds_sp_off = a.lds_plan_off + max_plan + s_floats;
+  a.lds_x_off = a.lds_sp_off + 64;
   a.lds_y_off = a.lds_x_off + xs_floats;
   a.lds_b_off = a.lds_y_off + 64 * a.ys;
   const size_t lds = (size_t)(a.lds_b_off + 64 * a.bws) * 4;
