@@ -1123,14 +1123,24 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
 // ------------------------------------------------------------------ attend
 //
 // Split-T softmax-weighted value sum in the rotated value space.  Kernel 1:
-// one workgroup per (batch, KV head, chunk of ATT_CHUNK tokens) computes, for
-// each query head of the group, the chunk max of scale*s, sum exp(scale*s -
-// max) and the partial sum over tokens of p_t * C_v[code] (thread = (token
-// slot, coordinate); records staged transposed in LDS).  Kernel 2: one
-// workgroup per (batch, query head) combines the chunks in order (no atomics,
+// one wave per (batch, KV head, chunk of ATT_CHUNK tokens, block of 64
+// eigen-coordinates), lane = coordinate.  Per 64-token tile the record words
+// its coordinates touch are staged straight from HBM into LDS (word-major,
+// row stride ATT_RS, so lanes reading different words of one token hit
+// different banks); the query group's scores give an online softmax (running
+// max, rescaled sums) whose weights p are kept in LDS as bf16 hi/lo pairs.
+// Each lane decodes its coordinate for 4 tokens at a time into C_v[code] as
+// bf16 hi/lo pairs and v_mfma_f32_4x4x4_16b_bf16 forms sum_t p_t C_v[code_t]:
+// in block b, lane 4b+n supplies the 4 tokens of coordinate 4b+n (B operand),
+// lane 4b+m the weights of query head m (A operand), and the accumulator of
+// lane 4b+n holds head m in register m.  Three products (hi*hi + hi*lo +
+// lo*hi) give each term to ~2^-16 relative.  Kernel 2: one workgroup per
+// (batch, query head) combines the chunks in order (no atomics,
 // deterministic) and un-rotates once: o = R_v^T o_rot / L.
 
 static constexpr int ATT_CHUNK = 1024;
+static constexpr int ATT_RS = 68;  // staged record row stride (words): 16-byte aligned, bank-spread
+static constexpr int ATT_PS = 68;  // weight row stride (words): rows of different heads in different banks
 
 struct AttendArgs {
   const DevHead *heads;
@@ -1144,109 +1154,202 @@ struct AttendArgs {
   float scale;
   int first_head, cbs;
   int n_q_heads, n_kv_heads;
-  int n_chunks;
-  int lds_rec_off, lds_p_off, lds_red_off;  // floats
-  int max_W;
+  int n_chunks, n_parts;
+  int lds_wave_off;            // floats: per-wave areas (the centroid table starts at 0)
+  int wave_floats;             // one wave's area: two staging buffers, then the weights
+  int buf_floats;              // one staging buffer: [nwd][ATT_RS] words + [G][64] scores
 };
 
-template <int G>
+// Centroid table placement of the attend kernel: LM_COL = one column per lane
+// (entry code * 64 + lane: every lane reads its own bank; widths <= 6),
+// LM_PACK = the block's tables back to back with one pad entry each, LM_GLB =
+// read from the table blob (tables too large for LDS).
+enum { LM_COL = 0, LM_PACK = 1, LM_GLB = 2 };
+
+template <int G, int LM>
 __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
   extern __shared__ float smem[];
-  constexpr int GP = G <= 4 ? 4 : 8;
-  const int tid = threadIdx.x;
-  const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  constexpr int GR = (G + 3) / 4, GP = 4 * GR;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // a workgroup = 4 consecutive chunks of one (batch, KV head, coordinate block)
+  const int cgrp = blockIdx.x / a.n_parts, part = blockIdx.x % a.n_parts;
+  const int chunk = cgrp * 4 + wv;
+  const int hkv = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + hkv;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
-  const int d = hd->d, W = hd->W, n_cent = hd->n_cent;
+  const int d = hd->d, W = hd->W;
+  const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
+  const int c0 = part * 64, c1 = min(d, c0 + 64);
+  const int ci = c0 + lane;
+  // the block's record words [wlo, whi] and centroid pairs [lut0, lut1)
+  const int wlo = coords[c0].bit_off >> 5;
+  const int whi = min(W - 1, (coords[c1 - 1].bit_off + coords[c1 - 1].width) >> 5);
+  const int nwd = whi - wlo + 2;  // one spare row: the word after a field never goes past it
+  const int lut0 = coords[c0].cent_base;
+  uint32_t *lut = (uint32_t *)smem;
+  float *stage = smem + a.lds_wave_off + wv * a.wave_floats;  // two buffers: words, then scores
+  uint32_t *ph = (uint32_t *)(stage + 2 * a.buf_floats);      // [GP][ATT_PS] bf16 hi of p, twice
+  uint32_t *pl = ph + GP * ATT_PS;                             // [GP][ATT_PS] bf16 lo of p, twice
+  const uint32_t *glut = (const uint32_t *)(a.blob + hd->off_lutp) + lut0;
+  // this lane's field
+  int width = 0, bo = 0, cb = 0;
+  if (ci < c1) {
+    width = coords[ci].width;
+    bo = coords[ci].bit_off;
+    cb = coords[ci].cent_base - lut0;
+  }
+  const int n = width ? (1 << width) : 0;
+  if constexpr (LM == LM_COL) {
+    // column lane: entry f at f * 64 + lane; a zero-width lane reads 0 at f = 0
+    for (int k = wv; k < max(n, 1); k += 4) lut[k * 64 + lane] = n ? glut[cb + k] : 0u;
+    cb = lane;
+  } else if constexpr (LM == LM_PACK) {
+    // coordinate c0 + j's table at offset cb + j: lanes gathering the same code
+    // from tables of equal size fall in different banks; the slot after each
+    // table is 0, which a zero-width coordinate (field 0) reads
+    if (ci < c1) {  // lanes past the last coordinate (head_dim 32) write nothing
+      for (int k = wv; k < n; k += 4) lut[cb + lane + k] = glut[cb + k];
+      if (wv == 0) lut[cb + lane + n] = 0u;
+    }
+    cb += lane;
+  }
+  const uint32_t *lutv;
+  if constexpr (LM == LM_GLB) lutv = glut;
+  else lutv = lut;
+  const int lsh = LM == LM_COL ? 6 : 0;  // gather index: (field << lsh) + cb
+  const uint32_t fmask = width ? ((1u << width) - 1u) : 0u;
+  const int cwl = width ? (bo >> 5) - wlo : 0, cs = bo & 31;
+  __syncthreads();
+  if (chunk >= a.n_chunks) return;  // no barrier follows
+
   const int64_t tb = (int64_t)chunk * ATT_CHUNK;
   const int64_t te = min(a.n_tokens, tb + ATT_CHUNK);
-  float *cent = smem;                                  // [n_cent]
-  uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off);  // [64][W+1]
-  float *ps = smem + a.lds_p_off;                      // [64][GP]
-  float *red = smem + a.lds_red_off;                   // reduction scratch
-  {
-    const float *gc = (const float *)(a.blob + hd->off_cent);
-    for (int k = tid; k < n_cent; k += blockDim.x) cent[k] = gc[k];
-  }
-  // chunk max of scale * s per query head
   const float *srow = a.scores + ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * a.n_tokens;
-  float mx[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float v = -INFINITY;
-    for (int64_t t = tb + tid; t < te; t += blockDim.x) v = fmaxf(v, a.scale * srow[g * a.n_tokens + t]);
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    if ((tid & 63) == 0) red[(tid >> 6) * GP + g] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float v = red[g];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v = fmaxf(v, red[w * GP + g]);
-    mx[g] = v;
-  }
-  __syncthreads();
-
-  // thread -> (token slot, coordinate)
-  const int nslots = blockDim.x / d;
-  const int ci = tid % d, slotid = tid / d;
-  const DevCoord cd = ((const DevCoord *)(a.blob + hd->off_coord))[ci];
-  const uint32_t mask = cd.width ? ((1u << cd.width) - 1u) : 0u;
-  const int cw = cd.bit_off >> 5, cs = cd.bit_off & 31;
-  float acc[G];
-  float lsum[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = lsum[g] = 0.0f;
   const uint32_t *slot = a.vpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
-  for (int64_t t0 = tb; t0 < te; t0 += 64) {
-    const int64_t tile = t0 / 64;
-    const uint32_t *src = slot + tile * W * 64;
-    for (int k = tid; k < W * 64; k += blockDim.x) rec[(k & 63) * (W + 1) + (k >> 6)] = src[k];
-    for (int k = tid; k < 64; k += blockDim.x) rec[k * (W + 1) + W] = 0u;
-    for (int k = tid; k < 64 * G; k += blockDim.x) {
-      const int tt = k % 64, g = k / 64;
-      const int64_t t = t0 + tt;
-      float p = 0.0f;
-      if (t < te) p = expf(a.scale * srow[g * a.n_tokens + t] - mx[g]);
-      ps[tt * GP + g] = p;
-    }
-    __syncthreads();
-    if (slotid < nslots) {
-      for (int tt = slotid; tt < 64; tt += nslots) {
-        if (t0 + tt >= te) break;
-        const uint32_t lo = rec[tt * (W + 1) + cw], hi = rec[tt * (W + 1) + cw + 1];
-        const uint32_t field = __builtin_amdgcn_alignbit(hi, lo, cs) & mask;
-        const float c = cd.width ? cent[cd.cent_base + field] : 0.0f;
+  float mrun[G], lsum[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc[g] = fmaf(ps[tt * GP + g], c, acc[g]);
+  for (int g = 0; g < G; ++g) {
+    mrun[g] = -INFINITY;
+    lsum[g] = 0.0f;
+  }
+  // four independent accumulator sets (the products of a step alternate
+  // among them), summed at the end
+  f32x4 acc[4][GR];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int r = 0; r < GR; ++r) acc[h][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Staging, double-buffered: the words [wlo, wlo + nwd) of the tile's
+  // records and its G score rows go straight from HBM to LDS; tile i + 1 is
+  // requested before tile i is computed, so the one wait per tile covers
+  // loads issued a whole tile earlier.
+  auto stage_tile = [&](int64_t t0, int buf) {
+    uint32_t *rw = (uint32_t *)(stage + buf * a.buf_floats);
+    const uint32_t *src = slot + (t0 >> 6) * W * 64 + lane;
+    for (int w = 0; w < nwd; ++w)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + min(wlo + w, W - 1) * 64),
+                                       (__attribute__((address_space(3))) void *)(rw + w * ATT_RS), 4, 0, 0);
+    float *sr = stage + buf * a.buf_floats + nwd * ATT_RS;
+    // pad tokens of the last tile: any in-range address (their weight is 0)
+    const int64_t ts = min(t0 + lane, a.n_tokens - 1);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(srow + (int64_t)g * a.n_tokens + ts),
+                                       (__attribute__((address_space(3))) void *)(sr + g * 64), 4, 0, 0);
+  };
+  stage_tile(tb, 0);
+  int buf = 0;
+  for (int64_t t0 = tb; t0 < te; t0 += 64, buf ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this tile's staging has landed
+    wave_lds_sync();
+    if (t0 + 64 < te) stage_tile(t0 + 64, buf ^ 1);
+    const uint32_t *rec = (const uint32_t *)(stage + buf * a.buf_floats);
+    const float *sr = stage + buf * a.buf_floats + nwd * ATT_RS;
+    const uint32_t *rlo = rec + cwl * ATT_RS, *rhi = rlo + ATT_RS;
+    // ---- online softmax over the tile (lane = token)
+    const int64_t t = t0 + lane;
+    float sv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sv[g] = t < te ? a.scale * sr[g * 64 + lane] : -INFINITY;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = sv[g];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mn = fmaxf(mrun[g], mx);
+      const float corr = __expf(mrun[g] - mn);  // 0 on the first tile (mrun = -inf)
+      mrun[g] = mn;
+      const float pv = __expf(sv[g] - mn);       // 0 for tokens past the end
+      lsum[g] = fmaf(lsum[g], corr, pv);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) acc[h][g >> 2][g & 3] *= corr;
+      const uint16_t hi = f32_to_bf16_rne(pv);
+      ph[g * ATT_PS + lane] = bf16_pair(hi);
+      pl[g * ATT_PS + lane] = bf16_pair(f32_to_bf16_rne(pv - bf16_to_f32(hi)));
+    }
+#pragma unroll
+    for (int g = G; g < GP; ++g) {
+      ph[g * ATT_PS + lane] = 0u;
+      pl[g * ATT_PS + lane] = 0u;
+    }
+    wave_lds_sync();
+    // ---- 8 tokens per step: decode (all gathers in flight together), then
+    // the weighted sums on the MFMA.  A product takes 2 tokens: the k slots
+    // of coordinate n are (hi, lo) of C[code] for each token, the weights of
+    // head m are (p, p) per token, so it adds p_t0 (hi0 + lo0) + p_t1 (hi1 + lo1);
+    // once with bf16(p) and once with the remainder of p.
+    const int m = lane & 3;
+#pragma unroll 2
+    for (int k = 0; k < 64; k += 8) {
+      const uint4 lo0 = *(const uint4 *)(rlo + k), lo1 = *(const uint4 *)(rlo + k + 4);
+      const uint4 hi0 = *(const uint4 *)(rhi + k), hi1 = *(const uint4 *)(rhi + k + 4);
+      uint32_t pr[8];
+      pr[0] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.x, lo0.x, cs) & fmask) << lsh)];
+      pr[1] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.y, lo0.y, cs) & fmask) << lsh)];
+      pr[2] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.z, lo0.z, cs) & fmask) << lsh)];
+      pr[3] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.w, lo0.w, cs) & fmask) << lsh)];
+      pr[4] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.x, lo1.x, cs) & fmask) << lsh)];
+      pr[5] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.y, lo1.y, cs) & fmask) << lsh)];
+      pr[6] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.z, lo1.z, cs) & fmask) << lsh)];
+      pr[7] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.w, lo1.w, cs) & fmask) << lsh)];
+#pragma unroll
+      for (int r = 0; r < GR; ++r) {
+        const uint32_t *hrow = ph + (4 * r + m) * ATT_PS + k, *lrow = pl + (4 * r + m) * ATT_PS + k;
+        const uint4 ah0 = *(const uint4 *)hrow, ah1 = *(const uint4 *)(hrow + 4);
+        const uint4 al0 = *(const uint4 *)lrow, al1 = *(const uint4 *)(lrow + 4);
+        const uint2 ah[4] = {make_uint2(ah0.x, ah0.y), make_uint2(ah0.z, ah0.w),
+                             make_uint2(ah1.x, ah1.y), make_uint2(ah1.z, ah1.w)};
+        const uint2 al[4] = {make_uint2(al0.x, al0.y), make_uint2(al0.z, al0.w),
+                             make_uint2(al1.x, al1.y), make_uint2(al1.z, al1.w)};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint2 bv = make_uint2(pr[2 * h], pr[2 * h + 1]);
+          acc[h][r] = mfma4(ah[h], bv, acc[h][r]);
+          acc[h][r] = mfma4(al[h], bv, acc[h][r]);
+        }
       }
     }
-    if (tid < 64) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) lsum[g] += ps[tid * GP + g];
-    }
-    __syncthreads();
+    wave_lds_sync();  // every read of this tile's words and weights is done
   }
-  // reduce acc over slots in order; reduce lsum over the first wave
-  for (int g = 0; g < G; ++g) {
-    if (slotid < nslots) red[(slotid * G + g) * d + ci] = acc[g];
-  }
-  __syncthreads();
+  // ---- partials: o_rot for this block's coordinates; the running max and
+  // the weight sum (block 0)
   float *dst = a.ws + (((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * a.n_chunks + chunk) * (d + 2);
-  if (tid < d) {
-    for (int g = 0; g < G; ++g) {
-      float s = 0.0f;
-      for (int sl = 0; sl < nslots; ++sl) s += red[(sl * G + g) * d + tid];
-      dst[(int64_t)g * a.n_chunks * (d + 2) + 2 + tid] = s;
-    }
+  if (ci < c1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      dst[(int64_t)g * a.n_chunks * (d + 2) + 2 + ci] =
+          (acc[0][g >> 2][g & 3] + acc[1][g >> 2][g & 3]) + (acc[2][g >> 2][g & 3] + acc[3][g >> 2][g & 3]);
   }
-  if (tid < 64) {
+  if (part == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float v = lsum[g];
+#pragma unroll
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      if (tid == 0) {
-        dst[(int64_t)g * a.n_chunks * (d + 2) + 0] = mx[g];
+      if (lane == 0) {
+        dst[(int64_t)g * a.n_chunks * (d + 2) + 0] = mrun[g];
         dst[(int64_t)g * a.n_chunks * (d + 2) + 1] = v;
       }
     }
@@ -1632,8 +1735,10 @@ extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_
 }
 
 template <int G>
-static void launch_attend(dim3 grid, dim3 block, size_t lds, hipStream_t s, const AttendArgs &a) {
-  hipLaunchKernelGGL((attend_partial_kernel<G>), grid, block, lds, s, a);
+static void launch_attend(int lm, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
+  if (lm == LM_COL) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL>), grid, dim3(256), lds, s, a);
+  else if (lm == LM_PACK) hipLaunchKernelGGL((attend_partial_kernel<G, LM_PACK>), grid, dim3(256), lds, s, a);
+  else hipLaunchKernelGGL((attend_partial_kernel<G, LM_GLB>), grid, dim3(256), lds, s, a);
 }
 
 extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride, int batch,
@@ -1680,31 +1785,57 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
     return fail(SQ_ERR_ARG, "sq_attend: workspace too small");
   a.ws = (float *)workspace;
   a.n_chunks = (int)((n_tokens + ATT_CHUNK - 1) / ATT_CHUNK);
-  int max_cent = 1;
+  a.n_parts = (d + 63) / 64;
+  // LDS: centroid table of one 64-coordinate block | 4 x (two staging buffers, weights)
+  int max_lut = 1, max_nwd = 2, max_w = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
-    for (int h = 0; h < n_kv_heads; ++h)
-      max_cent = std::max(max_cent, vc->heads[first_head + bb * calib_batch_stride + h].n_cent);
+    for (int h = 0; h < n_kv_heads; ++h) {
+      const HeadCal &hc = vc->heads[first_head + bb * calib_batch_stride + h];
+      for (int pt = 0; pt < a.n_parts; ++pt) {
+        const int c0 = pt * 64, c1 = std::min(d, c0 + 64);
+        const int lut1 = c1 < d ? hc.cent_base[c1] : hc.n_cent;
+        max_lut = std::max(max_lut, lut1 - hc.cent_base[c0]);
+        const int wlo = hc.bit_off[c0] >> 5;
+        const int whi = std::min(hc.W - 1, (hc.bit_off[c1 - 1] + hc.widths[c1 - 1]) >> 5);
+        max_nwd = std::max(max_nwd, whi - wlo + 2);
+        for (int i = c0; i < c1; ++i) max_w = std::max(max_w, hc.widths[i]);
+      }
+    }
     if (calib_batch_stride == 0) break;
   }
-  const int GP = G <= 4 ? 4 : 8;
-  a.max_W = vc->W_max;
-  a.lds_rec_off = (max_cent + 3) & ~3;
-  a.lds_p_off = a.lds_rec_off + ((64 * (a.max_W + 1) + 3) & ~3);
-  a.lds_red_off = a.lds_p_off + 64 * GP;
-  const int red_floats = std::max(4 * GP, (256 / d) * G * d);
-  const size_t lds = (size_t)(a.lds_red_off + red_floats) * 4;
-  if (lds > (size_t)device_lds_limit()) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: tables exceed LDS");
-  dim3 grid(a.n_chunks, n_kv_heads, batch), block(256);
-  if (grid.z > 65535 || grid.y > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: grid too large");
+  const int GP = ((G + 3) / 4) * 4;
+  const int limit = device_lds_limit();
+  a.buf_floats = max_nwd * ATT_RS + G * 64;
+  a.wave_floats = 2 * a.buf_floats + 2 * GP * ATT_PS;
+  auto lds_for = [&](int lut_floats) {
+    a.lds_wave_off = (lut_floats + 3) & ~3;
+    return (size_t)(a.lds_wave_off + 4 * a.wave_floats) * 4;
+  };
+  int lm = LM_GLB;
+  size_t lds = 0;
+  if (max_w <= 6 && lds_for(64 << max_w) <= (size_t)std::min(limit, 64 * 1024)) {
+    lm = LM_COL;
+    lds = lds_for(64 << max_w);
+  } else if (lds_for(max_lut + 64) <= (size_t)std::min(limit, 64 * 1024)) {
+    lm = LM_PACK;
+    lds = lds_for(max_lut + 64);
+  } else {
+    lds = lds_for(0);
+  }
+  if (lds > (size_t)limit) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: tables exceed LDS");
+  const int64_t cgroups = (a.n_chunks + 3) / 4;
+  dim3 grid((unsigned)(cgroups * a.n_parts), n_kv_heads, batch);
+  if (grid.z > 65535 || grid.y > 65535 || cgroups * a.n_parts > INT32_MAX)
+    return fail(SQ_ERR_UNSUPPORTED, "sq_attend: grid too large");
   switch (G) {
-    case 1: launch_attend<1>(grid, block, lds, s, a); break;
-    case 2: launch_attend<2>(grid, block, lds, s, a); break;
-    case 3: launch_attend<3>(grid, block, lds, s, a); break;
-    case 4: launch_attend<4>(grid, block, lds, s, a); break;
-    case 5: launch_attend<5>(grid, block, lds, s, a); break;
-    case 6: launch_attend<6>(grid, block, lds, s, a); break;
-    case 7: launch_attend<7>(grid, block, lds, s, a); break;
-    case 8: launch_attend<8>(grid, block, lds, s, a); break;
+    case 1: launch_attend<1>(lm, grid, lds, s, a); break;
+    case 2: launch_attend<2>(lm, grid, lds, s, a); break;
+    case 3: launch_attend<3>(lm, grid, lds, s, a); break;
+    case 4: launch_attend<4>(lm, grid, lds, s, a); break;
+    case 5: launch_attend<5>(lm, grid, lds, s, a); break;
+    case 6: launch_attend<6>(lm, grid, lds, s, a); break;
+    case 7: launch_attend<7>(lm, grid, lds, s, a); break;
+    case 8: launch_attend<8>(lm, grid, lds, s, a); break;
   }
   sq_status s1 = launched(fn);
   if (s1 != SQ_OK) return s1;
