@@ -1141,6 +1141,7 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
 static constexpr int ATT_CHUNK = 1024;
 static constexpr int ATT_RS = 68;  // staged record row stride (words): 16-byte aligned, bank-spread
 static constexpr int ATT_PS = 68;  // weight row stride (words): rows of different heads in different banks
+static constexpr float ATT_TAU = 8.0f;  // lazy-rescale margin of the running softmax max
 
 struct AttendArgs {
   const DevHead *heads;
@@ -1159,6 +1160,20 @@ struct AttendArgs {
   int wave_floats;             // one wave's area: two staging buffers, then the weights
   int buf_floats;              // one staging buffer: [nwd][ATT_RS] words + [G][64] scores
 };
+
+// Maximum over the 64 lanes: rotations within each row of 16 (DPP), then the
+// four row results (returned in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 
 // Centroid table placement of the attend kernel: LM_COL = one column per lane
 // (entry code * 64 + lane: every lane reads its own bank; widths <= 6),
@@ -1220,6 +1235,7 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
   const int lsh = LM == LM_COL ? 6 : 0;  // gather index: (field << lsh) + cb
   const uint32_t fmask = width ? ((1u << width) - 1u) : 0u;
   const int cwl = width ? (bo >> 5) - wlo : 0, cs = bo & 31;
+  const bool straddle = cs + width > 32;
   __syncthreads();
   if (chunk >= a.n_chunks) return;  // no barrier follows
 
@@ -1273,18 +1289,20 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     float sv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sv[g] = t < te ? a.scale * sr[g * 64 + lane] : -INFINITY;
+    // The reference max moves only when a tile exceeds it by more than
+    // ATT_TAU: weights stay below e^ATT_TAU and the sums are rescaled rarely.
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mx = sv[g];
+      const float mx = wave_max(sv[g]);
+      if (mx > mrun[g] + ATT_TAU) {  // uniform; always taken on the first tile (mrun = -inf)
+        const float corr = __expf(mrun[g] - mx);
+        mrun[g] = mx;
+        lsum[g] *= corr;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      const float mn = fmaxf(mrun[g], mx);
-      const float corr = __expf(mrun[g] - mn);  // 0 on the first tile (mrun = -inf)
-      mrun[g] = mn;
-      const float pv = __expf(sv[g] - mn);       // 0 for tokens past the end
-      lsum[g] = fmaf(lsum[g], corr, pv);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) acc[h][g >> 2][g & 3] *= corr;
+        for (int h = 0; h < 4; ++h) acc[h][g >> 2][g & 3] *= corr;
+      }
+      const float pv = __expf(sv[g] - mrun[g]);  // 0 for tokens past the end
+      lsum[g] += pv;
       const uint16_t hi = f32_to_bf16_rne(pv);
       ph[g * ATT_PS + lane] = bf16_pair(hi);
       pl[g * ATT_PS + lane] = bf16_pair(f32_to_bf16_rne(pv - bf16_to_f32(hi)));
@@ -1304,7 +1322,11 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
 #pragma unroll 2
     for (int k = 0; k < 64; k += 8) {
       const uint4 lo0 = *(const uint4 *)(rlo + k), lo1 = *(const uint4 *)(rlo + k + 4);
-      const uint4 hi0 = *(const uint4 *)(rhi + k), hi1 = *(const uint4 *)(rhi + k + 4);
+      uint4 hi0 = make_uint4(0, 0, 0, 0), hi1 = hi0;
+      if (straddle) {  // only lanes whose field runs into the next word read it
+        hi0 = *(const uint4 *)(rhi + k);
+        hi1 = *(const uint4 *)(rhi + k + 4);
+      }
       uint32_t pr[8];
       pr[0] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.x, lo0.x, cs) & fmask) << lsh)];
       pr[1] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.y, lo0.y, cs) & fmask) << lsh)];
