@@ -29,13 +29,33 @@ struct DevCoord {
 // + c * 2^b + k - 1, and its signal centroids at signal base + c * 2^b + code.
 constexpr int PLAN_WORDS = 16;
 
+// Score schedule (sq_scores).  Coordinates are taken in order as "halves":
+// two adjacent coordinates whose widths sum to at most 8 bits form one half
+// (their codes are adjacent in the record, so one bit field of the summed
+// width indexes a joint table), any other coordinate is a half of its own.
+// Two halves make a quad = the 4 k-slots of one v_mfma_f32_4x4x4_16b_bf16.
+// Quad (SCHED_WORDS): [0], [1] bit position | summed width << 16 of its two
+// halves, [2], [3] their first entry in the joint table, [4] k-slot
+// coordinates 0 | 1 << 16, [5] k-slots 2 | 3 << 16 (0xFFFF = empty slot).
+// Joint table entry v of a half (a, b): C_a[v & (2^w_a - 1)] and C_b[v >> w_a]
+// as bf16 hi pair (hi_a | hi_b << 16) and bf16 lo pair (lo_a | lo_b << 16),
+// stored (lo pair, hi pair) for the first half of a quad and (hi pair, lo
+// pair) for the second, so that the two entries of a quad read into four
+// consecutive registers (lo_ab, hi_ab, hi_cd, lo_cd) give the MFMA B
+// operands hi|lo of ab, hi|lo of cd and the four hi parts.
+constexpr int SCHED_WORDS = 8;
+
 struct DevHead {
   int32_t d, d_eff, m, W;
   int32_t code_bits, n_tree, n_cent, has_gamma;
   float qjl_scale;      // sqrt(pi/2) / m  (0 when m == 0)
   int32_t n_csig;       // floats in the signal-centroid table of the plan
-  int32_t n_chunks, pad2;
+  int32_t n_chunks;
+  int32_t n_quads;      // score schedule quads
+  int32_t n_plut;       // joint-table entries (the last one is all zero)
+  int32_t pad[3];
   int64_t off_R;        // float [d][d], row i = eigenvector i (y = R x)
+  int64_t off_RT;       // float [d][d], R transposed
   int64_t off_Rfrag;    // bf16 [3][d/16][d/32][64][8]: hi/mid/lo split of R in
                         // MFMA 16x16x32 A-operand order (see compress kernel)
   int64_t off_coord;    // DevCoord [d]
@@ -44,13 +64,14 @@ struct DevHead {
   int64_t off_cent;     // float [n_cent]  centroids * sigma_i
   int64_t off_S;        // float [m][d_eff] QJL sketch
   int64_t off_plan;     // uint32 [d/16 + n_chunks + 1][PLAN_WORDS] compress plan
-  int64_t off_desc;     // uint32 [d]: bit offset | width << 12 | centroid base << 16
+  int64_t off_sched;    // uint32 [n_quads][SCHED_WORDS] score schedule
+  int64_t off_plut;     // uint32 [n_plut][2] joint tables (hi pair, lo pair)
   int64_t off_lutp;     // uint32 [n_cent]: each centroid as bf16 hi | bf16 lo << 16
                         // (hi + lo reproduces the fp32 centroid to ~2^-17)
   int64_t off_csig;     // float [n_csig]  signal centroids * sigma_i per plan chunk
 };
 
 static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
-static_assert(sizeof(DevHead) == 128, "DevHead layout");
+static_assert(sizeof(DevHead) == 160, "DevHead layout");
 
 }  // namespace sq

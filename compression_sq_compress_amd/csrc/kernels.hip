@@ -16,6 +16,7 @@
 #include <cstring>
 #include <limits>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "internal.h"
@@ -68,6 +69,98 @@ __device__ __forceinline__ DevCoord load_coord(const SQ_CONST DevCoord *p) {
 // ------------------------------------------------------------------ upload
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Score schedule of one head (layout: SCHED_WORDS).  Adjacent coordinates
+// are paired greedily when their widths sum to at most 8 bits; while the
+// joint tables exceed SCORE_LUT_BYTES, the pair with the largest table is
+// split again.  An odd number of halves gets an empty half (table entry:
+// the trailing zero entry).
+constexpr int SCORE_PAIR_BITS = 8;
+constexpr size_t SCORE_LUT_BYTES = 80 * 1024;
+
+struct ScoreSched {
+  std::vector<uint32_t> quads;  // [n_quads][SCHED_WORDS]
+  std::vector<uint32_t> lut;    // [n_plut][2]
+  int n_quads = 0, n_plut = 0;
+};
+
+static void bf16_split(float v, uint16_t &hi, uint16_t &lo) {
+  hi = f32_to_bf16_rne(v);
+  float vh;
+  const uint32_t u = (uint32_t)hi << 16;
+  std::memcpy(&vh, &u, 4);
+  lo = f32_to_bf16_rne(v - vh);
+}
+
+static ScoreSched build_score_sched(const HeadCal &hc) {
+  const int d = hc.d;
+  const std::vector<int32_t> &w = hc.widths;
+  std::vector<char> paired(d, 0);  // paired[i]: coordinates i and i+1 form one half
+  for (int i = 0; i + 1 < d;) {
+    if (w[i] + w[i + 1] <= SCORE_PAIR_BITS) {
+      paired[i] = 1;
+      i += 2;
+    } else {
+      i += 1;
+    }
+  }
+  auto entries = [&]() {
+    size_t n = 1;  // trailing zero entry
+    for (int i = 0; i < d;) {
+      if (paired[i]) { n += (size_t)1 << (w[i] + w[i + 1]); i += 2; }
+      else { n += (size_t)1 << w[i]; i += 1; }
+    }
+    return n;
+  };
+  while (entries() * 8 > SCORE_LUT_BYTES) {
+    int best = -1, bw = -1;
+    for (int i = 0; i + 1 < d; ++i)
+      if (paired[i] && w[i] + w[i + 1] > bw) { bw = w[i] + w[i + 1]; best = i; }
+    if (best < 0) break;
+    paired[best] = 0;
+  }
+  struct Half { int a, b, pos, width; uint32_t first; };
+  std::vector<Half> halves;
+  ScoreSched S;
+  auto cent = [&](int i, int code) -> float {
+    return w[i] > 0 ? hc.cent[hc.cent_base[i] + code] : 0.0f;
+  };
+  for (int i = 0; i < d;) {
+    Half h;
+    h.a = i;
+    h.b = paired[i] ? i + 1 : -1;
+    h.pos = hc.bit_off[i];
+    const int wa = w[i], wb = h.b >= 0 ? w[h.b] : 0;
+    h.width = wa + wb;
+    h.first = (uint32_t)(S.lut.size() / 2);
+    for (int v = 0; v < (1 << h.width); ++v) {
+      uint16_t ah, al, bh = 0, bl = 0;
+      bf16_split(cent(i, v & ((1 << wa) - 1)), ah, al);
+      if (h.b >= 0) bf16_split(cent(h.b, v >> wa), bh, bl);
+      const uint32_t hp = (uint32_t)ah | ((uint32_t)bh << 16), lp = (uint32_t)al | ((uint32_t)bl << 16);
+      const bool first = (halves.size() & 1) == 0;  // first half of its quad: (lo, hi), second: (hi, lo)
+      S.lut.push_back(first ? lp : hp);
+      S.lut.push_back(first ? hp : lp);
+    }
+    halves.push_back(h);
+    i += paired[i] ? 2 : 1;
+  }
+  const uint32_t zero = (uint32_t)(S.lut.size() / 2);
+  S.lut.push_back(0u);
+  S.lut.push_back(0u);
+  if (halves.size() & 1) halves.push_back(Half{-1, -1, 0, 0, zero});
+  S.n_quads = (int)halves.size() / 2;
+  S.n_plut = (int)(S.lut.size() / 2);
+  auto slot = [](int c) { return c < 0 ? 0xFFFFu : (uint32_t)c; };
+  for (int q = 0; q < S.n_quads; ++q) {
+    const Half &h0 = halves[2 * q], &h1 = halves[2 * q + 1];
+    const uint32_t e[SCHED_WORDS] = {
+        (uint32_t)h0.pos | ((uint32_t)h0.width << 16), (uint32_t)h1.pos | ((uint32_t)h1.width << 16),
+        h0.first, h1.first, slot(h0.a) | (slot(h0.b) << 16), slot(h1.a) | (slot(h1.b) << 16), 0u, 0u};
+    S.quads.insert(S.quads.end(), e, e + SCHED_WORDS);
+  }
+  return S;
+}
 
 static sq_status hip_fail(const char *what, hipError_t e) {
   return fail(SQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -284,6 +377,8 @@ sq_status upload_tables(sq_calib *c, void *stream) {
   const int nh = (int)c->heads.size();
   std::vector<HostPlan> plans(nh);
   for (int h = 0; h < nh; ++h) plans[h] = build_plan(c->heads[h]);
+  std::vector<ScoreSched> scheds(nh);
+  for (int h = 0; h < nh; ++h) scheds[h] = build_score_sched(c->heads[h]);
   // host image of the blob: [DevHead x nh] then per-head sections
   std::vector<DevHead> desc(nh);
   size_t off = align256(sizeof(DevHead) * nh);
@@ -304,14 +399,19 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.qjl_scale = hc.m > 0 ? (float)(std::sqrt(M_PI / 2.0) / hc.m) : 0.0f;
     D.n_csig = (int)P.csig.size();
     D.n_chunks = P.n_chunks;
+    D.n_quads = scheds[h].n_quads;
+    D.n_plut = scheds[h].n_plut;
     D.off_R = off;       off = align256(off + sizeof(float) * d * d);
+    D.off_RT = off;      off = align256(off + sizeof(float) * d * d);
     D.off_Rfrag = off;   off = align256(off + sizeof(uint16_t) * 3 * d * d);
     D.off_coord = off;   off = align256(off + sizeof(DevCoord) * d);
     D.off_tree = off;    off = align256(off + sizeof(float) * std::max<size_t>(1, P.tree.size()));
     D.off_cent = off;    off = align256(off + sizeof(float) * std::max(1, hc.n_cent));
     D.off_S = off;       off = align256(off + sizeof(float) * std::max(1, hc.m * hc.d_eff));
     D.off_plan = off;    off = align256(off + sizeof(uint32_t) * P.words.size());
-    D.off_desc = off;    off = align256(off + sizeof(uint32_t) * d);
+    D.off_sched = off;   off = align256(off + sizeof(uint32_t) * scheds[h].quads.size());
+    D.off_plut = off;    // read in whole 1 KB pieces: reserve them
+    off = align256(off + ((sizeof(uint32_t) * scheds[h].lut.size() + 1023) & ~(size_t)1023));
     D.off_lutp = off;    off = align256(off + sizeof(uint32_t) * std::max(1, hc.n_cent));
     D.off_csig = off;    off = align256(off + sizeof(float) * std::max<size_t>(1, P.csig.size()));
   }
@@ -324,6 +424,9 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     const int d = hc.d;
     float *R = (float *)(img.data() + D.off_R);
     for (int k = 0; k < d * d; ++k) R[k] = (float)hc.R[k];
+    float *RT = (float *)(img.data() + D.off_RT);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) RT[(size_t)j * d + i] = (float)hc.R[(size_t)i * d + j];
     // bf16 x3 split of R (hi + mid + lo reproduces R to ~2^-24 relative), laid
     // out as MFMA 16x16x32 A operands: fragment (s, mb, kb), lane l, element e
     // holds R_s[mb*16 + l%16][kb*32 + 8*(l/16) + e].
@@ -347,11 +450,9 @@ sq_status upload_tables(sq_calib *c, void *stream) {
               F[((((size_t)s * MB + mb) * KB + kb) * 64 + l) * 8 + e] = parts[s];
           }
     DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
-    uint32_t *Dd = (uint32_t *)(img.data() + D.off_desc);
-    for (int i = 0; i < d; ++i) {
-      Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
-      Dd[i] = (uint32_t)hc.bit_off[i] | ((uint32_t)hc.widths[i] << 12) | ((uint32_t)hc.cent_base[i] << 16);
-    }
+    for (int i = 0; i < d; ++i) Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
+    std::memcpy(img.data() + D.off_sched, scheds[h].quads.data(), sizeof(uint32_t) * scheds[h].quads.size());
+    std::memcpy(img.data() + D.off_plut, scheds[h].lut.data(), sizeof(uint32_t) * scheds[h].lut.size());
     if (!P.tree.empty()) std::memcpy(img.data() + D.off_tree, P.tree.data(), sizeof(float) * P.tree.size());
     if (!P.csig.empty()) std::memcpy(img.data() + D.off_csig, P.csig.data(), sizeof(float) * P.csig.size());
     std::memcpy(img.data() + D.off_plan, P.words.data(), sizeof(uint32_t) * P.words.size());
@@ -359,12 +460,8 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     {
       uint32_t *Pp = (uint32_t *)(img.data() + D.off_lutp);
       for (int k = 0; k < hc.n_cent; ++k) {
-        const float v = hc.cent[k];
-        const uint16_t hi = f32_to_bf16_rne(v);
-        float vh;
-        uint32_t u = (uint32_t)hi << 16;
-        std::memcpy(&vh, &u, 4);
-        const uint16_t lo = f32_to_bf16_rne(v - vh);
+        uint16_t hi, lo;
+        bf16_split(hc.cent[k], hi, lo);
         Pp[k] = (uint32_t)hi | ((uint32_t)lo << 16);
       }
     }
@@ -871,22 +968,34 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
 
 // ------------------------------------------------------------------ scores
 //
-// A workgroup serves one (batch, KV head) and a run of 64-token tiles; each
-// of its 4 waves takes NT tiles per pass, lane = token.
-// Prologue: q~ = R q for the query heads of the group (fp32), w = S q~[:d_eff]
-// scaled by sqrt(pi/2)/m, and the MFMA A operands built from q~ (below); the
-// head's centroid table, as bf16 hi/lo pairs, goes to LDS.
-// Pass: the NT tiles' record words are staged in lane-private LDS rows.  The
-// lane walks the coordinates in order (wave-uniform bit positions, a two-word
-// window per tile), fetches the pair (hi, lo) of C_i[code] and feeds it to
-// v_mfma_f32_4x4x4_16b_bf16 as the B operand: in block b, lane 4b+n supplies
-// column n = its own token.  The A operand rows are the query heads: for a
-// coordinate pair (i, i+1) the k-slots are (hi_i, lo_i, hi_i+1, lo_i+1) x
-// (qhi_i, qhi_i, qhi_i+1, qhi_i+1); every four coordinates one more MFMA adds
-// (hi_i..hi_i+3) x (qlo_i..qlo_i+3).  So each token's score is accumulated
-// for 4 query heads per MFMA, exact to ~2^-16 relative per term, and lands
-// in the token's own lane (register m = head m), where the QJL term
-// gamma * sum_j w_j (2 z_j - 1) is added before one coalesced store per head.
+// s_t = sum_i q~_i C_i[code_ti] + sqrt(pi/2)/m * gamma_t * sum_j w_j (2 z_tj - 1),
+// q~ = R q, w = S q~[:d_eff] (SpectralQuant README, "Overview": the query is
+// rotated once and scored against the codes; QJL estimator as in the QJL
+// paper, section 3).
+//
+// A workgroup serves one (batch, KV head) and a run of 64-token tiles with 8
+// consumer waves and SC_LOADERS loader waves.  The score schedule (SCHED_WORDS) cuts
+// the head's coordinates into quads of 4 MFMA k-slots; the consumer waves
+// are split into KS wave groups over the quads ("split-K") times TS tile
+// streams (KS * TS = 8), so each wave keeps its own quads' MFMA A operands
+// (q~ of 4 query heads as bf16 hi and lo parts) and their bit positions,
+// masks and table addresses in registers for the whole kernel.  Per tile
+// and half the lane (= token) reads its two record words, extracts the
+// half's bit field and fetches the joint-table entry; per quad three
+// v_mfma_f32_4x4x4_16b_bf16 (qhi*chi + qhi*clo + qlo*chi) accumulate 4 query
+// heads x 64 tokens with every product exact and each term good to ~2^-16,
+// software-pipelined over three quads.
+// Record tiles stream from HBM into a ring of R LDS slots (TS tiles each)
+// with direct-to-LDS loads issued by the loader waves, DS super-steps of NS
+// slots ahead; one workgroup barrier per super-step.  The partial sums of a
+// wave group meet in LDS and are added in a fixed order (deterministic) one
+// super-step later, the last wave of each group adding the QJL term.
+
+constexpr int SC_WAVES = 8;    // consumer waves per workgroup
+constexpr int SC_LOADERS = 3;  // waves issuing the record loads
+constexpr int SC_BLOCK = 64 * (SC_WAVES + SC_LOADERS);
+// quads held in registers per consumer wave (4 or 8 query heads per MFMA row set)
+__host__ __device__ constexpr int sc_qmax(int gr) { return gr == 1 ? 9 : 5; }
 
 struct ScoresArgs {
   const DevHead *heads;
@@ -897,11 +1006,13 @@ struct ScoresArgs {
   int64_t ps_b, ps_h;
   int64_t n_tokens;
   int first_head, cbs;
-  int n_q_heads, n_kv_heads;
+  int n_q_heads, n_kv_heads, G;
   int q_f32;
-  int n_tiles, tiles_per_block;
-  int lds_lut_off, lds_aq_off, lds_w_off, lds_rec_off;  // floats
-  int rec_tile;                                         // words per staged tile
+  int n_tiles, tiles_per_wg;
+  int ks, ts;             // wave groups over quads, tile streams (ks * ts = SC_WAVES)
+  int pass;               // quads [pass * ks * sc_qmax(GR), ...) of every head
+  int dma16;              // records 16-byte aligned: 1 KB direct-to-LDS loads
+  int lds_lut, lds_qt, lds_wq, lds_slot, lds_pbuf;  // byte offsets
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -913,211 +1024,361 @@ __device__ __forceinline__ f32x4 mfma4(uint2 a, uint2 b, f32x4 c) {
 
 __device__ __forceinline__ uint32_t bf16_pair(uint16_t x) { return (uint32_t)x | ((uint32_t)x << 16); }
 
-template <int G, int NT, bool LG>
-__global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
-  extern __shared__ float smem[];
-  constexpr int GR = (G + 3) / 4, GP = 4 * GR;
+// s_waitcnt vmcnt(n) for a wave-uniform n (the counter field is an immediate)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define SQ_VMW(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | ((k) & 15) | (((k) >> 4) << 14)); break;
+#define SQ_VMW8(k) SQ_VMW(k) SQ_VMW(k + 1) SQ_VMW(k + 2) SQ_VMW(k + 3) SQ_VMW(k + 4) SQ_VMW(k + 5) SQ_VMW(k + 6) SQ_VMW(k + 7)
+    SQ_VMW8(0) SQ_VMW8(8) SQ_VMW8(16) SQ_VMW8(24) SQ_VMW8(32) SQ_VMW8(40) SQ_VMW8(48) SQ_VMW8(56)
+#undef SQ_VMW8
+#undef SQ_VMW
+    default: __builtin_amdgcn_s_waitcnt(0xCF7F); break;  // vmcnt(63): waits for more, never less
+  }
+}
+
+// workgroup barrier without the memory fence of __syncthreads (the producer
+// must not wait for its later loads); LDS writes of the wave are complete.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS loads (global_load_lds_dword / _dwordx4): lane l's 4 (16)
+// bytes land at LDS address lds + 4l (16l).  Written as asm so that the
+// compiler does not treat every later LDS read of the workgroup as a possible
+// reader of these writes (it would wait for all vector memory there); the
+// loads are ordered explicitly by wait_vmcnt and step_barrier.  They have no
+// register results.
+// Address = wave-uniform base (scalar pair) + per-lane byte offset.
+__device__ __forceinline__ void lds_dma16(const void *base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void *base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+// a wave-uniform value kept in a vector register (it is combined with
+// another uniform operand in one VOP3 instruction, which takes one scalar)
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(x));
+  return v;
+}
+
+template <int GR, int SLOTB, int R, bool LG>
+__global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
+  constexpr int GP = 4 * GR;
+  constexpr int SC_QMAX = sc_qmax(GR);
+  constexpr int NS = SLOTB == 8192 ? 2 : 1;  // ring slots (steps of TS tiles) per barrier ("super-step")
+  // In use during super-step ss: ss (consumers), ss + 1 .. ss + DS (loads in
+  // flight or being issued).
+  constexpr int DS = R / NS - 1;              // super-steps loaded ahead
+  static_assert(R % NS == 0 && DS >= 1, "ring of whole super-steps");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + hkv;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
-  const int d = hd->d, d_eff = hd->d_eff, m = hd->m, W = hd->W, n_cent = hd->n_cent;
-  const int code_bits = hd->code_bits;
-  const int NP = d / 2, NQ = d / 4;
-  uint32_t *lut = (uint32_t *)(smem + a.lds_lut_off);
-  uint2 *aq = (uint2 *)(smem + a.lds_aq_off);
-  float *wq = smem + a.lds_w_off;
-
-  // ---- prologue (scratch aliases the record area)
-  {
-    float *qraw = smem + a.lds_rec_off;  // [G][d]
-    float *qt = qraw + G * d;            // [GP][d]
-    const int64_t qbase = ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * d;
-    for (int k = threadIdx.x; k < G * d; k += blockDim.x)
-      qraw[k] = a.q_f32 ? ((const float *)a.q)[qbase + k]
-                        : bf16_to_f32(((const uint16_t *)a.q)[qbase + k]);
-    __syncthreads();
-    const float *R = (const float *)(a.blob + hd->off_R);
-    for (int k = threadIdx.x; k < GP * d; k += blockDim.x) {
-      const int g = k / d, i = k % d;
-      float acc = 0.0f;
-      if (g < G) {
-        const float *Ri = R + (size_t)i * d;
-        const float *qg = qraw + g * d;
-        for (int j = 0; j < d; ++j) acc = fmaf(Ri[j], qg[j], acc);
-      }
-      qt[g * d + i] = acc;
-    }
-    __syncthreads();
-    if (m > 0) {
-      const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
-      const float sc = hd->qjl_scale;
-      for (int k = threadIdx.x; k < m * GP; k += blockDim.x) {
-        const int j = k / GP, g = k % GP;
-        float acc = 0.0f;
-        for (int i = 0; i < d_eff; ++i) acc = fmaf(S[j * d_eff + i], qt[g * d + i], acc);
-        wq[k] = sc * acc;
-      }
-    }
-    for (int k = threadIdx.x; k < GR * (NP + NQ) * 4; k += blockDim.x) {
-      const int mm = k & 3, rest = k >> 2;
-      const int r = rest / (NP + NQ), e = rest % (NP + NQ);
-      const float *qh = qt + (4 * r + mm) * d;
-      uint2 v;
-      if (e < NP) {
-        v.x = bf16_pair(f32_to_bf16_rne(qh[2 * e]));
-        v.y = bf16_pair(f32_to_bf16_rne(qh[2 * e + 1]));
-      } else {
-        uint16_t lo[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float x = qh[4 * (e - NP) + t];
-          lo[t] = f32_to_bf16_rne(x - bf16_to_f32(f32_to_bf16_rne(x)));
-        }
-        v.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-        v.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
-      }
-      aq[k] = v;
-    }
-    if constexpr (!LG) {
-      const uint32_t *gl = (const uint32_t *)(a.blob + hd->off_lutp);
-      for (int k = threadIdx.x; k < n_cent; k += blockDim.x) lut[k] = gl[k];
-    }
-    __syncthreads();
-  }
-  // centroid pairs: LDS copy, or (tables too large for LDS) the global table
-  const uint32_t *lutv;
-  if constexpr (LG) lutv = (const uint32_t *)(a.blob + hd->off_lutp);
-  else lutv = lut;
-
+  const int d = hd->d, d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
+  const int KS = a.ks, TS = a.ts, G = a.G;
+  const int qp0 = a.pass * KS * SC_QMAX;
+  const int nq_pass = min(hd->n_quads - qp0, KS * SC_QMAX);
+  if (nq_pass <= 0) return;  // whole workgroup: this head has no quads in this pass
+  const int tb = blockIdx.x * a.tiles_per_wg;
+  const int te = min(a.n_tiles, tb + a.tiles_per_wg);
+  const int nsteps = (te - tb + TS - 1) / TS;  // ring slots to fill, TS tiles each
+  const int nsup = (nsteps + NS - 1) / NS;
   const uint32_t *slot = a.kpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
-  uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off) + wave * NT * a.rec_tile;
-  const int tb = blockIdx.x * a.tiles_per_block;
-  const int te = min(a.n_tiles, tb + a.tiles_per_block);
-  const uint2 *aqm = aq + (lane & 3);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)sm;
+  const bool loader = wave >= SC_WAVES;  // (a wave's own direct-to-LDS loads hold up its LDS reads)
 
-  for (int tp = tb + wave * NT; tp < te; tp += 4 * NT) {
-    const int ntl = min(NT, te - tp);
-    // ---- stage the records: direct global -> LDS loads (lane l's word lands
-    // in column l of row w), all issued before the first wait; row W is zero
+  // Direct-to-LDS loads of super-step sp (slots sp*NS ..) are spread over the
+  // loader waves: its load instructions (1 KB pieces, then 256-byte rows) are
+  // numbered in order and loader l issues those with number % SC_LOADERS == l.
+  // Returns how many this wave issued (wave-uniform).
+  auto dma_super = [&](int sp, bool go) -> int {
+    int mine = 0, base = 0;
 #pragma unroll
-    for (int tq = 0; tq < NT; ++tq) {
-      if (tq < ntl) {
-        const uint32_t *src = slot + (int64_t)(tp + tq) * W * 64 + lane;
-        uint32_t *dstr = rec + tq * a.rec_tile;
-        for (int w = 0; w < W; ++w)
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + w * 64),
-                                           (__attribute__((address_space(3))) void *)(dstr + w * 64), 4, 0, 0);
-        dstr[W * 64 + lane] = 0u;
+    for (int t = 0; t < NS; ++t) {
+      const int j = sp * NS + t;
+      if (j >= nsteps) break;
+      const int t0 = tb + j * TS;
+      const int rows = min(TS, te - t0) * W;
+      const uint32_t *src = slot + (int64_t)t0 * W * 64;
+      const uint32_t dst = lds0 + a.lds_slot + (j % R) * SLOTB;
+      const int n4 = a.dma16 ? rows >> 2 : 0, n1 = rows - 4 * n4;
+      // ops [base, base + n4 + n1): this wave's are base + i with (base + i) % SC_LOADERS == l
+      int i = (wave - SC_WAVES - base) % SC_LOADERS;
+      if (i < 0) i += SC_LOADERS;
+      for (; i < n4; i += SC_LOADERS) {
+        if (go) lds_dma16(src + i * 256, lane * 16, dst + i * 1024);
+        ++mine;
+      }
+      for (; i < n4 + n1; i += SC_LOADERS) {
+        const int r = 4 * n4 + (i - n4);
+        if (go) lds_dma4(src + r * 64, lane * 4, dst + r * 256);
+        ++mine;
+      }
+      base += n4 + n1;
+    }
+    return mine;
+  };
+
+  if (loader)
+    for (int sp = 0; sp < min(DS, nsup); ++sp) dma_super(sp, true);
+
+  // ---- prologue (consumer waves): tables, q~ = R q, w = scale * S q~
+  const int ct = threadIdx.x;  // < 64 * SC_WAVES for consumers
+  const bool consumer = wave < SC_WAVES;
+  float *qraw = (float *)(sm + a.lds_pbuf);  // scratch until the first step
+  float *qt = (float *)(sm + a.lds_qt);      // [G][d]
+  float *wq = (float *)(sm + a.lds_wq);      // [m][GP]
+  if (consumer) {
+    if constexpr (!LG) {  // joint tables: 1 KB direct-to-LDS loads (table size rounded up in the blob)
+      const uint8_t *src = a.blob + hd->off_plut;
+      const int nkb = (hd->n_plut * 8 + 1023) >> 10;
+      for (int k = wave; k < nkb; k += SC_WAVES) lds_dma16(src + k * 1024, lane * 16, lds0 + a.lds_lut + k * 1024);
+    }
+    const int64_t qbase = ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * d;
+    for (int k = ct; k < G * d; k += 64 * SC_WAVES)
+      qraw[k] = a.q_f32 ? ((const float *)a.q)[qbase + k] : bf16_to_f32(((const uint16_t *)a.q)[qbase + k]);
+  }
+  __syncthreads();  // (its fence waits for every load issued so far)
+  if (consumer) {
+    const float *RT = (const float *)(a.blob + hd->off_RT);
+    for (int k = ct; k < G * d; k += 64 * SC_WAVES) {
+      const int g = k / d, i = k - g * d;
+      const float *qg = qraw + g * d;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < d; j0 += 16) {  // d is a multiple of 16: 16 loads in flight
+        float r[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) r[u] = RT[(size_t)(j0 + u) * d + i];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u & 3] = fmaf(r[u], qg[j0 + u], acc[u & 3]);
+      }
+      qt[k] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+  }
+  __syncthreads();
+  if (consumer && m > 0) {
+    const SQ_CONST float *S = cptr<float>(a.blob + hd->off_S);
+    for (int k = ct; k < m * GP; k += 64 * SC_WAVES) {
+      const int j = k / GP, g = k - j * GP;
+      float acc = 0.0f;
+      if (g < G)
+        for (int i = 0; i < d_eff; ++i) acc = fmaf(S[j * d_eff + i], qt[g * d + i], acc);
+      wq[k] = hd->qjl_scale * acc;
+    }
+  }
+  float *pbuf = (float *)(sm + a.lds_pbuf);
+
+  if (loader) {
+    for (int ss = 0; ss < nsup; ++ss) {
+      int pend = 0;  // this wave's loads issued after those of super-step ss
+      for (int sp = ss + 1; sp <= min(ss + DS - 1, nsup - 1); ++sp) pend += dma_super(sp, false);
+      wait_vmcnt(pend);
+      step_barrier();
+      // loads for super-step ss + DS go to the slots of ss - 1, which the
+      // consumers left before this barrier
+      if (ss + DS < nsup) dma_super(ss + DS, true);
+    }
+    step_barrier();
+    return;
+  }
+
+  // ---- consumer wave (tau, kk): tile stream tau, quads [q0, q0 + nq)
+  const int tau = wave / KS, kk = wave - tau * KS;
+  const int nqb = nq_pass / KS, nqr = nq_pass - nqb * KS;
+  const int nq = nqb + (kk < nqr ? 1 : 0);
+  const int q0 = qp0 + kk * nqb + min(kk, nqr);
+  const bool qjl_wave = kk == KS - 1 && m > 0 && a.pass == 0;
+  const SQ_CONST uint32_t *sch = cptr<uint32_t>(a.blob + hd->off_sched);
+  // Every wave runs SC_QMAX quads; those past its share are empty (mask 0,
+  // A operands 0) so that the quads form one straight-line block.  Table
+  // addresses are wave-uniform scalars; shifts and masks, also uniform, sit
+  // in vector registers (the instructions using them take one scalar each),
+  // word addresses per lane.
+  uint32_t hsh[2 * SC_QMAX], hmk[2 * SC_QMAX], hlut[2 * SC_QMAX], wad[2 * SC_QMAX];
+  uint2 aqa[SC_QMAX][GR], aqb[SC_QMAX][GR], aql[SC_QMAX][GR];
+  const uint32_t tile_lds = a.lds_slot + tau * W * 256 + lane * 4;  // this stream's tile in slot 0
+#pragma unroll
+  for (int qi = 0; qi < SC_QMAX; ++qi) {
+    const bool real = qi < nq;
+    const SQ_CONST uint32_t *e = sch + (size_t)(q0 + (real ? qi : 0)) * SCHED_WORDS;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t pw = e[hh];
+      const uint32_t pos = pw & 0xFFFFu, wd = pw >> 16;
+      hsh[2 * qi + hh] = to_vgpr(pos & 31u);
+      hmk[2 * qi + hh] = to_vgpr(real ? (1u << wd) - 1u : 0u);
+      hlut[2 * qi + hh] = (LG ? 0u : (uint32_t)a.lds_lut) + e[2 + hh] * 8u;
+      wad[2 * qi + hh] = tile_lds + (pos >> 5) * 256u;
+    }
+    const uint32_t s01 = e[4], s23 = e[5];
+    const uint32_t sl[4] = {s01 & 0xFFFFu, s01 >> 16, s23 & 0xFFFFu, s23 >> 16};
+#pragma unroll
+    for (int g = 0; g < GR; ++g) {
+      const int head = 4 * g + (lane & 3);
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = (real && head < G && sl[k] != 0xFFFFu) ? qt[head * d + (int)sl[k]] : 0.0f;
+        hi[k] = f32_to_bf16_rne(v);
+        lo[k] = f32_to_bf16_rne(v - bf16_to_f32(hi[k]));
+      }
+      const uint32_t hab = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16), hcd = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+      aqa[qi][g] = make_uint2(hab, hab);
+      aqb[qi][g] = make_uint2(hcd, hcd);
+      aql[qi][g] = make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+    }
+  }
+  const uint2 *glut = (const uint2 *)(a.blob + hd->off_plut);
+  const int zsh = code_bits & 31;
+
+  // sum the wave group's partials of super-step sp (fixed order) and store
+  auto reduce_k = [&](int sp, auto ksc) __attribute__((always_inline)) {
+    constexpr int K = decltype(ksc)::value;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int tile = tb + (sp * NS + t) * TS + tau;
+      if (tile >= te) continue;
+      const float *pr = pbuf + (((sp & 1) * NS + t) * TS + tau) * K * GP * 64 + lane;
+      const int64_t tok = (int64_t)tile * 64 + lane;
+#pragma unroll
+      for (int row0 = 0; row0 < GP; row0 += K) {
+        const int row = row0 + kk;
+        if (row >= GP) continue;
+        float pv[K];
+#pragma unroll
+        for (int k2 = 0; k2 < K; ++k2) pv[k2] = pr[(k2 * GP + row) * 64];
+        float v = pv[0];
+#pragma unroll
+        for (int k2 = 1; k2 < K; ++k2) v += pv[k2];
+        if (row < G && tok < a.n_tokens) {
+          float *o = a.scores + ((int64_t)b * a.n_q_heads + (int64_t)hkv * G + row) * a.n_tokens + tok;
+          if (a.pass) __hip_atomic_fetch_add(o, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // one add per pass
+          else *o = v;
+        }
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged words are in LDS
-    f32x4 acc[NT][GR];
+  };
+  auto reduce = [&](int sp) __attribute__((always_inline)) {
+    switch (KS) {
+      case 1: reduce_k(sp, std::integral_constant<int, 1>()); break;
+      case 2: reduce_k(sp, std::integral_constant<int, 2>()); break;
+      case 4: reduce_k(sp, std::integral_constant<int, 4>()); break;
+      default: reduce_k(sp, std::integral_constant<int, 8>()); break;
+    }
+  };
+
+
+  for (int ss0 = 0; ss0 < nsup; ss0 += R / NS) {
 #pragma unroll
-    for (int tq = 0; tq < NT; ++tq)
+    for (int u = 0; u < R / NS; ++u) {
+      const int ss = ss0 + u;
+      if (ss >= nsup) break;
+      step_barrier();
+      if (ss > 0) reduce(ss - 1);
+      f32x4 acc[NS][GR];
 #pragma unroll
-      for (int r = 0; r < GR; ++r) acc[tq][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int cur = -1;
-    uint32_t wlo[NT], whi[NT];
+      for (int t = 0; t < NS; ++t)
 #pragma unroll
-    for (int tq = 0; tq < NT; ++tq) wlo[tq] = whi[tq] = 0u;
-    // coordinate descriptors, 16 at a time (one scalar load), next block prefetched
-    const SQ_CONST uint32_t *dsc = cptr<uint32_t>(a.blob + hd->off_desc);
-    uint32_t dnext[16];
+        for (int g = 0; g < GR; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // three-stage pipeline over the quads: record words of quad it, joint
+      // table entries of quad it - 1, MFMAs of quad it - 2
+      uint32_t wlo[SC_QMAX][NS][2], whi[SC_QMAX][NS][2];
+      uint2 ent[SC_QMAX][NS][2];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) dnext[c] = dsc[c];
-    for (int q16 = 0; q16 < d / 16; ++q16) {
-      uint32_t dcur[16];
+      for (int it = 0; it < SC_QMAX + 2; ++it) {
+        if (it < SC_QMAX) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) dcur[c] = dnext[c];
-      if (q16 + 1 < d / 16) {
+          for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) dnext[c] = dsc[16 * (q16 + 1) + c];
-      }
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int qd = 4 * q16 + qq;
-        uint32_t dv[4][NT];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t e = dcur[4 * qq + c];
-          const int bo = e & 0xFFF, wd = (e >> 12) & 0xF, cb = e >> 16;
-          if (wd == 0) {
-#pragma unroll
-            for (int tq = 0; tq < NT; ++tq) dv[c][tq] = 0u;
-            continue;
-          }
-          const int w = bo >> 5;
-          if (w != cur) {
-#pragma unroll
-            for (int tq = 0; tq < NT; ++tq) {
-              wlo[tq] = rec[tq * a.rec_tile + w * 64 + lane];
-              whi[tq] = rec[tq * a.rec_tile + (w + 1) * 64 + lane];
+            for (int hh = 0; hh < 2; ++hh) {
+              const uint32_t ad = wad[2 * it + hh] + ((u * NS + t) % R) * SLOTB;
+              wlo[it][t][hh] = *(const uint32_t *)(sm + ad);
+              whi[it][t][hh] = *(const uint32_t *)(sm + ad + 256);
             }
-            cur = w;
-          }
-          const uint32_t mask = (1u << wd) - 1u;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (it >= 1 && it - 1 < SC_QMAX) {
+          const int qi = it - 1;
 #pragma unroll
-          for (int tq = 0; tq < NT; ++tq) {
-            const uint32_t f = __builtin_amdgcn_alignbit(whi[tq], wlo[tq], bo & 31) & mask;
-            dv[c][tq] = lutv[cb + f];
+          for (int t = 0; t < NS; ++t)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int h = 2 * qi + hh;
+              const uint32_t x = __builtin_amdgcn_alignbit(whi[qi][t][hh], wlo[qi][t][hh], hsh[h]) & hmk[h];
+              if constexpr (LG) ent[qi][t][hh] = glut[(hlut[h] >> 3) + x];
+              else ent[qi][t][hh] = *(const uint2 *)(sm + hlut[h] + x * 8u);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (it >= 2) {
+          const int qi = it - 2;
+#pragma unroll
+          for (int t = 0; t < NS; ++t) {
+            // E = (lo_ab, hi_ab, hi_cd, lo_cd): three consecutive register pairs
+            const uint4 E = make_uint4(ent[qi][t][0].x, ent[qi][t][0].y, ent[qi][t][1].x, ent[qi][t][1].y);
+#pragma unroll
+            for (int g = 0; g < GR; ++g) {
+              acc[t][g] = mfma4(aqa[qi][g], make_uint2(E.x, E.y), acc[t][g]);
+              acc[t][g] = mfma4(aqb[qi][g], make_uint2(E.z, E.w), acc[t][g]);
+              acc[t][g] = mfma4(aql[qi][g], make_uint2(E.y, E.z), acc[t][g]);
+            }
           }
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the stages in this order
+      }
+      if (qjl_wave) {  // + gamma * sum_j w_j (2 z_j - 1), w already scaled by sqrt(pi/2)/m
 #pragma unroll
-        for (int r = 0; r < GR; ++r) {
-          const uint2 a0 = aqm[(r * (NP + NQ) + 2 * qd) * 4];
-          const uint2 a1 = aqm[(r * (NP + NQ) + 2 * qd + 1) * 4];
-          const uint2 ac = aqm[(r * (NP + NQ) + NP + qd) * 4];
+        for (int t = 0; t < NS; ++t) {
+          float qa[GP];
 #pragma unroll
-          for (int tq = 0; tq < NT; ++tq) {
-            acc[tq][r] = mfma4(a0, make_uint2(dv[0][tq], dv[1][tq]), acc[tq][r]);
-            acc[tq][r] = mfma4(a1, make_uint2(dv[2][tq], dv[3][tq]), acc[tq][r]);
-            const uint2 bh = make_uint2(__builtin_amdgcn_perm(dv[1][tq], dv[0][tq], 0x05040100u),
-                                        __builtin_amdgcn_perm(dv[3][tq], dv[2][tq], 0x05040100u));
-            acc[tq][r] = mfma4(ac, bh, acc[tq][r]);
+          for (int g = 0; g < GP; ++g) qa[g] = 0.0f;
+          const uint32_t tl = tile_lds + (u * NS + t) * SLOTB;
+          for (int j0 = 0; j0 < m; j0 += 32) {
+            const uint32_t ad = tl + ((code_bits + j0) >> 5) * 256u;
+            const uint32_t z = __builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
+                                                         *(const uint32_t *)(sm + ad), zsh);
+            const int jn = min(32, m - j0);
+            for (int j = 0; j < jn; ++j) {
+              const float sg = ((z >> j) & 1u) ? 1.0f : -1.0f;
+#pragma unroll
+              for (int g = 0; g < GP; g += 4) {
+                const float4 w4 = *(const float4 *)(wq + (j0 + j) * GP + g);
+                qa[g] = fmaf(sg, w4.x, qa[g]);
+                qa[g + 1] = fmaf(sg, w4.y, qa[g + 1]);
+                qa[g + 2] = fmaf(sg, w4.z, qa[g + 2]);
+                qa[g + 3] = fmaf(sg, w4.w, qa[g + 3]);
+              }
+            }
           }
+          const float gm = half_bits_to_f32(*(const uint32_t *)(sm + tl + (W - 1) * 256u) >> 16);
+#pragma unroll
+          for (int g = 0; g < GR; ++g)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[t][g][rr] = fmaf(gm, qa[4 * g + rr], acc[t][g][rr]);
         }
       }
-    }
-    // ---- QJL term and stores
 #pragma unroll
-    for (int tq = 0; tq < NT; ++tq) {
-      if (tq >= ntl) continue;
-      const uint32_t *rr = rec + tq * a.rec_tile + lane;
-      float qa[GP];
+      for (int t = 0; t < NS; ++t) {
+        float *pw = pbuf + ((((ss & 1) * NS + t) * TS + tau) * KS + kk) * GP * 64 + lane;
 #pragma unroll
-      for (int g = 0; g < GP; ++g) qa[g] = 0.0f;
-      float gm = 0.0f;
-      if (m > 0) {
-        for (int j = 0; j < m; ++j) {
-          const int pos = code_bits + j;
-          const float sgn = ((rr[(pos >> 5) * 64] >> (pos & 31)) & 1u) ? 1.0f : -1.0f;
+        for (int g = 0; g < GR; ++g)
 #pragma unroll
-          for (int g = 0; g < GP; g += 4) {
-            const float4 wv = *(const float4 *)(wq + j * GP + g);
-            qa[g] = fmaf(sgn, wv.x, qa[g]);
-            qa[g + 1] = fmaf(sgn, wv.y, qa[g + 1]);
-            qa[g + 2] = fmaf(sgn, wv.z, qa[g + 2]);
-            qa[g + 3] = fmaf(sgn, wv.w, qa[g + 3]);
-          }
-        }
-        gm = half_bits_to_f32(rr[(W - 1) * 64] >> 16);
-      }
-      const int64_t t = (int64_t)(tp + tq) * 64 + lane;
-      if (t < a.n_tokens) {
-#pragma unroll
-        for (int r = 0; r < GR; ++r)
-#pragma unroll
-          for (int mm = 0; mm < 4; ++mm) {
-            const int g = 4 * r + mm;
-            if (g < G)
-              a.scores[((int64_t)b * a.n_q_heads + (int64_t)hkv * G + g) * a.n_tokens + t] =
-                  fmaf(gm, qa[g], acc[tq][r][mm]);
-          }
+          for (int rr = 0; rr < 4; ++rr) pw[(4 * g + rr) * 64] = acc[t][g][rr];
       }
     }
   }
+  step_barrier();
+  if (nsup > 0) reduce(nsup - 1);
 }
 
 // ------------------------------------------------------------------ attend
@@ -1647,17 +1908,15 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   return launched(fn);
 }
 
-template <int G, int NT, bool LG>
+template <int GR, int SLOTB, int R, bool LG>
 static void launch_scores(dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
-  hipLaunchKernelGGL((scores_kernel<G, NT, LG>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((scores_kernel<GR, SLOTB, R, LG>), grid, dim3(SC_BLOCK), lds, s, a);
 }
 
-template <int G>
-static void launch_scores_nt(int nt, bool lg, dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
-  if (lg) launch_scores<G, 4, true>(grid, lds, s, a);
-  else if (nt == 4) launch_scores<G, 4, false>(grid, lds, s, a);
-  else if (nt == 2) launch_scores<G, 2, false>(grid, lds, s, a);
-  else launch_scores<G, 1, false>(grid, lds, s, a);
+template <int GR, bool LG>
+static void launch_scores_slot(int slotb, dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
+  if (slotb == 8192) launch_scores<GR, 8192, 6, LG>(grid, lds, s, a);
+  else launch_scores<GR, 16384, 3, LG>(grid, lds, s, a);
 }
 
 extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_batch_stride, int batch,
@@ -1681,36 +1940,48 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
   if (st != SQ_OK) return st;
   if (n_tokens > ((int64_t)1 << 36)) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: too many tokens");
   const int d = kc->heads[first_head].d;
-  int max_cent = 1, max_m = 0;
+  int max_q = 1, max_plut = 1, max_m = 0, max_W = 1;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
     for (int h = 0; h < n_kv_heads; ++h) {
-      const HeadCal &hc = kc->heads[first_head + bb * calib_batch_stride + h];
-      max_cent = std::max(max_cent, hc.n_cent);
-      max_m = std::max(max_m, hc.m);
+      const DevHead &D = kc->host_desc[first_head + bb * calib_batch_stride + h];
+      if (D.d != d) return fail(SQ_ERR_ARG, "sq_scores: heads of one call must share head_dim");
+      max_q = std::max(max_q, D.n_quads);
+      max_plut = std::max(max_plut, D.n_plut);
+      max_m = std::max(max_m, D.m);
+      max_W = std::max(max_W, D.W);
     }
     if (calib_batch_stride == 0) break;
   }
-  const int GR = (G + 3) / 4, GP = 4 * GR;
+  const int GR = (G + 3) / 4, GP = 4 * GR, QM = sc_qmax(GR);
+  int ks = 1;
+  while (ks < SC_WAVES && ((max_q + ks - 1) / ks > QM || (SC_WAVES / ks) * max_W * 256 + 256 > 16384)) ks *= 2;
+  const int ts = SC_WAVES / ks;
+  const int passes = (max_q + ks * QM - 1) / (ks * QM);
+  const int need = ts * max_W * 256 + 256;  // a stream tile may read one row past its end
+  int slotb;
+  if (need <= 8192) slotb = 8192;
+  else if (need <= 16384) slotb = 16384;
+  else return fail(SQ_ERR_UNSUPPORTED, "sq_scores: records too long");
+  const int R = slotb == 8192 ? 6 : 3;  // ring slots (kernel template)
   ScoresArgs a{};
   const int limit = device_lds_limit();
-  const int scratch = (G + GP) * d;                          // prologue floats
-  int nt = 4;
-  bool lg = false;
-  // LDS: centroid pairs | MFMA A operands | QJL weights | record tiles
-  auto layout = [&](bool lut_in_lds, int n) {
-    a.lds_lut_off = 0;
-    a.lds_aq_off = lut_in_lds ? ((max_cent + 3) & ~3) : 0;  // 16-byte aligned
-    a.lds_w_off = a.lds_aq_off + 2 * GR * (d / 2 + d / 4) * 4;
-    a.lds_rec_off = a.lds_w_off + ((std::max(1, max_m) * GP + 3) & ~3);
-    a.rec_tile = (kc->W_max + 1) * 64;
-    return (size_t)(a.lds_rec_off + std::max(scratch, 4 * n * a.rec_tile)) * 4;
+  auto layout = [&](bool lut_in_lds) {
+    size_t off = 0;
+    a.lds_lut = 0;
+    off = lut_in_lds ? (((size_t)max_plut * 8 + 1023) & ~(size_t)1023) : 0;  // copied in 1 KB pieces
+    a.lds_qt = (int)off;   off += (size_t)G * d * 4;
+    off = (off + 15) & ~(size_t)15;
+    a.lds_wq = (int)off;   off += (size_t)std::max(1, max_m) * GP * 4;
+    off = (off + 1023) & ~(size_t)1023;
+    a.lds_slot = (int)off; off += (size_t)R * slotb;
+    a.lds_pbuf = (int)off; off += (size_t)2 * (slotb == 8192 ? 2 : 1) * SC_WAVES * GP * 64 * 4;  // parity x slots per barrier
+    return off;
   };
-  size_t lds = layout(true, nt);
-  while (nt > 1 && lds > (size_t)std::min(limit, 72 * 1024)) lds = layout(true, nt >>= 1);
-  if (lds > (size_t)limit) {  // centroid table too large: read it from the L1/L2
+  bool lg = false;
+  size_t lds = layout(true);
+  if (lds > (size_t)limit) {  // joint tables too large for LDS: read them through the caches
     lg = true;
-    nt = 4;
-    lds = layout(false, nt);
+    lds = layout(false);
   }
   if (lds > (size_t)limit) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: tables exceed LDS");
   a.heads = kc->dev_heads;
@@ -1724,28 +1995,31 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
   a.cbs = calib_batch_stride;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
+  a.G = G;
   a.q_f32 = qdt == SQ_F32;
+  a.ks = ks;
+  a.ts = ts;
+  a.dma16 = ((uintptr_t)kpacked % 16 == 0) && ps_batch % 4 == 0 && ps_head % 4 == 0;
   a.n_tiles = (int)((n_tokens + 63) / 64);
-  // workgroups: enough to fill the chip, each a multiple of one pass (4 waves x nt tiles)
+  // one workgroup per CU at a time: about two per CU over the launch
   const int64_t pairs = (int64_t)batch * n_kv_heads;
-  const int64_t want = (int64_t)device_cu_count() * 8;
-  int blocks_t = (int)std::min<int64_t>((a.n_tiles + 4 * nt - 1) / (4 * nt),
-                                        std::max<int64_t>(1, (want + pairs - 1) / pairs));
-  a.tiles_per_block = (a.n_tiles + blocks_t - 1) / blocks_t;
-  a.tiles_per_block = ((a.tiles_per_block + 4 * nt - 1) / (4 * nt)) * (4 * nt);
-  blocks_t = (a.n_tiles + a.tiles_per_block - 1) / a.tiles_per_block;
-  dim3 grid(blocks_t, n_kv_heads, batch);
+  const int64_t want = (int64_t)device_cu_count() * 2;
+  const int64_t steps = (a.n_tiles + ts - 1) / ts;
+  int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(steps, (want + pairs - 1) / pairs));
+  a.tiles_per_wg = (int)(((steps + chunks - 1) / chunks) * ts);
+  chunks = (a.n_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  dim3 grid((unsigned)chunks, n_kv_heads, batch);
   if (grid.z > 65535 || grid.y > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_scores: grid too large");
   hipStream_t s = (hipStream_t)stream;
-  switch (G) {
-    case 1: launch_scores_nt<1>(nt, lg, grid, lds, s, a); break;
-    case 2: launch_scores_nt<2>(nt, lg, grid, lds, s, a); break;
-    case 3: launch_scores_nt<3>(nt, lg, grid, lds, s, a); break;
-    case 4: launch_scores_nt<4>(nt, lg, grid, lds, s, a); break;
-    case 5: launch_scores_nt<5>(nt, lg, grid, lds, s, a); break;
-    case 6: launch_scores_nt<6>(nt, lg, grid, lds, s, a); break;
-    case 7: launch_scores_nt<7>(nt, lg, grid, lds, s, a); break;
-    case 8: launch_scores_nt<8>(nt, lg, grid, lds, s, a); break;
+  for (int p = 0; p < passes; ++p) {
+    a.pass = p;
+    if (GR == 1) {
+      if (lg) launch_scores_slot<1, true>(slotb, grid, lds, s, a);
+      else launch_scores_slot<1, false>(slotb, grid, lds, s, a);
+    } else {
+      if (lg) launch_scores_slot<2, true>(slotb, grid, lds, s, a);
+      else launch_scores_slot<2, false>(slotb, grid, lds, s, a);
+    }
   }
   return launched(fn);
 }
