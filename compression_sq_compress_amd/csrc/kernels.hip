@@ -130,27 +130,39 @@ static ScoreSched build_score_sched(const HeadCal &hc) {
     h.a = i;
     h.b = paired[i] ? i + 1 : -1;
     h.pos = hc.bit_off[i];
-    const int wa = w[i], wb = h.b >= 0 ? w[h.b] : 0;
-    h.width = wa + wb;
-    h.first = (uint32_t)(S.lut.size() / 2);
-    for (int v = 0; v < (1 << h.width); ++v) {
-      uint16_t ah, al, bh = 0, bl = 0;
-      bf16_split(cent(i, v & ((1 << wa) - 1)), ah, al);
-      if (h.b >= 0) bf16_split(cent(h.b, v >> wa), bh, bl);
-      const uint32_t hp = (uint32_t)ah | ((uint32_t)bh << 16), lp = (uint32_t)al | ((uint32_t)bl << 16);
-      const bool first = (halves.size() & 1) == 0;  // first half of its quad: (lo, hi), second: (hi, lo)
-      S.lut.push_back(first ? lp : hp);
-      S.lut.push_back(first ? hp : lp);
-    }
+    h.width = w[i] + (h.b >= 0 ? w[h.b] : 0);
+    h.first = 0;
     halves.push_back(h);
     i += paired[i] ? 2 : 1;
   }
-  const uint32_t zero = (uint32_t)(S.lut.size() / 2);
-  S.lut.push_back(0u);
-  S.lut.push_back(0u);
-  if (halves.size() & 1) halves.push_back(Half{-1, -1, 0, 0, zero});
+  if (halves.size() & 1) halves.push_back(Half{-1, -1, 0, 0, 0});  // empty half: one zero entry
+  // tables placed largest first, so each starts at a multiple of its own size
+  // (entry address = table base | code << 3)
+  std::vector<int> order(halves.size());
+  for (size_t k = 0; k < order.size(); ++k) order[k] = (int)k;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return halves[x].width > halves[y].width; });
+  uint32_t next = 0;
+  for (int k : order) {
+    halves[k].first = next;
+    next += 1u << halves[k].width;
+  }
+  S.lut.assign((size_t)next * 2, 0u);
+  for (size_t k = 0; k < halves.size(); ++k) {
+    const Half &h = halves[k];
+    if (h.a < 0) continue;
+    const int wa = w[h.a];
+    const bool first = (k & 1) == 0;  // first half of its quad: (lo, hi), second: (hi, lo)
+    for (int v = 0; v < (1 << h.width); ++v) {
+      uint16_t ah, al, bh = 0, bl = 0;
+      bf16_split(cent(h.a, v & ((1 << wa) - 1)), ah, al);
+      if (h.b >= 0) bf16_split(cent(h.b, v >> wa), bh, bl);
+      const uint32_t hp = (uint32_t)ah | ((uint32_t)bh << 16), lp = (uint32_t)al | ((uint32_t)bl << 16);
+      S.lut[2 * ((size_t)h.first + v)] = first ? lp : hp;
+      S.lut[2 * ((size_t)h.first + v) + 1] = first ? hp : lp;
+    }
+  }
   S.n_quads = (int)halves.size() / 2;
-  S.n_plut = (int)(S.lut.size() / 2);
+  S.n_plut = (int)next;
   auto slot = [](int c) { return c < 0 ? 0xFFFFu : (uint32_t)c; };
   for (int q = 0; q < S.n_quads; ++q) {
     const Half &h0 = halves[2 * q], &h1 = halves[2 * q + 1];
@@ -1176,6 +1188,7 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
       wq[k] = hd->qjl_scale * acc;
     }
   }
+  __syncthreads();  // wq complete
   float *pbuf = (float *)(sm + a.lds_pbuf);
 
   if (loader) {
@@ -1197,7 +1210,14 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
   const int nqb = nq_pass / KS, nqr = nq_pass - nqb * KS;
   const int nq = nqb + (kk < nqr ? 1 : 0);
   const int q0 = qp0 + kk * nqb + min(kk, nqr);
-  const bool qjl_wave = kk == KS - 1 && m > 0 && a.pass == 0;
+  // QJL term: wave kk adds it for the query heads (rows) r = kk, kk + KS, ..
+  // to its own partial sum, so that every row gets it exactly once
+  const bool qjl = m > 0 && a.pass == 0 && kk < min(G, GP);
+  const bool qjl_fast = qjl && KS >= GP && m <= 8;  // one row per wave, weights in scalars
+  uint32_t qw[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    qw[j] = qjl_fast && j < m ? __float_as_uint(wq[j * GP + kk]) : 0u;  // (vector registers)
   const SQ_CONST uint32_t *sch = cptr<uint32_t>(a.blob + hd->off_sched);
   // Every wave runs SC_QMAX quads; those past its share are empty (mask 0,
   // A operands 0) so that the quads form one straight-line block.  Table
@@ -1213,12 +1233,15 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
     const SQ_CONST uint32_t *e = sch + (size_t)(q0 + (real ? qi : 0)) * SCHED_WORDS;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+      // the 64-bit window starts 3 bits before the field (one row earlier
+      // when the field starts in the first 3 bits of a word), so that
+      // alignbit & (mask << 3) gives code * 8, the entry's byte offset
       const uint32_t pw = e[hh];
-      const uint32_t pos = pw & 0xFFFFu, wd = pw >> 16;
-      hsh[2 * qi + hh] = to_vgpr(pos & 31u);
-      hmk[2 * qi + hh] = to_vgpr(real ? (1u << wd) - 1u : 0u);
+      const int pos = (int)(pw & 0xFFFFu) - 3, wd = (int)(pw >> 16);
+      hsh[2 * qi + hh] = to_vgpr((uint32_t)pos & 31u);
+      hmk[2 * qi + hh] = to_vgpr(real ? ((1u << wd) - 1u) << 3 : 0u);
       hlut[2 * qi + hh] = (LG ? 0u : (uint32_t)a.lds_lut) + e[2 + hh] * 8u;
-      wad[2 * qi + hh] = tile_lds + (pos >> 5) * 256u;
+      wad[2 * qi + hh] = tile_lds + (uint32_t)(pos >> 5) * 256u;  // (pos >> 5) may be -1
     }
     const uint32_t s01 = e[4], s23 = e[5];
     const uint32_t sl[4] = {s01 & 0xFFFFu, s01 >> 16, s23 & 0xFFFFu, s23 >> 16};
@@ -1314,9 +1337,10 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const int h = 2 * qi + hh;
-              const uint32_t x = __builtin_amdgcn_alignbit(whi[qi][t][hh], wlo[qi][t][hh], hsh[h]) & hmk[h];
-              if constexpr (LG) ent[qi][t][hh] = glut[(hlut[h] >> 3) + x];
-              else ent[qi][t][hh] = *(const uint2 *)(sm + hlut[h] + x * 8u);
+              // table base | code * 8 (tables are aligned to their size)
+              const uint32_t ea = (__builtin_amdgcn_alignbit(whi[qi][t][hh], wlo[qi][t][hh], hsh[h]) & hmk[h]) | hlut[h];
+              if constexpr (LG) ent[qi][t][hh] = *(const uint2 *)((const uint8_t *)glut + ea);
+              else ent[qi][t][hh] = *(const uint2 *)(sm + ea);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1336,35 +1360,44 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the stages in this order
       }
-      if (qjl_wave) {  // + gamma * sum_j w_j (2 z_j - 1), w already scaled by sqrt(pi/2)/m
+      if (qjl) {  // + gamma * sum_j w_j (2 z_j - 1), w already scaled by sqrt(pi/2)/m
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-          float qa[GP];
-#pragma unroll
-          for (int g = 0; g < GP; ++g) qa[g] = 0.0f;
           const uint32_t tl = tile_lds + (u * NS + t) * SLOTB;
-          for (int j0 = 0; j0 < m; j0 += 32) {
-            const uint32_t ad = tl + ((code_bits + j0) >> 5) * 256u;
-            const uint32_t z = __builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
-                                                         *(const uint32_t *)(sm + ad), zsh);
-            const int jn = min(32, m - j0);
-            for (int j = 0; j < jn; ++j) {
-              const float sg = ((z >> j) & 1u) ? 1.0f : -1.0f;
+          const float gm = half_bits_to_f32(*(const uint32_t *)(sm + tl + (W - 1) * 256u) >> 16);
+          if (qjl_fast) {
+            const uint32_t ad = tl + (code_bits >> 5) * 256u;
+            const uint32_t nz = ~__builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
+                                                          *(const uint32_t *)(sm + ad), zsh);
+            float qa = 0.0f;
 #pragma unroll
-              for (int g = 0; g < GP; g += 4) {
-                const float4 w4 = *(const float4 *)(wq + (j0 + j) * GP + g);
-                qa[g] = fmaf(sg, w4.x, qa[g]);
-                qa[g + 1] = fmaf(sg, w4.y, qa[g + 1]);
-                qa[g + 2] = fmaf(sg, w4.z, qa[g + 2]);
-                qa[g + 3] = fmaf(sg, w4.w, qa[g + 3]);
+            for (int j = 0; j < 8; ++j)  // +w_j where z_j = 1, -w_j where z_j = 0 (w_j = 0 past m)
+              qa += __uint_as_float(qw[j] ^ ((nz << (31 - j)) & 0x80000000u));
+#pragma unroll
+            for (int g = 0; g < GR; ++g)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                if (4 * g + rr == kk) acc[t][g][rr] = fmaf(gm, qa, acc[t][g][rr]);
+          } else {
+            for (int row = kk; row < min(G, GP); row += KS) {
+              float qa = 0.0f;
+              for (int j0 = 0; j0 < m; j0 += 32) {
+                const uint32_t ad = tl + ((code_bits + j0) >> 5) * 256u;
+                const uint32_t z = __builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
+                                                             *(const uint32_t *)(sm + ad), zsh);
+                const int jn = min(32, m - j0);
+                for (int j = 0; j < jn; ++j) {
+                  const float wv = wq[(j0 + j) * GP + row];
+                  qa += ((z >> j) & 1u) ? wv : -wv;
+                }
               }
+#pragma unroll
+              for (int g = 0; g < GR; ++g)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                  if (4 * g + rr == row) acc[t][g][rr] = fmaf(gm, qa, acc[t][g][rr]);
             }
           }
-          const float gm = half_bits_to_f32(*(const uint32_t *)(sm + tl + (W - 1) * 256u) >> 16);
-#pragma unroll
-          for (int g = 0; g < GR; ++g)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[t][g][rr] = fmaf(gm, qa[4 * g + rr], acc[t][g][rr]);
         }
       }
 #pragma unroll
