@@ -241,7 +241,7 @@ def main():
                      "achieved": comp_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": comp_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                      "alg_bytes_per_launch": comp_launch_bytes, "launch_ms": comp_launch_ms},
-        "roofline_scores": {"bound": "hbm", "kernel": "scores_kernel<4,4> (4x4x4 bf16 MFMA)",
+        "roofline_scores": {"bound": "hbm", "kernel": "scores_kernel (split-K waves, 4x4x4 bf16 MFMA, joint tables)",
                             "achieved": gbps(bytes_sc, ms_sc), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": gbps(bytes_sc, ms_sc) / HBM_PEAK_GBPS,
                             "traffic": None, "alg_bytes_per_launch": bytes_sc, "launch_ms": ms_sc},
