@@ -385,12 +385,133 @@ static HostPlan build_plan(const HeadCal &hc) {
   return P;
 }
 
+// Register-quantising compress plan (layout: P2_WAVE, P2_WORD).  Groups of 4
+// consecutive coordinates (depth = largest width) are dealt to the waves'
+// accumulator registers largest depth first, each to the least loaded wave
+// with a free register; record words are dealt the same way by the number of
+// codes they hold (the words with QJL bits and gamma count extra).
+struct HostPlan2 {
+  std::vector<uint32_t> words;
+  std::vector<float> tree, csig;
+  std::vector<int> row_coord;  // [d]: coordinate of MFMA row (w*16 + rho)
+  bool ok = false;
+};
+
+static HostPlan2 build_plan2(const HeadCal &hc) {
+  HostPlan2 P;
+  const int d = hc.d;
+  if (d != 32 && d != 64 && d != 128) return P;
+  if (hc.m > 0 && (hc.d_eff > 16 || hc.m > 32)) return P;
+  const int NW = d / 16, NG = d / 4;
+  std::vector<int> depth(NG, 0);
+  for (int g = 0; g < NG; ++g)
+    for (int s = 0; s < 4; ++s) depth[g] = std::max(depth[g], hc.widths[4 * g + s]);
+  std::vector<int> order(NG);
+  for (int g = 0; g < NG; ++g) order[g] = g;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return depth[x] > depth[y]; });
+  std::vector<int> load(NW, 0), nslot(NW, 0), slot_g((size_t)NW * 4, -1);
+  for (int g : order) {
+    int best = -1;
+    for (int w = 0; w < NW; ++w)
+      if (nslot[w] < 4 && (best < 0 || load[w] < load[best])) best = w;
+    slot_g[(size_t)best * 4 + nslot[best]++] = g;
+    load[best] += 4 * depth[g] + 3;
+  }
+  // the kernel's descent relies on each wave's registers by decreasing depth
+  for (int w = 0; w < NW; ++w)
+    std::stable_sort(slot_g.begin() + (size_t)w * 4, slot_g.begin() + (size_t)w * 4 + 4,
+                     [&](int x, int y) { return depth[x] > depth[y]; });
+  const float inf = std::numeric_limits<float>::infinity();
+  auto canon = [](float v) { return v == 0.0f ? 0.0f : v; };
+  P.row_coord.assign(d, 0);
+  std::vector<uint32_t> hdr((size_t)NW * P2_WAVE, 0u);
+  for (int w = 0; w < NW; ++w) {
+    uint32_t *H = hdr.data() + (size_t)w * P2_WAVE;
+    for (int r = 0; r < 4; ++r) {
+      const int g = slot_g[(size_t)w * 4 + r], D = depth[g], L = 1 << D;
+      H[r] = (uint32_t)D;
+      for (int s = 0; s < 4; ++s) {
+        const int c = 4 * g + s, b = hc.widths[c];
+        P.row_coord[w * 16 + 4 * s + r] = c;
+        H[36 + 4 * r + s] = (uint32_t)c;
+        const size_t tb = P.tree.size();
+        H[4 + 4 * r + s] = (uint32_t)tb;
+        if (D > 0) {
+          // sorted thresholds padded with +inf to L - 1; node n (depth k,
+          // position p = n - 2^k) holds padded entry (2p + 1) * 2^(D - 1 - k) - 1
+          std::vector<float> padded(L - 1, inf);
+          for (int k = 0; k + 1 < (1 << b); ++k) padded[k] = canon(hc.thr[hc.thr_base[c] + k]);
+          P.tree.resize(tb + L - 1, inf);
+          for (int n = 1; n < L; ++n) {
+            int k = 0;
+            while ((2 << k) <= n) ++k;
+            const int pos = n - (1 << k);
+            P.tree[tb + n - 1] = padded[(size_t)(2 * pos + 1) * (1 << (D - 1 - k)) - 1];
+          }
+        }
+        if (hc.m > 0 && c < hc.d_eff) {
+          const size_t cb = P.csig.size();
+          H[20 + 4 * r + s] = (uint32_t)cb;
+          P.csig.resize(cb + L, 0.0f);
+          for (int k = 0; k < (1 << b) && b > 0; ++k) P.csig[cb + k] = hc.cent[hc.cent_base[c] + k];
+        } else {
+          H[20 + 4 * r + s] = 0xFFFFFFFFu;
+        }
+      }
+    }
+  }
+  // record words: the coordinates with bits in each, then dealt to the waves
+  struct Wd { int k, c0, c1, q, cost; };
+  std::vector<Wd> wds;
+  for (int k = 0; k < hc.W; ++k) {
+    Wd e{k, 1, 0, 0, 1};
+    for (int c = 0; c < d; ++c) {
+      const int b = hc.widths[c], lo = hc.bit_off[c];
+      if (b > 0 && lo < 32 * k + 32 && lo + b > 32 * k) {
+        if (e.c0 > e.c1) e.c0 = c;
+        e.c1 = c;
+      }
+    }
+    if (hc.m > 0 && ((hc.code_bits < 32 * k + 32 && hc.code_bits + hc.m > 32 * k) || k == hc.W - 1)) e.q = 1;
+    e.cost = (e.c1 >= e.c0 ? e.c1 - e.c0 + 1 : 0) + (e.q ? 8 + hc.m * hc.d_eff / 4 : 0) + 2;
+    wds.push_back(e);
+  }
+  std::vector<int> word_order(wds.size());
+  for (size_t k = 0; k < wds.size(); ++k) word_order[k] = (int)k;
+  std::stable_sort(word_order.begin(), word_order.end(), [&](int x, int y) { return wds[x].cost > wds[y].cost; });
+  std::vector<std::vector<int>> per_wave(NW);
+  std::vector<int> wload(NW, 0);
+  for (int k : word_order) {
+    int best = 0;
+    for (int w = 1; w < NW; ++w)
+      if (wload[w] < wload[best]) best = w;
+    per_wave[best].push_back(k);
+    wload[best] += wds[k].cost;
+  }
+  P.words = hdr;
+  int nxt = 0;
+  for (int w = 0; w < NW; ++w) {
+    P.words[(size_t)w * P2_WAVE + 52] = (uint32_t)per_wave[w].size();
+    P.words[(size_t)w * P2_WAVE + 53] = (uint32_t)nxt;
+    for (int k : per_wave[w]) {
+      const Wd &e = wds[k];
+      const uint32_t E[P2_WORD] = {(uint32_t)e.k, (uint32_t)e.c0, (uint32_t)e.c1, (uint32_t)e.q};
+      P.words.insert(P.words.end(), E, E + P2_WORD);
+      ++nxt;
+    }
+  }
+  P.ok = P.tree.size() < 65536 && hc.W < 256;  // 16-bit tree bases, 8-bit word indices in the kernel
+  return P;
+}
+
 sq_status upload_tables(sq_calib *c, void *stream) {
   const int nh = (int)c->heads.size();
   std::vector<HostPlan> plans(nh);
   for (int h = 0; h < nh; ++h) plans[h] = build_plan(c->heads[h]);
   std::vector<ScoreSched> scheds(nh);
   for (int h = 0; h < nh; ++h) scheds[h] = build_score_sched(c->heads[h]);
+  std::vector<HostPlan2> plans2(nh);
+  for (int h = 0; h < nh; ++h) plans2[h] = build_plan2(c->heads[h]);
   // host image of the blob: [DevHead x nh] then per-head sections
   std::vector<DevHead> desc(nh);
   size_t off = align256(sizeof(DevHead) * nh);
@@ -426,6 +547,14 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     off = align256(off + ((sizeof(uint32_t) * scheds[h].lut.size() + 1023) & ~(size_t)1023));
     D.off_lutp = off;    off = align256(off + sizeof(uint32_t) * std::max(1, hc.n_cent));
     D.off_csig = off;    off = align256(off + sizeof(float) * std::max<size_t>(1, P.csig.size()));
+    const HostPlan2 &P2 = plans2[h];
+    D.n_p2 = P2.ok ? (int)P2.words.size() : 0;
+    D.n_tree2 = (int)P2.tree.size();
+    D.n_csig2 = (int)P2.csig.size();
+    D.off_p2 = off;      off = align256(off + sizeof(uint32_t) * std::max<size_t>(1, P2.words.size()));
+    D.off_tree2 = off;   off = align256(off + sizeof(float) * std::max<size_t>(1, P2.tree.size()));
+    D.off_csig2 = off;   off = align256(off + sizeof(float) * std::max<size_t>(1, P2.csig.size()));
+    D.off_Rfrag2 = off;  off = align256(off + (P2.ok ? sizeof(uint16_t) * 3 * d * d : 1));
   }
   std::vector<uint8_t> img(off, 0);
   std::memcpy(img.data(), desc.data(), sizeof(DevHead) * nh);
@@ -461,6 +590,27 @@ sq_status upload_tables(sq_calib *c, void *stream) {
             for (int s = 0; s < 3; ++s)
               F[((((size_t)s * MB + mb) * KB + kb) * 64 + l) * 8 + e] = parts[s];
           }
+    {
+      const HostPlan2 &P2 = plans2[h];
+      if (P2.ok) {
+        std::memcpy(img.data() + D.off_p2, P2.words.data(), sizeof(uint32_t) * P2.words.size());
+        if (!P2.tree.empty()) std::memcpy(img.data() + D.off_tree2, P2.tree.data(), sizeof(float) * P2.tree.size());
+        if (!P2.csig.empty()) std::memcpy(img.data() + D.off_csig2, P2.csig.data(), sizeof(float) * P2.csig.size());
+        // the bf16 x3 split of R with rows permuted: MFMA row w*16 + rho holds coordinate row_coord[...]
+        uint16_t *F2 = (uint16_t *)(img.data() + D.off_Rfrag2);
+        const uint16_t *F1 = (const uint16_t *)(img.data() + D.off_Rfrag);
+        const int MB2 = d / 16, KB2 = d / 32;
+        for (int sp = 0; sp < 3; ++sp)
+          for (int mb = 0; mb < MB2; ++mb)
+            for (int kb = 0; kb < KB2; ++kb)
+              for (int l = 0; l < 64; ++l) {
+                const int c = P2.row_coord[mb * 16 + (l & 15)];
+                const int mb1 = c / 16, l1 = (c % 16) | (l & 48);
+                std::memcpy(F2 + ((((size_t)sp * MB2 + mb) * KB2 + kb) * 64 + l) * 8,
+                            F1 + ((((size_t)sp * MB2 + mb1) * KB2 + kb) * 64 + l1) * 8, 16);
+              }
+      }
+    }
     DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
     for (int i = 0; i < d; ++i) Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
     std::memcpy(img.data() + D.off_sched, scheds[h].quads.data(), sizeof(uint32_t) * scheds[h].quads.size());
@@ -978,6 +1128,325 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
   if (pdst) store_prev();
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n (the counter field is an immediate)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define SQ_VMW(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | ((k) & 15) | (((k) >> 4) << 14)); break;
+#define SQ_VMW8(k) SQ_VMW(k) SQ_VMW(k + 1) SQ_VMW(k + 2) SQ_VMW(k + 3) SQ_VMW(k + 4) SQ_VMW(k + 5) SQ_VMW(k + 6) SQ_VMW(k + 7)
+    SQ_VMW8(0) SQ_VMW8(8) SQ_VMW8(16) SQ_VMW8(24) SQ_VMW8(32) SQ_VMW8(40) SQ_VMW8(48) SQ_VMW8(56)
+#undef SQ_VMW8
+#undef SQ_VMW
+    default: __builtin_amdgcn_s_waitcnt(0xCF7F); break;  // vmcnt(63): waits for more, never less
+  }
+}
+
+// workgroup barrier without the memory fence of __syncthreads (the producer
+// must not wait for its later loads); LDS writes of the wave are complete.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS loads (global_load_lds_dword / _dwordx4): lane l's 4 (16)
+// bytes land at LDS address lds + 4l (16l).  Written as asm so that the
+// compiler does not treat every later LDS read of the workgroup as a possible
+// reader of these writes (it would wait for all vector memory there); the
+// loads are ordered explicitly by wait_vmcnt and step_barrier.  They have no
+// register results.
+// Address = wave-uniform base (scalar pair) + per-lane byte offset.
+__device__ __forceinline__ void lds_dma16(const void *base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void *base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+// a wave-uniform value kept in a vector register (it is combined with
+// another uniform operand in one VOP3 instruction, which takes one scalar)
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(x));
+  return v;
+}
+
+// ------------------------------------------------------------------ compress, register quantiser
+//
+// Same contract as compress_kernel, for head_dim 32, 64 and 128 with at most
+// 16 signal coordinates and 32 QJL rows.  A workgroup of d/16 waves serves
+// one calibration head and walks 64-token tiles with one barrier per tile:
+//   rotate:   wave w forms its 16 MFMA rows of y^T for the tile (16x16x32 bf16,
+//             R as three bf16 terms in registers); its rows are the four
+//             coordinate groups of the register plan (P2_WAVE), so lane l
+//             holds in accumulator register r the values of one coordinate
+//             for tokens l % 16 + 16 j.
+//   quantise: straight from the accumulators: per register, four independent
+//             descents (one per token block) of the lane's own padded
+//             threshold tree in LDS, all lanes of the register to the same
+//             depth; each code is OR-ed into its record word(s) in an LDS
+//             record tile [token][word], and signal residuals y - C[code]
+//             go to a small float tile.
+//   store:    after the barrier each wave takes whole record words (adding
+//             the QJL bits and gamma from the residuals where they belong),
+//             stores them as coalesced 256-byte rows and clears them.
+// The x tile, the record tile and the residual tile are double-buffered, so
+// the barrier of tile t also separates tile t+1's writes from tile t-1's reads.
+
+struct Compress2Args {
+  const DevHead *heads;
+  const uint8_t *blob;
+  const void *x;
+  uint32_t *packed;
+  int64_t xs_b, xs_h, xs_t;
+  int64_t ps_b, ps_h;
+  int64_t n_tokens;
+  int first_head, cbs;
+  int n_tiles, items;
+  int lds_tree_off, lds_csig_off, lds_s_off, lds_x_off, lds_rec_off, lds_res_off;  // floats
+  int x_buf_floats, rec_stride;  // record tile row stride (words, odd)
+};
+
+constexpr int C2_RS = 17;  // residual tile row stride (floats)
+
+template <int D, bool F32>
+__global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
+  extern __shared__ float smem[];
+  constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y, bz = blockIdx.z;
+  const int ch = a.first_head + bz * a.cbs + h;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
+  const int d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
+  float *trees = smem + a.lds_tree_off;
+  float *csig = smem + a.lds_csig_off;
+  float *Sl = smem + a.lds_s_off;  // [m][d_eff]
+  {
+    const float *g = (const float *)(a.blob + hd->off_tree2);
+    for (int k = threadIdx.x; k < hd->n_tree2; k += NT) trees[k] = g[k];
+    const float *gc = (const float *)(a.blob + hd->off_csig2);
+    for (int k = threadIdx.x; k < hd->n_csig2; k += NT) csig[k] = gc[k];
+    const float *gs = (const float *)(a.blob + hd->off_S);
+    for (int k = threadIdx.x; k < m * d_eff; k += NT) Sl[k] = gs[k];
+  }
+  const SQ_CONST uint32_t *p2 = cptr<uint32_t>(a.blob + hd->off_p2);
+  const SQ_CONST uint32_t *H = p2 + w * P2_WAVE;
+  const int s4 = lane >> 4;
+  int dep[4];
+  // per lane and register: tree base | (record word | bit shift << 8 |
+  // straddles << 13) << 16; coordinate | signal-centroid base << 8 (0xFFFFFF: none)
+  uint32_t tw[4], cc[4];
+  {
+    const uint32_t *Hv = (const uint32_t *)(a.blob + hd->off_p2) + w * P2_WAVE;  // per-lane reads
+    const DevCoord *cd = (const DevCoord *)(a.blob + hd->off_coord);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dep[r] = (int)H[r];
+      const uint32_t cb = Hv[20 + 4 * r + s4], c = Hv[36 + 4 * r + s4];
+      cc[r] = c | ((cb == 0xFFFFFFFFu ? 0xFFFFFFu : cb) << 8);
+      const int bo = cd[c].bit_off, wd = cd[c].width;
+      const uint32_t wsh = (uint32_t)(bo >> 5) | ((uint32_t)(bo & 31) << 8) | ((bo & 31) + wd > 32 ? 1u << 13 : 0u);
+      tw[r] = Hv[4 + 4 * r + s4] | (wsh << 16);
+    }
+  }
+  const int nwords = (int)H[52];
+  const SQ_CONST uint32_t *wlist = p2 + NW * P2_WAVE + H[53] * P2_WORD;
+  const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag2);
+  uint4 rf[3][KB];
+#pragma unroll
+  for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) rf[sp][kb] = Rf[((sp * MB + w) * KB + kb) * 64 + lane];
+
+  // x tiles are loaded straight into LDS (1 KB per load instruction), rows of
+  // RB bytes back to back; chunk c (16 bytes) of row t sits at slot
+  // c ^ swz(t) of the row, which keeps the MFMA operand reads conflict-free.
+  constexpr int ESZ = F32 ? 4 : 2;
+  constexpr int RB = D * ESZ;                    // bytes per token row
+  constexpr int CPR = RB / 16;                   // chunks per row
+  constexpr int RPB = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256 bytes
+  constexpr int NB = CPR / NW;                   // 1 KB blocks per wave and tile
+  const uint32_t lds_x = (uint32_t)(uintptr_t)(smem + a.lds_x_off);
+  const uint32_t row_bytes = (uint32_t)a.xs_t * ESZ;  // 64 rows fit 32 bits (host check)
+  auto dma_x = [&](int item, int buf) __attribute__((always_inline)) {
+    const int bb = a.cbs ? bz : item / a.n_tiles;
+    const int tl = a.cbs ? item : item % a.n_tiles;
+    const int64_t t0 = (int64_t)tl * 64;
+    const char *src = (const char *)a.x + ((int64_t)bb * a.xs_b + (int64_t)h * a.xs_h + t0 * a.xs_t) * ESZ;
+    const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);  // rows past the end re-read the last token
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = w * NB + i;
+      const int byte = q * 1024 + lane * 16, row = byte / RB, slot = (byte % RB) / 16;
+      const int c = slot ^ ((row / RPB) & (CPR - 1));
+      lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)c * 16u,
+                lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
+    }
+  };
+  for (int k = threadIdx.x; k < 2 * 64 * a.rec_stride; k += NT) smem[a.lds_rec_off + k] = 0.0f;
+  // All set-up loads complete here, so that no wait inside the tile loop has
+  // to cover them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (blockIdx.x < a.items) dma_x(blockIdx.x, 0);
+  if (blockIdx.x + (int)gridDim.x < a.items) dma_x(blockIdx.x + gridDim.x, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  int par = 0;
+  for (int item = blockIdx.x; item < a.items; item += gridDim.x, par ^= 1) {
+    const int b = a.cbs ? bz : item / a.n_tiles;
+    const int tile = a.cbs ? item : item % a.n_tiles;
+    const int64_t t0 = (int64_t)tile * 64;
+    // ---- rotate: 16 rows x 64 tokens (4 blocks of 16)
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint4 r0 = rf[0][kb], r1 = rf[1][kb], r2 = rf[2][kb];
+      const char *xt = (const char *)(smem + a.lds_x_off + par * a.x_buf_floats);
+      if constexpr (!F32) {
+        const int kc = kb * 4 + (lane >> 4);  // chunk of elements kb*32 + 8*(lane/16) ..
+        uint4 xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * j + (lane & 15);
+          xv[j] = *(const uint4 *)(xt + row * RB + ((kc ^ ((row / RPB) & (CPR - 1))) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r0, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r1, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r2, xv[j], acc[j]);
+      } else {
+        const int kc = kb * 8 + 2 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * j + (lane & 15), sw = (row / RPB) & (CPR - 1);
+          float v[8];
+          const float4 u0 = *(const float4 *)(xt + row * RB + ((kc ^ sw) << 4));
+          const float4 u1 = *(const float4 *)(xt + row * RB + (((kc + 1) ^ sw) << 4));
+          v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+          v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+          uint4 x0, x1, x2;
+          split3(v, x0, x1, x2);
+          acc[j] = mfma16(r0, x0, acc[j]);
+          acc[j] = mfma16(r0, x1, acc[j]);
+          acc[j] = mfma16(r1, x0, acc[j]);
+          acc[j] = mfma16(r0, x2, acc[j]);
+          acc[j] = mfma16(r2, x0, acc[j]);
+          acc[j] = mfma16(r1, x1, acc[j]);
+        }
+      }
+    }
+    // ---- quantise from the accumulators: code = #{thresholds < y} by a
+    // descent of the padded tree; a NaN y counts as -inf (code 0).  The 16
+    // descents of a wave (4 registers x 4 token blocks) advance level by
+    // level together, so their LDS reads overlap; the plan orders a wave's
+    // registers by decreasing depth, so the registers still descending at a
+    // level are a prefix.  (The descriptors are decoded per tile: hoisting the
+    // decoded fields out of the loop would not fit the register budget.)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(tw[r]), "+v"(cc[r]));
+    uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off) + par * 64 * a.rec_stride;
+    float *rtile = smem + a.lds_res_off + par * 64 * C2_RS;
+    uint32_t k[4][4];
+    const float *tr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      tr[r] = trees + (tw[r] & 0xFFFFu) - 1;  // node k at tr[k]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j][r] = fmaxf(acc[j][r], -INFINITY);
+        k[r][j] = 1u;
+      }
+    }
+    auto level = [&](auto nr) __attribute__((always_inline)) {
+      float t[decltype(nr)::value][4];
+#pragma unroll
+      for (int r = 0; r < decltype(nr)::value; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[r][j] = tr[r][k[r][j]];
+#pragma unroll
+      for (int r = 0; r < decltype(nr)::value; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          k[r][j] = __builtin_amdgcn_alignbit(k[r][j], __float_as_uint(t[r][j] - acc[j][r]), 31);
+    };
+    {
+      int l = 0;
+      for (; l < dep[3]; ++l) level(std::integral_constant<int, 4>{});
+      for (; l < dep[2]; ++l) level(std::integral_constant<int, 3>{});
+      for (; l < dep[1]; ++l) level(std::integral_constant<int, 2>{});
+      for (; l < dep[0]; ++l) level(std::integral_constant<int, 1>{});
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t kw = (tw[r] >> 16) & 0xFFu, sh = (tw[r] >> 24) & 31u;
+      uint32_t *rw = rec + (lane & 15) * a.rec_stride + kw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * a.rec_stride, (k[r][j] - (1u << dep[r])) << sh);
+      if (tw[r] & (1u << 29)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * a.rec_stride + 1, (k[r][j] - (1u << dep[r])) >> (32u - sh));
+      }
+    }
+    if (m > 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t crd = cc[r] & 0xFFu, cb = cc[r] >> 8;
+        if (cb != 0xFFFFFFu) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            rtile[((lane & 15) + 16 * j) * C2_RS + crd] = acc[j][r] - csig[cb + k[r][j] - (1u << dep[r])];
+        }
+      }
+    }
+    // ---- the next tile's x has landed (this wave's loads; the barrier covers
+    // every wave's); then the tile after it goes into the buffer just read
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (item + 2 * (int)gridDim.x < a.items) dma_x(item + 2 * gridDim.x, par);
+    // ---- store whole record words, lane = token
+    {
+      uint32_t *rrec = rec + lane * a.rec_stride;
+      const float *rrow = rtile + lane * C2_RS;
+      const bool valid = t0 + lane < a.n_tokens;
+      uint32_t *dst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
+      uint32_t zb = 0u, gb = 0u;
+      bool qdone = false;
+      for (int e = 0; e < nwords; ++e) {
+        const int k = (int)wlist[e * P2_WORD];
+        const bool q = wlist[e * P2_WORD + 3] != 0u;
+        uint32_t word = rrec[k];
+        rrec[k] = 0u;  // cleared for tile + 2 (its writers pass the next barrier first)
+        if (q) {
+          if (!qdone) {  // z_j = [(S r)_j >= 0], gamma = |r| as IEEE half (RNE)
+            float g2 = 0.0f;
+            for (int i = 0; i < d_eff; ++i) g2 = fmaf(rrow[i], rrow[i], g2);
+            for (int j = 0; j < m; ++j) {
+              float dot = 0.0f;
+              for (int i = 0; i < d_eff; ++i) dot = fmaf(Sl[j * d_eff + i], rrow[i], dot);
+              zb |= (dot >= 0.0f ? 1u : 0u) << j;
+            }
+            gb = half_bits_rne(sqrtf(g2)) << 16;
+            qdone = true;
+          }
+          const int lo = code_bits - 32 * k;  // position of z_0 in this word
+          if (lo >= 0 && lo < 32) word |= zb << lo;
+          else if (lo < 0 && lo > -32) word |= zb >> (-lo);
+          if (k == W - 1) word |= gb;
+        }
+        dst[(int64_t)k * 64] = valid ? word : 0u;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ scores
 //
 // s_t = sum_i q~_i C_i[code_ti] + sqrt(pi/2)/m * gamma_t * sum_j w_j (2 z_tj - 1),
@@ -1036,50 +1505,6 @@ __device__ __forceinline__ f32x4 mfma4(uint2 a, uint2 b, f32x4 c) {
 
 __device__ __forceinline__ uint32_t bf16_pair(uint16_t x) { return (uint32_t)x | ((uint32_t)x << 16); }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n (the counter field is an immediate)
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-#define SQ_VMW(k) \
-  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | ((k) & 15) | (((k) >> 4) << 14)); break;
-#define SQ_VMW8(k) SQ_VMW(k) SQ_VMW(k + 1) SQ_VMW(k + 2) SQ_VMW(k + 3) SQ_VMW(k + 4) SQ_VMW(k + 5) SQ_VMW(k + 6) SQ_VMW(k + 7)
-    SQ_VMW8(0) SQ_VMW8(8) SQ_VMW8(16) SQ_VMW8(24) SQ_VMW8(32) SQ_VMW8(40) SQ_VMW8(48) SQ_VMW8(56)
-#undef SQ_VMW8
-#undef SQ_VMW
-    default: __builtin_amdgcn_s_waitcnt(0xCF7F); break;  // vmcnt(63): waits for more, never less
-  }
-}
-
-// workgroup barrier without the memory fence of __syncthreads (the producer
-// must not wait for its later loads); LDS writes of the wave are complete.
-__device__ __forceinline__ void step_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Direct-to-LDS loads (global_load_lds_dword / _dwordx4): lane l's 4 (16)
-// bytes land at LDS address lds + 4l (16l).  Written as asm so that the
-// compiler does not treat every later LDS read of the workgroup as a possible
-// reader of these writes (it would wait for all vector memory there); the
-// loads are ordered explicitly by wait_vmcnt and step_barrier.  They have no
-// register results.
-// Address = wave-uniform base (scalar pair) + per-lane byte offset.
-__device__ __forceinline__ void lds_dma16(const void *base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void *base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-// a wave-uniform value kept in a vector register (it is combined with
-// another uniform operand in one VOP3 instruction, which takes one scalar)
-__device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
-  uint32_t v;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(x));
-  return v;
-}
 
 template <int GR, int SLOTB, int R, bool LG>
 __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
@@ -1842,6 +2267,11 @@ static void launch_compress(dim3 grid, size_t lds, hipStream_t s, const Compress
   hipLaunchKernelGGL((compress_kernel<D, F32, TG>), grid, dim3(4 * D), lds, s, a);
 }
 
+template <int D, bool F32>
+static void launch_compress2(dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
+  hipLaunchKernelGGL((compress2_kernel<D, F32>), grid, dim3(4 * D), lds, s, a);
+}
+
 template <int D>
 static void launch_compress_d(bool f32, bool tg, dim3 grid, size_t lds, hipStream_t s, const CompressArgs &a) {
   if (f32) tg ? launch_compress<D, true, true>(grid, lds, s, a) : launch_compress<D, true, false>(grid, lds, s, a);
@@ -1889,6 +2319,60 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
       max_s = std::max(max_s, hd.m * hd.d_eff);
     }
     if (calib_batch_stride == 0) break;  // every batch entry uses the same heads
+  }
+  // register-quantising kernel when every head has its plan and the tables fit
+  {
+    // (the kernel's per-lane load offsets within a 64-token tile are 32-bit)
+    bool use2 = d <= 128 && 64 * xs_token * esz < ((int64_t)1 << 32);
+    int mt = 0, mc = 0, ms = 0;
+    for (int bb = 0; bb < std::max(1, batch) && use2; ++bb) {
+      for (int h = 0; h < n_heads; ++h) {
+        const DevHead &hd = c->host_desc[first_head + bb * calib_batch_stride + h];
+        if (hd.n_p2 == 0) use2 = false;
+        mt = std::max(mt, hd.n_tree2);
+        mc = std::max(mc, hd.n_csig2);
+        ms = std::max(ms, hd.m * hd.d_eff);
+      }
+      if (calib_batch_stride == 0) break;
+    }
+    if (use2) {
+      Compress2Args b2{};
+      const bool f32 = dt == SQ_F32;
+      b2.lds_tree_off = 0;
+      b2.lds_csig_off = (mt + 3) & ~3;
+      b2.lds_s_off = b2.lds_csig_off + ((mc + 3) & ~3);
+      b2.lds_x_off = (b2.lds_s_off + ms + 255) & ~255;  // 1 KB aligned: direct-to-LDS blocks
+      b2.x_buf_floats = 16 * d * (f32 ? 4 : 2);        // 64 rows of d elements
+      b2.lds_rec_off = b2.lds_x_off + 2 * b2.x_buf_floats;
+      b2.rec_stride = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
+      b2.lds_res_off = b2.lds_rec_off + 2 * 64 * b2.rec_stride;
+      const size_t lds2 = (size_t)(b2.lds_res_off + 2 * 64 * C2_RS) * 4;
+      if (lds2 <= (size_t)device_lds_limit()) {
+        b2.heads = c->dev_heads;
+        b2.blob = (const uint8_t *)c->dev_blob;
+        b2.x = x;
+        b2.packed = packed;
+        b2.xs_b = xs_batch; b2.xs_h = xs_head; b2.xs_t = xs_token;
+        b2.ps_b = ps_batch; b2.ps_h = ps_head;
+        b2.n_tokens = n_tokens;
+        b2.first_head = first_head;
+        b2.cbs = calib_batch_stride;
+        b2.n_tiles = (int)((n_tokens + 63) / 64);
+        const int gz = calib_batch_stride ? batch : 1;
+        b2.items = calib_batch_stride ? b2.n_tiles : (int)std::min<int64_t>((int64_t)batch * b2.n_tiles, INT32_MAX);
+        const int64_t want = (int64_t)device_cu_count() * 2 * 2;
+        int gx = (int)std::max<int64_t>(1, std::min<int64_t>(b2.items, (want + (int64_t)n_heads * gz - 1) / ((int64_t)n_heads * gz)));
+        dim3 grid(gx, n_heads, gz);
+        if (grid.y > 65535 || grid.z > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many heads or batch entries");
+        hipStream_t s = (hipStream_t)stream;
+        switch (d) {
+          case 32: f32 ? launch_compress2<32, true>(grid, lds2, s, b2) : launch_compress2<32, false>(grid, lds2, s, b2); break;
+          case 64: f32 ? launch_compress2<64, true>(grid, lds2, s, b2) : launch_compress2<64, false>(grid, lds2, s, b2); break;
+          default: f32 ? launch_compress2<128, true>(grid, lds2, s, b2) : launch_compress2<128, false>(grid, lds2, s, b2); break;
+        }
+        return launched(fn);
+      }
+    }
   }
   CompressArgs a{};
   a.ys = d + 3;  // odd, and conflict-free for the MFMA-layout stores
