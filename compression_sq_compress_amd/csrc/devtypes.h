@@ -71,7 +71,7 @@ struct DevHead {
   int64_t off_csig;     // float [n_csig]  signal centroids * sigma_i per plan chunk
   // register-quantising compress plan (P2_* layout below); n_p2 = 0: not available
   int32_t n_p2, n_tree2, n_csig2, pad3;
-  int64_t off_p2;       // uint32 [d/16][P2_WAVE], then [n_words][P2_WORD]
+  int64_t off_p2;       // uint32 [d/16][P2_WAVE]
   int64_t off_tree2;    // float [n_tree2] per-coordinate padded trees (see P2_WAVE)
   int64_t off_csig2;    // float [n_csig2] signal centroids * sigma_i, padded per coordinate
   int64_t off_Rfrag2;   // bf16 [3][d/16][d/32][64][8] like off_Rfrag, rows permuted (see P2_WAVE)
@@ -80,19 +80,16 @@ struct DevHead {
 // Register-quantising compress plan.  Coordinates are taken in groups of 4
 // consecutive ones (group g = 4g .. 4g+3, depth = the group's largest width);
 // each wave gets 4 groups, one per MFMA accumulator register r, chosen to
-// balance the waves' total depth.  Row 4s + r of wave w's 16 MFMA rows holds
-// coordinate 4 g(w, r) + s, so lane l (s = l / 16) finds in register r the
-// value of that coordinate for tokens l % 16 + 16 j.  Wave header (P2_WAVE):
-// [r] depth of register r's group, [4 + 4r + s] tree base (floats) of its
-// coordinate, [20 + 4r + s] signal-centroid base or 0xFFFFFFFF (not a signal
-// coordinate), [36 + 4r + s] the coordinate, [52] record words the wave
-// packs, [53] index of its first word entry.  A tree holds the coordinate's
-// sorted thresholds padded with +inf to 2^depth - 1 entries in breadth-first
-// order (node k = 1 .. 2^depth - 1 at base + k - 1).  Word entry (P2_WORD):
-// [0] word index, [1] first coordinate with bits in it, [2] last one,
-// [3] 1 if the word holds QJL bits or gamma.
+// balance the waves' total depth and ordered by decreasing depth.  Row 4s + r
+// of wave w's 16 MFMA rows holds coordinate 4 g(w, r) + s, so lane l
+// (s = l / 16) finds in register r the value of that coordinate for tokens
+// l % 16 + 16 j.  Wave header (P2_WAVE): [r] depth of register r's group,
+// [4 + 4r + s] tree base (floats) of its coordinate, [20 + 4r + s]
+// signal-centroid base or 0xFFFFFFFF (not a signal coordinate), [36 + 4r + s]
+// the coordinate.  A tree holds the coordinate's sorted thresholds padded
+// with +inf to 2^depth - 1 entries in breadth-first order (node k = 1 ..
+// 2^depth - 1 at base + k - 1).
 constexpr int P2_WAVE = 64;
-constexpr int P2_WORD = 4;
 
 static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
 static_assert(sizeof(DevHead) == 208, "DevHead layout");

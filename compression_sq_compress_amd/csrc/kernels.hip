@@ -385,11 +385,10 @@ static HostPlan build_plan(const HeadCal &hc) {
   return P;
 }
 
-// Register-quantising compress plan (layout: P2_WAVE, P2_WORD).  Groups of 4
+// Register-quantising compress plan (layout: P2_WAVE).  Groups of 4
 // consecutive coordinates (depth = largest width) are dealt to the waves'
 // accumulator registers largest depth first, each to the least loaded wave
-// with a free register; record words are dealt the same way by the number of
-// codes they hold (the words with QJL bits and gamma count extra).
+// with a free register.
 struct HostPlan2 {
   std::vector<uint32_t> words;
   std::vector<float> tree, csig;
@@ -460,46 +459,7 @@ static HostPlan2 build_plan2(const HeadCal &hc) {
       }
     }
   }
-  // record words: the coordinates with bits in each, then dealt to the waves
-  struct Wd { int k, c0, c1, q, cost; };
-  std::vector<Wd> wds;
-  for (int k = 0; k < hc.W; ++k) {
-    Wd e{k, 1, 0, 0, 1};
-    for (int c = 0; c < d; ++c) {
-      const int b = hc.widths[c], lo = hc.bit_off[c];
-      if (b > 0 && lo < 32 * k + 32 && lo + b > 32 * k) {
-        if (e.c0 > e.c1) e.c0 = c;
-        e.c1 = c;
-      }
-    }
-    if (hc.m > 0 && ((hc.code_bits < 32 * k + 32 && hc.code_bits + hc.m > 32 * k) || k == hc.W - 1)) e.q = 1;
-    e.cost = (e.c1 >= e.c0 ? e.c1 - e.c0 + 1 : 0) + (e.q ? 8 + hc.m * hc.d_eff / 4 : 0) + 2;
-    wds.push_back(e);
-  }
-  std::vector<int> word_order(wds.size());
-  for (size_t k = 0; k < wds.size(); ++k) word_order[k] = (int)k;
-  std::stable_sort(word_order.begin(), word_order.end(), [&](int x, int y) { return wds[x].cost > wds[y].cost; });
-  std::vector<std::vector<int>> per_wave(NW);
-  std::vector<int> wload(NW, 0);
-  for (int k : word_order) {
-    int best = 0;
-    for (int w = 1; w < NW; ++w)
-      if (wload[w] < wload[best]) best = w;
-    per_wave[best].push_back(k);
-    wload[best] += wds[k].cost;
-  }
   P.words = hdr;
-  int nxt = 0;
-  for (int w = 0; w < NW; ++w) {
-    P.words[(size_t)w * P2_WAVE + 52] = (uint32_t)per_wave[w].size();
-    P.words[(size_t)w * P2_WAVE + 53] = (uint32_t)nxt;
-    for (int k : per_wave[w]) {
-      const Wd &e = wds[k];
-      const uint32_t E[P2_WORD] = {(uint32_t)e.k, (uint32_t)e.c0, (uint32_t)e.c1, (uint32_t)e.q};
-      P.words.insert(P.words.end(), E, E + P2_WORD);
-      ++nxt;
-    }
-  }
   P.ok = P.tree.size() < 65536 && hc.W < 256;  // 16-bit tree bases, 8-bit word indices in the kernel
   return P;
 }
@@ -1183,17 +1143,19 @@ __device__ __forceinline__ uint32_t to_vgpr(uint32_t x) {
 //             coordinate groups of the register plan (P2_WAVE), so lane l
 //             holds in accumulator register r the values of one coordinate
 //             for tokens l % 16 + 16 j.
-//   quantise: straight from the accumulators: per register, four independent
-//             descents (one per token block) of the lane's own padded
-//             threshold tree in LDS, all lanes of the register to the same
-//             depth; each code is OR-ed into its record word(s) in an LDS
-//             record tile [token][word], and signal residuals y - C[code]
-//             go to a small float tile.
-//   store:    after the barrier each wave takes whole record words (adding
-//             the QJL bits and gamma from the residuals where they belong),
-//             stores them as coalesced 256-byte rows and clears them.
-// The x tile, the record tile and the residual tile are double-buffered, so
-// the barrier of tile t also separates tile t+1's writes from tile t-1's reads.
+//   quantise: straight from the accumulators: 16 descents per wave of the
+//             lanes' own padded threshold trees in LDS, advancing level by
+//             level together; each code is OR-ed into its record word(s) in
+//             an LDS record tile [token][word], and signal residuals
+//             y - C[code] go to a small float tile.
+//   store:    after the barrier wave w stores record words w, w + d/16, ... as
+//             coalesced 256-byte rows (lane = token) and clears them, except
+//             the words with QJL bits or gamma: every wave first adds its
+//             share of the QJL rows (and one wave gamma) from the residual
+//             tile, and those words are stored after the next barrier.
+// x tiles are double-buffered and fetched two tiles ahead; the record tile
+// is triple-buffered, the residual tile double-buffered, so the barrier of
+// tile t also separates tile t+1's writes from the reads of tiles t-1, t-2.
 
 struct Compress2Args {
   const DevHead *heads;
@@ -1204,12 +1166,14 @@ struct Compress2Args {
   int64_t ps_b, ps_h;
   int64_t n_tokens;
   int first_head, cbs;
-  int n_tiles, items;
+  int n_tiles, tiles_per_wg;  // workgroup (x, head, batch entry) takes tiles [x * tiles_per_wg, ...)
   int lds_tree_off, lds_csig_off, lds_s_off, lds_x_off, lds_rec_off, lds_res_off;  // floats
   int x_buf_floats, rec_stride;  // record tile row stride (words, odd)
 };
 
-constexpr int C2_RS = 17;  // residual tile row stride (floats)
+constexpr int C2_RS = 17;   // residual tile row stride (floats)
+constexpr int C2_SP = 16;   // sketch row pitch in LDS (floats, zero padded past d_eff)
+constexpr int C2_WMAX = 6;  // record words stored per wave and tile (word k goes to wave k % waves)
 
 template <int D, bool F32>
 __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
@@ -1218,22 +1182,25 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.y, bz = blockIdx.z;
+  const int tb = blockIdx.x * a.tiles_per_wg, te = min(a.n_tiles, tb + a.tiles_per_wg);
+  if (tb >= te) return;  // (whole workgroup)
   const int ch = a.first_head + bz * a.cbs + h;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
+  const int rs = a.rec_stride;
   float *trees = smem + a.lds_tree_off;
   float *csig = smem + a.lds_csig_off;
-  float *Sl = smem + a.lds_s_off;  // [m][d_eff]
+  float *Sl = smem + a.lds_s_off;  // [m][C2_SP]
   {
     const float *g = (const float *)(a.blob + hd->off_tree2);
     for (int k = threadIdx.x; k < hd->n_tree2; k += NT) trees[k] = g[k];
     const float *gc = (const float *)(a.blob + hd->off_csig2);
     for (int k = threadIdx.x; k < hd->n_csig2; k += NT) csig[k] = gc[k];
     const float *gs = (const float *)(a.blob + hd->off_S);
-    for (int k = threadIdx.x; k < m * d_eff; k += NT) Sl[k] = gs[k];
+    for (int k = threadIdx.x; k < m * C2_SP; k += NT)
+      Sl[k] = (k % C2_SP) < d_eff ? gs[(k / C2_SP) * d_eff + k % C2_SP] : 0.0f;
   }
-  const SQ_CONST uint32_t *p2 = cptr<uint32_t>(a.blob + hd->off_p2);
-  const SQ_CONST uint32_t *H = p2 + w * P2_WAVE;
+  const SQ_CONST uint32_t *H = cptr<uint32_t>(a.blob + hd->off_p2) + w * P2_WAVE;
   const int s4 = lane >> 4;
   int dep[4];
   // per lane and register: tree base | (record word | bit shift << 8 |
@@ -1252,8 +1219,16 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
       tw[r] = Hv[4 + 4 * r + s4] | (wsh << 16);
     }
   }
-  const int nwords = (int)H[52];
-  const SQ_CONST uint32_t *wlist = p2 + NW * P2_WAVE + H[53] * P2_WORD;
+  // record words of this wave: w, w + NW, ...; qmask bit i: word w + NW i holds
+  // QJL bits or gamma (stored one tile late, once every wave has added its bits)
+  uint32_t qmask = 0u;
+#pragma unroll
+  for (int i = 0; i < C2_WMAX; ++i) {
+    const int k = w + NW * i;
+    if (m > 0 && k < W && ((32 * k < code_bits + m && 32 * k + 32 > code_bits) || k == W - 1)) qmask |= 1u << i;
+  }
+  // QJL rows of this wave (all 64 tokens): [jb, je)
+  const int jb = (w * m) / NW, je = ((w + 1) * m) / NW;
   const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag2);
   uint4 rf[3][KB];
 #pragma unroll
@@ -1261,61 +1236,60 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) rf[sp][kb] = Rf[((sp * MB + w) * KB + kb) * 64 + lane];
 
-  // x tiles are loaded straight into LDS (1 KB per load instruction), rows of
-  // RB bytes back to back; chunk c (16 bytes) of row t sits at slot
-  // c ^ swz(t) of the row, which keeps the MFMA operand reads conflict-free.
+  // x tiles go straight into LDS, 1 KB per load instruction.  A token row
+  // takes XR = RB + 16 bytes (CPR + 1 slots of 16 bytes, the last one a pad
+  // that is filled with a copy of chunk 0), which keeps the MFMA operand
+  // reads conflict-free and their addresses a lane constant plus immediates.
   constexpr int ESZ = F32 ? 4 : 2;
-  constexpr int RB = D * ESZ;                    // bytes per token row
-  constexpr int CPR = RB / 16;                   // chunks per row
-  constexpr int RPB = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256 bytes
-  constexpr int NB = CPR / NW;                   // 1 KB blocks per wave and tile
+  constexpr int RB = D * ESZ;   // bytes of x per token
+  constexpr int CPR = RB / 16;  // 16-byte chunks per token
+  constexpr int XR = RB + 16;   // LDS row pitch
+  constexpr int NBLK = CPR + 1; // 1 KB blocks per tile
   const uint32_t lds_x = (uint32_t)(uintptr_t)(smem + a.lds_x_off);
   const uint32_t row_bytes = (uint32_t)a.xs_t * ESZ;  // 64 rows fit 32 bits (host check)
-  auto dma_x = [&](int item, int buf) __attribute__((always_inline)) {
-    const int bb = a.cbs ? bz : item / a.n_tiles;
-    const int tl = a.cbs ? item : item % a.n_tiles;
+  const char *xbase = (const char *)a.x + ((int64_t)bz * a.xs_b + (int64_t)h * a.xs_h) * ESZ;
+  auto dma_x = [&](int tl, int buf) __attribute__((always_inline)) {
     const int64_t t0 = (int64_t)tl * 64;
-    const char *src = (const char *)a.x + ((int64_t)bb * a.xs_b + (int64_t)h * a.xs_h + t0 * a.xs_t) * ESZ;
+    const char *src = xbase + t0 * a.xs_t * ESZ;
     const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);  // rows past the end re-read the last token
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int q = w * NB + i;
-      const int byte = q * 1024 + lane * 16, row = byte / RB, slot = (byte % RB) / 16;
-      const int c = slot ^ ((row / RPB) & (CPR - 1));
-      lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)c * 16u,
-                lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
+    for (int i = 0; i < (NBLK + NW - 1) / NW; ++i) {
+      const int q = w + NW * i;
+      if (q < NBLK) {
+        const int sl = q * 64 + lane, row = sl / (CPR + 1), c = sl % (CPR + 1);
+        lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)(c == CPR ? 0 : c) * 16u,
+                  lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
+      }
     }
   };
-  for (int k = threadIdx.x; k < 2 * 64 * a.rec_stride; k += NT) smem[a.lds_rec_off + k] = 0.0f;
+  for (int k = threadIdx.x; k < 3 * 64 * rs; k += NT) smem[a.lds_rec_off + k] = 0.0f;
   // All set-up loads complete here, so that no wait inside the tile loop has
   // to cover them.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (blockIdx.x < a.items) dma_x(blockIdx.x, 0);
-  if (blockIdx.x + (int)gridDim.x < a.items) dma_x(blockIdx.x + gridDim.x, 1);
+  dma_x(tb, 0);
+  if (tb + 1 < te) dma_x(tb + 1, 1);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  int par = 0;
-  for (int item = blockIdx.x; item < a.items; item += gridDim.x, par ^= 1) {
-    const int b = a.cbs ? bz : item / a.n_tiles;
-    const int tile = a.cbs ? item : item % a.n_tiles;
-    const int64_t t0 = (int64_t)tile * 64;
+  const uint32_t xlane = (uint32_t)(lane & 15) * XR + (uint32_t)(lane >> 4) * (F32 ? 32u : 16u);
+  uint32_t *rec0 = (uint32_t *)(smem + a.lds_rec_off);
+  uint32_t *obase = a.packed + (int64_t)bz * a.ps_b + (int64_t)h * a.ps_h;
+  // record words of this wave: w + NW i for i < nmine
+  const int nmine = W > w ? (W - 1 - w) / NW + 1 : 0;
+  int par = 0, rb = 0;
+  for (int t = tb; t < te; ++t, par ^= 1, rb = rb == 2 ? 0 : rb + 1) {
     // ---- rotate: 16 rows x 64 tokens (4 blocks of 16)
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char *xt = (const char *)(smem + a.lds_x_off + par * a.x_buf_floats) + xlane;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint4 r0 = rf[0][kb], r1 = rf[1][kb], r2 = rf[2][kb];
-      const char *xt = (const char *)(smem + a.lds_x_off + par * a.x_buf_floats);
       if constexpr (!F32) {
-        const int kc = kb * 4 + (lane >> 4);  // chunk of elements kb*32 + 8*(lane/16) ..
-        uint4 xv[4];
+        uint4 xv[4];  // elements kb*32 + 8*(lane/16) .. of token 16j + lane%16
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * j + (lane & 15);
-          xv[j] = *(const uint4 *)(xt + row * RB + ((kc ^ ((row / RPB) & (CPR - 1))) << 4));
-        }
+        for (int j = 0; j < 4; ++j) xv[j] = *(const uint4 *)(xt + 16 * j * XR + kb * 64);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = mfma16(r0, xv[j], acc[j]);
 #pragma unroll
@@ -1323,13 +1297,11 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = mfma16(r2, xv[j], acc[j]);
       } else {
-        const int kc = kb * 8 + 2 * (lane >> 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int row = 16 * j + (lane & 15), sw = (row / RPB) & (CPR - 1);
           float v[8];
-          const float4 u0 = *(const float4 *)(xt + row * RB + ((kc ^ sw) << 4));
-          const float4 u1 = *(const float4 *)(xt + row * RB + (((kc + 1) ^ sw) << 4));
+          const float4 u0 = *(const float4 *)(xt + 16 * j * XR + kb * 128);
+          const float4 u1 = *(const float4 *)(xt + 16 * j * XR + kb * 128 + 16);
           v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
           v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
           uint4 x0, x1, x2;
@@ -1352,7 +1324,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     // decoded fields out of the loop would not fit the register budget.)
 #pragma unroll
     for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(tw[r]), "+v"(cc[r]));
-    uint32_t *rec = (uint32_t *)(smem + a.lds_rec_off) + par * 64 * a.rec_stride;
+    uint32_t *rec = rec0 + rb * 64 * rs;
     float *rtile = smem + a.lds_res_off + par * 64 * C2_RS;
     uint32_t k[4][4];
     const float *tr[4];
@@ -1384,18 +1356,20 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
       for (; l < dep[1]; ++l) level(std::integral_constant<int, 2>{});
       for (; l < dep[0]; ++l) level(std::integral_constant<int, 1>{});
     }
+    // codes into the record tile (k - 2^depth, shifted into place)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t kw = (tw[r] >> 16) & 0xFFu, sh = (tw[r] >> 24) & 31u;
-      uint32_t *rw = rec + (lane & 15) * a.rec_stride + kw;
+      const uint32_t top = 1u << dep[r];
+      uint32_t *rw = rec + (lane & 15) * rs + kw;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * a.rec_stride, (k[r][j] - (1u << dep[r])) << sh);
+      for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * rs, (k[r][j] << sh) - (top << sh));
       if (tw[r] & (1u << 29)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * a.rec_stride + 1, (k[r][j] - (1u << dep[r])) >> (32u - sh));
+        for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * rs + 1, (k[r][j] - top) >> (32u - sh));
       }
     }
-    if (m > 0) {
+    if (m > 0) {  // signal residuals y - C[code] for the QJL sketch and gamma
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t crd = cc[r] & 0xFFu, cb = cc[r] >> 8;
@@ -1410,40 +1384,88 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     // every wave's); then the tile after it goes into the buffer just read
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (item + 2 * (int)gridDim.x < a.items) dma_x(item + 2 * gridDim.x, par);
-    // ---- store whole record words, lane = token
+    if (t + 2 < te) dma_x(t + 2, par);
+    // ---- record words, lane = token: this tile's words without QJL bits,
+    // and the previous tile's words with QJL bits or gamma
     {
-      uint32_t *rrec = rec + lane * a.rec_stride;
-      const float *rrow = rtile + lane * C2_RS;
-      const bool valid = t0 + lane < a.n_tokens;
-      uint32_t *dst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
-      uint32_t zb = 0u, gb = 0u;
-      bool qdone = false;
-      for (int e = 0; e < nwords; ++e) {
-        const int k = (int)wlist[e * P2_WORD];
-        const bool q = wlist[e * P2_WORD + 3] != 0u;
-        uint32_t word = rrec[k];
-        rrec[k] = 0u;  // cleared for tile + 2 (its writers pass the next barrier first)
-        if (q) {
-          if (!qdone) {  // z_j = [(S r)_j >= 0], gamma = |r| as IEEE half (RNE)
-            float g2 = 0.0f;
-            for (int i = 0; i < d_eff; ++i) g2 = fmaf(rrow[i], rrow[i], g2);
-            for (int j = 0; j < m; ++j) {
-              float dot = 0.0f;
-              for (int i = 0; i < d_eff; ++i) dot = fmaf(Sl[j * d_eff + i], rrow[i], dot);
-              zb |= (dot >= 0.0f ? 1u : 0u) << j;
-            }
-            gb = half_bits_rne(sqrtf(g2)) << 16;
-            qdone = true;
-          }
-          const int lo = code_bits - 32 * k;  // position of z_0 in this word
-          if (lo >= 0 && lo < 32) word |= zb << lo;
-          else if (lo < 0 && lo > -32) word |= zb >> (-lo);
-          if (k == W - 1) word |= gb;
+      const bool has_prev = t != tb;
+      const int prb = rb == 0 ? 2 : rb - 1;
+      const uint32_t lrow = (uint32_t)lane * (uint32_t)rs;
+      uint32_t *ocur = obase + (int64_t)t * W * 64;
+      uint32_t *oprv = obase + (int64_t)(t - 1) * W * 64;
+      const bool valid = (int64_t)t * 64 + lane < a.n_tokens;
+      const bool pvalid = (int64_t)(t - 1) * 64 + lane < a.n_tokens;
+      // words w + NW i, two at a time: this tile's (no QJL bits) or the
+      // previous tile's; a slot past this wave's words reads and clears the
+      // pad column rs - 1
+      for (int i0 = 0; i0 < nmine; i0 += 2) {
+        uint32_t v[2], off[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = i0 + u;
+          const int kk = i < nmine ? w + NW * i : rs - 1;
+          const int bi = (qmask >> i & 1u) ? prb : rb;
+          off[u] = (uint32_t)(bi * 64 * rs + kk);
+          v[u] = rec0[lrow + off[u]];
         }
-        dst[(int64_t)k * 64] = valid ? word : 0u;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) rec0[lrow + off[u]] = 0u;  // for tile + 3 (two more barriers first)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = i0 + u;
+          const bool q = qmask >> i & 1u;
+          if (i < nmine && (!q || has_prev)) {
+            uint32_t *o = q ? oprv : ocur;
+            o[(uint32_t)(w + NW * i) * 64u + lane] = (q ? pvalid : valid) ? v[u] : 0u;
+          }
+        }
       }
     }
+    // ---- QJL rows [jb, je) of this tile: z_j = [(S r)_j >= 0]; the last
+    // wave adds gamma = |r| as IEEE half (RNE).  The words are stored after
+    // the next barrier.
+    if (m > 0) {
+      const float *rrow = rtile + lane * C2_RS;
+      float rv[C2_SP];
+#pragma unroll
+      for (int i = 0; i < C2_SP; ++i) rv[i] = i < d_eff ? rrow[i] : 0.0f;
+      uint32_t zb = 0u;
+      for (int j = jb; j < je; ++j) {
+        const float4 *srow = (const float4 *)(Sl + j * C2_SP);
+        float dot = 0.0f;
+#pragma unroll
+        for (int i4 = 0; i4 < C2_SP / 4; ++i4) {
+          const float4 s = srow[i4];
+          dot = fmaf(s.x, rv[4 * i4 + 0], dot);
+          dot = fmaf(s.y, rv[4 * i4 + 1], dot);
+          dot = fmaf(s.z, rv[4 * i4 + 2], dot);
+          dot = fmaf(s.w, rv[4 * i4 + 3], dot);
+        }
+        zb |= (dot >= 0.0f ? 1u : 0u) << (j - jb);
+      }
+      uint32_t *rrec = rec + lane * rs;
+      if (je > jb) {
+        const int p = code_bits + jb, pw = p >> 5, ps = p & 31;
+        atomicOr(rrec + pw, zb << ps);
+        if (ps + (je - jb) > 32) atomicOr(rrec + pw + 1, zb >> (32 - ps));
+      }
+      if (w == NW - 1) {
+        float g2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < C2_SP; ++i) g2 = fmaf(rv[i], rv[i], g2);
+        atomicOr(rrec + W - 1, half_bits_rne(sqrtf(g2)) << 16);
+      }
+    }
+  }
+  // ---- the last tile's words with QJL bits or gamma
+  if (m > 0) {
+    __syncthreads();
+    uint32_t *rlast = rec0 + ((te - 1 - tb) % 3) * 64 * rs + lane * rs;
+    uint32_t *dst = obase + (int64_t)(te - 1) * W * 64 + lane;
+    const bool valid = (int64_t)(te - 1) * 64 + lane < a.n_tokens;
+#pragma unroll
+    for (int i = 0; i < C2_WMAX; ++i)
+      if ((qmask >> i & 1u) && i < nmine) dst[(int64_t)(w + NW * i) * 64] = valid ? rlast[w + NW * i] : 0u;
   }
 }
 
@@ -2322,16 +2344,18 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   }
   // register-quantising kernel when every head has its plan and the tables fit
   {
-    // (the kernel's per-lane load offsets within a 64-token tile are 32-bit)
-    bool use2 = d <= 128 && 64 * xs_token * esz < ((int64_t)1 << 32);
-    int mt = 0, mc = 0, ms = 0;
+    // (the kernel's per-lane load offsets within a 64-token tile are 32-bit;
+    // each of its d/16 waves stores at most C2_WMAX record words per tile)
+    bool use2 = d <= 128 && 64 * xs_token * esz < ((int64_t)1 << 32) && c->W_max <= C2_WMAX * (d / 16) &&
+                n_heads <= 65535 && batch <= 65535;
+    int mt = 0, mc = 0, mq = 0;
     for (int bb = 0; bb < std::max(1, batch) && use2; ++bb) {
       for (int h = 0; h < n_heads; ++h) {
         const DevHead &hd = c->host_desc[first_head + bb * calib_batch_stride + h];
         if (hd.n_p2 == 0) use2 = false;
         mt = std::max(mt, hd.n_tree2);
         mc = std::max(mc, hd.n_csig2);
-        ms = std::max(ms, hd.m * hd.d_eff);
+        mq = std::max(mq, hd.m);
       }
       if (calib_batch_stride == 0) break;
     }
@@ -2341,11 +2365,11 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
       b2.lds_tree_off = 0;
       b2.lds_csig_off = (mt + 3) & ~3;
       b2.lds_s_off = b2.lds_csig_off + ((mc + 3) & ~3);
-      b2.lds_x_off = (b2.lds_s_off + ms + 255) & ~255;  // 1 KB aligned: direct-to-LDS blocks
-      b2.x_buf_floats = 16 * d * (f32 ? 4 : 2);        // 64 rows of d elements
+      b2.lds_x_off = (b2.lds_s_off + mq * C2_SP + 255) & ~255;  // 1 KB aligned: direct-to-LDS blocks
+      b2.x_buf_floats = 16 * (d * (f32 ? 4 : 2) + 16);          // 64 rows of d elements + 16 bytes
       b2.lds_rec_off = b2.lds_x_off + 2 * b2.x_buf_floats;
-      b2.rec_stride = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
-      b2.lds_res_off = b2.lds_rec_off + 2 * 64 * b2.rec_stride;
+      b2.rec_stride = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max + 2;  // odd, with a pad column
+      b2.lds_res_off = b2.lds_rec_off + 3 * 64 * b2.rec_stride;
       const size_t lds2 = (size_t)(b2.lds_res_off + 2 * 64 * C2_RS) * 4;
       if (lds2 <= (size_t)device_lds_limit()) {
         b2.heads = c->dev_heads;
@@ -2358,12 +2382,13 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
         b2.first_head = first_head;
         b2.cbs = calib_batch_stride;
         b2.n_tiles = (int)((n_tokens + 63) / 64);
-        const int gz = calib_batch_stride ? batch : 1;
-        b2.items = calib_batch_stride ? b2.n_tiles : (int)std::min<int64_t>((int64_t)batch * b2.n_tiles, INT32_MAX);
-        const int64_t want = (int64_t)device_cu_count() * 2 * 2;
-        int gx = (int)std::max<int64_t>(1, std::min<int64_t>(b2.items, (want + (int64_t)n_heads * gz - 1) / ((int64_t)n_heads * gz)));
-        dim3 grid(gx, n_heads, gz);
-        if (grid.y > 65535 || grid.z > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many heads or batch entries");
+        // about 4 workgroups per CU, each a run of consecutive tiles of one
+        // (batch entry, head)
+        const int64_t want = (int64_t)device_cu_count() * 4;
+        const int64_t bh = (int64_t)n_heads * batch;
+        const int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(b2.n_tiles, (want + bh - 1) / bh));
+        b2.tiles_per_wg = (int)((b2.n_tiles + chunks - 1) / chunks);
+        dim3 grid((unsigned)((b2.n_tiles + b2.tiles_per_wg - 1) / b2.tiles_per_wg), n_heads, batch);
         hipStream_t s = (hipStream_t)stream;
         switch (d) {
           case 32: f32 ? launch_compress2<32, true>(grid, lds2, s, b2) : launch_compress2<32, false>(grid, lds2, s, b2); break;
