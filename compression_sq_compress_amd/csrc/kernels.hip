@@ -1168,14 +1168,16 @@ struct Compress2Args {
   int first_head, cbs;
   int n_tiles, tiles_per_wg;  // workgroup (x, head, batch entry) takes tiles [x * tiles_per_wg, ...)
   int lds_tree_off, lds_csig_off, lds_s_off, lds_x_off, lds_rec_off, lds_res_off;  // floats
-  int x_buf_floats, rec_stride;  // record tile row stride (words, odd)
+  int x_buf_floats;
 };
 
-constexpr int C2_RS = 17;   // residual tile row stride (floats)
+constexpr int C2_RS = 20;   // residual tile row stride (floats; 16-byte rows, conflict-free)
 constexpr int C2_SP = 16;   // sketch row pitch in LDS (floats, zero padded past d_eff)
 constexpr int C2_WMAX = 6;  // record words stored per wave and tile (word k goes to wave k % waves)
 
-template <int D, bool F32>
+// RS: record tile row stride in words (odd, above the record length: the
+// last column is a pad), a constant so that token-block offsets are immediates
+template <int D, bool F32, int RS>
 __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   extern __shared__ float smem[];
   constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
@@ -1187,7 +1189,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   const int ch = a.first_head + bz * a.cbs + h;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
-  const int rs = a.rec_stride;
+  constexpr int rs = RS;
   float *trees = smem + a.lds_tree_off;
   float *csig = smem + a.lds_csig_off;
   float *Sl = smem + a.lds_s_off;  // [m][C2_SP]
@@ -1263,6 +1265,8 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     }
   };
   for (int k = threadIdx.x; k < 3 * 64 * rs; k += NT) smem[a.lds_rec_off + k] = 0.0f;
+  // residual columns past d_eff stay zero (the QJL step reads whole rows)
+  for (int k = threadIdx.x; k < 2 * 64 * C2_RS; k += NT) smem[a.lds_res_off + k] = 0.0f;
   // All set-up loads complete here, so that no wait inside the tile loop has
   // to cover them.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -1361,9 +1365,10 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     for (int r = 0; r < 4; ++r) {
       const uint32_t kw = (tw[r] >> 16) & 0xFFu, sh = (tw[r] >> 24) & 31u;
       const uint32_t top = 1u << dep[r];
+      const uint32_t ntop = 0u - (top << sh);  // (k << sh) + ntop = (k - 2^depth) << sh
       uint32_t *rw = rec + (lane & 15) * rs + kw;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * rs, (k[r][j] << sh) - (top << sh));
+      for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * rs, (k[r][j] << sh) + ntop);
       if (tw[r] & (1u << 29)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * rs + 1, (k[r][j] - top) >> (32u - sh));
@@ -1425,10 +1430,13 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     // wave adds gamma = |r| as IEEE half (RNE).  The words are stored after
     // the next barrier.
     if (m > 0) {
-      const float *rrow = rtile + lane * C2_RS;
+      const float4 *rrow = (const float4 *)(rtile + lane * C2_RS);
       float rv[C2_SP];
 #pragma unroll
-      for (int i = 0; i < C2_SP; ++i) rv[i] = i < d_eff ? rrow[i] : 0.0f;
+      for (int i4 = 0; i4 < C2_SP / 4; ++i4) {
+        const float4 u = rrow[i4];
+        rv[4 * i4] = u.x; rv[4 * i4 + 1] = u.y; rv[4 * i4 + 2] = u.z; rv[4 * i4 + 3] = u.w;
+      }
       uint32_t zb = 0u;
       for (int j = jb; j < je; ++j) {
         const float4 *srow = (const float4 *)(Sl + j * C2_SP);
@@ -2290,8 +2298,14 @@ static void launch_compress(dim3 grid, size_t lds, hipStream_t s, const Compress
 }
 
 template <int D, bool F32>
-static void launch_compress2(dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
-  hipLaunchKernelGGL((compress2_kernel<D, F32>), grid, dim3(4 * D), lds, s, a);
+static void launch_compress2(int rsc, dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
+  // record strides this head size can need (at most C2_WMAX words per wave)
+  if (rsc == 17) {
+    hipLaunchKernelGGL((compress2_kernel<D, F32, 17>), grid, dim3(4 * D), lds, s, a);
+  } else if constexpr (D >= 64) {
+    if (rsc == 33) hipLaunchKernelGGL((compress2_kernel<D, F32, 33>), grid, dim3(4 * D), lds, s, a);
+    else if constexpr (D == 128) hipLaunchKernelGGL((compress2_kernel<D, F32, 49>), grid, dim3(4 * D), lds, s, a);
+  }
 }
 
 template <int D>
@@ -2368,8 +2382,9 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
       b2.lds_x_off = (b2.lds_s_off + mq * C2_SP + 255) & ~255;  // 1 KB aligned: direct-to-LDS blocks
       b2.x_buf_floats = 16 * (d * (f32 ? 4 : 2) + 16);          // 64 rows of d elements + 16 bytes
       b2.lds_rec_off = b2.lds_x_off + 2 * b2.x_buf_floats;
-      b2.rec_stride = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max + 2;  // odd, with a pad column
-      b2.lds_res_off = b2.lds_rec_off + 3 * 64 * b2.rec_stride;
+      // record tile stride: odd, above W_max (pad column)
+      const int rsc = c->W_max < 17 ? 17 : c->W_max < 33 ? 33 : 49;
+      b2.lds_res_off = (b2.lds_rec_off + 3 * 64 * rsc + 3) & ~3;
       const size_t lds2 = (size_t)(b2.lds_res_off + 2 * 64 * C2_RS) * 4;
       if (lds2 <= (size_t)device_lds_limit()) {
         b2.heads = c->dev_heads;
@@ -2391,9 +2406,9 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
         dim3 grid((unsigned)((b2.n_tiles + b2.tiles_per_wg - 1) / b2.tiles_per_wg), n_heads, batch);
         hipStream_t s = (hipStream_t)stream;
         switch (d) {
-          case 32: f32 ? launch_compress2<32, true>(grid, lds2, s, b2) : launch_compress2<32, false>(grid, lds2, s, b2); break;
-          case 64: f32 ? launch_compress2<64, true>(grid, lds2, s, b2) : launch_compress2<64, false>(grid, lds2, s, b2); break;
-          default: f32 ? launch_compress2<128, true>(grid, lds2, s, b2) : launch_compress2<128, false>(grid, lds2, s, b2); break;
+          case 32: f32 ? launch_compress2<32, true>(rsc, grid, lds2, s, b2) : launch_compress2<32, false>(rsc, grid, lds2, s, b2); break;
+          case 64: f32 ? launch_compress2<64, true>(rsc, grid, lds2, s, b2) : launch_compress2<64, false>(rsc, grid, lds2, s, b2); break;
+          default: f32 ? launch_compress2<128, true>(rsc, grid, lds2, s, b2) : launch_compress2<128, false>(rsc, grid, lds2, s, b2); break;
         }
         return launched(fn);
       }
