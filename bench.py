@@ -237,7 +237,7 @@ def main():
         "score_packedK_GBps": gbps(n_vec * 4 * Wk, ms_sc),
         "attend_GBps": gbps(bytes_at, ms_at),
         "attend_hbm_frac": gbps(bytes_at, ms_at) / HBM_PEAK_GBPS,
-        "roofline": {"bound": "hbm", "kernel": "compress_kernel<128,bf16> (per launch, K and V averaged)",
+        "roofline": {"bound": "hbm", "kernel": "compress2_kernel<128,bf16> (register quantiser; per launch, K and V averaged)",
                      "achieved": comp_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": comp_gbps / HBM_PEAK_GBPS, "traffic": traffic,
                      "alg_bytes_per_launch": comp_launch_bytes, "launch_ms": comp_launch_ms},
