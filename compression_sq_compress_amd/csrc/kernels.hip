@@ -784,7 +784,7 @@ __device__ __forceinline__ void quant_chunk(const ChunkArgs &cd, float *yrow, co
 #pragma unroll
     for (int c = 0; c < NS; ++c)
       if (c < nsig) {
-        float r = y[c];
+        float r = ys[c];  // (a NaN y keeps a NaN residual: no QJL bit, NaN gamma)
         if constexpr (B > 0) r -= cs[c * L + code[c]];
         if constexpr (QJ) {  // signal coordinate start + c < 8: column of the padded sketch
           qa.g2 = fmaf(r, r, qa.g2);
@@ -1320,7 +1320,10 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
       }
     }
     // ---- quantise from the accumulators: code = #{thresholds < y} by a
-    // descent of the padded tree; a NaN y counts as -inf (code 0).  The 16
+    // descent of the padded tree.  A NaN y codes as 0: the MFMA returns the
+    // positive quiet NaN for any NaN input, and (threshold - NaN) keeps its
+    // clear sign bit, so every level goes left (checked for NaN inputs of
+    // either sign).  The 16
     // descents of a wave (4 registers x 4 token blocks) advance level by
     // level together, so their LDS reads overlap; the plan orders a wave's
     // registers by decreasing depth, so the registers still descending at a
@@ -1335,12 +1338,21 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       tr[r] = trees + (tw[r] & 0xFFFFu) - 1;  // node k at tr[k]
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j][r] = fmaxf(acc[j][r], -INFINITY);
-        k[r][j] = 1u;
-      }
     }
+    // level 1: the root is the same node for the lane's four token blocks
+    auto first = [&](auto nr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < decltype(nr)::value) {
+          const float t = tr[r][1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) k[r][j] = __builtin_amdgcn_alignbit(1u, __float_as_uint(t - acc[j][r]), 31);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) k[r][j] = 1u;  // depth 0: code 0
+        }
+      }
+    };
     auto level = [&](auto nr) __attribute__((always_inline)) {
       float t[decltype(nr)::value][4];
 #pragma unroll
@@ -1354,7 +1366,12 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
           k[r][j] = __builtin_amdgcn_alignbit(k[r][j], __float_as_uint(t[r][j] - acc[j][r]), 31);
     };
     {
-      int l = 0;
+      if (dep[3] > 0) first(std::integral_constant<int, 4>{});
+      else if (dep[2] > 0) first(std::integral_constant<int, 3>{});
+      else if (dep[1] > 0) first(std::integral_constant<int, 2>{});
+      else if (dep[0] > 0) first(std::integral_constant<int, 1>{});
+      else first(std::integral_constant<int, 0>{});
+      int l = 1;
       for (; l < dep[3]; ++l) level(std::integral_constant<int, 4>{});
       for (; l < dep[2]; ++l) level(std::integral_constant<int, 3>{});
       for (; l < dep[1]; ++l) level(std::integral_constant<int, 2>{});
@@ -1380,7 +1397,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
         const uint32_t crd = cc[r] & 0xFFu, cb = cc[r] >> 8;
         if (cb != 0xFFFFFFu) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j)  // (a NaN y leaves a NaN residual: no QJL bit, NaN gamma)
             rtile[((lane & 15) + 16 * j) * C2_RS + crd] = acc[j][r] - csig[cb + k[r][j] - (1u << dep[r])];
         }
       }

@@ -221,6 +221,48 @@ def test_fp32_inputs_every_head_dim(torch_dev, sq, d):
                              H.score_floor(ors[k], qg, xt)[:, same], f"fp32 d={d} head {k}")
 
 
+@pytest.mark.parametrize("name,dt", [("llama8b", "bf16"), ("llama8b", "f32"), ("gemma9b", "bf16")])
+def test_nan_inputs(torch_dev, sq, name, dt):
+    """NaN entries of either sign in K and V (reading R7: a NaN coordinate
+    codes as 0).  One NaN entry makes the whole rotated token NaN on both
+    sides, so those tokens must carry all-zero codes and QJL bits and a NaN
+    gamma; the other tokens follow the usual acceptance rules."""
+    torch = torch_dev
+    cfg = wl.CONFIGS[name]
+    heads = [(0, 0)]
+    T = 100
+    _case(f"NaN inputs {dt} {name} T={T}")
+    nan_tok = [3, 70, 99]
+    for which in ("k", "v"):
+        cal, ors = H.calibrate_both(sq, cfg, heads, which, 3.0)
+        cal.upload()
+        x = H.data_block(cfg, heads, which, T)[0].astype(np.float32)
+        if dt == "bf16":
+            xd = _dev(torch, x[None, None], torch.bfloat16)
+            bits = xd.view(torch.int16)
+            bits[0, 0, 3, 7] = 0x7FC0           # +NaN
+            bits[0, 0, 70, 0] = -64             # 0xFFC0: -NaN
+            bits[0, 0, 99, :] = -127            # 0xFF81: -NaN, signalling payload
+        else:
+            xd = _dev(torch, x[None, None])
+            bits = xd.view(torch.int32)
+            bits[0, 0, 3, 7] = 0x7FC00000
+            bits[0, 0, 70, 0] = -4194304        # 0xFFC00000
+            bits[0, 0, 99, :] = -8388607        # 0xFF800001
+        x[nan_tok] = np.nan
+        kp = torch.full((1, 1, cal.packed_head_words(T)), -1, dtype=torch.int32, device="cuda")
+        sq.sq_compress(cal, xd, kp)
+        torch.cuda.synchronize()
+        got = kp.cpu().numpy().view(np.uint32)[0, 0]
+        oc = ors[0]
+        H.compare_compress(oc, got, x, T)
+        gc, gz, gg = oracle.unpack(oc.widths, oc.m, got, T)
+        assert np.all(gc[nan_tok] == 0), f"{which}: NaN tokens must code as 0"
+        if oc.m > 0:
+            assert np.all(gz[nan_tok] == 0), "NaN tokens must have all QJL bits clear"
+            assert np.all(np.isnan(gg[nan_tok].astype(np.float32))), "NaN tokens must have a NaN gamma"
+
+
 def test_degenerate_zero_calibration(torch_dev, sq):
     """All-zero calibration data: every threshold and centroid is 0 and the
     basis is arbitrary, so only what is unique is compared: zero vectors give
