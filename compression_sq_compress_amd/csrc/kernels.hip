@@ -429,18 +429,23 @@ static HostPlan2 build_plan2(const HeadCal &hc) {
     for (int r = 0; r < 4; ++r) {
       const int g = slot_g[(size_t)w * 4 + r], D = depth[g], L = 1 << D;
       H[r] = (uint32_t)D;
+      // the register's four trees start at 16 s (mod 64) words, so that the
+      // nodes of one level (up to 16 of them per tree) that the four lane
+      // groups read together fall in disjoint LDS banks
+      const size_t stride = L - 1 <= 16 ? 16 : 16 + 64 * (((size_t)L - 1 - 16 + 63) / 64);
+      const size_t rbase = (P.tree.size() + 63) & ~(size_t)63;
+      if (D > 0) P.tree.resize(rbase + 4 * stride, inf);
       for (int s = 0; s < 4; ++s) {
         const int c = 4 * g + s, b = hc.widths[c];
         P.row_coord[w * 16 + 4 * s + r] = c;
         H[36 + 4 * r + s] = (uint32_t)c;
-        const size_t tb = P.tree.size();
+        const size_t tb = D > 0 ? rbase + s * stride : 0;
         H[4 + 4 * r + s] = (uint32_t)tb;
         if (D > 0) {
           // sorted thresholds padded with +inf to L - 1; node n (depth k,
           // position p = n - 2^k) holds padded entry (2p + 1) * 2^(D - 1 - k) - 1
           std::vector<float> padded(L - 1, inf);
           for (int k = 0; k + 1 < (1 << b); ++k) padded[k] = canon(hc.thr[hc.thr_base[c] + k]);
-          P.tree.resize(tb + L - 1, inf);
           for (int n = 1; n < L; ++n) {
             int k = 0;
             while ((2 << k) <= n) ++k;
@@ -1238,15 +1243,15 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) rf[sp][kb] = Rf[((sp * MB + w) * KB + kb) * 64 + lane];
 
-  // x tiles go straight into LDS, 1 KB per load instruction.  A token row
-  // takes XR = RB + 16 bytes (CPR + 1 slots of 16 bytes, the last one a pad
-  // that is filled with a copy of chunk 0), which keeps the MFMA operand
-  // reads conflict-free and their addresses a lane constant plus immediates.
+  // x tiles go straight into LDS, 1 KB per load instruction, rows of RB
+  // bytes back to back; chunk c (16 bytes) of row t sits at slot c ^ swz(t)
+  // of the row, which keeps the MFMA operand reads free of bank conflicts
+  // (measured: a 16-byte row pad instead doubles their LDS time).
   constexpr int ESZ = F32 ? 4 : 2;
-  constexpr int RB = D * ESZ;   // bytes of x per token
-  constexpr int CPR = RB / 16;  // 16-byte chunks per token
-  constexpr int XR = RB + 16;   // LDS row pitch
-  constexpr int NBLK = CPR + 1; // 1 KB blocks per tile
+  constexpr int RB = D * ESZ;                    // bytes of x per token
+  constexpr int CPR = RB / 16;                   // 16-byte chunks per token
+  constexpr int RPB = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256 bytes
+  constexpr int NB = CPR / NW;                   // 1 KB blocks per wave and tile
   const uint32_t lds_x = (uint32_t)(uintptr_t)(smem + a.lds_x_off);
   const uint32_t row_bytes = (uint32_t)a.xs_t * ESZ;  // 64 rows fit 32 bits (host check)
   const char *xbase = (const char *)a.x + ((int64_t)bz * a.xs_b + (int64_t)h * a.xs_h) * ESZ;
@@ -1255,13 +1260,12 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     const char *src = xbase + t0 * a.xs_t * ESZ;
     const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);  // rows past the end re-read the last token
 #pragma unroll
-    for (int i = 0; i < (NBLK + NW - 1) / NW; ++i) {
-      const int q = w + NW * i;
-      if (q < NBLK) {
-        const int sl = q * 64 + lane, row = sl / (CPR + 1), c = sl % (CPR + 1);
-        lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)(c == CPR ? 0 : c) * 16u,
-                  lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
-      }
+    for (int i = 0; i < NB; ++i) {
+      const int q = w * NB + i;
+      const int byte = q * 1024 + lane * 16, row = byte / RB, slot = (byte % RB) / 16;
+      const int c = slot ^ ((row / RPB) & (CPR - 1));
+      lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)c * 16u,
+                lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
     }
   };
   for (int k = threadIdx.x; k < 3 * 64 * rs; k += NT) smem[a.lds_rec_off + k] = 0.0f;
@@ -1275,7 +1279,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  const uint32_t xlane = (uint32_t)(lane & 15) * XR + (uint32_t)(lane >> 4) * (F32 ? 32u : 16u);
+  // the lane's operand rows are 16 j + lane % 16: their swizzle is a lane constant for bf16
+  const int xsw = ((lane & 15) / RPB) & (CPR - 1);
+  const uint32_t xrow = (uint32_t)(lane & 15) * RB;
   uint32_t *rec0 = (uint32_t *)(smem + a.lds_rec_off);
   uint32_t *obase = a.packed + (int64_t)bz * a.ps_b + (int64_t)h * a.ps_h;
   // record words of this wave: w + NW i for i < nmine
@@ -1286,14 +1292,15 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const char *xt = (const char *)(smem + a.lds_x_off + par * a.x_buf_floats) + xlane;
+    const char *xt = (const char *)(smem + a.lds_x_off + par * a.x_buf_floats) + xrow;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint4 r0 = rf[0][kb], r1 = rf[1][kb], r2 = rf[2][kb];
       if constexpr (!F32) {
-        uint4 xv[4];  // elements kb*32 + 8*(lane/16) .. of token 16j + lane%16
+        uint4 xv[4];  // elements kb*32 + 8*(lane/16) .. (chunk kc) of token 16j + lane%16
+        const char *xc = xt + (((kb * 4 + (lane >> 4)) ^ xsw) << 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xv[j] = *(const uint4 *)(xt + 16 * j * XR + kb * 64);
+        for (int j = 0; j < 4; ++j) xv[j] = *(const uint4 *)(xc + 16 * j * RB);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = mfma16(r0, xv[j], acc[j]);
 #pragma unroll
@@ -1304,8 +1311,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float v[8];
-          const float4 u0 = *(const float4 *)(xt + 16 * j * XR + kb * 128);
-          const float4 u1 = *(const float4 *)(xt + 16 * j * XR + kb * 128 + 16);
+          const int kc = kb * 8 + 2 * (lane >> 4), sw = ((16 * j + (lane & 15)) / RPB) & (CPR - 1);
+          const float4 u0 = *(const float4 *)(xt + 16 * j * RB + ((kc ^ sw) << 4));
+          const float4 u1 = *(const float4 *)(xt + 16 * j * RB + (((kc + 1) ^ sw) << 4));
           v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
           v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
           uint4 x0, x1, x2;
@@ -1478,7 +1486,8 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
         float g2 = 0.0f;
 #pragma unroll
         for (int i = 0; i < C2_SP; ++i) g2 = fmaf(rv[i], rv[i], g2);
-        atomicOr(rrec + W - 1, half_bits_rne(sqrtf(g2)) << 16);
+        // v_sqrt_f32 (within 1 ulp of fp32) before the fp16 rounding
+        atomicOr(rrec + W - 1, half_bits_rne(__builtin_amdgcn_sqrtf(g2)) << 16);
       }
     }
   }
@@ -1889,13 +1898,13 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
 // ------------------------------------------------------------------ attend
 //
 // Split-T softmax-weighted value sum in the rotated value space.  Kernel 1:
-// one wave per (batch, KV head, chunk of ATT_CHUNK tokens, block of 64
-// eigen-coordinates), lane = coordinate.  Per 64-token tile the record words
-// its coordinates touch are staged straight from HBM into LDS (word-major,
-// row stride ATT_RS, so lanes reading different words of one token hit
-// different banks); the query group's scores give an online softmax (running
-// max, rescaled sums) whose weights p are kept in LDS as bf16 hi/lo pairs.
-// Each lane decodes its coordinate for 4 tokens at a time into C_v[code] as
+// one wave per (batch, KV head, chunk of ATT_CHUNK tokens), lane = coordinate
+// within each block of 64 eigen-coordinates.  Per 64-token tile the record
+// words are staged straight from HBM into LDS (word-major, row stride
+// ATT_RS, so lanes reading different words of one token hit different
+// banks); the query group's scores give an online softmax (running max,
+// rescaled sums) whose weights p are kept in LDS as bf16 hi/lo pairs, once
+// for all blocks.  Each lane decodes its coordinate for 4 tokens at a time into C_v[code] as
 // bf16 hi/lo pairs and v_mfma_f32_4x4x4_16b_bf16 forms sum_t p_t C_v[code_t]:
 // in block b, lane 4b+n supplies the 4 tokens of coordinate 4b+n (B operand),
 // lane 4b+m the weights of query head m (A operand), and the accumulator of
@@ -1921,10 +1930,11 @@ struct AttendArgs {
   float scale;
   int first_head, cbs;
   int n_q_heads, n_kv_heads;
-  int n_chunks, n_parts;
-  int lds_wave_off;            // floats: per-wave areas (the centroid table starts at 0)
+  int n_chunks;
+  int lut_block;               // floats: stride of the 64-coordinate blocks' centroid tables
+  int lds_wave_off;            // floats: per-wave areas (the centroid tables start at 0)
   int wave_floats;             // one wave's area: two staging buffers, then the weights
-  int buf_floats;              // one staging buffer: [nwd][ATT_RS] words + [G][64] scores
+  int buf_floats;              // one staging buffer: [W + 1][ATT_RS] words + [G][64] scores
 };
 
 // Maximum over the 64 lanes: rotations within each row of 16 (DPP), then the
@@ -1943,65 +1953,72 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Centroid table placement of the attend kernel: LM_COL = one column per lane
 // (entry code * 64 + lane: every lane reads its own bank; widths <= 6),
-// LM_PACK = the block's tables back to back with one pad entry each, LM_GLB =
+// LM_PACK = a block's tables back to back with one pad entry each, LM_GLB =
 // read from the table blob (tables too large for LDS).
 enum { LM_COL = 0, LM_PACK = 1, LM_GLB = 2 };
 
-template <int G, int LM>
+// NP = 64-coordinate blocks per head (head_dim / 64, at least 1): one wave
+// serves every block of its chunk, so the chunk's scores are read and its
+// softmax computed once.
+template <int G, int LM, int NP>
 __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
   extern __shared__ float smem[];
   constexpr int GR = (G + 3) / 4, GP = 4 * GR;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // a workgroup = 4 consecutive chunks of one (batch, KV head, coordinate block)
-  const int cgrp = blockIdx.x / a.n_parts, part = blockIdx.x % a.n_parts;
-  const int chunk = cgrp * 4 + wv;
+  // a workgroup = 4 consecutive chunks of one (batch, KV head)
+  const int chunk = blockIdx.x * 4 + wv;
   const int hkv = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + hkv;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d, W = hd->W;
   const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
-  const int c0 = part * 64, c1 = min(d, c0 + 64);
-  const int ci = c0 + lane;
-  // the block's record words [wlo, whi] and centroid pairs [lut0, lut1)
-  const int wlo = coords[c0].bit_off >> 5;
-  const int whi = min(W - 1, (coords[c1 - 1].bit_off + coords[c1 - 1].width) >> 5);
-  const int nwd = whi - wlo + 2;  // one spare row: the word after a field never goes past it
-  const int lut0 = coords[c0].cent_base;
   uint32_t *lut = (uint32_t *)smem;
   float *stage = smem + a.lds_wave_off + wv * a.wave_floats;  // two buffers: words, then scores
   uint32_t *ph = (uint32_t *)(stage + 2 * a.buf_floats);      // [GP][ATT_PS] bf16 hi of p, twice
   uint32_t *pl = ph + GP * ATT_PS;                             // [GP][ATT_PS] bf16 lo of p, twice
-  const uint32_t *glut = (const uint32_t *)(a.blob + hd->off_lutp) + lut0;
-  // this lane's field
-  int width = 0, bo = 0, cb = 0;
-  if (ci < c1) {
-    width = coords[ci].width;
-    bo = coords[ci].bit_off;
-    cb = coords[ci].cent_base - lut0;
-  }
-  const int n = width ? (1 << width) : 0;
-  if constexpr (LM == LM_COL) {
-    // column lane: entry f at f * 64 + lane; a zero-width lane reads 0 at f = 0
-    for (int k = wv; k < max(n, 1); k += 4) lut[k * 64 + lane] = n ? glut[cb + k] : 0u;
-    cb = lane;
-  } else if constexpr (LM == LM_PACK) {
-    // coordinate c0 + j's table at offset cb + j: lanes gathering the same code
-    // from tables of equal size fall in different banks; the slot after each
-    // table is 0, which a zero-width coordinate (field 0) reads
-    if (ci < c1) {  // lanes past the last coordinate (head_dim 32) write nothing
-      for (int k = wv; k < n; k += 4) lut[cb + lane + k] = glut[cb + k];
-      if (wv == 0) lut[cb + lane + n] = 0u;
+  const uint32_t *glut = (const uint32_t *)(a.blob + hd->off_lutp);
+  // this lane's field in each block p (coordinate 64 p + lane)
+  int cb[NP], cwl[NP], cs[NP];
+  uint32_t fmask[NP];
+  bool straddle[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c0 = p * 64, ci = c0 + lane;
+    const int lut0 = c0 < d ? coords[c0].cent_base : 0;
+    int width = 0, bo = 0, cbv = 0;
+    if (ci < d) {
+      width = coords[ci].width;
+      bo = coords[ci].bit_off;
+      cbv = coords[ci].cent_base - lut0;
     }
-    cb += lane;
+    const int n = width ? (1 << width) : 0;
+    const int base = p * a.lut_block;
+    if constexpr (LM == LM_COL) {
+      // column lane: entry f at f * 64 + lane; a zero-width lane reads 0 at f = 0
+      for (int k = wv; k < max(n, 1); k += 4) lut[base + k * 64 + lane] = n ? glut[lut0 + cbv + k] : 0u;
+      cb[p] = base + lane;
+    } else if constexpr (LM == LM_PACK) {
+      // coordinate c0 + j's table at offset cbv + j: lanes gathering the same
+      // code from tables of equal size fall in different banks; the slot after
+      // each table is 0, which a zero-width coordinate (field 0) reads
+      if (ci < d) {  // lanes past the last coordinate (head_dim 32) write nothing
+        for (int k = wv; k < n; k += 4) lut[base + cbv + lane + k] = glut[lut0 + cbv + k];
+        if (wv == 0) lut[base + cbv + lane + n] = 0u;
+      }
+      cb[p] = base + cbv + lane;
+    } else {
+      cb[p] = lut0 + cbv;
+    }
+    fmask[p] = width ? ((1u << width) - 1u) : 0u;
+    cwl[p] = width ? (bo >> 5) : 0;
+    cs[p] = bo & 31;
+    straddle[p] = cs[p] + width > 32;
   }
   const uint32_t *lutv;
   if constexpr (LM == LM_GLB) lutv = glut;
   else lutv = lut;
   const int lsh = LM == LM_COL ? 6 : 0;  // gather index: (field << lsh) + cb
-  const uint32_t fmask = width ? ((1u << width) - 1u) : 0u;
-  const int cwl = width ? (bo >> 5) - wlo : 0, cs = bo & 31;
-  const bool straddle = cs + width > 32;
   __syncthreads();
   if (chunk >= a.n_chunks) return;  // no barrier follows
 
@@ -2015,25 +2032,28 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     mrun[g] = -INFINITY;
     lsum[g] = 0.0f;
   }
-  // four independent accumulator sets (the products of a step alternate
-  // among them), summed at the end
-  f32x4 acc[4][GR];
+  // per block, four independent accumulator sets (the products of a step
+  // alternate among them), summed at the end
+  f32x4 acc[NP][4][GR];
 #pragma unroll
-  for (int h = 0; h < 4; ++h)
+  for (int p = 0; p < NP; ++p)
 #pragma unroll
-    for (int r = 0; r < GR; ++r) acc[h][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int r = 0; r < GR; ++r) acc[p][h][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Staging, double-buffered: the words [wlo, wlo + nwd) of the tile's
-  // records and its G score rows go straight from HBM to LDS; tile i + 1 is
+  // Staging, double-buffered: the W words of the tile's records (plus one
+  // spare row, a copy of the last word: the word after a field never goes
+  // past it) and its G score rows go straight from HBM to LDS; tile i + 1 is
   // requested before tile i is computed, so the one wait per tile covers
   // loads issued a whole tile earlier.
   auto stage_tile = [&](int64_t t0, int buf) {
     uint32_t *rw = (uint32_t *)(stage + buf * a.buf_floats);
     const uint32_t *src = slot + (t0 >> 6) * W * 64 + lane;
-    for (int w = 0; w < nwd; ++w)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + min(wlo + w, W - 1) * 64),
+    for (int w = 0; w <= W; ++w)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + min(w, W - 1) * 64),
                                        (__attribute__((address_space(3))) void *)(rw + w * ATT_RS), 4, 0, 0);
-    float *sr = stage + buf * a.buf_floats + nwd * ATT_RS;
+    float *sr = stage + buf * a.buf_floats + (W + 1) * ATT_RS;
     // pad tokens of the last tile: any in-range address (their weight is 0)
     const int64_t ts = min(t0 + lane, a.n_tokens - 1);
 #pragma unroll
@@ -2048,8 +2068,7 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     wave_lds_sync();
     if (t0 + 64 < te) stage_tile(t0 + 64, buf ^ 1);
     const uint32_t *rec = (const uint32_t *)(stage + buf * a.buf_floats);
-    const float *sr = stage + buf * a.buf_floats + nwd * ATT_RS;
-    const uint32_t *rlo = rec + cwl * ATT_RS, *rhi = rlo + ATT_RS;
+    const float *sr = stage + buf * a.buf_floats + (W + 1) * ATT_RS;
     // ---- online softmax over the tile (lane = token)
     const int64_t t = t0 + lane;
     float sv[G];
@@ -2065,7 +2084,9 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
         mrun[g] = mx;
         lsum[g] *= corr;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) acc[h][g >> 2][g & 3] *= corr;
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) acc[p][h][g >> 2][g & 3] *= corr;
       }
       const float pv = __expf(sv[g] - mrun[g]);  // 0 for tokens past the end
       lsum[g] += pv;
@@ -2079,67 +2100,79 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
       pl[g * ATT_PS + lane] = 0u;
     }
     wave_lds_sync();
-    // ---- 8 tokens per step: decode (all gathers in flight together), then
-    // the weighted sums on the MFMA.  A product takes 2 tokens: the k slots
-    // of coordinate n are (hi, lo) of C[code] for each token, the weights of
-    // head m are (p, p) per token, so it adds p_t0 (hi0 + lo0) + p_t1 (hi1 + lo1);
-    // once with bf16(p) and once with the remainder of p.
+    // ---- 8 tokens per step: the weights once, then per block decode (all
+    // gathers in flight together) and the weighted sums on the MFMA.  A
+    // product takes 2 tokens: the k slots of coordinate n are (hi, lo) of
+    // C[code] for each token, the weights of head m are (p, p) per token, so
+    // it adds p_t0 (hi0 + lo0) + p_t1 (hi1 + lo1); once with bf16(p) and once
+    // with the remainder of p.
     const int m = lane & 3;
 #pragma unroll 2
     for (int k = 0; k < 64; k += 8) {
-      const uint4 lo0 = *(const uint4 *)(rlo + k), lo1 = *(const uint4 *)(rlo + k + 4);
-      uint4 hi0 = make_uint4(0, 0, 0, 0), hi1 = hi0;
-      if (straddle) {  // only lanes whose field runs into the next word read it
-        hi0 = *(const uint4 *)(rhi + k);
-        hi1 = *(const uint4 *)(rhi + k + 4);
-      }
-      uint32_t pr[8];
-      pr[0] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.x, lo0.x, cs) & fmask) << lsh)];
-      pr[1] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.y, lo0.y, cs) & fmask) << lsh)];
-      pr[2] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.z, lo0.z, cs) & fmask) << lsh)];
-      pr[3] = lutv[cb + ((__builtin_amdgcn_alignbit(hi0.w, lo0.w, cs) & fmask) << lsh)];
-      pr[4] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.x, lo1.x, cs) & fmask) << lsh)];
-      pr[5] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.y, lo1.y, cs) & fmask) << lsh)];
-      pr[6] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.z, lo1.z, cs) & fmask) << lsh)];
-      pr[7] = lutv[cb + ((__builtin_amdgcn_alignbit(hi1.w, lo1.w, cs) & fmask) << lsh)];
+      uint2 ah[GR][4], al[GR][4];
 #pragma unroll
       for (int r = 0; r < GR; ++r) {
         const uint32_t *hrow = ph + (4 * r + m) * ATT_PS + k, *lrow = pl + (4 * r + m) * ATT_PS + k;
         const uint4 ah0 = *(const uint4 *)hrow, ah1 = *(const uint4 *)(hrow + 4);
         const uint4 al0 = *(const uint4 *)lrow, al1 = *(const uint4 *)(lrow + 4);
-        const uint2 ah[4] = {make_uint2(ah0.x, ah0.y), make_uint2(ah0.z, ah0.w),
-                             make_uint2(ah1.x, ah1.y), make_uint2(ah1.z, ah1.w)};
-        const uint2 al[4] = {make_uint2(al0.x, al0.y), make_uint2(al0.z, al0.w),
-                             make_uint2(al1.x, al1.y), make_uint2(al1.z, al1.w)};
+        ah[r][0] = make_uint2(ah0.x, ah0.y); ah[r][1] = make_uint2(ah0.z, ah0.w);
+        ah[r][2] = make_uint2(ah1.x, ah1.y); ah[r][3] = make_uint2(ah1.z, ah1.w);
+        al[r][0] = make_uint2(al0.x, al0.y); al[r][1] = make_uint2(al0.z, al0.w);
+        al[r][2] = make_uint2(al1.x, al1.y); al[r][3] = make_uint2(al1.z, al1.w);
+      }
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint2 bv = make_uint2(pr[2 * h], pr[2 * h + 1]);
-          acc[h][r] = mfma4(ah[h], bv, acc[h][r]);
-          acc[h][r] = mfma4(al[h], bv, acc[h][r]);
+      for (int p = 0; p < NP; ++p) {
+        const uint32_t *rlo = rec + cwl[p] * ATT_RS, *rhi = rlo + ATT_RS;
+        const uint4 lo0 = *(const uint4 *)(rlo + k), lo1 = *(const uint4 *)(rlo + k + 4);
+        uint4 hi0 = make_uint4(0, 0, 0, 0), hi1 = hi0;
+        if (straddle[p]) {  // only lanes whose field runs into the next word read it
+          hi0 = *(const uint4 *)(rhi + k);
+          hi1 = *(const uint4 *)(rhi + k + 4);
         }
+        const int c = cb[p], s = cs[p];
+        const uint32_t fm = fmask[p];
+        uint32_t pr[8];
+        pr[0] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.x, lo0.x, s) & fm) << lsh)];
+        pr[1] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.y, lo0.y, s) & fm) << lsh)];
+        pr[2] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.z, lo0.z, s) & fm) << lsh)];
+        pr[3] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.w, lo0.w, s) & fm) << lsh)];
+        pr[4] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.x, lo1.x, s) & fm) << lsh)];
+        pr[5] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.y, lo1.y, s) & fm) << lsh)];
+        pr[6] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.z, lo1.z, s) & fm) << lsh)];
+        pr[7] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.w, lo1.w, s) & fm) << lsh)];
+#pragma unroll
+        for (int r = 0; r < GR; ++r)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint2 bv = make_uint2(pr[2 * h], pr[2 * h + 1]);
+            acc[p][h][r] = mfma4(ah[r][h], bv, acc[p][h][r]);
+            acc[p][h][r] = mfma4(al[r][h], bv, acc[p][h][r]);
+          }
       }
     }
     wave_lds_sync();  // every read of this tile's words and weights is done
   }
-  // ---- partials: o_rot for this block's coordinates; the running max and
-  // the weight sum (block 0)
+  // ---- partials: o_rot for the head's coordinates, the running max and the
+  // weight sum
   float *dst = a.ws + (((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * a.n_chunks + chunk) * (d + 2);
-  if (ci < c1) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      dst[(int64_t)g * a.n_chunks * (d + 2) + 2 + ci] =
-          (acc[0][g >> 2][g & 3] + acc[1][g >> 2][g & 3]) + (acc[2][g >> 2][g & 3] + acc[3][g >> 2][g & 3]);
+  for (int p = 0; p < NP; ++p) {
+    const int ci = p * 64 + lane;
+    if (ci < d) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        dst[(int64_t)g * a.n_chunks * (d + 2) + 2 + ci] =
+            (acc[p][0][g >> 2][g & 3] + acc[p][1][g >> 2][g & 3]) + (acc[p][2][g >> 2][g & 3] + acc[p][3][g >> 2][g & 3]);
+    }
   }
-  if (part == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float v = lsum[g];
+  for (int g = 0; g < G; ++g) {
+    float v = lsum[g];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0) {
-        dst[(int64_t)g * a.n_chunks * (d + 2) + 0] = mrun[g];
-        dst[(int64_t)g * a.n_chunks * (d + 2) + 1] = v;
-      }
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) {
+      dst[(int64_t)g * a.n_chunks * (d + 2) + 0] = mrun[g];
+      dst[(int64_t)g * a.n_chunks * (d + 2) + 1] = v;
     }
   }
 }
@@ -2397,7 +2430,7 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
       b2.lds_csig_off = (mt + 3) & ~3;
       b2.lds_s_off = b2.lds_csig_off + ((mc + 3) & ~3);
       b2.lds_x_off = (b2.lds_s_off + mq * C2_SP + 255) & ~255;  // 1 KB aligned: direct-to-LDS blocks
-      b2.x_buf_floats = 16 * (d * (f32 ? 4 : 2) + 16);          // 64 rows of d elements + 16 bytes
+      b2.x_buf_floats = 16 * d * (f32 ? 4 : 2);                 // 64 rows of d elements
       b2.lds_rec_off = b2.lds_x_off + 2 * b2.x_buf_floats;
       // record tile stride: odd, above W_max (pad column)
       const int rsc = c->W_max < 17 ? 17 : c->W_max < 33 ? 33 : 49;
@@ -2604,11 +2637,18 @@ extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_
   return (size_t)batch * n_q_heads * nch * (head_dim + 2) * sizeof(float);
 }
 
+template <int G, int NP>
+static void launch_attend_np(int lm, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
+  if (lm == LM_COL) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP>), grid, dim3(256), lds, s, a);
+  else if (lm == LM_PACK) hipLaunchKernelGGL((attend_partial_kernel<G, LM_PACK, NP>), grid, dim3(256), lds, s, a);
+  else hipLaunchKernelGGL((attend_partial_kernel<G, LM_GLB, NP>), grid, dim3(256), lds, s, a);
+}
+
 template <int G>
-static void launch_attend(int lm, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  if (lm == LM_COL) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL>), grid, dim3(256), lds, s, a);
-  else if (lm == LM_PACK) hipLaunchKernelGGL((attend_partial_kernel<G, LM_PACK>), grid, dim3(256), lds, s, a);
-  else hipLaunchKernelGGL((attend_partial_kernel<G, LM_GLB>), grid, dim3(256), lds, s, a);
+static void launch_attend(int lm, int np, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
+  if (np == 1) launch_attend_np<G, 1>(lm, grid, lds, s, a);
+  else if (np == 2) launch_attend_np<G, 2>(lm, grid, lds, s, a);
+  else launch_attend_np<G, 4>(lm, grid, lds, s, a);
 }
 
 extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride, int batch,
@@ -2655,19 +2695,18 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
     return fail(SQ_ERR_ARG, "sq_attend: workspace too small");
   a.ws = (float *)workspace;
   a.n_chunks = (int)((n_tokens + ATT_CHUNK - 1) / ATT_CHUNK);
-  a.n_parts = (d + 63) / 64;
-  // LDS: centroid table of one 64-coordinate block | 4 x (two staging buffers, weights)
-  int max_lut = 1, max_nwd = 2, max_w = 0;
+  const int np = (d + 63) / 64;  // 64-coordinate blocks, all served by one wave
+  if (np != 1 && np != 2 && np != 4) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: unsupported head_dim");
+  // LDS: centroid tables of the blocks | 4 x (two staging buffers, weights)
+  int max_lut = 1, max_wd = 1, max_w = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
     for (int h = 0; h < n_kv_heads; ++h) {
       const HeadCal &hc = vc->heads[first_head + bb * calib_batch_stride + h];
-      for (int pt = 0; pt < a.n_parts; ++pt) {
+      max_wd = std::max(max_wd, hc.W);
+      for (int pt = 0; pt < np; ++pt) {
         const int c0 = pt * 64, c1 = std::min(d, c0 + 64);
         const int lut1 = c1 < d ? hc.cent_base[c1] : hc.n_cent;
         max_lut = std::max(max_lut, lut1 - hc.cent_base[c0]);
-        const int wlo = hc.bit_off[c0] >> 5;
-        const int whi = std::min(hc.W - 1, (hc.bit_off[c1 - 1] + hc.widths[c1 - 1]) >> 5);
-        max_nwd = std::max(max_nwd, whi - wlo + 2);
         for (int i = c0; i < c1; ++i) max_w = std::max(max_w, hc.widths[i]);
       }
     }
@@ -2675,18 +2714,25 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   }
   const int GP = ((G + 3) / 4) * 4;
   const int limit = device_lds_limit();
-  a.buf_floats = max_nwd * ATT_RS + G * 64;
+  a.buf_floats = (max_wd + 1) * ATT_RS + G * 64;
   a.wave_floats = 2 * a.buf_floats + 2 * GP * ATT_PS;
-  auto lds_for = [&](int lut_floats) {
-    a.lds_wave_off = (lut_floats + 3) & ~3;
+  auto lds_for = [&](int block_floats) {
+    a.lut_block = block_floats;
+    a.lds_wave_off = (np * block_floats + 3) & ~3;
     return (size_t)(a.lds_wave_off + 4 * a.wave_floats) * 4;
   };
+  // table placement: column tables (conflict-free) unless packed tables let
+  // more workgroups share a CU
   int lm = LM_GLB;
   size_t lds = 0;
-  if (max_w <= 6 && lds_for(64 << max_w) <= (size_t)std::min(limit, 64 * 1024)) {
+  const size_t cap = (size_t)std::min(limit, 64 * 1024);
+  const size_t lds_col = max_w <= 6 ? lds_for(64 << max_w) : cap + 1;
+  const size_t lds_pack = lds_for(max_lut + 64);
+  const size_t cu_lds = (size_t)limit;  // one workgroup may use all of a CU's LDS
+  if (lds_col <= cap && cu_lds / lds_col >= cu_lds / lds_pack) {
     lm = LM_COL;
     lds = lds_for(64 << max_w);
-  } else if (lds_for(max_lut + 64) <= (size_t)std::min(limit, 64 * 1024)) {
+  } else if (lds_pack <= cap) {
     lm = LM_PACK;
     lds = lds_for(max_lut + 64);
   } else {
@@ -2694,18 +2740,18 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   }
   if (lds > (size_t)limit) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: tables exceed LDS");
   const int64_t cgroups = (a.n_chunks + 3) / 4;
-  dim3 grid((unsigned)(cgroups * a.n_parts), n_kv_heads, batch);
-  if (grid.z > 65535 || grid.y > 65535 || cgroups * a.n_parts > INT32_MAX)
+  dim3 grid((unsigned)cgroups, n_kv_heads, batch);
+  if (grid.z > 65535 || grid.y > 65535 || cgroups > INT32_MAX)
     return fail(SQ_ERR_UNSUPPORTED, "sq_attend: grid too large");
   switch (G) {
-    case 1: launch_attend<1>(lm, grid, lds, s, a); break;
-    case 2: launch_attend<2>(lm, grid, lds, s, a); break;
-    case 3: launch_attend<3>(lm, grid, lds, s, a); break;
-    case 4: launch_attend<4>(lm, grid, lds, s, a); break;
-    case 5: launch_attend<5>(lm, grid, lds, s, a); break;
-    case 6: launch_attend<6>(lm, grid, lds, s, a); break;
-    case 7: launch_attend<7>(lm, grid, lds, s, a); break;
-    case 8: launch_attend<8>(lm, grid, lds, s, a); break;
+    case 1: launch_attend<1>(lm, np, grid, lds, s, a); break;
+    case 2: launch_attend<2>(lm, np, grid, lds, s, a); break;
+    case 3: launch_attend<3>(lm, np, grid, lds, s, a); break;
+    case 4: launch_attend<4>(lm, np, grid, lds, s, a); break;
+    case 5: launch_attend<5>(lm, np, grid, lds, s, a); break;
+    case 6: launch_attend<6>(lm, np, grid, lds, s, a); break;
+    case 7: launch_attend<7>(lm, np, grid, lds, s, a); break;
+    case 8: launch_attend<8>(lm, np, grid, lds, s, a); break;
   }
   sq_status s1 = launched(fn);
   if (s1 != SQ_OK) return s1;
