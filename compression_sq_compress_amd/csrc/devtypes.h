@@ -78,17 +78,18 @@ struct DevHead {
 };
 
 // Register-quantising compress plan.  Coordinates are taken in groups of 4
-// consecutive ones (group g = 4g .. 4g+3, depth = the group's largest width);
-// each wave gets 4 groups, one per MFMA accumulator register r, chosen to
-// balance the waves' total depth and ordered by decreasing depth.  Row 4s + r
-// of wave w's 16 MFMA rows holds coordinate 4 g(w, r) + s, so lane l
-// (s = l / 16) finds in register r the value of that coordinate for tokens
-// l % 16 + 16 j.  Wave header (P2_WAVE): [r] depth of register r's group,
-// [4 + 4r + s] tree base (floats) of its coordinate, [20 + 4r + s]
-// signal-centroid base or 0xFFFFFFFF (not a signal coordinate), [36 + 4r + s]
-// the coordinate.  A tree holds the coordinate's sorted thresholds padded
-// with +inf to 2^depth - 1 entries in breadth-first order (node k = 1 ..
-// 2^depth - 1 at base + k - 1).
+// (equal widths where possible, spread over different record words; depth =
+// the group's largest width); each wave gets 4 groups, one per MFMA
+// accumulator register r, chosen to balance the waves' total depth and
+// ordered by decreasing depth.  Row 4s + r of wave w's 16 MFMA rows holds
+// coordinate s of group g(w, r), so lane l (s = l / 16) finds in register r
+// the value of that coordinate for tokens l % 16 + 16 j.  Wave header
+// (P2_WAVE): [r] depth of register r's group, [4 + 4r + s] tree base
+// (floats) of its coordinate, [20 + 4r + s] signal-centroid base or
+// 0xFFFFFFFF (not a signal coordinate), [36 + 4r + s] the coordinate.  A
+// tree holds the coordinate's sorted thresholds padded with +inf to
+// 2^depth - 1 entries in breadth-first order (node k = 1 .. 2^depth - 1 at
+// base + k - 1); the four trees of a register start at 16 s (mod 64).
 constexpr int P2_WAVE = 64;
 
 static_assert(sizeof(DevCoord) == 16, "DevCoord layout");

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -402,9 +403,29 @@ static HostPlan2 build_plan2(const HeadCal &hc) {
   if (d != 32 && d != 64 && d != 128) return P;
   if (hc.m > 0 && (hc.d_eff > 16 || hc.m > 32)) return P;
   const int NW = d / 16, NG = d / 4;
+  // Groups of 4 coordinates of equal width where possible (depth = the
+  // largest width): each width class, in coordinate order, is cut into four
+  // equal runs and group t takes the t-th coordinate of each run, so the four
+  // codes of a group usually sit in different record words (the lane groups
+  // of a register OR them into the record tile in one instruction); the
+  // remainders of the classes are grouped by decreasing width.
+  std::vector<int> byw(d);
+  for (int c = 0; c < d; ++c) byw[c] = c;
+  std::stable_sort(byw.begin(), byw.end(), [&](int x, int y) { return hc.widths[x] > hc.widths[y]; });
+  std::vector<std::array<int, 4>> grp;
+  std::vector<int> rest;
+  for (int i = 0; i < d;) {
+    int j = i;
+    while (j < d && hc.widths[byw[j]] == hc.widths[byw[i]]) ++j;
+    const int q = (j - i) / 4;
+    for (int t = 0; t < q; ++t) grp.push_back({byw[i + t], byw[i + q + t], byw[i + 2 * q + t], byw[i + 3 * q + t]});
+    for (int k = i + 4 * q; k < j; ++k) rest.push_back(byw[k]);
+    i = j;
+  }
+  for (size_t k = 0; k < rest.size(); k += 4) grp.push_back({rest[k], rest[k + 1], rest[k + 2], rest[k + 3]});
   std::vector<int> depth(NG, 0);
   for (int g = 0; g < NG; ++g)
-    for (int s = 0; s < 4; ++s) depth[g] = std::max(depth[g], hc.widths[4 * g + s]);
+    for (int s = 0; s < 4; ++s) depth[g] = std::max(depth[g], hc.widths[grp[g][s]]);
   std::vector<int> order(NG);
   for (int g = 0; g < NG; ++g) order[g] = g;
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return depth[x] > depth[y]; });
@@ -436,7 +457,7 @@ static HostPlan2 build_plan2(const HeadCal &hc) {
       const size_t rbase = (P.tree.size() + 63) & ~(size_t)63;
       if (D > 0) P.tree.resize(rbase + 4 * stride, inf);
       for (int s = 0; s < 4; ++s) {
-        const int c = 4 * g + s, b = hc.widths[c];
+        const int c = grp[g][s], b = hc.widths[c];
         P.row_coord[w * 16 + 4 * s + r] = c;
         H[36 + 4 * r + s] = (uint32_t)c;
         const size_t tb = D > 0 ? rbase + s * stride : 0;
