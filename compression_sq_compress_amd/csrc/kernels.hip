@@ -1955,7 +1955,7 @@ struct AttendArgs {
   int lut_block;               // floats: stride of the 64-coordinate blocks' centroid tables
   int lds_wave_off;            // floats: per-wave areas (the centroid tables start at 0)
   int wave_floats;             // one wave's area: two staging buffers, then the weights
-  int buf_floats;              // one staging buffer: [W + 1][ATT_RS] words + [G][64] scores
+  int buf_floats;              // one staging buffer: [W + 2][ATT_RS] words + [G][64] scores
 };
 
 // Maximum over the 64 lanes: rotations within each row of 16 (DPP), then the
@@ -2003,6 +2003,11 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
   int cb[NP], cwl[NP], cs[NP];
   uint32_t fmask[NP];
   bool straddle[NP];
+  // column tables: the field is taken from the 64-bit window of staged rows
+  // wrow, wrow + 1 that starts 8 bits below it, so that one shift and one
+  // and-or give the entry's byte address (field << 8 | lane << 2 | block base)
+  int wrow[NP];
+  uint32_t wsh[NP], m8[NP], orv[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int c0 = p * 64, ci = c0 + lane;
@@ -2035,10 +2040,16 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     cwl[p] = width ? (bo >> 5) : 0;
     cs[p] = bo & 31;
     straddle[p] = cs[p] + width > 32;
+    // staged row 0 is zero (the word before word 0), row w + 1 is word w
+    wrow[p] = width ? ((bo - 8) >> 5) + 1 : 1;
+    wsh[p] = width ? (uint32_t)(bo - 8) & 31u : 0u;
+    m8[p] = fmask[p] << 8;
+    orv[p] = ((uint32_t)lane << 2) | ((uint32_t)(p * a.lut_block) << 2);
   }
   const uint32_t *lutv;
   if constexpr (LM == LM_GLB) lutv = glut;
   else lutv = lut;
+
   const int lsh = LM == LM_COL ? 6 : 0;  // gather index: (field << lsh) + cb
   __syncthreads();
   if (chunk >= a.n_chunks) return;  // no barrier follows
@@ -2069,12 +2080,12 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
   // requested before tile i is computed, so the one wait per tile covers
   // loads issued a whole tile earlier.
   auto stage_tile = [&](int64_t t0, int buf) {
-    uint32_t *rw = (uint32_t *)(stage + buf * a.buf_floats);
+    uint32_t *rw = (uint32_t *)(stage + buf * a.buf_floats) + ATT_RS;  // row 1 = word 0
     const uint32_t *src = slot + (t0 >> 6) * W * 64 + lane;
     for (int w = 0; w <= W; ++w)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + min(w, W - 1) * 64),
                                        (__attribute__((address_space(3))) void *)(rw + w * ATT_RS), 4, 0, 0);
-    float *sr = stage + buf * a.buf_floats + (W + 1) * ATT_RS;
+    float *sr = stage + buf * a.buf_floats + (W + 2) * ATT_RS;
     // pad tokens of the last tile: any in-range address (their weight is 0)
     const int64_t ts = min(t0 + lane, a.n_tokens - 1);
 #pragma unroll
@@ -2082,6 +2093,9 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(srow + (int64_t)g * a.n_tokens + ts),
                                        (__attribute__((address_space(3))) void *)(sr + g * 64), 4, 0, 0);
   };
+  // row 0 of both staging buffers: zeros (the word before word 0)
+  ((uint32_t *)stage)[lane] = 0u;
+  ((uint32_t *)(stage + a.buf_floats))[lane] = 0u;
   stage_tile(tb, 0);
   int buf = 0;
   for (int64_t t0 = tb; t0 < te; t0 += 64, buf ^= 1) {
@@ -2089,7 +2103,7 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     wave_lds_sync();
     if (t0 + 64 < te) stage_tile(t0 + 64, buf ^ 1);
     const uint32_t *rec = (const uint32_t *)(stage + buf * a.buf_floats);
-    const float *sr = stage + buf * a.buf_floats + (W + 1) * ATT_RS;
+    const float *sr = stage + buf * a.buf_floats + (W + 2) * ATT_RS;
     // ---- online softmax over the tile (lane = token)
     const int64_t t = t0 + lane;
     float sv[G];
@@ -2143,24 +2157,45 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
       }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const uint32_t *rlo = rec + cwl[p] * ATT_RS, *rhi = rlo + ATT_RS;
-        const uint4 lo0 = *(const uint4 *)(rlo + k), lo1 = *(const uint4 *)(rlo + k + 4);
-        uint4 hi0 = make_uint4(0, 0, 0, 0), hi1 = hi0;
-        if (straddle[p]) {  // only lanes whose field runs into the next word read it
-          hi0 = *(const uint4 *)(rhi + k);
-          hi1 = *(const uint4 *)(rhi + k + 4);
-        }
-        const int c = cb[p], s = cs[p];
-        const uint32_t fm = fmask[p];
         uint32_t pr[8];
-        pr[0] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.x, lo0.x, s) & fm) << lsh)];
-        pr[1] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.y, lo0.y, s) & fm) << lsh)];
-        pr[2] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.z, lo0.z, s) & fm) << lsh)];
-        pr[3] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.w, lo0.w, s) & fm) << lsh)];
-        pr[4] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.x, lo1.x, s) & fm) << lsh)];
-        pr[5] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.y, lo1.y, s) & fm) << lsh)];
-        pr[6] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.z, lo1.z, s) & fm) << lsh)];
-        pr[7] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.w, lo1.w, s) & fm) << lsh)];
+        if constexpr (LM == LM_COL) {
+          const uint32_t *ra = rec + wrow[p] * ATT_RS, *rb = ra + ATT_RS;
+          const uint4 a0 = *(const uint4 *)(ra + k), a1 = *(const uint4 *)(ra + k + 4);
+          const uint4 b0 = *(const uint4 *)(rb + k), b1 = *(const uint4 *)(rb + k + 4);
+          const uint32_t s = wsh[p], mk = m8[p], ov = orv[p];
+          uint32_t ix[8];  // byte offsets of the entries from the start of the tables
+          ix[0] = (__builtin_amdgcn_alignbit(b0.x, a0.x, s) & mk) | ov;
+          ix[1] = (__builtin_amdgcn_alignbit(b0.y, a0.y, s) & mk) | ov;
+          ix[2] = (__builtin_amdgcn_alignbit(b0.z, a0.z, s) & mk) | ov;
+          ix[3] = (__builtin_amdgcn_alignbit(b0.w, a0.w, s) & mk) | ov;
+          ix[4] = (__builtin_amdgcn_alignbit(b1.x, a1.x, s) & mk) | ov;
+          ix[5] = (__builtin_amdgcn_alignbit(b1.y, a1.y, s) & mk) | ov;
+          ix[6] = (__builtin_amdgcn_alignbit(b1.z, a1.z, s) & mk) | ov;
+          ix[7] = (__builtin_amdgcn_alignbit(b1.w, a1.w, s) & mk) | ov;
+          // the tables open the kernel's LDS (the launcher checks that the
+          // kernel has no static LDS), so the offsets are LDS addresses
+          typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pr[i] = *(lds_u32 *)(uintptr_t)ix[i];
+        } else {
+          const uint32_t *rlo = rec + (cwl[p] + 1) * ATT_RS, *rhi = rlo + ATT_RS;
+          const uint4 lo0 = *(const uint4 *)(rlo + k), lo1 = *(const uint4 *)(rlo + k + 4);
+          uint4 hi0 = make_uint4(0, 0, 0, 0), hi1 = hi0;
+          if (straddle[p]) {  // only lanes whose field runs into the next word read it
+            hi0 = *(const uint4 *)(rhi + k);
+            hi1 = *(const uint4 *)(rhi + k + 4);
+          }
+          const int c = cb[p], s = cs[p];
+          const uint32_t fm = fmask[p];
+          pr[0] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.x, lo0.x, s) & fm) << lsh)];
+          pr[1] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.y, lo0.y, s) & fm) << lsh)];
+          pr[2] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.z, lo0.z, s) & fm) << lsh)];
+          pr[3] = lutv[c + ((__builtin_amdgcn_alignbit(hi0.w, lo0.w, s) & fm) << lsh)];
+          pr[4] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.x, lo1.x, s) & fm) << lsh)];
+          pr[5] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.y, lo1.y, s) & fm) << lsh)];
+          pr[6] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.z, lo1.z, s) & fm) << lsh)];
+          pr[7] = lutv[c + ((__builtin_amdgcn_alignbit(hi1.w, lo1.w, s) & fm) << lsh)];
+        }
 #pragma unroll
         for (int r = 0; r < GR; ++r)
 #pragma unroll
@@ -2658,9 +2693,21 @@ extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_
   return (size_t)batch * n_q_heads * nch * (head_dim + 2) * sizeof(float);
 }
 
+// The column-table kernel addresses its tables at LDS address 0: true when
+// the kernel declares no static LDS (the dynamic area then starts at 0).
+template <int G, int NP>
+static bool attend_col_ok() {
+  static const bool ok = [] {
+    hipFuncAttributes fa{};
+    return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&attend_partial_kernel<G, LM_COL, NP>)) ==
+               hipSuccess && fa.sharedSizeBytes == 0;
+  }();
+  return ok;
+}
+
 template <int G, int NP>
 static void launch_attend_np(int lm, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  if (lm == LM_COL) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP>), grid, dim3(256), lds, s, a);
+  if (lm == LM_COL && attend_col_ok<G, NP>()) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP>), grid, dim3(256), lds, s, a);
   else if (lm == LM_PACK) hipLaunchKernelGGL((attend_partial_kernel<G, LM_PACK, NP>), grid, dim3(256), lds, s, a);
   else hipLaunchKernelGGL((attend_partial_kernel<G, LM_GLB, NP>), grid, dim3(256), lds, s, a);
 }
@@ -2735,7 +2782,7 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   }
   const int GP = ((G + 3) / 4) * 4;
   const int limit = device_lds_limit();
-  a.buf_floats = (max_wd + 1) * ATT_RS + G * 64;
+  a.buf_floats = (max_wd + 2) * ATT_RS + G * 64;
   a.wave_floats = 2 * a.buf_floats + 2 * GP * ATT_PS;
   auto lds_for = [&](int block_floats) {
     a.lut_block = block_floats;
