@@ -1958,18 +1958,28 @@ struct AttendArgs {
   int buf_floats;              // one staging buffer: [W + 2][ATT_RS] words + [G][64] scores
 };
 
-// Maximum over the 64 lanes: rotations within each row of 16 (DPP), then the
-// four row results (returned in every lane).
+// Maximum over the 64 lanes (returned in every lane), on order-preserving
+// integer keys of the floats (sign-magnitude to two's complement): rotations
+// within each row of 16 (DPP), then the four row results.  A positive NaN
+// wins and a negative NaN loses; either way its token's weight is NaN.
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  int k = __float_as_int(v);
+  k ^= (k >> 31) & 0x7FFFFFFF;
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x128, 0xF, 0xF, true));  // (row rotations: every lane valid)
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x124, 0xF, 0xF, true));
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x122, 0xF, 0xF, true));
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x121, 0xF, 0xF, true));
+  int m = max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
+              max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+  m ^= (m >> 31) & 0x7FFFFFFF;
+  return __int_as_float(m);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// (bf16(x), bf16(x)) packed, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t bf16_pair_rne(float x) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x, x}, bf16x2_t));
 }
 
 // Centroid table placement of the attend kernel: LM_COL = one column per lane
@@ -2125,9 +2135,9 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
       }
       const float pv = __expf(sv[g] - mrun[g]);  // 0 for tokens past the end
       lsum[g] += pv;
-      const uint16_t hi = f32_to_bf16_rne(pv);
-      ph[g * ATT_PS + lane] = bf16_pair(hi);
-      pl[g * ATT_PS + lane] = bf16_pair(f32_to_bf16_rne(pv - bf16_to_f32(hi)));
+      const uint32_t hp = bf16_pair_rne(pv);
+      ph[g * ATT_PS + lane] = hp;
+      pl[g * ATT_PS + lane] = bf16_pair_rne(pv - __uint_as_float(hp << 16));
     }
 #pragma unroll
     for (int g = G; g < GP; ++g) {
