@@ -27,7 +27,9 @@
  *     on different streams that share it are safe.  Calls that write the same
  *     output buffer from different streams race.
  *   - NaN inputs are not checked on the hot path: a NaN coordinate compares
- *     false against every threshold and gets code 0.
+ *     false against every threshold and gets code 0.  A NaN entry of x makes
+ *     every rotated coordinate of that vector NaN: all codes 0, for keys no
+ *     QJL bit set and a NaN gamma.
  *
  * Packed record layout (one record per (head, token); identical in the CPU
  * oracle, which implements it independently):
