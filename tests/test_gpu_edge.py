@@ -263,6 +263,29 @@ def test_nan_inputs(torch_dev, sq, name, dt):
             assert np.all(np.isnan(gg[nan_tok].astype(np.float32))), "NaN tokens must have a NaN gamma"
 
 
+@pytest.mark.parametrize("d", [32, 64])
+def test_bf16_inputs_small_head_dims(torch_dev, sq, d):
+    """bf16 keys at head_dim 32 and 64 (the register-quantising compress kernel
+    with 2 and 4 waves), several tiles and a ragged tail."""
+    torch = torch_dev
+    _case(f"bf16 flat d={d}")
+    T, nkv = 300, 2
+    X = np.stack([wl.flat_data(400, d, seed=s) for s in (3, 4)]).astype(np.float32)
+    Gm = np.stack([np.random.default_rng(200 + s).standard_normal((d, d)).astype(np.float32)
+                   for s in range(nkv)])
+    cal = sq.sq_calibrate(X, 3.0, 1, Gm).upload()
+    ors = [oracle.calibrate(X[k], 3.0, 1, Gm[k]) for k in range(nkv)]
+    xd = _dev(torch, np.stack([wl.flat_data(T, d, seed=20 + s) for s in range(nkv)])[None], torch.bfloat16)
+    x = xd.float().cpu().numpy()[0]  # the bf16-rounded values the kernel sees
+    kp = torch.zeros((1, nkv, cal.packed_head_words(T)), dtype=torch.int32, device="cuda")
+    sq.sq_compress(cal, xd, kp)
+    torch.cuda.synchronize()
+    kpn = kp.cpu().numpy().view(np.uint32)[0]
+    for k in range(nkv):
+        assert cal.info(k).record_words == ors[k].W
+        H.compare_compress(ors[k], kpn[k], x[k], T)
+
+
 def test_degenerate_zero_calibration(torch_dev, sq):
     """All-zero calibration data: every threshold and centroid is 0 and the
     basis is arbitrary, so only what is unique is compared: zero vectors give
