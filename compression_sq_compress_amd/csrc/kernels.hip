@@ -1841,8 +1841,13 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
               const int h = 2 * qi + hh;
               // table base | code * 8 (tables are aligned to their size)
               const uint32_t ea = (__builtin_amdgcn_alignbit(whi[qi][t][hh], wlo[qi][t][hh], hsh[h]) & hmk[h]) | hlut[h];
-              if constexpr (LG) ent[qi][t][hh] = *(const uint2 *)((const uint8_t *)glut + ea);
-              else ent[qi][t][hh] = *(const uint2 *)(sm + ea);
+              if constexpr (LG) {
+                ent[qi][t][hh] = *(const uint2 *)((const uint8_t *)glut + ea);
+              } else {  // the LDS area starts at address 0 (the launcher checks the kernel has no static LDS)
+                typedef const __attribute__((address_space(3))) uint64_t lds_u64;
+                const uint64_t v = *(lds_u64 *)(uintptr_t)ea;
+                ent[qi][t][hh] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+              }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -2586,6 +2591,19 @@ static void launch_scores(dim3 grid, size_t lds, hipStream_t s, const ScoresArgs
   hipLaunchKernelGGL((scores_kernel<GR, SLOTB, R, LG>), grid, dim3(SC_BLOCK), lds, s, a);
 }
 
+// The LDS-table kernels address their tables at absolute LDS addresses: true
+// when the kernel declares no static LDS (the dynamic area then starts at 0).
+template <int GR>
+static bool scores_lds0_ok(int slotb) {
+  auto ok = [](const void *k) {
+    hipFuncAttributes fa{};
+    return hipFuncGetAttributes(&fa, k) == hipSuccess && fa.sharedSizeBytes == 0;
+  };
+  static const bool ok8 = ok(reinterpret_cast<const void *>(&scores_kernel<GR, 8192, 6, false>));
+  static const bool ok16 = ok(reinterpret_cast<const void *>(&scores_kernel<GR, 16384, 3, false>));
+  return slotb == 8192 ? ok8 : ok16;
+}
+
 template <int GR, bool LG>
 static void launch_scores_slot(int slotb, dim3 grid, size_t lds, hipStream_t s, const ScoresArgs &a) {
   if (slotb == 8192) launch_scores<GR, 8192, 6, LG>(grid, lds, s, a);
@@ -2652,7 +2670,8 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
   };
   bool lg = false;
   size_t lds = layout(true);
-  if (lds > (size_t)limit) {  // joint tables too large for LDS: read them through the caches
+  const bool lds0 = GR == 1 ? scores_lds0_ok<1>(slotb) : scores_lds0_ok<2>(slotb);
+  if (lds > (size_t)limit || !lds0) {  // joint tables too large for LDS: read them through the caches
     lg = true;
     lds = layout(false);
   }
