@@ -196,6 +196,19 @@ def main():
     ms_ck, ms_cv, ms_sc, ms_at = per.mean(axis=0)
     ms_step = wall * 1e3 / args.steps
 
+    # decode-time append, outside the timed step: the last token of every
+    # (sequence, KV head) compressed again into its slot (same words), K then V
+    ka, va = K[:, :, T - 1:T], V[:, :, T - 1:T]
+    aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+    for k in range(len(aev) + 3):
+        e = aev[k - 3] if k >= 3 else None
+        if e: e[0].record(stream)
+        sq.sq_compress_append(kcal, ka, kp, T - 1, stream=sh)
+        sq.sq_compress_append(vcal, va, vp, T - 1, stream=sh)
+        if e: e[1].record(stream)
+    torch.cuda.synchronize()
+    append_us = float(np.mean([e[0].elapsed_time(e[1]) for e in aev])) * 1e3
+
     n_vec = B * Hkv * T
     # algorithmic bytes: compress reads d bf16 and writes one record per vector
     bytes_ck = n_vec * (2 * d + 4 * Wk)
@@ -237,6 +250,8 @@ def main():
         "score_packedK_GBps": gbps(n_vec * 4 * Wk, ms_sc),
         "attend_GBps": gbps(bytes_at, ms_at),
         "attend_hbm_frac": gbps(bytes_at, ms_at) / HBM_PEAK_GBPS,
+        "append_decode": {"what": f"1 new token per (sequence, KV head), K and V: {2 * B * Hkv} vectors "
+                                  f"into slots at token {T - 1}", "us": append_us},
         "roofline": {"bound": "hbm", "kernel": "compress2_kernel<128,bf16> (register quantiser; per launch, K and V averaged)",
                      "achieved": comp_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": comp_gbps / HBM_PEAK_GBPS, "traffic": traffic,

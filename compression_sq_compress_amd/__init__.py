@@ -27,7 +27,7 @@ _STATUS = {0: "SQ_OK", 1: "SQ_ERR_ARG", 2: "SQ_ERR_UNSUPPORTED", 3: "SQ_ERR_NUME
 # symbols declared in include/sq.h
 EXPORTS = ("sq_calib_default_opts", "sq_calibrate", "sq_calib_upload", "sq_calib_n_heads",
            "sq_calib_info", "sq_calib_export", "sq_calib_save", "sq_calib_load",
-           "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_scores",
+           "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_compress_append", "sq_scores",
            "sq_attend_workspace_bytes", "sq_attend", "sq_dequantize", "sq_unpack",
            "sq_last_error")
 
@@ -76,6 +76,7 @@ def _load():
         "sq_calib_destroy": (None, [P]),
         "sq_packed_head_words": (I64, [P, I64]),
         "sq_compress": (I, [P, I, I, I, I, P, I, I64, I64, I64, I64, P, I64, I64, P]),
+        "sq_compress_append": (I, [P, I, I, I, I, P, I, I64, I64, I64, I64, P, I64, I64, I64, P]),
         "sq_scores": (I, [P, I, I, I, I, I, P, I, P, I64, I64, I64, P, P]),
         "sq_attend_workspace_bytes": (U64, [I, I, I64, I]),
         "sq_attend": (I, [P, I, I, I, I, I, P, C.c_float, P, I64, I64, I64, P, U64, P, P]),
@@ -220,6 +221,19 @@ def sq_compress(cal: Calibration, x, packed, first_head: int = 0, calib_batch_st
     _check(_load().sq_compress(cal.handle, first_head, H, B, calib_batch_stride, _ptr(x),
                                _dtype_code(x), T, x.stride(0), x.stride(1), x.stride(2),
                                _ptr(packed), packed.stride(0), packed.stride(1), _stream(stream)))
+
+
+def sq_compress_append(cal: Calibration, x, packed, token0: int, first_head: int = 0,
+                       calib_batch_stride: int = 0, stream=None):
+    """As sq_compress, with token t of x going to token slot token0 + t of each
+    head's packed slot (packed: [batch][n_heads][>= packed_head_words(token0 + T)])."""
+    assert x.dim() == 4 and x.stride(3) == 1 and x.is_cuda
+    B, H, T, d = x.shape
+    assert packed.dim() == 3 and packed.stride(2) == 1 and packed.element_size() == 4
+    _check(_load().sq_compress_append(cal.handle, first_head, H, B, calib_batch_stride, _ptr(x),
+                                      _dtype_code(x), T, x.stride(0), x.stride(1), x.stride(2),
+                                      _ptr(packed), packed.stride(0), packed.stride(1), int(token0),
+                                      _stream(stream)))
 
 
 def sq_scores(cal: Calibration, q, kpacked, n_tokens: int, scores, n_kv_heads: int,

@@ -669,6 +669,7 @@ struct CompressArgs {
   int64_t xs_b, xs_h, xs_t;
   int64_t ps_b, ps_h;
   int64_t n_tokens;
+  int64_t token0;       // source token i goes to token slot token0 + i
   int first_head, cbs;
   int n_tiles;          // ceil(T / 64) per (batch, head)
   int items;            // tiles one head's workgroups share
@@ -957,12 +958,20 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
   for (int k = threadIdx.x; k < 64 * a.bws; k += NT) bwords[k] = 0u;
   uint32_t *const bwrow = bwords + lane * a.bws;
   uint32_t *pdst = nullptr;  // destination of the previous tile's records
-  bool pvalid = false;
+  bool pvalid = false, pin = false;
+  // Source token i lands in slot token token0 + i: lane l of a source tile
+  // writes destination lane (token0 + l) % 64 of its tile or of the next.
+  // Lanes past the last token zero their words up to the end of the last
+  // destination tile and write nothing beyond it.
+  const int ol = (int)(a.token0 & 63) + lane;
+  const int64_t lofs = (int64_t)(ol >> 6) * W * 64 + (ol & 63);
+  const int64_t send = ((a.token0 + T + 63) & ~(int64_t)63) - a.token0;
   auto store_prev = [&]() {
-    for (int k = dfirst; k < dend; ++k) pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
+    for (int k = dfirst; k < dend; ++k)
+      if (pin) pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
     for (int k = own_f; k < own_e; ++k) {
       if (k >= dfirst && k < dend) continue;
-      pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
+      if (pin) pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
       bwrow[k] = 0u;
     }
   };
@@ -1105,8 +1114,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
       }
       bwrow[k] = word;
     }
-    pdst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + (int64_t)tile * W * 64 + lane;
+    pdst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + ((a.token0 >> 6) + tile) * W * 64 + lofs;
     pvalid = t0 + lane < T;
+    pin = t0 + lane < send;
     // The x tile was last read by the MFMAs, which every wave finished before
     // the barrier above; the y tile and the word buffer are rewritten only
     // after the barrier that follows the next x store.
@@ -1191,6 +1201,7 @@ struct Compress2Args {
   int64_t xs_b, xs_h, xs_t;
   int64_t ps_b, ps_h;
   int64_t n_tokens;
+  int64_t token0;             // source token i goes to token slot token0 + i
   int first_head, cbs;
   int n_tiles, tiles_per_wg;  // workgroup (x, head, batch entry) takes tiles [x * tiles_per_wg, ...)
   int lds_tree_off, lds_csig_off, lds_s_off, lds_x_off, lds_rec_off, lds_res_off;  // floats
@@ -1277,9 +1288,11 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   const uint32_t row_bytes = (uint32_t)a.xs_t * ESZ;  // 64 rows fit 32 bits (host check)
   const char *xbase = (const char *)a.x + ((int64_t)bz * a.xs_b + (int64_t)h * a.xs_h) * ESZ;
   auto dma_x = [&](int tl, int buf) __attribute__((always_inline)) {
-    const int64_t t0 = (int64_t)tl * 64;
+    // rows past the end re-read the last token (a whole tile past it, which
+    // only zero-fills destination words, reads nothing else)
+    const int64_t t0 = min<int64_t>((int64_t)tl * 64, a.n_tokens - 1);
     const char *src = xbase + t0 * a.xs_t * ESZ;
-    const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);  // rows past the end re-read the last token
+    const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int q = w * NB + i;
@@ -1304,7 +1317,14 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   const int xsw = ((lane & 15) / RPB) & (CPR - 1);
   const uint32_t xrow = (uint32_t)(lane & 15) * RB;
   uint32_t *rec0 = (uint32_t *)(smem + a.lds_rec_off);
-  uint32_t *obase = a.packed + (int64_t)bz * a.ps_b + (int64_t)h * a.ps_h;
+  // source token i lands in slot token token0 + i: lane l of a source tile
+  // writes destination lane (token0 + l) % 64 of its tile or of the next;
+  // lanes past the last token zero their words up to the end of the last
+  // destination tile and write nothing beyond it
+  uint32_t *obase = a.packed + (int64_t)bz * a.ps_b + (int64_t)h * a.ps_h + (a.token0 >> 6) * W * 64;
+  const int ol = (int)(a.token0 & 63) + lane;
+  const uint32_t lofs = (uint32_t)((ol >> 6) * W * 64 + (ol & 63));
+  const int64_t send = ((a.token0 + a.n_tokens + 63) & ~(int64_t)63) - a.token0;
   // record words of this wave: w + NW i for i < nmine
   const int nmine = W > w ? (W - 1 - w) / NW + 1 : 0;
   int par = 0, rb = 0;
@@ -1446,6 +1466,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
       uint32_t *oprv = obase + (int64_t)(t - 1) * W * 64;
       const bool valid = (int64_t)t * 64 + lane < a.n_tokens;
       const bool pvalid = (int64_t)(t - 1) * 64 + lane < a.n_tokens;
+      const bool in = (int64_t)t * 64 + lane < send, pin = (int64_t)(t - 1) * 64 + lane < send;
       // words w + NW i, two at a time: this tile's (no QJL bits) or the
       // previous tile's; a slot past this wave's words reads and clears the
       // pad column rs - 1
@@ -1465,9 +1486,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
         for (int u = 0; u < 2; ++u) {
           const int i = i0 + u;
           const bool q = qmask >> i & 1u;
-          if (i < nmine && (!q || has_prev)) {
+          if (i < nmine && (!q || has_prev) && (q ? pin : in)) {
             uint32_t *o = q ? oprv : ocur;
-            o[(uint32_t)(w + NW * i) * 64u + lane] = (q ? pvalid : valid) ? v[u] : 0u;
+            o[(uint32_t)(w + NW * i) * 64u + lofs] = (q ? pvalid : valid) ? v[u] : 0u;
           }
         }
       }
@@ -1516,11 +1537,12 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   if (m > 0) {
     __syncthreads();
     uint32_t *rlast = rec0 + ((te - 1 - tb) % 3) * 64 * rs + lane * rs;
-    uint32_t *dst = obase + (int64_t)(te - 1) * W * 64 + lane;
+    uint32_t *dst = obase + (int64_t)(te - 1) * W * 64 + lofs;
     const bool valid = (int64_t)(te - 1) * 64 + lane < a.n_tokens;
+    const bool in = (int64_t)(te - 1) * 64 + lane < send;
 #pragma unroll
     for (int i = 0; i < C2_WMAX; ++i)
-      if ((qmask >> i & 1u) && i < nmine) dst[(int64_t)(w + NW * i) * 64] = valid ? rlast[w + NW * i] : 0u;
+      if ((qmask >> i & 1u) && i < nmine && in) dst[(int64_t)(w + NW * i) * 64] = valid ? rlast[w + NW * i] : 0u;
   }
 }
 
@@ -2442,28 +2464,35 @@ static int device_cu_count() {
   return v;
 }
 
-extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
-                                 int calib_batch_stride, const void *x, sq_dtype dt,
-                                 int64_t n_tokens, int64_t xs_batch, int64_t xs_head,
-                                 int64_t xs_token, uint32_t *packed, int64_t ps_batch,
-                                 int64_t ps_head, sq_stream stream) {
-  const char *fn = "sq_compress";
+// sq_compress and sq_compress_append: source token i of x goes to token slot
+// token0 + i of every head's packed slot.
+static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head, int n_heads, int batch,
+                               int calib_batch_stride, const void *x, sq_dtype dt, int64_t n_tokens,
+                               int64_t xs_batch, int64_t xs_head, int64_t xs_token, uint32_t *packed,
+                               int64_t ps_batch, int64_t ps_head, int64_t token0, sq_stream stream) {
+  const std::string f(fn);
   sq_status st = check_handle(c, fn);
   if (st != SQ_OK) return st;
   st = check_heads(c, first_head, n_heads, batch, calib_batch_stride, fn);
   if (st != SQ_OK) return st;
-  if (n_tokens < 0) return fail(SQ_ERR_ARG, "sq_compress: n_tokens < 0");
-  if (dt != SQ_F32 && dt != SQ_BF16) return fail(SQ_ERR_ARG, "sq_compress: bad dtype");
+  if (n_tokens < 0) return fail(SQ_ERR_ARG, f + ": n_tokens < 0");
+  if (token0 < 0) return fail(SQ_ERR_ARG, f + ": token0 < 0");
+  if (dt != SQ_F32 && dt != SQ_BF16) return fail(SQ_ERR_ARG, f + ": bad dtype");
   if (n_tokens == 0 || batch == 0) { clear_error(); return SQ_OK; }
-  if (!x || !packed) return fail(SQ_ERR_ARG, "sq_compress: NULL pointer");
-  st = check_slots(c, n_tokens, n_heads, batch, ps_batch, ps_head, fn);
+  if (!x || !packed) return fail(SQ_ERR_ARG, f + ": NULL pointer");
+  if (n_tokens > ((int64_t)1 << 36) || token0 > ((int64_t)1 << 36))
+    return fail(SQ_ERR_UNSUPPORTED, f + ": too many tokens");
+  st = check_slots(c, token0 + n_tokens, n_heads, batch, ps_batch, ps_head, fn);
   if (st != SQ_OK) return st;
   const int esz = dt == SQ_F32 ? 4 : 2;
   if (((uintptr_t)x % 16) || (xs_token * esz) % 16 || (xs_head * esz) % 16 || (xs_batch * esz) % 16)
-    return fail(SQ_ERR_ARG, "sq_compress: x and its strides must be 16-byte aligned");
+    return fail(SQ_ERR_ARG, f + ": x and its strides must be 16-byte aligned");
   const int d = c->heads[first_head].d;
-  if (xs_token < d) return fail(SQ_ERR_ARG, "sq_compress: xs_token < head_dim");
-  if (n_tokens > ((int64_t)1 << 36)) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many tokens");
+  if (xs_token < d) return fail(SQ_ERR_ARG, f + ": xs_token < head_dim");
+  // source tiles: enough to reach the end of the last destination tile (with
+  // token0 % 64 != 0 the last one only zero-fills the tail of that tile)
+  const int64_t send = ((token0 + n_tokens + 63) / 64) * 64 - token0;
+  const int n_src_tiles = (int)((send + 63) / 64);
   // LDS: threshold trees | signal centroids | x tile | y tile | word buffer
   int max_tree = 0, max_csig = 0, max_plan = 0, max_s = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
@@ -2515,9 +2544,10 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
         b2.xs_b = xs_batch; b2.xs_h = xs_head; b2.xs_t = xs_token;
         b2.ps_b = ps_batch; b2.ps_h = ps_head;
         b2.n_tokens = n_tokens;
+        b2.token0 = token0;
         b2.first_head = first_head;
         b2.cbs = calib_batch_stride;
-        b2.n_tiles = (int)((n_tokens + 63) / 64);
+        b2.n_tiles = n_src_tiles;
         // about 4 workgroups per CU, each a run of consecutive tiles of one
         // (batch entry, head)
         const int64_t want = (int64_t)device_cu_count() * 4;
@@ -2556,7 +2586,7 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   a.lds_b_off = a.lds_y_off + 64 * a.ys;
   const size_t lds = (size_t)(a.lds_b_off + 64 * a.bws) * 4;
   if (lds > limit)
-    return fail(SQ_ERR_UNSUPPORTED, "sq_compress: calibration tables exceed the LDS of one workgroup");
+    return fail(SQ_ERR_UNSUPPORTED, f + ": calibration tables exceed the LDS of one workgroup");
   a.heads = c->dev_heads;
   a.blob = (const uint8_t *)c->dev_blob;
   a.x = x;
@@ -2564,16 +2594,17 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
   a.xs_b = xs_batch; a.xs_h = xs_head; a.xs_t = xs_token;
   a.ps_b = ps_batch; a.ps_h = ps_head;
   a.n_tokens = n_tokens;
+  a.token0 = token0;
   a.first_head = first_head;
   a.cbs = calib_batch_stride;
-  a.n_tiles = (int)((n_tokens + 63) / 64);
+  a.n_tiles = n_src_tiles;
   const int gz = calib_batch_stride ? batch : 1;
   a.items = calib_batch_stride ? a.n_tiles : (int)std::min<int64_t>((int64_t)batch * a.n_tiles, INT32_MAX);
   // enough resident workgroups to keep every CU busy; each walks many tiles
   const int64_t want = (int64_t)device_cu_count() * (d >= 256 ? 1 : 2) * 2;
   int gx = (int)std::max<int64_t>(1, std::min<int64_t>(a.items, (want + (int64_t)n_heads * gz - 1) / ((int64_t)n_heads * gz)));
   dim3 grid(gx, n_heads, gz);
-  if (grid.y > 65535 || grid.z > 65535) return fail(SQ_ERR_UNSUPPORTED, "sq_compress: too many heads or batch entries");
+  if (grid.y > 65535 || grid.z > 65535) return fail(SQ_ERR_UNSUPPORTED, f + ": too many heads or batch entries");
   hipStream_t s = (hipStream_t)stream;
   const bool f32 = dt == SQ_F32;
   switch (d) {
@@ -2581,9 +2612,27 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
     case 64:  launch_compress_d<64>(f32, tg, grid, lds, s, a); break;
     case 128: launch_compress_d<128>(f32, tg, grid, lds, s, a); break;
     case 256: launch_compress_d<256>(f32, tg, grid, lds, s, a); break;
-    default: return fail(SQ_ERR_UNSUPPORTED, "sq_compress: head_dim");
+    default: return fail(SQ_ERR_UNSUPPORTED, f + ": head_dim");
   }
   return launched(fn);
+}
+
+extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
+                                 int calib_batch_stride, const void *x, sq_dtype dt,
+                                 int64_t n_tokens, int64_t xs_batch, int64_t xs_head,
+                                 int64_t xs_token, uint32_t *packed, int64_t ps_batch,
+                                 int64_t ps_head, sq_stream stream) {
+  return compress_impl("sq_compress", c, first_head, n_heads, batch, calib_batch_stride, x, dt, n_tokens,
+                       xs_batch, xs_head, xs_token, packed, ps_batch, ps_head, 0, stream);
+}
+
+extern "C" sq_status sq_compress_append(const sq_calib *c, int first_head, int n_heads, int batch,
+                                        int calib_batch_stride, const void *x, sq_dtype dt,
+                                        int64_t n_tokens, int64_t xs_batch, int64_t xs_head,
+                                        int64_t xs_token, uint32_t *packed, int64_t ps_batch,
+                                        int64_t ps_head, int64_t token0, sq_stream stream) {
+  return compress_impl("sq_compress_append", c, first_head, n_heads, batch, calib_batch_stride, x, dt,
+                       n_tokens, xs_batch, xs_head, xs_token, packed, ps_batch, ps_head, token0, stream);
 }
 
 template <int GR, int SLOTB, int R, bool LG>

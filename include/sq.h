@@ -170,6 +170,32 @@ sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
                       int64_t ps_head, sq_stream stream);
 
 /*
+ * sq_compress_append -- sq_compress of n_tokens new vectors into token slots
+ * token0 .. token0 + n_tokens - 1 of an existing packed cache: the decode-time
+ * producer of the compressed cache (SpectralQuant README "Overview": the
+ * method compresses the KV cache during inference; TurboQuant reference
+ * implementation page, "Key Findings" 5, "Compressed Storage": records are
+ * kept compressed, not simulated).  The record of a token depends only on
+ * its own vector, so appending in pieces gives the same words as one
+ * sq_compress over the whole sequence.
+ * x       DEVICE, as in sq_compress; token i of x is cache token token0 + i.
+ * packed  DEVICE, as in sq_compress; ps_head >=
+ *         sq_packed_head_words(c, token0 + n_tokens).  Written: the words of
+ *         tokens token0 .. token0 + n_tokens - 1, and zeros for the tokens
+ *         after them up to the end of their 64-token tile.  Tokens below
+ *         token0 and tiles past the last one are not touched.
+ * token0  >= 0, any alignment.  token0 == 0 is exactly sq_compress.
+ * Errors: token0 < 0 -> SQ_ERR_ARG; otherwise as sq_compress.
+ */
+sq_status sq_compress_append(const sq_calib *c, int first_head, int n_heads,
+                             int batch, int calib_batch_stride, const void *x,
+                             sq_dtype dt, int64_t n_tokens, int64_t xs_batch,
+                             int64_t xs_head, int64_t xs_token,
+                             uint32_t *packed, int64_t ps_batch,
+                             int64_t ps_head, int64_t token0,
+                             sq_stream stream);
+
+/*
  * sq_scores -- raw q.k scores read from the packed keys (no softmax scale).
  * The query of each query head is rotated once, q~ = R q; then
  *   s_t = sum_i q~_i C_i[code_ti] + sqrt(pi/2)/m * gamma_t * sum_j w_j (2 z_tj - 1),

@@ -172,6 +172,8 @@ def test_error_paths():
     # device calls on a handle that was never uploaded: rejected before any HIP call
     st = lib.sq_compress(cal.handle, 0, 1, 1, 0, None, 1, 64, 0, 0, d, None, 0, 64, None)
     assert st == 7 and b"upload" in lib.sq_last_error()
+    st = lib.sq_compress_append(cal.handle, 0, 1, 1, 0, None, 1, 64, 0, 0, d, None, 0, 64, 0, None)
+    assert st == 7 and b"sq_compress_append" in lib.sq_last_error()
     st = lib.sq_scores(None, 0, 0, 1, 4, 1, None, 1, None, 0, 0, 64, None, None)
     assert st == 1
     o = sq.CalibOpts()
