@@ -1747,26 +1747,31 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
   // A operands 0) so that the quads form one straight-line block.  Table
   // addresses are wave-uniform scalars; shifts and masks, also uniform, sit
   // in vector registers (the instructions using them take one scalar each),
-  // word addresses per lane.
-  uint32_t hsh[2 * SC_QMAX], hmk[2 * SC_QMAX], hlut[2 * SC_QMAX], wad[2 * SC_QMAX];
+  // word addresses per lane.  The two halves of a quad are adjacent fields
+  // spanning at most 16 bits, so one pair of record words (a 64-bit window
+  // starting at the word that holds the first field's bit - 3) serves both.
+  uint32_t hsh[2 * SC_QMAX], hmk[2 * SC_QMAX], hlut[2 * SC_QMAX], wad[SC_QMAX];
   uint2 aqa[SC_QMAX][GR], aqb[SC_QMAX][GR], aql[SC_QMAX][GR];
   const uint32_t tile_lds = a.lds_slot + tau * W * 256 + lane * 4;  // this stream's tile in slot 0
 #pragma unroll
   for (int qi = 0; qi < SC_QMAX; ++qi) {
     const bool real = qi < nq;
     const SQ_CONST uint32_t *e = sch + (size_t)(q0 + (real ? qi : 0)) * SCHED_WORDS;
+    // the window starts at the word holding bit pos0 - 3 of the first field
+    // (one row earlier when that field starts in the first 3 bits of a
+    // word), so that (window >> (pos - 3 - 32 j)) & (mask << 3) gives
+    // code * 8, the entry's byte offset; the second field starts at most
+    // 8 + 31 bits in and ends below bit 64 (an empty half has mask 0)
+    const int j = ((int)(e[0] & 0xFFFFu) - 3) >> 5;  // may be -1
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      // the 64-bit window starts 3 bits before the field (one row earlier
-      // when the field starts in the first 3 bits of a word), so that
-      // alignbit & (mask << 3) gives code * 8, the entry's byte offset
       const uint32_t pw = e[hh];
       const int pos = (int)(pw & 0xFFFFu) - 3, wd = (int)(pw >> 16);
-      hsh[2 * qi + hh] = to_vgpr((uint32_t)pos & 31u);
+      hsh[2 * qi + hh] = to_vgpr((uint32_t)(pos - 32 * j) & 63u);
       hmk[2 * qi + hh] = to_vgpr(real ? ((1u << wd) - 1u) << 3 : 0u);
       hlut[2 * qi + hh] = (LG ? 0u : (uint32_t)a.lds_lut) + e[2 + hh] * 8u;
-      wad[2 * qi + hh] = tile_lds + (uint32_t)(pos >> 5) * 256u;  // (pos >> 5) may be -1
     }
+    wad[qi] = tile_lds + (uint32_t)j * 256u;
     const uint32_t s01 = e[4], s23 = e[5];
     const uint32_t sl[4] = {s01 & 0xFFFFu, s01 >> 16, s23 & 0xFFFFu, s23 >> 16};
 #pragma unroll
@@ -1839,19 +1844,17 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
         for (int g = 0; g < GR; ++g) acc[t][g] = f32x4{0.f, 0.f, 0.f, 0.f};
       // three-stage pipeline over the quads: record words of quad it, joint
       // table entries of quad it - 1, MFMAs of quad it - 2
-      uint32_t wlo[SC_QMAX][NS][2], whi[SC_QMAX][NS][2];
+      uint32_t wlo[SC_QMAX][NS], whi[SC_QMAX][NS];
       uint2 ent[SC_QMAX][NS][2];
 #pragma unroll
       for (int it = 0; it < SC_QMAX + 2; ++it) {
         if (it < SC_QMAX) {
 #pragma unroll
-          for (int t = 0; t < NS; ++t)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const uint32_t ad = wad[2 * it + hh] + ((u * NS + t) % R) * SLOTB;
-              wlo[it][t][hh] = *(const uint32_t *)(sm + ad);
-              whi[it][t][hh] = *(const uint32_t *)(sm + ad + 256);
-            }
+          for (int t = 0; t < NS; ++t) {
+            const uint32_t ad = wad[it] + ((u * NS + t) % R) * SLOTB;
+            wlo[it][t] = *(const uint32_t *)(sm + ad);
+            whi[it][t] = *(const uint32_t *)(sm + ad + 256);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         if (it >= 1 && it - 1 < SC_QMAX) {
@@ -1861,8 +1864,11 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const int h = 2 * qi + hh;
-              // table base | code * 8 (tables are aligned to their size)
-              const uint32_t ea = (__builtin_amdgcn_alignbit(whi[qi][t][hh], wlo[qi][t][hh], hsh[h]) & hmk[h]) | hlut[h];
+              // table base | code * 8 (tables are aligned to their size); the
+              // first field's shift is below 32, the second's below 64
+              const uint32_t win = hh == 0 ? __builtin_amdgcn_alignbit(whi[qi][t], wlo[qi][t], hsh[h])
+                                           : (uint32_t)((((uint64_t)whi[qi][t] << 32) | wlo[qi][t]) >> hsh[h]);
+              const uint32_t ea = (win & hmk[h]) | hlut[h];
               if constexpr (LG) {
                 ent[qi][t][hh] = *(const uint2 *)((const uint8_t *)glut + ea);
               } else {  // the LDS area starts at address 0 (the launcher checks the kernel has no static LDS)
