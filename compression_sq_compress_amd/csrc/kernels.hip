@@ -2024,14 +2024,16 @@ enum { LM_COL = 0, LM_PACK = 1, LM_GLB = 2 };
 // NP = 64-coordinate blocks per head (head_dim / 64, at least 1): one wave
 // serves every block of its chunk, so the chunk's scores are read and its
 // softmax computed once.
-template <int G, int LM, int NP>
-__global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
+// WPB = waves (chunks) per workgroup, sharing the centroid tables: 8 with
+// column tables when the LDS allows, else 4.
+template <int G, int LM, int NP, int WPB>
+__global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) {
   extern __shared__ float smem[];
   constexpr int GR = (G + 3) / 4, GP = 4 * GR;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // a workgroup = 4 consecutive chunks of one (batch, KV head)
-  const int chunk = blockIdx.x * 4 + wv;
+  // a workgroup = WPB consecutive chunks of one (batch, KV head)
+  const int chunk = blockIdx.x * WPB + wv;
   const int hkv = blockIdx.y, b = blockIdx.z;
   const int ch = a.first_head + b * a.cbs + hkv;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
@@ -2065,14 +2067,14 @@ __global__ __launch_bounds__(256) void attend_partial_kernel(AttendArgs a) {
     const int base = p * a.lut_block;
     if constexpr (LM == LM_COL) {
       // column lane: entry f at f * 64 + lane; a zero-width lane reads 0 at f = 0
-      for (int k = wv; k < max(n, 1); k += 4) lut[base + k * 64 + lane] = n ? glut[lut0 + cbv + k] : 0u;
+      for (int k = wv; k < max(n, 1); k += WPB) lut[base + k * 64 + lane] = n ? glut[lut0 + cbv + k] : 0u;
       cb[p] = base + lane;
     } else if constexpr (LM == LM_PACK) {
       // coordinate c0 + j's table at offset cbv + j: lanes gathering the same
       // code from tables of equal size fall in different banks; the slot after
       // each table is 0, which a zero-width coordinate (field 0) reads
       if (ci < d) {  // lanes past the last coordinate (head_dim 32) write nothing
-        for (int k = wv; k < n; k += 4) lut[base + cbv + lane + k] = glut[lut0 + cbv + k];
+        for (int k = wv; k < n; k += WPB) lut[base + cbv + lane + k] = glut[lut0 + cbv + k];
         if (wv == 0) lut[base + cbv + lane + n] = 0u;
       }
       cb[p] = base + cbv + lane;
@@ -2779,28 +2781,41 @@ extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_
 
 // The column-table kernel addresses its tables at LDS address 0: true when
 // the kernel declares no static LDS (the dynamic area then starts at 0).
-template <int G, int NP>
+template <int G, int NP, int WPB>
 static bool attend_col_ok() {
   static const bool ok = [] {
     hipFuncAttributes fa{};
-    return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&attend_partial_kernel<G, LM_COL, NP>)) ==
+    return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&attend_partial_kernel<G, LM_COL, NP, WPB>)) ==
                hipSuccess && fa.sharedSizeBytes == 0;
   }();
   return ok;
 }
 
+// lm == LM_COL with wpb 8, or any placement with wpb 4 (the host checked
+// that the column kernel has no static LDS before choosing LM_COL)
 template <int G, int NP>
-static void launch_attend_np(int lm, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  if (lm == LM_COL && attend_col_ok<G, NP>()) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP>), grid, dim3(256), lds, s, a);
-  else if (lm == LM_PACK) hipLaunchKernelGGL((attend_partial_kernel<G, LM_PACK, NP>), grid, dim3(256), lds, s, a);
-  else hipLaunchKernelGGL((attend_partial_kernel<G, LM_GLB, NP>), grid, dim3(256), lds, s, a);
+static void launch_attend_np(int lm, int wpb, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
+  if (lm == LM_COL && wpb == 8) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP, 8>), grid, dim3(512), lds, s, a);
+  else if (lm == LM_COL) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP, 4>), grid, dim3(256), lds, s, a);
+  else if (lm == LM_PACK) hipLaunchKernelGGL((attend_partial_kernel<G, LM_PACK, NP, 4>), grid, dim3(256), lds, s, a);
+  else hipLaunchKernelGGL((attend_partial_kernel<G, LM_GLB, NP, 4>), grid, dim3(256), lds, s, a);
+}
+
+template <int G, int NP>
+static bool attend_col_ok_np(int wpb) {
+  return wpb == 8 ? attend_col_ok<G, NP, 8>() : attend_col_ok<G, NP, 4>();
 }
 
 template <int G>
-static void launch_attend(int lm, int np, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  if (np == 1) launch_attend_np<G, 1>(lm, grid, lds, s, a);
-  else if (np == 2) launch_attend_np<G, 2>(lm, grid, lds, s, a);
-  else launch_attend_np<G, 4>(lm, grid, lds, s, a);
+static bool attend_col_ok_g(int np, int wpb) {
+  return np == 1 ? attend_col_ok_np<G, 1>(wpb) : np == 2 ? attend_col_ok_np<G, 2>(wpb) : attend_col_ok_np<G, 4>(wpb);
+}
+
+template <int G>
+static void launch_attend(int lm, int np, int wpb, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
+  if (np == 1) launch_attend_np<G, 1>(lm, wpb, grid, lds, s, a);
+  else if (np == 2) launch_attend_np<G, 2>(lm, wpb, grid, lds, s, a);
+  else launch_attend_np<G, 4>(lm, wpb, grid, lds, s, a);
 }
 
 extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride, int batch,
@@ -2849,7 +2864,7 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   a.n_chunks = (int)((n_tokens + ATT_CHUNK - 1) / ATT_CHUNK);
   const int np = (d + 63) / 64;  // 64-coordinate blocks, all served by one wave
   if (np != 1 && np != 2 && np != 4) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: unsupported head_dim");
-  // LDS: centroid tables of the blocks | 4 x (two staging buffers, weights)
+  // LDS: centroid tables of the blocks | ATT_WAVES x (two staging buffers, weights)
   int max_lut = 1, max_wd = 1, max_w = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
     for (int h = 0; h < n_kv_heads; ++h) {
@@ -2868,42 +2883,61 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   const int limit = device_lds_limit();
   a.buf_floats = (max_wd + 2) * ATT_RS + G * 64;
   a.wave_floats = 2 * a.buf_floats + 2 * GP * ATT_PS;
-  auto lds_for = [&](int block_floats) {
+  auto lds_for = [&](int block_floats, int wpb) {
     a.lut_block = block_floats;
     a.lds_wave_off = (np * block_floats + 3) & ~3;
-    return (size_t)(a.lds_wave_off + 4 * a.wave_floats) * 4;
+    return (size_t)(a.lds_wave_off + wpb * a.wave_floats) * 4;
   };
-  // table placement: column tables (conflict-free) unless packed tables let
-  // more workgroups share a CU
-  int lm = LM_GLB;
+  auto col_ok = [&](int wpb) {
+    switch (G) {
+      case 1: return attend_col_ok_g<1>(np, wpb);
+      case 2: return attend_col_ok_g<2>(np, wpb);
+      case 3: return attend_col_ok_g<3>(np, wpb);
+      case 4: return attend_col_ok_g<4>(np, wpb);
+      case 5: return attend_col_ok_g<5>(np, wpb);
+      case 6: return attend_col_ok_g<6>(np, wpb);
+      case 7: return attend_col_ok_g<7>(np, wpb);
+      default: return attend_col_ok_g<8>(np, wpb);
+    }
+  };
+  // table placement: column tables (conflict-free), shared by 8 waves when
+  // that keeps as many waves per CU as 4-wave workgroups would (fewer table
+  // copies); else 4-wave workgroups with column tables unless packed tables
+  // let more of them share a CU
+  int lm = LM_GLB, wpb = 4;
   size_t lds = 0;
-  const size_t cap = (size_t)std::min(limit, 64 * 1024);
-  const size_t lds_col = max_w <= 6 ? lds_for(64 << max_w) : cap + 1;
-  const size_t lds_pack = lds_for(max_lut + 64);
   const size_t cu_lds = (size_t)limit;  // one workgroup may use all of a CU's LDS
-  if (lds_col <= cap && cu_lds / lds_col >= cu_lds / lds_pack) {
+  const size_t cap = (size_t)std::min(limit, 64 * 1024);
+  const size_t lds_col = max_w <= 6 ? lds_for(64 << max_w, 4) : cap + 1;
+  const size_t lds_col8 = max_w <= 6 ? lds_for(64 << max_w, 8) : cu_lds + 1;
+  const size_t lds_pack = lds_for(max_lut + 64, 4);
+  if (lds_col8 <= cu_lds && 8 * (cu_lds / lds_col8) >= 4 * (cu_lds / std::min(lds_col, lds_pack)) && col_ok(8)) {
     lm = LM_COL;
-    lds = lds_for(64 << max_w);
+    wpb = 8;
+    lds = lds_for(64 << max_w, 8);
+  } else if (lds_col <= cap && cu_lds / lds_col >= cu_lds / lds_pack && col_ok(4)) {
+    lm = LM_COL;
+    lds = lds_for(64 << max_w, 4);
   } else if (lds_pack <= cap) {
     lm = LM_PACK;
-    lds = lds_for(max_lut + 64);
+    lds = lds_for(max_lut + 64, 4);
   } else {
-    lds = lds_for(0);
+    lds = lds_for(0, 4);
   }
   if (lds > (size_t)limit) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: tables exceed LDS");
-  const int64_t cgroups = (a.n_chunks + 3) / 4;
+  const int64_t cgroups = (a.n_chunks + wpb - 1) / wpb;
   dim3 grid((unsigned)cgroups, n_kv_heads, batch);
   if (grid.z > 65535 || grid.y > 65535 || cgroups > INT32_MAX)
     return fail(SQ_ERR_UNSUPPORTED, "sq_attend: grid too large");
   switch (G) {
-    case 1: launch_attend<1>(lm, np, grid, lds, s, a); break;
-    case 2: launch_attend<2>(lm, np, grid, lds, s, a); break;
-    case 3: launch_attend<3>(lm, np, grid, lds, s, a); break;
-    case 4: launch_attend<4>(lm, np, grid, lds, s, a); break;
-    case 5: launch_attend<5>(lm, np, grid, lds, s, a); break;
-    case 6: launch_attend<6>(lm, np, grid, lds, s, a); break;
-    case 7: launch_attend<7>(lm, np, grid, lds, s, a); break;
-    case 8: launch_attend<8>(lm, np, grid, lds, s, a); break;
+    case 1: launch_attend<1>(lm, np, wpb, grid, lds, s, a); break;
+    case 2: launch_attend<2>(lm, np, wpb, grid, lds, s, a); break;
+    case 3: launch_attend<3>(lm, np, wpb, grid, lds, s, a); break;
+    case 4: launch_attend<4>(lm, np, wpb, grid, lds, s, a); break;
+    case 5: launch_attend<5>(lm, np, wpb, grid, lds, s, a); break;
+    case 6: launch_attend<6>(lm, np, wpb, grid, lds, s, a); break;
+    case 7: launch_attend<7>(lm, np, wpb, grid, lds, s, a); break;
+    case 8: launch_attend<8>(lm, np, wpb, grid, lds, s, a); break;
   }
   sq_status s1 = launched(fn);
   if (s1 != SQ_OK) return s1;
