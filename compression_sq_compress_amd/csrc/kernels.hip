@@ -1952,7 +1952,7 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
 // ------------------------------------------------------------------ attend
 //
 // Split-T softmax-weighted value sum in the rotated value space.  Kernel 1:
-// one wave per (batch, KV head, chunk of ATT_CHUNK tokens), lane = coordinate
+// one wave per (batch, KV head, chunk of tokens), lane = coordinate
 // within each block of 64 eigen-coordinates.  Per 64-token tile the record
 // words are staged straight from HBM into LDS (word-major, row stride
 // ATT_RS, so lanes reading different words of one token hit different
@@ -1967,7 +1967,12 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
 // (batch, query head) combines the chunks in order (no atomics,
 // deterministic) and un-rotates once: o = R_v^T o_rot / L.
 
-static constexpr int ATT_CHUNK = 1024;
+// Tokens per chunk: 2048 when that still gives about two waves per CU or
+// more (fewer partials to combine and table loads), else 1024.  A function of
+// (batch, query heads, tokens) only, so the workspace size follows it.
+static int64_t attend_chunk_tokens(int batch, int n_q_heads, int64_t n_tokens) {
+  return (int64_t)batch * n_q_heads * (n_tokens / 2048) >= 4096 ? 2048 : 1024;
+}
 static constexpr int ATT_RS = 68;  // staged record row stride (words): 16-byte aligned, bank-spread
 static constexpr int ATT_PS = 68;  // weight row stride (words): rows of different heads in different banks
 static constexpr float ATT_TAU = 8.0f;  // lazy-rescale margin of the running softmax max
@@ -1985,6 +1990,7 @@ struct AttendArgs {
   int first_head, cbs;
   int n_q_heads, n_kv_heads;
   int n_chunks;
+  int chunk_tokens;            // tokens per chunk (a multiple of 64)
   int lut_block;               // floats: stride of the 64-coordinate blocks' centroid tables
   int lds_wave_off;            // floats: per-wave areas (the centroid tables start at 0)
   int wave_floats;             // one wave's area: two staging buffers, then the weights
@@ -2099,8 +2105,8 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   __syncthreads();
   if (chunk >= a.n_chunks) return;  // no barrier follows
 
-  const int64_t tb = (int64_t)chunk * ATT_CHUNK;
-  const int64_t te = min(a.n_tokens, tb + ATT_CHUNK);
+  const int64_t tb = (int64_t)chunk * a.chunk_tokens;
+  const int64_t te = min(a.n_tokens, tb + a.chunk_tokens);
   const float *srow = a.scores + ((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * a.n_tokens;
   const uint32_t *slot = a.vpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
   float mrun[G], lsum[G];
@@ -2775,7 +2781,8 @@ extern "C" sq_status sq_scores(const sq_calib *kc, int first_head, int calib_bat
 
 extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_tokens, int head_dim) {
   if (batch <= 0 || n_q_heads <= 0 || n_tokens <= 0 || head_dim <= 0) return 0;
-  const int64_t nch = (n_tokens + ATT_CHUNK - 1) / ATT_CHUNK;
+  const int64_t ct = attend_chunk_tokens(batch, n_q_heads, n_tokens);
+  const int64_t nch = (n_tokens + ct - 1) / ct;
   return (size_t)batch * n_q_heads * nch * (head_dim + 2) * sizeof(float);
 }
 
@@ -2861,7 +2868,8 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   if (ws_bytes < sq_attend_workspace_bytes(batch, n_q_heads, n_tokens, d))
     return fail(SQ_ERR_ARG, "sq_attend: workspace too small");
   a.ws = (float *)workspace;
-  a.n_chunks = (int)((n_tokens + ATT_CHUNK - 1) / ATT_CHUNK);
+  a.chunk_tokens = (int)attend_chunk_tokens(batch, n_q_heads, n_tokens);
+  a.n_chunks = (int)((n_tokens + a.chunk_tokens - 1) / a.chunk_tokens);
   const int np = (d + 63) / 64;  // 64-coordinate blocks, all served by one wave
   if (np != 1 && np != 2 && np != 4) return fail(SQ_ERR_UNSUPPORTED, "sq_attend: unsupported head_dim");
   // LDS: centroid tables of the blocks | ATT_WAVES x (two staging buffers, weights)

@@ -134,3 +134,36 @@ def test_append_argument_errors(torch_dev, sq):
         sq.sq_compress_append(cal, x, slot, 62)
     torch.cuda.synchronize()
     assert torch.all(slot == SENTINEL)
+
+
+def test_append_batched_per_layer_calibration_strided_input(torch_dev, sq):
+    """batch = 2 layers addressed through the calibration batch stride, input
+    in [T][H][d] storage viewed as [H][T][d] (strided), appended in pieces:
+    the same words as one sq_compress of the whole sequence."""
+    torch = torch_dev
+    _case("append qwen14b k: 2 layers (stride 4), strided input, pieces [1, 70, 1, 56]")
+    cfg = wl.CONFIGS["qwen14b"]
+    lheads = [(l, h) for l in (20, 21) for h in range(4)]
+    cal, ors = H.calibrate_both(sq, cfg, lheads, "k", 2.5)
+    cal.upload()
+    T, pieces = 128, [1, 70, 1, 56]
+    xl = np.stack([H.data_block(cfg, lheads[4 * b:4 * b + 4], "k", T) for b in range(2)])  # [B][H][T][d]
+    xd = _dev(torch, np.ascontiguousarray(xl.transpose(0, 2, 1, 3)), torch.bfloat16).permute(0, 2, 1, 3)
+    assert not xd.is_contiguous()
+    words = cal.packed_head_words(T)
+    whole = torch.zeros((2, 4, words), dtype=torch.int32, device="cuda")
+    sq.sq_compress(cal, xd, whole, calib_batch_stride=4)
+    inc = torch.full((2, 4, words), SENTINEL, dtype=torch.int32, device="cuda")
+    t0 = 0
+    for n in pieces:
+        sq.sq_compress_append(cal, xd[:, :, t0:t0 + n], inc, t0, calib_batch_stride=4)
+        t0 += n
+    torch.cuda.synchronize()
+    wn = whole.cpu().numpy().view(np.uint32)
+    gn = inc.cpu().numpy().view(np.uint32)
+    for b in range(2):
+        for h in range(4):
+            oc = ors[4 * b + h]
+            used = 2 * 64 * oc.W
+            assert np.array_equal(gn[b, h, :used], wn[b, h, :used]), f"batch {b} head {h}"
+            H.compare_compress(oc, gn[b, h], xl[b, h], T)

@@ -183,6 +183,9 @@ def test_error_paths():
 
 
 def test_workspace_size_formula():
-    assert sq.sq_attend_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * 32 * 130 * 4
+    # [batch][q head][chunk][d + 2] fp32; chunks of 2048 tokens when batch * q heads *
+    # (tokens / 2048) >= 4096, else 1024
+    assert sq.sq_attend_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * 16 * 130 * 4
+    assert sq.sq_attend_workspace_bytes(1, 32, 32768, 128) == 32 * 32 * 130 * 4
     assert sq.sq_attend_workspace_bytes(1, 4, 1, 32) == 4 * 1 * 34 * 4
     assert sq.sq_attend_workspace_bytes(1, 4, 0, 32) == 0
