@@ -2030,9 +2030,10 @@ enum { LM_COL = 0, LM_PACK = 1, LM_GLB = 2 };
 // NP = 64-coordinate blocks per head (head_dim / 64, at least 1): one wave
 // serves every block of its chunk, so the chunk's scores are read and its
 // softmax computed once.
-// WPB = waves (chunks) per workgroup, sharing the centroid tables: 8 with
-// column tables when the LDS allows, else 4.
-template <int G, int LM, int NP, int WPB>
+// WPB = waves (chunks) per workgroup, sharing the centroid tables; NBUF =
+// staging buffers per wave.  Column tables: 16 single-buffered waves (four
+// per SIMD) when the LDS allows, else 8 double-buffered; otherwise 4.
+template <int G, int LM, int NP, int WPB, int NBUF = 2>
 __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) {
   extern __shared__ float smem[];
   constexpr int GR = (G + 3) / 4, GP = 4 * GR;
@@ -2047,7 +2048,7 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
   uint32_t *lut = (uint32_t *)smem;
   float *stage = smem + a.lds_wave_off + wv * a.wave_floats;  // two buffers: words, then scores
-  uint32_t *ph = (uint32_t *)(stage + 2 * a.buf_floats);      // [GP][ATT_PS] bf16 hi of p, twice
+  uint32_t *ph = (uint32_t *)(stage + NBUF * a.buf_floats);   // [GP][ATT_PS] bf16 hi of p, twice
   uint32_t *pl = ph + GP * ATT_PS;                             // [GP][ATT_PS] bf16 lo of p, twice
   const uint32_t *glut = (const uint32_t *)(a.blob + hd->off_lutp);
   // this lane's field in each block p (coordinate 64 p + lane)
@@ -2125,11 +2126,13 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
 #pragma unroll
       for (int r = 0; r < GR; ++r) acc[p][h][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Staging, double-buffered: the W words of the tile's records (plus one
-  // spare row, a copy of the last word: the word after a field never goes
-  // past it) and its G score rows go straight from HBM to LDS; tile i + 1 is
-  // requested before tile i is computed, so the one wait per tile covers
-  // loads issued a whole tile earlier.
+  // Staging: the W words of the tile's records (plus one spare row, a copy
+  // of the last word: the word after a field never goes past it) and its G
+  // score rows go straight from HBM to LDS.  Double-buffered (NBUF 2), tile
+  // i + 1 is requested before tile i is computed, so the one wait per tile
+  // covers loads issued a whole tile earlier; single-buffered (NBUF 1), a
+  // tile is requested when the previous one is done and the other waves of
+  // the SIMD cover the wait.
   auto stage_tile = [&](int64_t t0, int buf) {
     uint32_t *rw = (uint32_t *)(stage + buf * a.buf_floats) + ATT_RS;  // row 1 = word 0
     const uint32_t *src = slot + (t0 >> 6) * W * 64 + lane;
@@ -2146,13 +2149,15 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   };
   // row 0 of both staging buffers: zeros (the word before word 0)
   ((uint32_t *)stage)[lane] = 0u;
-  ((uint32_t *)(stage + a.buf_floats))[lane] = 0u;
-  stage_tile(tb, 0);
+  if constexpr (NBUF == 2) ((uint32_t *)(stage + a.buf_floats))[lane] = 0u;
+  if constexpr (NBUF == 2) stage_tile(tb, 0);
   int buf = 0;
-  for (int64_t t0 = tb; t0 < te; t0 += 64, buf ^= 1) {
+  for (int64_t t0 = tb; t0 < te; t0 += 64, buf ^= NBUF - 1) {
+    if constexpr (NBUF == 1) stage_tile(t0, 0);  // (the last sync of the previous tile ended its reads)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this tile's staging has landed
     wave_lds_sync();
-    if (t0 + 64 < te) stage_tile(t0 + 64, buf ^ 1);
+    if constexpr (NBUF == 2)
+      if (t0 + 64 < te) stage_tile(t0 + 64, buf ^ 1);
     const uint32_t *rec = (const uint32_t *)(stage + buf * a.buf_floats);
     const float *sr = stage + buf * a.buf_floats + (W + 2) * ATT_RS;
     // ---- online softmax over the tile (lane = token)
@@ -2788,21 +2793,23 @@ extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_
 
 // The column-table kernel addresses its tables at LDS address 0: true when
 // the kernel declares no static LDS (the dynamic area then starts at 0).
-template <int G, int NP, int WPB>
+template <int G, int NP, int WPB, int NBUF = 2>
 static bool attend_col_ok() {
   static const bool ok = [] {
     hipFuncAttributes fa{};
-    return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&attend_partial_kernel<G, LM_COL, NP, WPB>)) ==
+    return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&attend_partial_kernel<G, LM_COL, NP, WPB, NBUF>)) ==
                hipSuccess && fa.sharedSizeBytes == 0;
   }();
   return ok;
 }
 
-// lm == LM_COL with wpb 8, or any placement with wpb 4 (the host checked
-// that the column kernel has no static LDS before choosing LM_COL)
+// lm == LM_COL with wpb 16 (single-buffered) or 8, or any placement with wpb
+// 4 (the host checked that the column kernel has no static LDS before
+// choosing LM_COL)
 template <int G, int NP>
 static void launch_attend_np(int lm, int wpb, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  if (lm == LM_COL && wpb == 8) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP, 8>), grid, dim3(512), lds, s, a);
+  if (lm == LM_COL && wpb == 16) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP, 16, 1>), grid, dim3(1024), lds, s, a);
+  else if (lm == LM_COL && wpb == 8) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP, 8>), grid, dim3(512), lds, s, a);
   else if (lm == LM_COL) hipLaunchKernelGGL((attend_partial_kernel<G, LM_COL, NP, 4>), grid, dim3(256), lds, s, a);
   else if (lm == LM_PACK) hipLaunchKernelGGL((attend_partial_kernel<G, LM_PACK, NP, 4>), grid, dim3(256), lds, s, a);
   else hipLaunchKernelGGL((attend_partial_kernel<G, LM_GLB, NP, 4>), grid, dim3(256), lds, s, a);
@@ -2810,7 +2817,7 @@ static void launch_attend_np(int lm, int wpb, dim3 grid, size_t lds, hipStream_t
 
 template <int G, int NP>
 static bool attend_col_ok_np(int wpb) {
-  return wpb == 8 ? attend_col_ok<G, NP, 8>() : attend_col_ok<G, NP, 4>();
+  return wpb == 16 ? attend_col_ok<G, NP, 16, 1>() : wpb == 8 ? attend_col_ok<G, NP, 8>() : attend_col_ok<G, NP, 4>();
 }
 
 template <int G>
@@ -2908,10 +2915,11 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
       default: return attend_col_ok_g<8>(np, wpb);
     }
   };
-  // table placement: column tables (conflict-free), shared by 8 waves when
-  // that keeps as many waves per CU as 4-wave workgroups would (fewer table
-  // copies); else 4-wave workgroups with column tables unless packed tables
-  // let more of them share a CU
+  // table placement: column tables (conflict-free), shared by 16 waves with
+  // one staging buffer each when that fits a CU (four waves per SIMD), else
+  // by 8 double-buffered waves when that keeps as many waves per CU as
+  // 4-wave workgroups would (fewer table copies); else 4-wave workgroups with
+  // column tables unless packed tables let more of them share a CU
   int lm = LM_GLB, wpb = 4;
   size_t lds = 0;
   const size_t cu_lds = (size_t)limit;  // one workgroup may use all of a CU's LDS
@@ -2919,7 +2927,16 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   const size_t lds_col = max_w <= 6 ? lds_for(64 << max_w, 4) : cap + 1;
   const size_t lds_col8 = max_w <= 6 ? lds_for(64 << max_w, 8) : cu_lds + 1;
   const size_t lds_pack = lds_for(max_lut + 64, 4);
-  if (lds_col8 <= cu_lds && 8 * (cu_lds / lds_col8) >= 4 * (cu_lds / std::min(lds_col, lds_pack)) && col_ok(8)) {
+  const int wf2 = a.wave_floats, wf1 = a.buf_floats + 2 * GP * ATT_PS;
+  a.wave_floats = wf1;
+  const size_t lds_col16 = max_w <= 6 ? lds_for(64 << max_w, 16) : cu_lds + 1;
+  a.wave_floats = wf2;
+  if (lds_col16 <= cu_lds && col_ok(16)) {
+    lm = LM_COL;
+    wpb = 16;
+    a.wave_floats = wf1;
+    lds = lds_for(64 << max_w, 16);
+  } else if (lds_col8 <= cu_lds && 8 * (cu_lds / lds_col8) >= 4 * (cu_lds / std::min(lds_col, lds_pack)) && col_ok(8)) {
     lm = LM_COL;
     wpb = 8;
     lds = lds_for(64 << max_w, 8);
