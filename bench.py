@@ -16,6 +16,8 @@ are reported beside it.
 
 Every launch goes to one dedicated stream (default priority); the per-kernel
 times come from HIP events recorded on that stream around each launch.
+After the timed steps (outside them) the decode-time append is timed: one
+new token per (sequence, KV head) for K and V through sq_compress_append.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                        [--cpu-sample-seqs 4] [--copy-ref-mb 0]
