@@ -1952,15 +1952,17 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
 // ------------------------------------------------------------------ attend
 //
 // Split-T softmax-weighted value sum in the rotated value space.  Kernel 1:
-// one wave per (batch, KV head, chunk of tokens), lane = coordinate
-// within each block of 64 eigen-coordinates.  Per 64-token tile the record
+// one wave per (batch, KV head, chunk of tokens); in pass p of the
+// head_dim / 64 passes a lane serves one coordinate (with column tables
+// coordinate NP lane + p, so a lane's fields share their record words; else
+// 64 p + lane).  Per 64-token tile the record
 // words are staged straight from HBM into LDS (word-major, row stride
 // ATT_RS, so lanes reading different words of one token hit different
 // banks); the query group's scores give an online softmax (running max,
 // rescaled sums) whose weights p are kept in LDS as bf16 hi/lo pairs, once
-// for all blocks.  Each lane decodes its coordinate for 4 tokens at a time into C_v[code] as
+// for all passes.  Each lane decodes its coordinate for 4 tokens at a time into C_v[code] as
 // bf16 hi/lo pairs and v_mfma_f32_4x4x4_16b_bf16 forms sum_t p_t C_v[code_t]:
-// in block b, lane 4b+n supplies the 4 tokens of coordinate 4b+n (B operand),
+// in block b, lane 4b+n supplies the 4 tokens of its coordinate (B operand),
 // lane 4b+m the weights of query head m (A operand), and the accumulator of
 // lane 4b+n holds head m in register m.  Three products (hi*hi + hi*lo +
 // lo*hi) give each term to ~2^-16 relative.  Kernel 2: one workgroup per
@@ -2051,18 +2053,20 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   uint32_t *ph = (uint32_t *)(stage + NBUF * a.buf_floats);   // [GP][ATT_PS] bf16 hi of p, twice
   uint32_t *pl = ph + GP * ATT_PS;                             // [GP][ATT_PS] bf16 lo of p, twice
   const uint32_t *glut = (const uint32_t *)(a.blob + hd->off_lutp);
-  // this lane's field in each block p (coordinate 64 p + lane)
+  // this lane's field in each block p: coordinate NP lane + p with column
+  // tables (the lane's NP fields are adjacent in the record), else 64 p + lane
   int cb[NP], cwl[NP], cs[NP];
   uint32_t fmask[NP];
   bool straddle[NP];
-  // column tables: the field is taken from the 64-bit window of staged rows
-  // wrow, wrow + 1 that starts 8 bits below it, so that one shift and one
-  // and-or give the entry's byte address (field << 8 | lane << 2 | block base)
-  int wrow[NP];
+  // column tables: the lane's fields are taken from one 64-bit window of
+  // staged rows wrow, wrow + 1 that starts 8 bits below the first, so that
+  // one shift and one and-or give each entry's byte address (field << 8 |
+  // lane << 2 | block base); NP fields of at most 6 bits end below bit 64
+  int wrow = 1;
   uint32_t wsh[NP], m8[NP], orv[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int c0 = p * 64, ci = c0 + lane;
+    const int c0 = p * 64, ci = LM == LM_COL ? NP * lane + p : c0 + lane;
     const int lut0 = c0 < d ? coords[c0].cent_base : 0;
     int width = 0, bo = 0, cbv = 0;
     if (ci < d) {
@@ -2093,8 +2097,8 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
     cs[p] = bo & 31;
     straddle[p] = cs[p] + width > 32;
     // staged row 0 is zero (the word before word 0), row w + 1 is word w
-    wrow[p] = width ? ((bo - 8) >> 5) + 1 : 1;
-    wsh[p] = width ? (uint32_t)(bo - 8) & 31u : 0u;
+    if (p == 0) wrow = ci < d ? ((bo - 8) >> 5) + 1 : 1;
+    wsh[p] = ci < d ? (uint32_t)(bo - 8 - 32 * (wrow - 1)) & 63u : 0u;
     m8[p] = fmask[p] << 8;
     orv[p] = ((uint32_t)lane << 2) | ((uint32_t)(p * a.lut_block) << 2);
   }
@@ -2211,23 +2215,30 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
         al[r][0] = make_uint2(al0.x, al0.y); al[r][1] = make_uint2(al0.z, al0.w);
         al[r][2] = make_uint2(al1.x, al1.y); al[r][3] = make_uint2(al1.z, al1.w);
       }
+      uint4 a0, a1, b0, b1;  // column tables: this lane's window rows for the 8 tokens
+      if constexpr (LM == LM_COL) {
+        const uint32_t *ra = rec + wrow * ATT_RS, *rb = ra + ATT_RS;
+        a0 = *(const uint4 *)(ra + k); a1 = *(const uint4 *)(ra + k + 4);
+        b0 = *(const uint4 *)(rb + k); b1 = *(const uint4 *)(rb + k + 4);
+      }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         uint32_t pr[8];
         if constexpr (LM == LM_COL) {
-          const uint32_t *ra = rec + wrow[p] * ATT_RS, *rb = ra + ATT_RS;
-          const uint4 a0 = *(const uint4 *)(ra + k), a1 = *(const uint4 *)(ra + k + 4);
-          const uint4 b0 = *(const uint4 *)(rb + k), b1 = *(const uint4 *)(rb + k + 4);
           const uint32_t s = wsh[p], mk = m8[p], ov = orv[p];
+          // the first field's shift is below 32, a later one's below 64
+          auto win = [&](uint32_t hi, uint32_t lo) __attribute__((always_inline)) {
+            return p == 0 ? __builtin_amdgcn_alignbit(hi, lo, s) : (uint32_t)((((uint64_t)hi << 32) | lo) >> s);
+          };
           uint32_t ix[8];  // byte offsets of the entries from the start of the tables
-          ix[0] = (__builtin_amdgcn_alignbit(b0.x, a0.x, s) & mk) | ov;
-          ix[1] = (__builtin_amdgcn_alignbit(b0.y, a0.y, s) & mk) | ov;
-          ix[2] = (__builtin_amdgcn_alignbit(b0.z, a0.z, s) & mk) | ov;
-          ix[3] = (__builtin_amdgcn_alignbit(b0.w, a0.w, s) & mk) | ov;
-          ix[4] = (__builtin_amdgcn_alignbit(b1.x, a1.x, s) & mk) | ov;
-          ix[5] = (__builtin_amdgcn_alignbit(b1.y, a1.y, s) & mk) | ov;
-          ix[6] = (__builtin_amdgcn_alignbit(b1.z, a1.z, s) & mk) | ov;
-          ix[7] = (__builtin_amdgcn_alignbit(b1.w, a1.w, s) & mk) | ov;
+          ix[0] = (win(b0.x, a0.x) & mk) | ov;
+          ix[1] = (win(b0.y, a0.y) & mk) | ov;
+          ix[2] = (win(b0.z, a0.z) & mk) | ov;
+          ix[3] = (win(b0.w, a0.w) & mk) | ov;
+          ix[4] = (win(b1.x, a1.x) & mk) | ov;
+          ix[5] = (win(b1.y, a1.y) & mk) | ov;
+          ix[6] = (win(b1.z, a1.z) & mk) | ov;
+          ix[7] = (win(b1.w, a1.w) & mk) | ov;
           // the tables open the kernel's LDS (the launcher checks that the
           // kernel has no static LDS), so the offsets are LDS addresses
           typedef const __attribute__((address_space(3))) uint32_t lds_u32;
@@ -2269,7 +2280,7 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   float *dst = a.ws + (((int64_t)b * a.n_q_heads + (int64_t)hkv * G) * a.n_chunks + chunk) * (d + 2);
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int ci = p * 64 + lane;
+    const int ci = LM == LM_COL ? NP * lane + p : p * 64 + lane;
     if (ci < d) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -2792,13 +2803,14 @@ extern "C" size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_
 }
 
 // The column-table kernel addresses its tables at LDS address 0: true when
-// the kernel declares no static LDS (the dynamic area then starts at 0).
+// the kernel declares no static LDS (the dynamic area then starts at 0).  The
+// 16-wave kernel (at most 128 VGPRs) is taken only where it needs no scratch.
 template <int G, int NP, int WPB, int NBUF = 2>
 static bool attend_col_ok() {
   static const bool ok = [] {
     hipFuncAttributes fa{};
     return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&attend_partial_kernel<G, LM_COL, NP, WPB, NBUF>)) ==
-               hipSuccess && fa.sharedSizeBytes == 0;
+               hipSuccess && fa.sharedSizeBytes == 0 && (WPB < 16 || fa.localSizeBytes == 0);
   }();
   return ok;
 }
