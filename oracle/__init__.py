@@ -38,19 +38,29 @@ from .record import record_words, field_offsets, pack, unpack  # noqa: F401
 from .turboquant import tq_prod_keys, tq_mse_values, tq_mse_unit  # noqa: F401
 from .metrics import cosine, rel_mse, bits_per_coord, compression_ratio  # noqa: F401
 
-# Every oracle function is pinned by at least one test in tests/test_oracle_*.py
-# against something other than itself (closed forms, printed values, brute
-# force, invariants).  The exceptions are listed here and in the design notes.
+# Pin map: every oracle function and the tests that hold it to something other
+# than itself (closed forms, printed values, brute force, invariants).  A
+# function with no such test would be listed as "parity unpinned"; none is.
 PARITY = {
-    "calibrate": "pinned",
-    "lloyd_max_samples": "pinned",
-    "lloyd_max_gaussian": "pinned",
-    "water_fill": "pinned",
-    "compress": "pinned",
-    "dequantize": "pinned",
-    "scores_plain": "pinned",
-    "scores_rotated": "pinned",
-    "attend": "pinned",
-    "pack/unpack": "pinned",
-    "tq_prod_keys/tq_mse_values": "pinned",
+    "second_moment": "pinned: test_second_moment_is_uncentered",
+    "eigenbasis": "pinned: planted-basis recovery, R R^T = I, eigen-residuals, sign rule",
+    "participation_ratio/effective_dim": "pinned: identity, isotropic rank-k, Wishart mean, "
+                                         "half-to-even rounding, PR <= rank",
+    "spectral_gap": "pinned: test_spectral_gap",
+    "water_fill": "pinned: brute-force optimum, monotone widths, real-valued water level, caps, ties",
+    "regions": "pinned: hand-worked map; uniform vs Gaussian laws at equal width give the "
+               "closed-form Lloyd-Max levels of each law (test_oracle_regions_bands_tq.py)",
+    "lloyd_max_samples": "pinned: midpoint and cell-mean conditions by direct masks, "
+                         "convergence to Max (1960)",
+    "lloyd_max_gaussian/gaussian_distortion": "pinned: Max (1960) table, closed form vs sampling",
+    "quantize": "pinned: brute-force nearest centroid, tie and NaN rules",
+    "compress (QJL, gamma)": "pinned: estimator mean and variance over 6000 sketches",
+    "dequantize/scores_plain/scores_rotated": "pinned: the two score routes agree; S = 0 identity",
+    "softmax/attend": "pinned: sum p = 1, one-hot limit, linearity",
+    "band_mask/qjl_band_mask": "pinned: brute-force distance loops",
+    "pack/unpack/record_words": "pinned: hand-worked word, brute-force bit writer",
+    "tq_mse_unit/tq_mse_values": "pinned: scos-lab distortion table; nearest Max level",
+    "tq_prod_keys": "pinned: estimator unbiased with closed-form variance over 5000 sketches",
+    "cosine/rel_mse/bits_per_coord/compression_ratio": "pinned: README headline ratios; "
+                                                       "SQ > TQ ordering on every workload",
 }
