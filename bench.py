@@ -42,7 +42,6 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_kernel_decode_traffic.md")
-KERNEL_SRC = os.path.join(ROOT, "compression_sq_compress_amd", "csrc", "kernels.hip")
 
 
 def parse():
@@ -62,8 +61,8 @@ def parse():
 
 
 def kernel_source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    from compression_sq_compress_amd.digest import source_digest
+    return source_digest()
 
 
 def measured_traffic():

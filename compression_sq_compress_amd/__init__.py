@@ -7,7 +7,8 @@ device; work is enqueued on torch's current stream.
 
 The library is built in-tree (``python -m compression_sq_compress_amd.build``);
 if it is missing it is built once on first import, and any failure raises --
-there is no fallback implementation.
+there is no fallback implementation.  A library built from other sources than
+the ones beside it (its compiled-in source digest differs) is refused.
 """
 from __future__ import annotations
 
@@ -29,7 +30,11 @@ EXPORTS = ("sq_calib_default_opts", "sq_calibrate", "sq_calib_upload", "sq_calib
            "sq_calib_info", "sq_calib_export", "sq_calib_save", "sq_calib_load",
            "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_compress_append", "sq_scores",
            "sq_attend_workspace_bytes", "sq_attend", "sq_dequantize", "sq_unpack",
-           "sq_last_error")
+           "sq_last_error", "sq_build_digest", "sq_plan_decode")
+
+
+class StaleLibraryError(RuntimeError):
+    """libsq.so does not match the sources beside it."""
 
 
 class SQError(RuntimeError):
@@ -52,6 +57,12 @@ class HeadInfo(C.Structure):
                 ("participation_ratio", C.c_double), ("kappa", C.c_double)]
 
 
+class DecodePlan(C.Structure):
+    _fields_ = [("score_passes", C.c_int), ("score_quads", C.c_int), ("score_wave_groups", C.c_int),
+                ("attend_placement", C.c_int), ("attend_waves", C.c_int), ("attend_blocks", C.c_int),
+                ("attend_chunks", C.c_int)]
+
+
 _lib = None
 
 
@@ -63,6 +74,14 @@ def _load():
         from .build import build
         build()
     lib = C.CDLL(LIB_PATH)
+    from .digest import source_digest
+    lib.sq_build_digest.restype = C.c_char_p
+    lib.sq_build_digest.argtypes = []
+    built, want = lib.sq_build_digest().decode(), source_digest()
+    if built != want:
+        raise StaleLibraryError(
+            f"{LIB_PATH} was built from other sources (digest {built}, sources {want}); "
+            "rebuild it with: python -m compression_sq_compress_amd.build")
     P, I, I64, U64 = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
     sig = {
         "sq_calib_default_opts": (I, [C.POINTER(CalibOpts), I]),
@@ -83,6 +102,8 @@ def _load():
         "sq_dequantize": (I, [P, I, I, I, I, P, I64, I64, I64, P, P]),
         "sq_unpack": (I, [P, I, P, I64, P, P, P]),
         "sq_last_error": (C.c_char_p, []),
+        "sq_build_digest": (C.c_char_p, []),
+        "sq_plan_decode": (I, [P, P, I, I, I, I, I, I64, C.POINTER(DecodePlan)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -276,6 +297,17 @@ def sq_dequantize(cal: Calibration, packed, n_tokens: int, out, first_head: int 
     _check(_load().sq_dequantize(cal.handle, first_head, H, B, calib_batch_stride,
                                  _ptr(packed), packed.stride(0), packed.stride(1), n_tokens,
                                  _ptr(out), _stream(stream)))
+
+
+def sq_plan_decode(kcal: Optional[Calibration], vcal: Optional[Calibration], batch: int,
+                   n_q_heads: int, n_kv_heads: int, n_tokens: int, first_head: int = 0,
+                   calib_batch_stride: int = 0) -> DecodePlan:
+    """Diagnostic: how sq_scores / sq_attend would launch for these sizes."""
+    out = DecodePlan()
+    _check(_load().sq_plan_decode(kcal.handle if kcal else None, vcal.handle if vcal else None,
+                                  first_head, calib_batch_stride, batch, n_q_heads, n_kv_heads,
+                                  n_tokens, C.byref(out)))
+    return out
 
 
 def sq_unpack(cal: Calibration, head: int, packed_host: np.ndarray, n_tokens: int):

@@ -28,6 +28,11 @@ using namespace sq;
 
 extern "C" const char *sq_last_error(void) { return g_last_error.c_str(); }
 
+#ifndef SQ_SOURCE_DIGEST
+#define SQ_SOURCE_DIGEST "unknown"
+#endif
+extern "C" const char *sq_build_digest(void) { return SQ_SOURCE_DIGEST; }
+
 static bool supported_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 extern "C" sq_status sq_calib_default_opts(sq_calib_opts *o, int head_dim) {

@@ -1,0 +1,1062 @@
+// sq_compress and sq_compress_append: rotation, quantisation, selective QJL
+// and packing of K/V vectors (gfx950).
+
+#include "devcommon.h"
+
+namespace sq {
+
+// ------------------------------------------------------------------ compress
+//
+// A workgroup of D/16 waves serves one calibration head and walks many
+// 64-token tiles.
+//   rotate:   wave w computes y^T[coord][token] = R x^T for eigen-coordinates
+//             [16w, 16w+16) with MFMA 16x16x32 bf16.  R is split into three
+//             bf16 terms (Henry, Tang & Heinecke, ARITH 2019: bf16x3) so every
+//             product is exact in the fp32 accumulator; for head_dim <= 128 the
+//             wave's 16 rows of the three terms stay in registers for the
+//             workgroup's whole life, for 256 they are read per tile from the
+//             L2.  fp32 inputs are split into three terms as well and the six
+//             leading cross products are accumulated.  The x tile (B operand)
+//             is shared through LDS; the accumulators go to an LDS y tile.
+//   quantise: each wave owns a contiguous coordinate range (balanced on the
+//             search cost, not tied to its MFMA rows) cut into chunks of 1, 2,
+//             4 or 8 equal-width coordinates; lane = token, the chunk's binary
+//             searches advance in lock-step (see quant_chunk) and its codes are
+//             appended to a bit window that emits the record words.
+//   pack:     words wholly inside one wave's code bits are stored from its
+//             window; words shared between ranges are OR-ed together in LDS
+//             and, after a barrier, stored by one wave, the last one adding
+//             the QJL bits z_j = [(S r)_j >= 0] and gamma = |r| as IEEE half
+//             in word W-1.  Every store is one coalesced 256-byte row.
+
+struct CompressArgs {
+  const DevHead *heads;
+  const uint8_t *blob;
+  const void *x;
+  uint32_t *packed;
+  int64_t xs_b, xs_h, xs_t;
+  int64_t ps_b, ps_h;
+  int64_t n_tokens;
+  int64_t token0;       // source token i goes to token slot token0 + i
+  int first_head, cbs;
+  int n_tiles;          // ceil(T / 64) per (batch, head)
+  int items;            // tiles one head's workgroups share
+  int lds_csig_off;     // floats: signal-centroid table (after the trees)
+  int lds_plan_off;     // floats: the head's compress plan
+  int lds_s_off;        // floats: QJL sketch S [m][d_eff], or -1: read from the table blob
+  int lds_sp_off;       // floats: S zero-padded to [8][8] (used when m, d_eff <= 8)
+  int lds_x_off;        // floats: x tile
+  int lds_y_off;        // floats: y tile; residuals replace y in place
+  int lds_b_off;        // floats: shared record-word buffer
+  int ys;               // y tile row stride (floats, d + 3)
+  int bws;              // word buffer row stride (words, odd)
+};
+
+__device__ __forceinline__ void split3(const float *v, uint4 &p0, uint4 &p1, uint4 &p2) {
+  uint16_t a[8], b[8], c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = v[e];
+    a[e] = f32_to_bf16_rne(x);
+    x -= __uint_as_float((uint32_t)a[e] << 16);
+    b[e] = f32_to_bf16_rne(x);
+    x -= __uint_as_float((uint32_t)b[e] << 16);
+    c[e] = f32_to_bf16_rne(x);
+  }
+  p0 = make_uint4(a[0] | (a[1] << 16), a[2] | (a[3] << 16), a[4] | (a[5] << 16), a[6] | (a[7] << 16));
+  p1 = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+  p2 = make_uint4(c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16));
+}
+
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+
+// Bit window of one wave's record words while it appends code fields:
+// bits [0, fill) of lo are filled; lo is word kw of the record.
+struct PackWin {
+  uint32_t lo;
+  int fill, kw;
+};
+
+// Emit the window's full word into the LDS word buffer and move on to the
+// next one.  A word wholly inside the wave's code bits is written; a word
+// shared with another wave's range is OR-ed in.
+__device__ __forceinline__ void win_flush(PackWin &pw, uint32_t next, uint32_t *bwrow, int dfirst,
+                                          int dend) {
+  if (pw.kw >= dfirst && pw.kw < dend) bwrow[pw.kw] = pw.lo;
+  else atomicOr(bwrow + pw.kw, pw.lo);
+  ++pw.kw;
+  pw.lo = next;
+  pw.fill -= 32;
+}
+
+// One chunk of NS (1, 2, 4 or 8) coordinates of equal width B (lane =
+// token).  The NS searches advance together down their breadth-first trees:
+// the root comes from a scalar register, each further level is one table
+// read at a compile-time offset; the step is decided by the sign of
+// (threshold - y), so a tie goes to the lower cell and the code is
+// #{thresholds < y}.  NaN coordinates are mapped to -inf first (code 0).
+// The chunk's NS * B code bits are assembled at compile-time shifts into one
+// 64-bit value and appended to the window at once.  Residuals of signal
+// coordinates replace y in the tile.
+struct ChunkArgs {
+  float root[8];  // per coordinate (wave-uniform values)
+  int tbase, start, nsig, cbase;
+};
+
+// Running QJL sums of the wave that holds the signal range: the dots
+// (S r)_j and |r|^2, from residuals still in registers.
+struct QjlAcc {
+  float dot[8];
+  float g2;
+};
+
+template <int B, int NS, bool TG, bool QJ>
+__device__ __forceinline__ void quant_chunk(const ChunkArgs &cd, float *yrow, const float *trees,
+                                            const float *csig, PackWin &pw, uint32_t *bwrow,
+                                            int dfirst, int dend, const float *sp, QjlAcc &qa) {
+  constexpr int L = 1 << B;
+  const int start = cd.start, nsig = cd.nsig;
+  float y[NS];
+  uint32_t code[NS];
+  const float *ys = yrow + start;
+#pragma unroll
+  for (int c = 0; c < NS; ++c) y[c] = fmaxf(ys[c], -INFINITY);
+  if constexpr (B > 0) {
+#pragma unroll
+    for (int c = 0; c < NS; ++c) code[c] = __float_as_uint(cd.root[c] - y[c]) >> 31;
+    const float *tb = trees + cd.tbase;
+#pragma unroll
+    for (int l = 1; l < B; ++l) {
+      float th[NS];
+#pragma unroll
+      for (int c = 0; c < NS; ++c) th[c] = tb[c * L + (1 << l) - 1 + (int)code[c]];
+#pragma unroll
+      for (int c = 0; c < NS; ++c)
+        code[c] = __builtin_amdgcn_alignbit(code[c], __float_as_uint(th[c] - y[c]), 31);
+    }
+    uint32_t v0 = 0u, v1 = 0u;
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      const int sh = c * B;
+      if (sh < 32) {
+        v0 |= code[c] << sh;
+        if (sh + B > 32) v1 |= code[c] >> (32 - sh);
+      } else {
+        v1 |= code[c] << (sh - 32);
+      }
+    }
+    // append the NS * B bits of (v1:v0) at bit fill of the window; the
+    // double shifts keep every shift count below 32
+    const int f = pw.fill;
+    pw.lo |= v0 << f;
+    uint32_t w1 = (v0 >> 1) >> (31 - f);
+    uint32_t w2 = 0u;
+    if constexpr (NS * B > 32) {
+      w1 |= v1 << f;
+      w2 = (v1 >> 1) >> (31 - f);
+    }
+    pw.fill += NS * B;
+    if (pw.fill >= 32) {
+      win_flush(pw, w1, bwrow, dfirst, dend);
+      if constexpr (NS * B > 32) {
+        if (pw.fill >= 32) win_flush(pw, w2, bwrow, dfirst, dend);
+      }
+    }
+  }
+  if (nsig > 0) {
+    const float *cs = csig + cd.cbase;
+#pragma unroll
+    for (int c = 0; c < NS; ++c)
+      if (c < nsig) {
+        float r = ys[c];  // (a NaN y keeps a NaN residual: no QJL bit, NaN gamma)
+        if constexpr (B > 0) r -= cs[c * L + code[c]];
+        if constexpr (QJ) {  // signal coordinate start + c < 8: column of the padded sketch
+          qa.g2 = fmaf(r, r, qa.g2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) qa.dot[j] = fmaf(sp[j * 8 + start + c], r, qa.dot[j]);
+        } else {
+          yrow[start + c] = r;
+        }
+      }
+  }
+}
+
+template <int B, bool TG, bool QJ>
+__device__ __forceinline__ void quant_chunk_ns(int lg, const ChunkArgs &cd, float *yrow,
+                                               const float *trees, const float *csig, PackWin &pw,
+                                               uint32_t *bwrow, int dfirst, int dend,
+                                               const float *sp, QjlAcc &qa) {
+  switch (lg) {
+    case 0: quant_chunk<B, 1, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 1: quant_chunk<B, 2, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 2: quant_chunk<B, 4, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    default: quant_chunk<B, 8, TG, QJ>(cd, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+  }
+}
+
+// Decode one chunk descriptor (four 16-byte words from the LDS plan) and run
+// the chunk's quantiser for its width and size.
+template <bool TG, bool QJ>
+__device__ __forceinline__ void run_chunk(uint4 c0, uint4 c1, uint4 c2, uint4 c3, float *yrow,
+                                          const float *trees, const float *csig, PackWin &pw,
+                                          uint32_t *bwrow, int dfirst, int dend, const float *sp,
+                                          QjlAcc &qa) {
+  ChunkArgs ca;
+  ca.root[0] = __uint_as_float(c0.x); ca.root[1] = __uint_as_float(c0.y);
+  ca.root[2] = __uint_as_float(c0.z); ca.root[3] = __uint_as_float(c0.w);
+  ca.root[4] = __uint_as_float(c1.x); ca.root[5] = __uint_as_float(c1.y);
+  ca.root[6] = __uint_as_float(c1.z); ca.root[7] = __uint_as_float(c1.w);
+  ca.tbase = __builtin_amdgcn_readfirstlane(c2.x);
+  ca.start = __builtin_amdgcn_readfirstlane(c2.y);
+  const int bw = __builtin_amdgcn_readfirstlane(c2.w);
+  ca.nsig = __builtin_amdgcn_readfirstlane(c3.x);
+  ca.cbase = __builtin_amdgcn_readfirstlane(c3.y);
+  const int lg = __builtin_amdgcn_readfirstlane(c3.z);  // log2 of the coordinate count
+  switch (bw) {
+    case 0: quant_chunk_ns<0, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 1: quant_chunk_ns<1, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 2: quant_chunk_ns<2, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 3: quant_chunk_ns<3, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 4: quant_chunk_ns<4, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 5: quant_chunk_ns<5, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 6: quant_chunk_ns<6, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    case 7: quant_chunk_ns<7, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+    default: quant_chunk_ns<8, TG, QJ>(lg, ca, yrow, trees, csig, pw, bwrow, dfirst, dend, sp, qa); break;
+  }
+}
+
+// At least 4 waves per SIMD (<= 128 VGPRs): two workgroups per CU for
+// head_dim 128, and what a 16-wave workgroup needs for 256.
+template <int D, bool F32, bool TG>
+__global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
+  extern __shared__ float smem[];
+  constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
+  constexpr bool RES = D <= 128;           // rotation rows resident in registers
+  constexpr int XS = F32 ? D + 4 : D + 8;  // x tile row stride (elements)
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
+  const int h = blockIdx.y, bz = blockIdx.z;
+  const int ch = a.first_head + bz * a.cbs + h;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
+  const int d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
+  float *ytile = smem + a.lds_y_off;             // [64][ys]
+  uint32_t *bwords = (uint32_t *)(smem + a.lds_b_off);  // [64][bws] shared record words
+  const float *trees;
+  float *s_csig = smem + a.lds_csig_off;
+  {
+    const int n_tree = hd->n_tree, n_csig = hd->n_csig;
+    const float *g_tree = (const float *)(a.blob + hd->off_tree);
+    if constexpr (TG) {
+      trees = g_tree;
+    } else {
+      for (int k = threadIdx.x; k < n_tree; k += NT) smem[k] = g_tree[k];
+      trees = smem;
+    }
+    const float *g_csig = (const float *)(a.blob + hd->off_csig);
+    for (int k = threadIdx.x; k < n_csig; k += NT) s_csig[k] = g_csig[k];
+    const uint32_t *g_plan = (const uint32_t *)(a.blob + hd->off_plan);
+    uint32_t *s_plan = (uint32_t *)(smem + a.lds_plan_off);
+    const int n_plan = (NW + hd->n_chunks + 1) * PLAN_WORDS;
+    for (int k = threadIdx.x; k < n_plan; k += NT) s_plan[k] = g_plan[k];
+    const float *g_S = (const float *)(a.blob + hd->off_S);
+    if (a.lds_s_off >= 0)
+      for (int k = threadIdx.x; k < hd->m * hd->d_eff; k += NT) smem[a.lds_s_off + k] = g_S[k];
+    if (threadIdx.x < 64) {
+      const int j = threadIdx.x >> 3, i = threadIdx.x & 7;
+      smem[a.lds_sp_off + threadIdx.x] = (j < hd->m && i < hd->d_eff) ? g_S[j * hd->d_eff + i] : 0.0f;
+    }
+  }
+  const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag);
+  uint4 rf[RES ? 3 : 1][RES ? KB : 1];
+  if constexpr (RES) {
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) rf[sp][kb] = Rf[((sp * MB + w) * KB + kb) * 64 + lane];
+  }
+  const SQ_CONST uint32_t *plan = cptr<uint32_t>(a.blob + hd->off_plan);
+  const float *S_lds = smem + max(0, a.lds_s_off);
+  const SQ_CONST float *S_glb = cptr<float>(a.blob + hd->off_S);
+  const int64_t T = a.n_tokens;
+  const SQ_CONST uint32_t *hdr = plan + w * PLAN_WORDS;
+  const int nch = (int)hdr[0];
+  const int sbit = (int)(hdr[1] & 0xFFFF);
+  const int own_f = (int)(hdr[2] & 0xFFFF), own_e = (int)(hdr[2] >> 16);
+  const int dfirst = (int)(hdr[3] & 0xFFFF), dend = (int)(hdr[3] >> 16);
+  const int nsc = (int)hdr[5];  // leading chunks with signal coordinates (small sketch, wave 0)
+  // chunk descriptors are read from the LDS copy of the plan: in-order LDS
+  // reads leave the compiler exact partial waits for the search reads
+  const uint4 *chunks = (const uint4 *)(smem + a.lds_plan_off) + (NW + (int)hdr[4]) * (PLAN_WORDS / 4);
+
+  // x tile chunks of 16 bytes: CPR per row, CH per thread; the next tile's
+  // chunks are prefetched into registers while the current tile is processed
+  constexpr int ESZ = F32 ? 4 : 2;
+  constexpr int CPR = D * ESZ / 16;
+  constexpr int CH = 64 * CPR / NT;
+  uint4 xr[CH];
+  auto load_x = [&](int item) {
+    const int bb = a.cbs ? bz : item / a.n_tiles;
+    const int tl = a.cbs ? item : item % a.n_tiles;
+    const char *xp = (const char *)a.x + ((int64_t)bb * a.xs_b + (int64_t)h * a.xs_h) * ESZ;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = threadIdx.x + q * NT;
+      const int tt = c / CPR, col = c % CPR;
+      const int64_t t = (int64_t)tl * 64 + tt;
+      xr[q] = t < T ? *(const uint4 *)(xp + t * a.xs_t * ESZ + col * 16) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (blockIdx.x < a.items) load_x(blockIdx.x);
+  // The record words of a tile are assembled in the LDS word buffer and stored
+  // at the top of the next tile, before the next prefetch is issued: each
+  // wait for a prefetch then covers only memory operations issued a whole
+  // tile earlier.  A wave stores the words it finalises (its direct words and
+  // the shared words it owns) and zeroes the shared ones for the next tile.
+  for (int k = threadIdx.x; k < 64 * a.bws; k += NT) bwords[k] = 0u;
+  uint32_t *const bwrow = bwords + lane * a.bws;
+  uint32_t *pdst = nullptr;  // destination of the previous tile's records
+  bool pvalid = false, pin = false;
+  // Source token i lands in slot token token0 + i: lane l of a source tile
+  // writes destination lane (token0 + l) % 64 of its tile or of the next.
+  // Lanes past the last token zero their words up to the end of the last
+  // destination tile and write nothing beyond it.
+  const int ol = (int)(a.token0 & 63) + lane;
+  const int64_t lofs = (int64_t)(ol >> 6) * W * 64 + (ol & 63);
+  const int64_t send = ((a.token0 + T + 63) & ~(int64_t)63) - a.token0;
+  auto store_prev = [&]() {
+    for (int k = dfirst; k < dend; ++k)
+      if (pin) pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
+    for (int k = own_f; k < own_e; ++k) {
+      if (k >= dfirst && k < dend) continue;
+      if (pin) pdst[(int64_t)k * 64] = pvalid ? bwrow[k] : 0u;
+      bwrow[k] = 0u;
+    }
+  };
+
+  for (int item = blockIdx.x; item < a.items; item += gridDim.x) {
+    const int b = a.cbs ? bz : item / a.n_tiles;
+    const int tile = a.cbs ? item : item % a.n_tiles;
+    const int64_t t0 = (int64_t)tile * 64;
+    // ---- prefetched x tile -> LDS, previous tile's records -> HBM, then
+    // start loading the next tile
+    {
+      char *xt = (char *)(smem + a.lds_x_off);
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        const int c = threadIdx.x + q * NT;
+        *(uint4 *)(xt + (c / CPR) * XS * ESZ + (c % CPR) * 16) = xr[q];
+      }
+    }
+    if (pdst) store_prev();
+    __syncthreads();
+    if (item + (int)gridDim.x < a.items) load_x(item + gridDim.x);
+    // ---- rotate this wave's 16 coordinates for the 64 tokens (4 blocks of 16)
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 r0, r1, r2;
+      if constexpr (RES) {
+        r0 = rf[0][kb]; r1 = rf[1][kb]; r2 = rf[2][kb];
+      } else {
+        r0 = Rf[((0 * MB + w) * KB + kb) * 64 + lane];
+        r1 = Rf[((1 * MB + w) * KB + kb) * 64 + lane];
+        r2 = Rf[((2 * MB + w) * KB + kb) * 64 + lane];
+      }
+      const int koff = kb * 32 + 8 * (lane >> 4);
+      if constexpr (!F32) {
+        const uint16_t *xt = (const uint16_t *)(smem + a.lds_x_off);
+        uint4 xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[j] = *(const uint4 *)(xt + (16 * j + (lane & 15)) * XS + koff);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r0, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r1, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r2, xv[j], acc[j]);
+      } else {
+        const float *xt = smem + a.lds_x_off;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float *src = xt + (16 * j + (lane & 15)) * XS + koff;
+          float v[8];
+          const float4 u0 = *(const float4 *)src, u1 = *(const float4 *)(src + 4);
+          v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+          v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+          uint4 x0, x1, x2;
+          split3(v, x0, x1, x2);
+          acc[j] = mfma16(r0, x0, acc[j]);
+          acc[j] = mfma16(r0, x1, acc[j]);
+          acc[j] = mfma16(r1, x0, acc[j]);
+          acc[j] = mfma16(r0, x2, acc[j]);
+          acc[j] = mfma16(r2, x0, acc[j]);
+          acc[j] = mfma16(r1, x1, acc[j]);
+        }
+      }
+    }
+    // accumulators (row = coordinate, column = token) -> y tile [token][coordinate]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ytile[(16 * j + (lane & 15)) * a.ys + 16 * w + 4 * (lane >> 4) + r] = acc[j][r];
+    __syncthreads();
+    // ---- quantise + pack (lane = token), chunk by chunk through the plan,
+    // into the LDS word buffer.  With a small sketch (m, d_eff <= 8) wave 0
+    // holds the whole signal range and adds the QJL bits and gamma itself.
+    float *yrow = ytile + lane * a.ys;
+    const bool qin = m > 0 && m <= 8 && d_eff <= 8 && w == 0;
+    const float *sp = smem + a.lds_sp_off;
+    {
+      PackWin pw{0u, sbit & 31, sbit >> 5};
+      int q = 0;
+      if (qin) {  // the leading signal chunks, then the QJL bits and gamma
+        QjlAcc qa;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qa.dot[j] = 0.0f;
+        qa.g2 = 0.0f;
+        for (; q < nsc; ++q)
+          run_chunk<TG, true>(chunks[q * 4], chunks[q * 4 + 1], chunks[q * 4 + 2], chunks[q * 4 + 3],
+                              yrow, trees, s_csig, pw, bwrow, dfirst, dend, sp, qa);
+        uint32_t z = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z |= (j < m && qa.dot[j] >= 0.0f ? 1u : 0u) << j;
+        const int k0 = code_bits >> 5, sh = code_bits & 31;
+        atomicOr(bwrow + k0, z << sh);
+        if (sh + m > 32) atomicOr(bwrow + k0 + 1, z >> (32 - sh));
+        atomicOr(bwrow + W - 1, half_bits_rne(sqrtf(qa.g2)) << 16);
+      }
+      QjlAcc no_qjl;  // unused by the chunks below
+      uint4 nx[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) nx[k] = chunks[q * 4 + k];
+      for (; q < nch; ++q) {
+        const uint4 c0 = nx[0], c1 = nx[1], c2 = nx[2], c3 = nx[3];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) nx[k] = chunks[(q + 1) * 4 + k];  // the plan ends with a spare chunk
+        run_chunk<TG, false>(c0, c1, c2, c3, yrow, trees, s_csig, pw, bwrow, dfirst, dend, sp, no_qjl);
+      }
+      if (pw.fill > 0) {  // last, partial word of the range
+        if (pw.kw >= dfirst && pw.kw < dend) bwrow[pw.kw] = pw.lo;
+        else atomicOr(bwrow + pw.kw, pw.lo);
+      }
+    }
+    __syncthreads();
+    // ---- larger sketches: the last wave adds the QJL bits and gamma to the
+    // words it owns, from the residuals, which replaced y of the signal
+    // coordinates in the tile
+    const bool qslow = m > 0 && !(m <= 8 && d_eff <= 8);
+    for (int k = own_f; k < own_e && qslow && w == NW - 1; ++k) {
+      if (k >= dfirst && k < dend) continue;
+      uint32_t word = bwrow[k];
+      {
+        const int lo_bit = 32 * k, hi_bit = lo_bit + 32;
+        const int jb = max(0, lo_bit - code_bits), je = min(m, hi_bit - code_bits);
+        for (int j = jb; j < je; ++j) {
+          float dot = 0.0f;
+          if (a.lds_s_off >= 0) {
+            for (int i = 0; i < d_eff; ++i) dot = fmaf(S_lds[j * d_eff + i], yrow[i], dot);
+          } else {
+            for (int i = 0; i < d_eff; ++i) dot = fmaf(S_glb[j * d_eff + i], yrow[i], dot);
+          }
+          word |= (dot >= 0.0f ? 1u : 0u) << (code_bits + j - lo_bit);
+        }
+        if (k == W - 1) {
+          float g2 = 0.0f;
+          for (int i = 0; i < d_eff; ++i) g2 = fmaf(yrow[i], yrow[i], g2);
+          word |= half_bits_rne(sqrtf(g2)) << 16;
+        }
+      }
+      bwrow[k] = word;
+    }
+    pdst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + ((a.token0 >> 6) + tile) * W * 64 + lofs;
+    pvalid = t0 + lane < T;
+    pin = t0 + lane < send;
+    // The x tile was last read by the MFMAs, which every wave finished before
+    // the barrier above; the y tile and the word buffer are rewritten only
+    // after the barrier that follows the next x store.
+  }
+  if (pdst) store_prev();
+}
+
+
+// ------------------------------------------------------------------ compress, register quantiser
+//
+// Same contract as compress_kernel, for head_dim 32, 64 and 128 with at most
+// 16 signal coordinates and 32 QJL rows.  A workgroup of d/16 waves serves
+// one calibration head and walks 64-token tiles with one barrier per tile:
+//   rotate:   wave w forms its 16 MFMA rows of y^T for the tile (16x16x32 bf16,
+//             R as three bf16 terms in registers); its rows are the four
+//             coordinate groups of the register plan (P2_WAVE), so lane l
+//             holds in accumulator register r the values of one coordinate
+//             for tokens l % 16 + 16 j.
+//   quantise: straight from the accumulators: 16 descents per wave of the
+//             lanes' own padded threshold trees in LDS, advancing level by
+//             level together; each code is OR-ed into its record word(s) in
+//             an LDS record tile [token][word], and signal residuals
+//             y - C[code] go to a small float tile.
+//   store:    after the barrier wave w stores record words w, w + d/16, ... as
+//             coalesced 256-byte rows (lane = token) and clears them, except
+//             the words with QJL bits or gamma: every wave first adds its
+//             share of the QJL rows (and one wave gamma) from the residual
+//             tile, and those words are stored after the next barrier.
+// x tiles are double-buffered and fetched two tiles ahead; the record tile
+// is triple-buffered, the residual tile double-buffered, so the barrier of
+// tile t also separates tile t+1's writes from the reads of tiles t-1, t-2.
+
+struct Compress2Args {
+  const DevHead *heads;
+  const uint8_t *blob;
+  const void *x;
+  uint32_t *packed;
+  int64_t xs_b, xs_h, xs_t;
+  int64_t ps_b, ps_h;
+  int64_t n_tokens;
+  int64_t token0;             // source token i goes to token slot token0 + i
+  int first_head, cbs;
+  int n_tiles, tiles_per_wg;  // workgroup (x, head, batch entry) takes tiles [x * tiles_per_wg, ...)
+  int lds_tree_off, lds_csig_off, lds_s_off, lds_x_off, lds_rec_off, lds_res_off;  // floats
+  int x_buf_floats;
+};
+
+constexpr int C2_RS = 20;   // residual tile row stride (floats; 16-byte rows, conflict-free)
+constexpr int C2_SP = 16;   // sketch row pitch in LDS (floats, zero padded past d_eff)
+constexpr int C2_WMAX = 6;  // record words stored per wave and tile (word k goes to wave k % waves)
+
+// RS: record tile row stride in words (odd, above the record length: the
+// last column is a pad), a constant so that token-block offsets are immediates
+template <int D, bool F32, int RS>
+__global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
+  extern __shared__ float smem[];
+  constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y, bz = blockIdx.z;
+  const int tb = blockIdx.x * a.tiles_per_wg, te = min(a.n_tiles, tb + a.tiles_per_wg);
+  if (tb >= te) return;  // (whole workgroup)
+  const int ch = a.first_head + bz * a.cbs + h;
+  const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
+  const int d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
+  constexpr int rs = RS;
+  float *trees = smem + a.lds_tree_off;
+  float *csig = smem + a.lds_csig_off;
+  float *Sl = smem + a.lds_s_off;  // [m][C2_SP]
+  {
+    const float *g = (const float *)(a.blob + hd->off_tree2);
+    for (int k = threadIdx.x; k < hd->n_tree2; k += NT) trees[k] = g[k];
+    const float *gc = (const float *)(a.blob + hd->off_csig2);
+    for (int k = threadIdx.x; k < hd->n_csig2; k += NT) csig[k] = gc[k];
+    const float *gs = (const float *)(a.blob + hd->off_S);
+    for (int k = threadIdx.x; k < m * C2_SP; k += NT)
+      Sl[k] = (k % C2_SP) < d_eff ? gs[(k / C2_SP) * d_eff + k % C2_SP] : 0.0f;
+  }
+  const SQ_CONST uint32_t *H = cptr<uint32_t>(a.blob + hd->off_p2) + w * P2_WAVE;
+  const int s4 = lane >> 4;
+  int dep[4];
+  // per lane and register: tree base | (record word | bit shift << 8 |
+  // straddles << 13) << 16; coordinate | signal-centroid base << 8 (0xFFFFFF: none)
+  uint32_t tw[4], cc[4];
+  {
+    const uint32_t *Hv = (const uint32_t *)(a.blob + hd->off_p2) + w * P2_WAVE;  // per-lane reads
+    const DevCoord *cd = (const DevCoord *)(a.blob + hd->off_coord);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dep[r] = (int)H[r];
+      const uint32_t cb = Hv[20 + 4 * r + s4], c = Hv[36 + 4 * r + s4];
+      cc[r] = c | ((cb == 0xFFFFFFFFu ? 0xFFFFFFu : cb) << 8);
+      const int bo = cd[c].bit_off, wd = cd[c].width;
+      const uint32_t wsh = (uint32_t)(bo >> 5) | ((uint32_t)(bo & 31) << 8) | ((bo & 31) + wd > 32 ? 1u << 13 : 0u);
+      tw[r] = Hv[4 + 4 * r + s4] | (wsh << 16);
+    }
+  }
+  // record words of this wave: w, w + NW, ...; qmask bit i: word w + NW i holds
+  // QJL bits or gamma (stored one tile late, once every wave has added its bits)
+  uint32_t qmask = 0u;
+#pragma unroll
+  for (int i = 0; i < C2_WMAX; ++i) {
+    const int k = w + NW * i;
+    if (m > 0 && k < W && ((32 * k < code_bits + m && 32 * k + 32 > code_bits) || k == W - 1)) qmask |= 1u << i;
+  }
+  // QJL rows of this wave (all 64 tokens): [jb, je)
+  const int jb = (w * m) / NW, je = ((w + 1) * m) / NW;
+  const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag2);
+  uint4 rf[3][KB];
+#pragma unroll
+  for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) rf[sp][kb] = Rf[((sp * MB + w) * KB + kb) * 64 + lane];
+
+  // x tiles go straight into LDS, 1 KB per load instruction, rows of RB
+  // bytes back to back; chunk c (16 bytes) of row t sits at slot c ^ swz(t)
+  // of the row, which keeps the MFMA operand reads free of bank conflicts
+  // (measured: a 16-byte row pad instead doubles their LDS time).
+  constexpr int ESZ = F32 ? 4 : 2;
+  constexpr int RB = D * ESZ;                    // bytes of x per token
+  constexpr int CPR = RB / 16;                   // 16-byte chunks per token
+  constexpr int RPB = CPR >= 16 ? 1 : 16 / CPR;  // rows per 256 bytes
+  constexpr int NB = CPR / NW;                   // 1 KB blocks per wave and tile
+  const uint32_t lds_x = (uint32_t)(uintptr_t)(smem + a.lds_x_off);
+  const uint32_t row_bytes = (uint32_t)a.xs_t * ESZ;  // 64 rows fit 32 bits (host check)
+  const char *xbase = (const char *)a.x + ((int64_t)bz * a.xs_b + (int64_t)h * a.xs_h) * ESZ;
+  auto dma_x = [&](int tl, int buf) __attribute__((always_inline)) {
+    // rows past the end re-read the last token (a whole tile past it, which
+    // only zero-fills destination words, reads nothing else)
+    const int64_t t0 = min<int64_t>((int64_t)tl * 64, a.n_tokens - 1);
+    const char *src = xbase + t0 * a.xs_t * ESZ;
+    const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = w * NB + i;
+      const int byte = q * 1024 + lane * 16, row = byte / RB, slot = (byte % RB) / 16;
+      const int c = slot ^ ((row / RPB) & (CPR - 1));
+      lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)c * 16u,
+                lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
+    }
+  };
+  for (int k = threadIdx.x; k < 3 * 64 * rs; k += NT) smem[a.lds_rec_off + k] = 0.0f;
+  // residual columns past d_eff stay zero (the QJL step reads whole rows)
+  for (int k = threadIdx.x; k < 2 * 64 * C2_RS; k += NT) smem[a.lds_res_off + k] = 0.0f;
+  // All set-up loads complete here, so that no wait inside the tile loop has
+  // to cover them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  dma_x(tb, 0);
+  if (tb + 1 < te) dma_x(tb + 1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  // the lane's operand rows are 16 j + lane % 16: their swizzle is a lane constant for bf16
+  const int xsw = ((lane & 15) / RPB) & (CPR - 1);
+  const uint32_t xrow = (uint32_t)(lane & 15) * RB;
+  uint32_t *rec0 = (uint32_t *)(smem + a.lds_rec_off);
+  // source token i lands in slot token token0 + i: lane l of a source tile
+  // writes destination lane (token0 + l) % 64 of its tile or of the next;
+  // lanes past the last token zero their words up to the end of the last
+  // destination tile and write nothing beyond it
+  uint32_t *obase = a.packed + (int64_t)bz * a.ps_b + (int64_t)h * a.ps_h + (a.token0 >> 6) * W * 64;
+  const int ol = (int)(a.token0 & 63) + lane;
+  const uint32_t lofs = (uint32_t)((ol >> 6) * W * 64 + (ol & 63));
+  const int64_t send = ((a.token0 + a.n_tokens + 63) & ~(int64_t)63) - a.token0;
+  // record words of this wave: w + NW i for i < nmine
+  const int nmine = W > w ? (W - 1 - w) / NW + 1 : 0;
+  int par = 0, rb = 0;
+  for (int t = tb; t < te; ++t, par ^= 1, rb = rb == 2 ? 0 : rb + 1) {
+    // ---- rotate: 16 rows x 64 tokens (4 blocks of 16)
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char *xt = (const char *)(smem + a.lds_x_off + par * a.x_buf_floats) + xrow;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint4 r0 = rf[0][kb], r1 = rf[1][kb], r2 = rf[2][kb];
+      if constexpr (!F32) {
+        uint4 xv[4];  // elements kb*32 + 8*(lane/16) .. (chunk kc) of token 16j + lane%16
+        const char *xc = xt + (((kb * 4 + (lane >> 4)) ^ xsw) << 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[j] = *(const uint4 *)(xc + 16 * j * RB);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r0, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r1, xv[j], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16(r2, xv[j], acc[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v[8];
+          const int kc = kb * 8 + 2 * (lane >> 4), sw = ((16 * j + (lane & 15)) / RPB) & (CPR - 1);
+          const float4 u0 = *(const float4 *)(xt + 16 * j * RB + ((kc ^ sw) << 4));
+          const float4 u1 = *(const float4 *)(xt + 16 * j * RB + (((kc + 1) ^ sw) << 4));
+          v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+          v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+          uint4 x0, x1, x2;
+          split3(v, x0, x1, x2);
+          acc[j] = mfma16(r0, x0, acc[j]);
+          acc[j] = mfma16(r0, x1, acc[j]);
+          acc[j] = mfma16(r1, x0, acc[j]);
+          acc[j] = mfma16(r0, x2, acc[j]);
+          acc[j] = mfma16(r2, x0, acc[j]);
+          acc[j] = mfma16(r1, x1, acc[j]);
+        }
+      }
+    }
+    // ---- quantise from the accumulators: code = #{thresholds < y} by a
+    // descent of the padded tree.  A NaN y codes as 0: the MFMA returns the
+    // positive quiet NaN for any NaN input, and (threshold - NaN) keeps its
+    // clear sign bit, so every level goes left (checked for NaN inputs of
+    // either sign).  The 16
+    // descents of a wave (4 registers x 4 token blocks) advance level by
+    // level together, so their LDS reads overlap; the plan orders a wave's
+    // registers by decreasing depth, so the registers still descending at a
+    // level are a prefix.  (The descriptors are decoded per tile: hoisting the
+    // decoded fields out of the loop would not fit the register budget.)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(tw[r]), "+v"(cc[r]));
+    uint32_t *rec = rec0 + rb * 64 * rs;
+    float *rtile = smem + a.lds_res_off + par * 64 * C2_RS;
+    uint32_t k[4][4];
+    const float *tr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      tr[r] = trees + (tw[r] & 0xFFFFu) - 1;  // node k at tr[k]
+    }
+    // level 1: the root is the same node for the lane's four token blocks
+    auto first = [&](auto nr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < decltype(nr)::value) {
+          const float t = tr[r][1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) k[r][j] = __builtin_amdgcn_alignbit(1u, __float_as_uint(t - acc[j][r]), 31);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) k[r][j] = 1u;  // depth 0: code 0
+        }
+      }
+    };
+    auto level = [&](auto nr) __attribute__((always_inline)) {
+      float t[decltype(nr)::value][4];
+#pragma unroll
+      for (int r = 0; r < decltype(nr)::value; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[r][j] = tr[r][k[r][j]];
+#pragma unroll
+      for (int r = 0; r < decltype(nr)::value; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          k[r][j] = __builtin_amdgcn_alignbit(k[r][j], __float_as_uint(t[r][j] - acc[j][r]), 31);
+    };
+    {
+      if (dep[3] > 0) first(std::integral_constant<int, 4>{});
+      else if (dep[2] > 0) first(std::integral_constant<int, 3>{});
+      else if (dep[1] > 0) first(std::integral_constant<int, 2>{});
+      else if (dep[0] > 0) first(std::integral_constant<int, 1>{});
+      else first(std::integral_constant<int, 0>{});
+      int l = 1;
+      for (; l < dep[3]; ++l) level(std::integral_constant<int, 4>{});
+      for (; l < dep[2]; ++l) level(std::integral_constant<int, 3>{});
+      for (; l < dep[1]; ++l) level(std::integral_constant<int, 2>{});
+      for (; l < dep[0]; ++l) level(std::integral_constant<int, 1>{});
+    }
+    // codes into the record tile (k - 2^depth, shifted into place)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t kw = (tw[r] >> 16) & 0xFFu, sh = (tw[r] >> 24) & 31u;
+      const uint32_t top = 1u << dep[r];
+      const uint32_t ntop = 0u - (top << sh);  // (k << sh) + ntop = (k - 2^depth) << sh
+      uint32_t *rw = rec + (lane & 15) * rs + kw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * rs, (k[r][j] << sh) + ntop);
+      if (tw[r] & (1u << 29)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) atomicOr(rw + 16 * j * rs + 1, (k[r][j] - top) >> (32u - sh));
+      }
+    }
+    if (m > 0) {  // signal residuals y - C[code] for the QJL sketch and gamma
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t crd = cc[r] & 0xFFu, cb = cc[r] >> 8;
+        if (cb != 0xFFFFFFu) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)  // (a NaN y leaves a NaN residual: no QJL bit, NaN gamma)
+            rtile[((lane & 15) + 16 * j) * C2_RS + crd] = acc[j][r] - csig[cb + k[r][j] - (1u << dep[r])];
+        }
+      }
+    }
+    // ---- the next tile's x has landed (this wave's loads; the barrier covers
+    // every wave's); then the tile after it goes into the buffer just read
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (t + 2 < te) dma_x(t + 2, par);
+    // ---- record words, lane = token: this tile's words without QJL bits,
+    // and the previous tile's words with QJL bits or gamma
+    {
+      const bool has_prev = t != tb;
+      const int prb = rb == 0 ? 2 : rb - 1;
+      const uint32_t lrow = (uint32_t)lane * (uint32_t)rs;
+      uint32_t *ocur = obase + (int64_t)t * W * 64;
+      uint32_t *oprv = obase + (int64_t)(t - 1) * W * 64;
+      const bool valid = (int64_t)t * 64 + lane < a.n_tokens;
+      const bool pvalid = (int64_t)(t - 1) * 64 + lane < a.n_tokens;
+      const bool in = (int64_t)t * 64 + lane < send, pin = (int64_t)(t - 1) * 64 + lane < send;
+      // words w + NW i, two at a time: this tile's (no QJL bits) or the
+      // previous tile's; a slot past this wave's words reads and clears the
+      // pad column rs - 1
+      for (int i0 = 0; i0 < nmine; i0 += 2) {
+        uint32_t v[2], off[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = i0 + u;
+          const int kk = i < nmine ? w + NW * i : rs - 1;
+          const int bi = (qmask >> i & 1u) ? prb : rb;
+          off[u] = (uint32_t)(bi * 64 * rs + kk);
+          v[u] = rec0[lrow + off[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) rec0[lrow + off[u]] = 0u;  // for tile + 3 (two more barriers first)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = i0 + u;
+          const bool q = qmask >> i & 1u;
+          if (i < nmine && (!q || has_prev) && (q ? pin : in)) {
+            uint32_t *o = q ? oprv : ocur;
+            o[(uint32_t)(w + NW * i) * 64u + lofs] = (q ? pvalid : valid) ? v[u] : 0u;
+          }
+        }
+      }
+    }
+    // ---- QJL rows [jb, je) of this tile: z_j = [(S r)_j >= 0]; the last
+    // wave adds gamma = |r| as IEEE half (RNE).  The words are stored after
+    // the next barrier.
+    if (m > 0) {
+      const float4 *rrow = (const float4 *)(rtile + lane * C2_RS);
+      float rv[C2_SP];
+#pragma unroll
+      for (int i4 = 0; i4 < C2_SP / 4; ++i4) {
+        const float4 u = rrow[i4];
+        rv[4 * i4] = u.x; rv[4 * i4 + 1] = u.y; rv[4 * i4 + 2] = u.z; rv[4 * i4 + 3] = u.w;
+      }
+      uint32_t zb = 0u;
+      for (int j = jb; j < je; ++j) {
+        const float4 *srow = (const float4 *)(Sl + j * C2_SP);
+        float dot = 0.0f;
+#pragma unroll
+        for (int i4 = 0; i4 < C2_SP / 4; ++i4) {
+          const float4 s = srow[i4];
+          dot = fmaf(s.x, rv[4 * i4 + 0], dot);
+          dot = fmaf(s.y, rv[4 * i4 + 1], dot);
+          dot = fmaf(s.z, rv[4 * i4 + 2], dot);
+          dot = fmaf(s.w, rv[4 * i4 + 3], dot);
+        }
+        zb |= (dot >= 0.0f ? 1u : 0u) << (j - jb);
+      }
+      uint32_t *rrec = rec + lane * rs;
+      if (je > jb) {
+        const int p = code_bits + jb, pw = p >> 5, ps = p & 31;
+        atomicOr(rrec + pw, zb << ps);
+        if (ps + (je - jb) > 32) atomicOr(rrec + pw + 1, zb >> (32 - ps));
+      }
+      if (w == NW - 1) {
+        float g2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < C2_SP; ++i) g2 = fmaf(rv[i], rv[i], g2);
+        // v_sqrt_f32 (within 1 ulp of fp32) before the fp16 rounding
+        atomicOr(rrec + W - 1, half_bits_rne(__builtin_amdgcn_sqrtf(g2)) << 16);
+      }
+    }
+  }
+  // ---- the last tile's words with QJL bits or gamma
+  if (m > 0) {
+    __syncthreads();
+    uint32_t *rlast = rec0 + ((te - 1 - tb) % 3) * 64 * rs + lane * rs;
+    uint32_t *dst = obase + (int64_t)(te - 1) * W * 64 + lofs;
+    const bool valid = (int64_t)(te - 1) * 64 + lane < a.n_tokens;
+    const bool in = (int64_t)(te - 1) * 64 + lane < send;
+#pragma unroll
+    for (int i = 0; i < C2_WMAX; ++i)
+      if ((qmask >> i & 1u) && i < nmine && in) dst[(int64_t)(w + NW * i) * 64] = valid ? rlast[w + NW * i] : 0u;
+  }
+}
+
+}  // namespace sq
+
+using namespace sq;
+
+template <int D, bool F32, bool TG>
+static void launch_compress(dim3 grid, size_t lds, hipStream_t s, const CompressArgs &a) {
+  hipLaunchKernelGGL((compress_kernel<D, F32, TG>), grid, dim3(4 * D), lds, s, a);
+}
+
+template <int D, bool F32>
+static void launch_compress2(int rsc, dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
+  // record strides this head size can need (at most C2_WMAX words per wave)
+  if (rsc == 17) {
+    hipLaunchKernelGGL((compress2_kernel<D, F32, 17>), grid, dim3(4 * D), lds, s, a);
+  } else if constexpr (D >= 64) {
+    if (rsc == 33) hipLaunchKernelGGL((compress2_kernel<D, F32, 33>), grid, dim3(4 * D), lds, s, a);
+    else if constexpr (D == 128) hipLaunchKernelGGL((compress2_kernel<D, F32, 49>), grid, dim3(4 * D), lds, s, a);
+  }
+}
+
+template <int D>
+static void launch_compress_d(bool f32, bool tg, dim3 grid, size_t lds, hipStream_t s, const CompressArgs &a) {
+  if (f32) tg ? launch_compress<D, true, true>(grid, lds, s, a) : launch_compress<D, true, false>(grid, lds, s, a);
+  else tg ? launch_compress<D, false, true>(grid, lds, s, a) : launch_compress<D, false, false>(grid, lds, s, a);
+}
+
+
+// sq_compress and sq_compress_append: source token i of x goes to token slot
+// token0 + i of every head's packed slot.
+static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head, int n_heads, int batch,
+                               int calib_batch_stride, const void *x, sq_dtype dt, int64_t n_tokens,
+                               int64_t xs_batch, int64_t xs_head, int64_t xs_token, uint32_t *packed,
+                               int64_t ps_batch, int64_t ps_head, int64_t token0, sq_stream stream) {
+  const std::string f(fn);
+  sq_status st = check_handle(c, fn);
+  if (st != SQ_OK) return st;
+  st = check_heads(c, first_head, n_heads, batch, calib_batch_stride, fn);
+  if (st != SQ_OK) return st;
+  if (n_tokens < 0) return fail(SQ_ERR_ARG, f + ": n_tokens < 0");
+  if (token0 < 0) return fail(SQ_ERR_ARG, f + ": token0 < 0");
+  if (dt != SQ_F32 && dt != SQ_BF16) return fail(SQ_ERR_ARG, f + ": bad dtype");
+  if (n_tokens == 0 || batch == 0) { clear_error(); return SQ_OK; }
+  if (!x || !packed) return fail(SQ_ERR_ARG, f + ": NULL pointer");
+  if (n_tokens > ((int64_t)1 << 36) || token0 > ((int64_t)1 << 36))
+    return fail(SQ_ERR_UNSUPPORTED, f + ": too many tokens");
+  st = check_slots(c, token0 + n_tokens, n_heads, batch, ps_batch, ps_head, fn);
+  if (st != SQ_OK) return st;
+  const int esz = dt == SQ_F32 ? 4 : 2;
+  if (((uintptr_t)x % 16) || (xs_token * esz) % 16 || (xs_head * esz) % 16 || (xs_batch * esz) % 16)
+    return fail(SQ_ERR_ARG, f + ": x and its strides must be 16-byte aligned");
+  const int d = c->heads[first_head].d;
+  if (xs_token < d) return fail(SQ_ERR_ARG, f + ": xs_token < head_dim");
+  // source tiles: enough to reach the end of the last destination tile (with
+  // token0 % 64 != 0 the last one only zero-fills the tail of that tile)
+  const int64_t send = ((token0 + n_tokens + 63) / 64) * 64 - token0;
+  const int n_src_tiles = (int)((send + 63) / 64);
+  // LDS: threshold trees | signal centroids | x tile | y tile | word buffer
+  int max_tree = 0, max_csig = 0, max_plan = 0, max_s = 0;
+  for (int bb = 0; bb < std::max(1, batch); ++bb) {
+    for (int h = 0; h < n_heads; ++h) {
+      const int k = first_head + bb * calib_batch_stride + h;
+      const DevHead &hd = c->host_desc[k];
+      max_tree = std::max(max_tree, hd.n_tree);
+      max_csig = std::max(max_csig, hd.n_csig);
+      max_plan = std::max(max_plan, (hd.d / 16 + hd.n_chunks + 1) * PLAN_WORDS);
+      max_s = std::max(max_s, hd.m * hd.d_eff);
+    }
+    if (calib_batch_stride == 0) break;  // every batch entry uses the same heads
+  }
+  // register-quantising kernel when every head has its plan and the tables fit
+  {
+    // (the kernel's per-lane load offsets within a 64-token tile are 32-bit;
+    // each of its d/16 waves stores at most C2_WMAX record words per tile)
+    bool use2 = d <= 128 && 64 * xs_token * esz < ((int64_t)1 << 32) && c->W_max <= C2_WMAX * (d / 16) &&
+                n_heads <= 65535 && batch <= 65535;
+    int mt = 0, mc = 0, mq = 0;
+    for (int bb = 0; bb < std::max(1, batch) && use2; ++bb) {
+      for (int h = 0; h < n_heads; ++h) {
+        const DevHead &hd = c->host_desc[first_head + bb * calib_batch_stride + h];
+        if (hd.n_p2 == 0) use2 = false;
+        mt = std::max(mt, hd.n_tree2);
+        mc = std::max(mc, hd.n_csig2);
+        mq = std::max(mq, hd.m);
+      }
+      if (calib_batch_stride == 0) break;
+    }
+    if (use2) {
+      Compress2Args b2{};
+      const bool f32 = dt == SQ_F32;
+      b2.lds_tree_off = 0;
+      b2.lds_csig_off = (mt + 3) & ~3;
+      b2.lds_s_off = b2.lds_csig_off + ((mc + 3) & ~3);
+      b2.lds_x_off = (b2.lds_s_off + mq * C2_SP + 255) & ~255;  // 1 KB aligned: direct-to-LDS blocks
+      b2.x_buf_floats = 16 * d * (f32 ? 4 : 2);                 // 64 rows of d elements
+      b2.lds_rec_off = b2.lds_x_off + 2 * b2.x_buf_floats;
+      // record tile stride: odd, above W_max (pad column)
+      const int rsc = c->W_max < 17 ? 17 : c->W_max < 33 ? 33 : 49;
+      b2.lds_res_off = (b2.lds_rec_off + 3 * 64 * rsc + 3) & ~3;
+      const size_t lds2 = (size_t)(b2.lds_res_off + 2 * 64 * C2_RS) * 4;
+      if (lds2 <= (size_t)device_lds_limit()) {
+        b2.heads = c->dev_heads;
+        b2.blob = (const uint8_t *)c->dev_blob;
+        b2.x = x;
+        b2.packed = packed;
+        b2.xs_b = xs_batch; b2.xs_h = xs_head; b2.xs_t = xs_token;
+        b2.ps_b = ps_batch; b2.ps_h = ps_head;
+        b2.n_tokens = n_tokens;
+        b2.token0 = token0;
+        b2.first_head = first_head;
+        b2.cbs = calib_batch_stride;
+        b2.n_tiles = n_src_tiles;
+        // about 4 workgroups per CU, each a run of consecutive tiles of one
+        // (batch entry, head)
+        const int64_t want = (int64_t)device_cu_count() * 4;
+        const int64_t bh = (int64_t)n_heads * batch;
+        const int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(b2.n_tiles, (want + bh - 1) / bh));
+        b2.tiles_per_wg = (int)((b2.n_tiles + chunks - 1) / chunks);
+        dim3 grid((unsigned)((b2.n_tiles + b2.tiles_per_wg - 1) / b2.tiles_per_wg), n_heads, batch);
+        hipStream_t s = (hipStream_t)stream;
+        switch (d) {
+          case 32: f32 ? launch_compress2<32, true>(rsc, grid, lds2, s, b2) : launch_compress2<32, false>(rsc, grid, lds2, s, b2); break;
+          case 64: f32 ? launch_compress2<64, true>(rsc, grid, lds2, s, b2) : launch_compress2<64, false>(rsc, grid, lds2, s, b2); break;
+          default: f32 ? launch_compress2<128, true>(rsc, grid, lds2, s, b2) : launch_compress2<128, false>(rsc, grid, lds2, s, b2); break;
+        }
+        return launched(fn);
+      }
+    }
+  }
+  CompressArgs a{};
+  a.ys = d + 3;  // odd, and conflict-free for the MFMA-layout stores
+  a.bws = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
+  const int xs_floats = dt == SQ_F32 ? 64 * (d + 4) : 64 * (d + 8) / 2;
+  const bool s_in_lds = max_s <= 4096;  // a large sketch is read from the L1/L2 instead
+  const int s_floats = s_in_lds ? ((max_s + 3) & ~3) : 0;
+  const int rest = ((max_csig + 3) & ~3) + max_plan + s_floats + 64 + xs_floats + 64 * a.ys + 64 * a.bws;
+  const size_t limit = (size_t)device_lds_limit();
+  const size_t lds_in = (size_t)(((max_tree + 3) & ~3) + rest) * 4, lds_out = (size_t)rest * 4;
+  // trees stay in LDS unless moving them out is what lets two workgroups share a CU
+  const bool tg = lds_in > limit || (lds_in > limit / 2 && lds_out <= limit / 2);
+  const int tree_floats = tg ? 0 : ((max_tree + 3) & ~3);
+  a.lds_csig_off = tree_floats;
+  a.lds_plan_off = a.lds_csig_off + ((max_csig + 3) & ~3);
+  a.lds_s_off = s_in_lds ? a.lds_plan_off + max_plan : -1;
+  a.lds_sp_off = a.lds_plan_off + max_plan + s_floats;
+  a.lds_x_off = a.lds_sp_off + 64;
+  a.lds_y_off = a.lds_x_off + xs_floats;
+  a.lds_b_off = a.lds_y_off + 64 * a.ys;
+  const size_t lds = (size_t)(a.lds_b_off + 64 * a.bws) * 4;
+  if (lds > limit)
+    return fail(SQ_ERR_UNSUPPORTED, f + ": calibration tables exceed the LDS of one workgroup");
+  a.heads = c->dev_heads;
+  a.blob = (const uint8_t *)c->dev_blob;
+  a.x = x;
+  a.packed = packed;
+  a.xs_b = xs_batch; a.xs_h = xs_head; a.xs_t = xs_token;
+  a.ps_b = ps_batch; a.ps_h = ps_head;
+  a.n_tokens = n_tokens;
+  a.token0 = token0;
+  a.first_head = first_head;
+  a.cbs = calib_batch_stride;
+  a.n_tiles = n_src_tiles;
+  const int gz = calib_batch_stride ? batch : 1;
+  a.items = calib_batch_stride ? a.n_tiles : (int)std::min<int64_t>((int64_t)batch * a.n_tiles, INT32_MAX);
+  // enough resident workgroups to keep every CU busy; each walks many tiles
+  const int64_t want = (int64_t)device_cu_count() * (d >= 256 ? 1 : 2) * 2;
+  int gx = (int)std::max<int64_t>(1, std::min<int64_t>(a.items, (want + (int64_t)n_heads * gz - 1) / ((int64_t)n_heads * gz)));
+  dim3 grid(gx, n_heads, gz);
+  if (grid.y > 65535 || grid.z > 65535) return fail(SQ_ERR_UNSUPPORTED, f + ": too many heads or batch entries");
+  hipStream_t s = (hipStream_t)stream;
+  const bool f32 = dt == SQ_F32;
+  switch (d) {
+    case 32:  launch_compress_d<32>(f32, tg, grid, lds, s, a); break;
+    case 64:  launch_compress_d<64>(f32, tg, grid, lds, s, a); break;
+    case 128: launch_compress_d<128>(f32, tg, grid, lds, s, a); break;
+    case 256: launch_compress_d<256>(f32, tg, grid, lds, s, a); break;
+    default: return fail(SQ_ERR_UNSUPPORTED, f + ": head_dim");
+  }
+  return launched(fn);
+}
+
+extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
+                                 int calib_batch_stride, const void *x, sq_dtype dt,
+                                 int64_t n_tokens, int64_t xs_batch, int64_t xs_head,
+                                 int64_t xs_token, uint32_t *packed, int64_t ps_batch,
+                                 int64_t ps_head, sq_stream stream) {
+  return compress_impl("sq_compress", c, first_head, n_heads, batch, calib_batch_stride, x, dt, n_tokens,
+                       xs_batch, xs_head, xs_token, packed, ps_batch, ps_head, 0, stream);
+}
+
+extern "C" sq_status sq_compress_append(const sq_calib *c, int first_head, int n_heads, int batch,
+                                        int calib_batch_stride, const void *x, sq_dtype dt,
+                                        int64_t n_tokens, int64_t xs_batch, int64_t xs_head,
+                                        int64_t xs_token, uint32_t *packed, int64_t ps_batch,
+                                        int64_t ps_head, int64_t token0, sq_stream stream) {
+  return compress_impl("sq_compress_append", c, first_head, n_heads, batch, calib_batch_stride, x, dt,
+                       n_tokens, xs_batch, xs_head, xs_token, packed, ps_batch, ps_head, token0, stream);
+}

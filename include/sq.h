@@ -234,6 +234,30 @@ sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride,
                     size_t ws_bytes, float *out, sq_stream stream);
 
 /*
+ * sq_plan_decode -- diagnostic: how sq_scores (keys handle kc) and sq_attend
+ * (values handle vc) would launch for these arguments on the current device,
+ * without launching anything.  Either handle may be NULL (its fields stay 0).
+ *   score_passes       launches of the scores kernel (passes over the quads of
+ *                      4 coordinates; passes after the first add into scores)
+ *   score_quads        the largest number of quads of one head
+ *   score_wave_groups  wave groups the quads are split over
+ *   attend_placement   centroid tables: 0 one column per lane in LDS, 1 packed
+ *                      in LDS, 2 read from device memory
+ *   attend_waves       waves (token chunks) per workgroup
+ *   attend_blocks      64-coordinate blocks each wave serves (head_dim / 64)
+ *   attend_chunks      token chunks per (batch, query head)
+ * Errors: as sq_scores / sq_attend for the head range; SQ_ERR_STATE when a
+ * handle is not uploaded.
+ */
+typedef struct {
+  int score_passes, score_quads, score_wave_groups;
+  int attend_placement, attend_waves, attend_blocks, attend_chunks;
+} sq_decode_plan;
+sq_status sq_plan_decode(const sq_calib *kc, const sq_calib *vc, int first_head,
+                         int calib_batch_stride, int batch, int n_q_heads, int n_kv_heads,
+                         int64_t n_tokens, sq_decode_plan *out);
+
+/*
  * sq_dequantize -- diagnostic: x~ = R^T (C[code] + pad_d(sqrt(pi/2)/m * gamma *
  * S^T (2z-1))) for every packed vector.
  * out DEVICE float [batch][n_heads][n_tokens][head_dim].
@@ -253,6 +277,11 @@ sq_status sq_unpack(const sq_calib *c, int head, const uint32_t *packed,
 
 /* Message of the last error on the calling thread ("" if none). */
 const char *sq_last_error(void);
+
+/* Digest of the sources this library was built from (16 hex digits of a
+ * SHA-256 over the library's source files and this header); the Python
+ * binding refuses a library whose digest differs from its sources. */
+const char *sq_build_digest(void);
 
 #ifdef __cplusplus
 }

@@ -64,10 +64,11 @@ def test_empty_inputs(torch_dev, sq):
     assert torch.all(out == 0.0)
 
 
-def _e2e(torch, sq, cfg, heads, T, budget, dt, x_layout="contiguous"):
+def _e2e(torch, sq, cfg, heads, T, budget, dt, x_layout="contiguous", require_attend=True):
     """Compress K and V on the GPU, score and attend; compare with the
     oracle (records by the acceptance rules, scores on matching tokens,
-    attend when every record matches)."""
+    attend when every record of the head matches; with require_attend at
+    least one head must have been compared)."""
     nkv = len(heads)
     G = cfg.q_heads // cfg.kv_heads
     kcal, kors = H.calibrate_both(sq, cfg, heads, "k", budget)
@@ -102,6 +103,7 @@ def _e2e(torch, sq, cfg, heads, T, budget, dt, x_layout="contiguous"):
     s_g = scores.cpu().numpy()[0]
     o_g = out.cpu().numpy()[0]
     flips = 0
+    compared = 0
     for k in range(nkv):
         sk, rk = H.compare_compress(kors[k], kpn[k], xk[k], T)
         sv, rv = H.compare_compress(vors[k], vpn[k], xv[k], T)
@@ -119,6 +121,10 @@ def _e2e(torch, sq, cfg, heads, T, budget, dt, x_layout="contiguous"):
             oref = oracle.attend(vors[k], ref, scale, rv.codes)
             fl = np.linalg.norm(oref, axis=1, keepdims=True) / math.sqrt(cfg.head_dim)
             H.assert_close_floor(o_g[k * G:(k + 1) * G], oref, fl, f"attend head {k}")
+            compared += 1
+    print(f"  heads with attend compared: {compared}/{nkv}", flush=True)
+    if require_attend:
+        assert compared > 0, "no head's attention output was compared"
     return kp, vp, flips
 
 
@@ -183,9 +189,14 @@ def test_batch_with_shared_and_per_batch_calibration(torch_dev, sq):
 @pytest.mark.parametrize("budget", [0.5, 1.0, 6.0, 8.0])
 def test_extreme_budgets(torch_dev, sq, budget):
     """Low budgets leave many zero-width coordinates; 8 bits/coord gives every
-    coordinate the maximum width and the longest records."""
+    coordinate the maximum width and the longest records.  With 255
+    thresholds per coordinate, in-band flips are common at high budgets, so
+    the attention output is compared where the records match and, for these
+    table placements, unconditionally on oracle records in
+    test_gpu_parity.test_attend_table_placements_on_oracle_records."""
     _case(f"budget {budget} llama8b e2e")
-    _e2e(torch_dev, sq, wl.CONFIGS["llama8b"], [(0, 2), (0, 6)], 200, budget, torch_dev.bfloat16)
+    _e2e(torch_dev, sq, wl.CONFIGS["llama8b"], [(0, 2), (0, 6)], 200, budget, torch_dev.bfloat16,
+         require_attend=budget < 6)
 
 
 @pytest.mark.parametrize("d", [32, 64, 128, 256])

@@ -82,13 +82,21 @@ def test_compress_matches_oracle(torch_dev, sq, name, cfgname, heads, T, budget,
             tot[key] += stats[key]
     print(f"  coords={tot['coords']} in-band={tot['band']} flips={tot['flips']} "
           f"flip-rate={tot['flips'] / tot['coords']:.2e}", flush=True)
-    assert tot["flips"] <= max(4, tot["band"])
+    # compare_compress allows a flip only inside the band; a flip needs the two
+    # sides' rotated values to straddle a threshold, i.e. to lie within the
+    # fp32 rounding of the rotation (~1e-6 sigma), far inside the 1e-4 sigma
+    # band, so flips are a small fraction of the in-band coordinates
+    assert tot["flips"] <= max(3, tot["band"] // 5), tot
 
 
-@pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES[:4], ids=[c[0] for c in CASES[:4]])
+@pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES, ids=[c[0] for c in CASES])
 def test_scores_attend_dequant_on_oracle_records(torch_dev, sq, name, cfgname, heads, T, budget):
     """sq_scores / sq_attend / sq_dequantize fed with ORACLE-packed records and
-    oracle scores, compared with the oracle on the same inputs."""
+    oracle scores, compared with the oracle on the same inputs, on every
+    workload.  The Gemma-shaped keys (head_dim 256) need two passes of the
+    scores kernel (the second adds into the scores) and their values the
+    attend kernel with four 64-coordinate blocks per wave; both are asserted
+    from the launch plan."""
     torch = torch_dev
     cfg = wl.CONFIGS[cfgname]
     _case(f"read-side {name} T={T}")
@@ -98,6 +106,12 @@ def test_scores_attend_dequant_on_oracle_records(torch_dev, sq, name, cfgname, h
     vcal, vors = H.calibrate_both(sq, cfg, heads, "v", budget, n_tokens=T)
     kcal.upload()
     vcal.upload()
+    plan = sq.sq_plan_decode(kcal, vcal, 1, nkv * G, nkv, T)
+    print(f"  plan: score passes {plan.score_passes} (quads {plan.score_quads}, groups "
+          f"{plan.score_wave_groups}); attend placement {plan.attend_placement}, waves "
+          f"{plan.attend_waves}, blocks {plan.attend_blocks}, chunks {plan.attend_chunks}", flush=True)
+    if cfg.head_dim == 256:
+        assert plan.score_passes >= 2 and plan.attend_blocks == 4
     xk = H.data_block(cfg, heads, "k", T)
     xv = H.data_block(cfg, heads, "v", T)
     slot_k = kcal.packed_head_words(T)
@@ -156,11 +170,17 @@ def test_scores_attend_dequant_on_oracle_records(torch_dev, sq, name, cfgname, h
         H.assert_close_floor(o_gpu[k * G:(k + 1) * G], ref, floor, f"attend head {k}")
 
 
-@pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES[:3], ids=[c[0] for c in CASES[:3]])
+@pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES, ids=[c[0] for c in CASES])
 def test_end_to_end(torch_dev, sq, name, cfgname, heads, T, budget):
     """GPU compress -> GPU scores -> GPU attend against the all-oracle pipeline;
     tokens whose key codes flipped inside the band are excluded from the score
-    comparison (and counted)."""
+    comparison (and counted); the attention output of a head is compared when
+    none of its key or value records differs from the oracle's (a flip changes
+    the exact result), and at head_dim <= 128 at least one head must be
+    compared (the Gemma-shaped keys' nine 8-bit coordinates make an in-band
+    flip likely in every head).  The attend kernel itself is compared on every
+    head and workload against oracle inputs in
+    test_scores_attend_dequant_on_oracle_records."""
     torch = torch_dev
     cfg = wl.CONFIGS[cfgname]
     _case(f"end-to-end {name} T={T}")
@@ -194,6 +214,7 @@ def test_end_to_end(torch_dev, sq, name, cfgname, heads, T, budget):
     kp_np = kp.cpu().numpy().view(np.uint32)[0]
     vp_np = vp.cpu().numpy().view(np.uint32)[0]
     excluded = 0
+    compared = 0
     for k in range(nkv):
         oc = kors[k]
         r = oracle.compress(oc, xk[k])
@@ -212,7 +233,11 @@ def test_end_to_end(torch_dev, sq, name, cfgname, heads, T, budget):
             oref = oracle.attend(vors[k], ref, scale, rvv.codes)
             floor = np.linalg.norm(oref, axis=1, keepdims=True) / math.sqrt(cfg.head_dim)
             H.assert_close_floor(o_gpu[k * G:(k + 1) * G], oref, floor, f"e2e attend head {k}")
-    print(f"  tokens excluded for in-band key flips: {excluded}", flush=True)
+            compared += 1
+    print(f"  tokens excluded for in-band key flips: {excluded}; heads with attend compared: "
+          f"{compared}/{nkv}", flush=True)
+    if cfg.head_dim <= 128:
+        assert compared > 0
 
 
 def test_compress_is_deterministic(torch_dev, sq):
@@ -226,3 +251,63 @@ def test_compress_is_deterministic(torch_dev, sq):
     a = _compress_gpu(torch, sq, cal, x[None], torch.bfloat16, 640)
     b = _compress_gpu(torch, sq, cal, x[None], torch.bfloat16, 640)
     assert np.array_equal(a, b)
+
+
+# Value calibrations whose widths reach 7 or 8 bits: the attend kernel's
+# centroid tables then no longer fit one column per lane; they are packed in
+# LDS (a few wide coordinates) or read from device memory (many).
+PLACEMENTS = [
+    # name, config, stream calibrated as values, budget, max_bits, expected placement
+    ("values-8b", "llama8b", "v", 8.0, 8, 2),
+    ("values-6b", "llama8b", "v", 6.0, 8, None),
+    ("keyspectrum-3b", "llama8b", "k", 3.0, 8, 1),
+    ("keyspectrum-3b-max7", "llama8b", "k", 3.0, 7, 1),
+]
+
+
+@pytest.mark.parametrize("name,cfgname,which,budget,max_bits,want", PLACEMENTS,
+                         ids=[c[0] for c in PLACEMENTS])
+def test_attend_table_placements_on_oracle_records(torch_dev, sq, name, cfgname, which, budget,
+                                                   max_bits, want):
+    """sq_attend on oracle-packed value records and oracle scores, compared
+    with oracle.attend unconditionally, for calibrations whose widths reach 7
+    and 8 bits (packed and device-memory centroid tables)."""
+    torch = torch_dev
+    cfg = wl.CONFIGS[cfgname]
+    heads = [(0, 2), (0, 6)]
+    T, nkv, G = 700, 2, cfg.q_heads // cfg.kv_heads
+    _case(f"attend placement {name} budget={budget} max_bits={max_bits}")
+    X = np.stack([wl.calibration_set(cfg, l, h, which) for l, h in heads]).astype(np.float32)
+    vcal = sq.sq_calibrate(X, budget, 0, None, max_bits=max_bits).upload()
+    vors = [oracle.calibrate(X[k], budget, 0, None, max_bits=max_bits) for k in range(nkv)]
+    for k in range(nkv):
+        assert np.array_equal(vcal.export(k)["widths"], vors[k].widths)
+    plan = sq.sq_plan_decode(None, vcal, 1, nkv * G, nkv, T)
+    mw = max(int(v.widths.max()) for v in vors)
+    print(f"  max width {mw}; attend placement {plan.attend_placement}, waves {plan.attend_waves}",
+          flush=True)
+    assert mw >= 7 and plan.attend_placement != 0
+    if want is not None:
+        assert plan.attend_placement == want
+    x = np.stack([wl.kv_block(cfg, l, h, which, T, "data") for l, h in heads])
+    slot = vcal.packed_head_words(T)
+    vp = np.zeros((1, nkv, slot), np.uint32)
+    rv = []
+    for k in range(nkv):
+        r = oracle.compress(vors[k], x[k])
+        p = oracle.pack(vors[k].widths, 0, r.codes, r.z, r.gamma)
+        vp[0, k, :len(p)] = p
+        rv.append(r)
+    s = (np.random.default_rng(17).standard_normal((nkv * G, T)) * 12.0).astype(np.float32)
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    ws = torch.zeros(sq.sq_attend_workspace_bytes(1, nkv * G, T, cfg.head_dim) // 4 + 1,
+                     dtype=torch.float32, device="cuda")
+    out = torch.zeros((1, nkv * G, cfg.head_dim), dtype=torch.float32, device="cuda")
+    sq.sq_attend(vcal, torch.from_numpy(s[None].copy()).cuda(), scale,
+                 torch.from_numpy(vp.view(np.int32)).cuda(), T, ws, out, nkv)
+    torch.cuda.synchronize()
+    o_gpu = out.cpu().numpy()[0]
+    for k in range(nkv):
+        ref = oracle.attend(vors[k], s[k * G:(k + 1) * G].astype(np.float64), scale, rv[k].codes)
+        floor = np.linalg.norm(ref, axis=1, keepdims=True) / math.sqrt(cfg.head_dim)
+        H.assert_close_floor(o_gpu[k * G:(k + 1) * G], ref, floor, f"attend {name} head {k}")

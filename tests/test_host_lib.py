@@ -189,3 +189,25 @@ def test_workspace_size_formula():
     assert sq.sq_attend_workspace_bytes(1, 32, 32768, 128) == 32 * 32 * 130 * 4
     assert sq.sq_attend_workspace_bytes(1, 4, 1, 32) == 4 * 1 * 34 * 4
     assert sq.sq_attend_workspace_bytes(1, 4, 0, 32) == 0
+
+
+def test_stale_library_is_refused(tmp_path):
+    """A libsq.so built from other sources than the ones beside it is refused
+    at load time (its compiled-in source digest differs), so a test or a
+    benchmark can never run an out-of-date binary."""
+    import shutil
+    import subprocess
+    import sys
+    sq.lib()  # the in-tree library exists and matches
+    pkg = os.path.join(ROOT, "compression_sq_compress_amd")
+    dst = tmp_path / "compression_sq_compress_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("_build", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    probe = ("import sys; sys.path.insert(0, %r); import compression_sq_compress_amd as m; "
+             "m.lib(); print('loaded')" % str(tmp_path))
+    r = subprocess.run([sys.executable, "-c", probe], capture_output=True, text=True)
+    assert r.returncode == 0 and "loaded" in r.stdout, r.stderr[-2000:]
+    with open(dst / "csrc" / "api.cpp", "a") as f:
+        f.write("\n// a later edit\n")
+    r = subprocess.run([sys.executable, "-c", probe], capture_output=True, text=True)
+    assert r.returncode != 0 and "StaleLibraryError" in r.stderr, (r.stdout, r.stderr[-2000:])
