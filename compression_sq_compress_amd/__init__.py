@@ -30,7 +30,8 @@ EXPORTS = ("sq_calib_default_opts", "sq_calibrate", "sq_calib_upload", "sq_calib
            "sq_calib_info", "sq_calib_export", "sq_calib_save", "sq_calib_load",
            "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_compress_append", "sq_scores",
            "sq_attend_workspace_bytes", "sq_attend", "sq_dequantize", "sq_unpack",
-           "sq_last_error", "sq_build_digest", "sq_plan_decode")
+           "sq_last_error", "sq_build_digest", "sq_plan_decode",
+           "sq_attend_noalloc")
 
 
 class StaleLibraryError(RuntimeError):
@@ -104,6 +105,7 @@ def _load():
         "sq_last_error": (C.c_char_p, []),
         "sq_build_digest": (C.c_char_p, []),
         "sq_plan_decode": (I, [P, P, I, I, I, I, I, I64, C.POINTER(DecodePlan)]),
+        "sq_attend_noalloc": (I, [P, I, I, I, I, I, P, C.c_float, P, I64, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -287,6 +289,19 @@ def sq_attend(cal: Calibration, scores, scale: float, vpacked, n_tokens: int, wo
                              _ptr(scores), float(scale), _ptr(vpacked), vpacked.stride(0),
                              vpacked.stride(1), n_tokens, _ptr(workspace), ws_bytes, _ptr(out),
                              _stream(stream)))
+
+
+def sq_attend_noalloc(cal: Calibration, scores, scale: float, vpacked, n_tokens: int, out,
+                      n_kv_heads: int, first_head: int = 0, calib_batch_stride: int = 0, stream=None):
+    """sq_attend with the partials in the library's fixed device scratch
+    (no workspace argument, nothing allocated)."""
+    import torch
+    B, Hq, d = out.shape
+    assert out.dtype == torch.float32 and out.is_contiguous()
+    assert scores.is_contiguous() and scores.dtype == torch.float32
+    _check(_load().sq_attend_noalloc(cal.handle, first_head, calib_batch_stride, B, Hq, n_kv_heads,
+                                     _ptr(scores), float(scale), _ptr(vpacked), vpacked.stride(0),
+                                     vpacked.stride(1), n_tokens, _ptr(out), _stream(stream)))
 
 
 def sq_dequantize(cal: Calibration, packed, n_tokens: int, out, first_head: int = 0,

@@ -1,5 +1,7 @@
 // sq_attend: softmax-weighted value sum over the packed values (gfx950).
 
+#include <mutex>
+
 #include "devcommon.h"
 
 namespace sq {
@@ -542,12 +544,44 @@ sq_status plan_attend(const sq_calib *vc, int first_head, int calib_batch_stride
 }
 }  // namespace sq
 
-extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride, int batch,
-                               int n_q_heads, int n_kv_heads, const float *scores, float scale,
-                               const uint32_t *vpacked, int64_t ps_batch, int64_t ps_head,
-                               int64_t n_tokens, void *workspace, size_t ws_bytes, float *out,
-                               sq_stream stream) {
-  const char *fn = "sq_attend";
+// Fixed device scratch of sq_attend_noalloc (the split-T partials), one copy
+// per GPU for the life of the process.  In host code `scratch` names a
+// host-side stand-in, never the device array: its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is handed to kernels.  Every chunk's partials are written
+// in full before the combine reads them, so nothing needs clearing between
+// calls; calls that overlap on one GPU share the array and race.
+namespace sq {
+__device__ __align__(256) float scratch[SQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+}  // namespace sq
+static std::mutex g_scratch_mu;
+static void *g_scratch_addr[64] = {};
+
+static sq_status scratch_for_current_device(const char *fn, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev < 0 || dev >= 64) return fail(SQ_ERR_UNSUPPORTED, std::string(fn) + ": device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(sq::scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (!p) return fail(SQ_ERR_HIP, std::string(fn) + ": no device address for the scratch array");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SQ_OK;
+}
+
+// sq_attend and sq_attend_noalloc.  With scratch_ok the partials go to the
+// library's fixed device scratch (workspace == nullptr on entry): its address
+// is taken only after every argument has been validated.
+static sq_status attend_impl(const char *fn, const sq_calib *vc, int first_head, int calib_batch_stride,
+                             int batch, int n_q_heads, int n_kv_heads, const float *scores, float scale,
+                             const uint32_t *vpacked, int64_t ps_batch, int64_t ps_head, int64_t n_tokens,
+                             void *workspace, size_t ws_bytes, float *out, sq_stream stream,
+                             bool scratch_ok) {
   sq_status st = check_handle(vc, fn);
   if (st != SQ_OK) return st;
   if (n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads)
@@ -574,11 +608,20 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
     hipLaunchKernelGGL(attend_combine_kernel, dim3(batch * n_q_heads), dim3(256), 0, s, a);
     return launched(fn);
   }
-  if (!scores || !vpacked || !workspace) return fail(SQ_ERR_ARG, "sq_attend: NULL pointer");
+  if (!scores || !vpacked || (!workspace && !scratch_ok)) return fail(SQ_ERR_ARG, "sq_attend: NULL pointer");
   st = check_slots(vc, n_tokens, n_kv_heads, batch, ps_batch, ps_head, fn);
   if (st != SQ_OK) return st;
-  if (ws_bytes < sq_attend_workspace_bytes(batch, n_q_heads, n_tokens, d))
-    return fail(SQ_ERR_ARG, "sq_attend: workspace too small");
+  const size_t ws_need = sq_attend_workspace_bytes(batch, n_q_heads, n_tokens, d);
+  if (scratch_ok) {
+    if (ws_need > SQ_NOALLOC_SCRATCH_BYTES)
+      return fail(SQ_ERR_UNSUPPORTED, std::string(fn) + ": the partials need " + std::to_string(ws_need) +
+                                          " bytes, more than the library's fixed scratch of " +
+                                          std::to_string((size_t)SQ_NOALLOC_SCRATCH_BYTES) + " bytes");
+    st = scratch_for_current_device(fn, &workspace);
+    if (st != SQ_OK) return st;
+    ws_bytes = SQ_NOALLOC_SCRATCH_BYTES;
+  }
+  if (ws_bytes < ws_need) return fail(SQ_ERR_ARG, "sq_attend: workspace too small");
   AttendPlan P;
   st = plan_attend(vc, first_head, calib_batch_stride, batch, n_q_heads, n_kv_heads, n_tokens, P);
   if (st != SQ_OK) return st;
@@ -604,6 +647,23 @@ extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_bat
   const size_t lds2 = (size_t)(a.n_chunks + d) * 4;
   hipLaunchKernelGGL(attend_combine_kernel, dim3(batch * n_q_heads), dim3(256), lds2, s, a);
   return launched(fn);
+}
+
+extern "C" sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride, int batch,
+                               int n_q_heads, int n_kv_heads, const float *scores, float scale,
+                               const uint32_t *vpacked, int64_t ps_batch, int64_t ps_head,
+                               int64_t n_tokens, void *workspace, size_t ws_bytes, float *out,
+                               sq_stream stream) {
+  return attend_impl("sq_attend", vc, first_head, calib_batch_stride, batch, n_q_heads, n_kv_heads, scores,
+                     scale, vpacked, ps_batch, ps_head, n_tokens, workspace, ws_bytes, out, stream, false);
+}
+
+extern "C" sq_status sq_attend_noalloc(const sq_calib *vc, int first_head, int calib_batch_stride,
+                                       int batch, int n_q_heads, int n_kv_heads, const float *scores,
+                                       float scale, const uint32_t *vpacked, int64_t ps_batch,
+                                       int64_t ps_head, int64_t n_tokens, float *out, sq_stream stream) {
+  return attend_impl("sq_attend_noalloc", vc, first_head, calib_batch_stride, batch, n_q_heads, n_kv_heads,
+                     scores, scale, vpacked, ps_batch, ps_head, n_tokens, nullptr, 0, out, stream, true);
 }
 
 // Diagnostic: how sq_scores and sq_attend launch for these arguments.

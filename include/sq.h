@@ -234,6 +234,25 @@ sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride,
                     size_t ws_bytes, float *out, sq_stream stream);
 
 /*
+ * sq_attend_noalloc -- sq_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same result, with the split-T
+ * partials in the library's fixed device scratch instead of a caller
+ * workspace.  The scratch is a SQ_NOALLOC_SCRATCH_BYTES (32 MiB) array that
+ * each GPU the library runs on holds until the process ends; calls that need
+ * more (sq_attend_workspace_bytes of the same sizes above the limit) fail
+ * with SQ_ERR_UNSUPPORTED before anything is enqueued.  The call allocates
+ * nothing.  All calls on one GPU share its array, so calls that overlap in
+ * time on one GPU (different streams) race; calls in stream order do not.
+ * Arguments, layout and errors otherwise as sq_attend.
+ */
+#define SQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+sq_status sq_attend_noalloc(const sq_calib *vc, int first_head, int calib_batch_stride,
+                            int batch, int n_q_heads, int n_kv_heads, const float *scores,
+                            float scale, const uint32_t *vpacked, int64_t ps_batch,
+                            int64_t ps_head, int64_t n_tokens, float *out, sq_stream stream);
+
+/*
  * sq_plan_decode -- diagnostic: how sq_scores (keys handle kc) and sq_attend
  * (values handle vc) would launch for these arguments on the current device,
  * without launching anything.  Either handle may be NULL (its fields stay 0).
