@@ -65,18 +65,30 @@ def kernel_source_digest() -> str:
     return source_digest()
 
 
-def measured_traffic():
-    """HBM bytes per compress launch from the committed counter summary, or
-    None when it is missing or was taken on a different kernel source."""
+def measured_traffic(kernel: str = "compress"):
+    """HBM bytes per launch of ``kernel`` (compress, scores, decode) from the
+    committed counter summary, or None when it is missing or was taken on
+    other kernel sources."""
     try:
         txt = open(TRAFFIC_FILE).read()
     except OSError:
         return None
     m_src = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]{16})", txt)
-    m_b = re.search(r"HBM bytes per compress launch \(scaled\):\s*([0-9.eE+]+)", txt)
+    m_b = re.search(r"HBM bytes per %s launch \(scaled\):\s*([0-9.eE+]+)" % kernel, txt)
     if not m_src or not m_b or m_src.group(1) != kernel_source_digest():
         return None
     return float(m_b.group(1))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(cfg, kcal_in, vcal_in, n_seqs, n_tokens):
@@ -114,6 +126,7 @@ def cpu_baseline(cfg, kcal_in, vcal_in, n_seqs, n_tokens):
             dt += time.perf_counter() - t0
     n_vec = 2 * n_seqs * H * n_tokens
     return dict(value=n_vec / dt, unit="KV vectors/s", cores=int(threads), kind="oracle",
+                cpu_model=cpu_model(), host_cpus=os.cpu_count(),
                 sample=(f"sequences 0-{n_seqs - 1}, {H} KV heads x {n_tokens} tokens each, K and V "
                         f"compress+pack, scores for the {G} query heads of each KV head, "
                         f"softmax+attend; {n_vec} vectors in {dt:.2f} s of oracle time"))
@@ -194,8 +207,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
-    ms_ck, ms_cv, ms_sc, ms_at = per.mean(axis=0)
+    ms_ck, ms_cv, ms_sc, ms_at = np.median(per, axis=0)  # median over the timed steps
     ms_step = wall * 1e3 / args.steps
+
+    # the fused decode step (scores, softmax and value sum in one pass, no score
+    # tensor), on the same records and queries, outside the timed steps
+    out2 = torch.empty_like(out)
+    for _ in range(args.warmup):
+        sq.sq_decode(kcal, vcal, q, kp, vp, T, scale, ws, out2, Hkv, stream=sh)
+    dev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        dev_[k][0].record(stream)
+        sq.sq_decode(kcal, vcal, q, kp, vp, T, scale, ws, out2, Hkv, stream=sh)
+        dev_[k][1].record(stream)
+    torch.cuda.synchronize()
+    ms_dec = float(np.median([e[0].elapsed_time(e[1]) for e in dev_]))
+    dec_err = float(((out2 - out).abs() / (out.abs() + out.norm(dim=-1, keepdim=True) / math.sqrt(d))).max())
 
     # decode-time append, outside the timed step: the last token of every
     # (sequence, KV head) compressed again into its slot (same words), K then V
@@ -216,6 +243,7 @@ def main():
     bytes_cv = n_vec * (2 * d + 4 * Wv)
     bytes_sc = n_vec * 4 * Wk + B * Hq * T * 4 + B * Hq * d * 2
     bytes_at = n_vec * 4 * Wv + B * Hq * T * 4 + B * Hq * d * 4
+    bytes_dec = n_vec * 4 * (Wk + Wv) + B * Hq * d * (2 + 4)   # both records, q in, out
     gbps = lambda b, ms: b / (ms * 1e-3) / 1e9
     comp_ms = ms_ck + ms_cv
     # the compress kernel runs twice per step (K, V): per-launch averages
@@ -251,6 +279,12 @@ def main():
         "score_packedK_GBps": gbps(n_vec * 4 * Wk, ms_sc),
         "attend_GBps": gbps(bytes_at, ms_at),
         "attend_hbm_frac": gbps(bytes_at, ms_at) / HBM_PEAK_GBPS,
+        "decode_fused": {"what": "sq_decode: scores, online softmax and value sum in one pass over the "
+                                 "packed K and V (no score tensor), same records and queries",
+                         "ms": ms_dec, "GBps": gbps(bytes_dec, ms_dec),
+                         "hbm_frac": gbps(bytes_dec, ms_dec) / HBM_PEAK_GBPS,
+                         "alg_bytes": bytes_dec, "split_path_ms": ms_sc + ms_at,
+                         "max_rel_diff_vs_split": dec_err},
         "append_decode": {"what": f"1 new token per (sequence, KV head), K and V: {2 * B * Hkv} vectors "
                                   f"into slots at token {T - 1}", "us": append_us},
         "roofline": {"bound": "hbm", "kernel": "compress2_kernel<128,bf16> (register quantiser; per launch, K and V averaged)",
@@ -260,7 +294,8 @@ def main():
         "roofline_scores": {"bound": "hbm", "kernel": "scores_kernel (split-K waves, 4x4x4 bf16 MFMA, joint tables)",
                             "achieved": gbps(bytes_sc, ms_sc), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": gbps(bytes_sc, ms_sc) / HBM_PEAK_GBPS,
-                            "traffic": None, "alg_bytes_per_launch": bytes_sc, "launch_ms": ms_sc},
+                            "traffic": measured_traffic("scores"), "alg_bytes_per_launch": bytes_sc,
+                            "launch_ms": ms_sc},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, (Xk, Gk), Xv, args.cpu_sample_seqs, T)

@@ -31,7 +31,7 @@ EXPORTS = ("sq_calib_default_opts", "sq_calibrate", "sq_calib_upload", "sq_calib
            "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_compress_append", "sq_scores",
            "sq_attend_workspace_bytes", "sq_attend", "sq_dequantize", "sq_unpack",
            "sq_last_error", "sq_build_digest", "sq_plan_decode",
-           "sq_attend_noalloc")
+           "sq_attend_noalloc", "sq_decode")
 
 
 class StaleLibraryError(RuntimeError):
@@ -61,7 +61,8 @@ class HeadInfo(C.Structure):
 class DecodePlan(C.Structure):
     _fields_ = [("score_passes", C.c_int), ("score_quads", C.c_int), ("score_wave_groups", C.c_int),
                 ("attend_placement", C.c_int), ("attend_waves", C.c_int), ("attend_blocks", C.c_int),
-                ("attend_chunks", C.c_int)]
+                ("attend_chunks", C.c_int), ("decode_launches", C.c_int),
+                ("decode_waves", C.c_int), ("decode_lds_bytes", C.c_int)]
 
 
 _lib = None
@@ -106,6 +107,8 @@ def _load():
         "sq_build_digest": (C.c_char_p, []),
         "sq_plan_decode": (I, [P, P, I, I, I, I, I, I64, C.POINTER(DecodePlan)]),
         "sq_attend_noalloc": (I, [P, I, I, I, I, I, P, C.c_float, P, I64, I64, I64, P, P]),
+        "sq_decode": (I, [P, P, I, I, I, I, I, P, I, P, I64, I64, P, I64, I64, I64, C.c_float, P, U64,
+                          P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -289,6 +292,23 @@ def sq_attend(cal: Calibration, scores, scale: float, vpacked, n_tokens: int, wo
                              _ptr(scores), float(scale), _ptr(vpacked), vpacked.stride(0),
                              vpacked.stride(1), n_tokens, _ptr(workspace), ws_bytes, _ptr(out),
                              _stream(stream)))
+
+
+def sq_decode(kcal: Calibration, vcal: Calibration, q, kpacked, vpacked, n_tokens: int, scale: float,
+              workspace, out, n_kv_heads: int, first_head: int = 0, calib_batch_stride: int = 0,
+              stream=None):
+    """Fused decode step: q device [batch][n_q_heads][d] contiguous; kpacked /
+    vpacked [batch][n_kv][slot]; workspace of sq_attend_workspace_bytes;
+    out float32 [batch][n_q_heads][d]."""
+    import torch
+    assert q.is_contiguous() and q.dim() == 3
+    B, Hq, d = q.shape
+    assert out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, d)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().sq_decode(kcal.handle, vcal.handle, first_head, calib_batch_stride, B, Hq, n_kv_heads,
+                             _ptr(q), _dtype_code(q), _ptr(kpacked), kpacked.stride(0), kpacked.stride(1),
+                             _ptr(vpacked), vpacked.stride(0), vpacked.stride(1), n_tokens, float(scale),
+                             _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
 
 
 def sq_attend_noalloc(cal: Calibration, scores, scale: float, vpacked, n_tokens: int, out,

@@ -53,7 +53,9 @@ struct DevHead {
   int32_t n_chunks;
   int32_t n_quads;      // score schedule quads
   int32_t n_plut;       // joint-table entries (the last one is all zero)
-  int32_t pad[3];
+  int32_t n_fgroups;    // fused decode schedule: groups (code groups, then QJL groups)
+  int32_t n_fent;       // fused decode schedule: table entries over all groups
+  int32_t n_fqjl;       // of the groups, the trailing QJL groups
   int64_t off_R;        // float [d][d], row i = eigenvector i (y = R x)
   int64_t off_RT;       // float [d][d], R transposed
   int64_t off_Rfrag;    // bf16 [3][d/16][d/32][64][8]: hi/mid/lo split of R in
@@ -75,6 +77,7 @@ struct DevHead {
   int64_t off_tree2;    // float [n_tree2] per-coordinate padded trees (see P2_WAVE)
   int64_t off_csig2;    // float [n_csig2] signal centroids * sigma_i, padded per coordinate
   int64_t off_Rfrag2;   // bf16 [3][d/16][d/32][64][8] like off_Rfrag, rows permuted (see P2_WAVE)
+  int64_t off_fsched;   // uint32 fused decode schedule (FS_* layout below)
 };
 
 // Register-quantising compress plan.  Coordinates are taken in groups of 4
@@ -93,6 +96,33 @@ struct DevHead {
 constexpr int P2_WAVE = 64;
 
 static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
-static_assert(sizeof(DevHead) == 208, "DevHead layout");
+// Fused decode schedule of a key head (sq_decode).  The record's code fields
+// are cut, in bit order, into groups of adjacent fields of at most FG_BITS
+// bits together (a wider field is a group of its own; zero-width coordinates
+// have no field), then the m QJL bits into groups of at most FG_BITS.  At run
+// time each group gets a table of 2^width entries per query head: for a code
+// group entry v = sum over its coordinates of q~_i C_i[the field of i in v],
+// for a QJL group entry v = sqrt(pi/2)/m sum over its bits j of
+// w_j (2 v_j - 1), w = S q~[0:d_eff]; a token's score is then one table
+// read per group (QJL groups scaled by gamma).  Tables are placed largest
+// first, so each starts at a multiple of its own size; one zero entry follows
+// them.  Layout (uint32), n = n_fgroups, nq = n_fqjl:
+//   [2n]   per group: width (bits 0-3) | QJL group (bit 4) | first table entry
+//          << 8; first coordinate or QJL bit (bits 0-11) | count << 12;
+//   [nq]   per QJL group: bit position relative to word W - 2 (bits 0-7) |
+//          width << 8 | first table entry << 12 (the QJL bits and gamma lie in
+//          the last two words when m <= 16);
+//   (padded to 16 words)
+//   [3][W + 1][FS_SLOTS][2]  for table entries of 4, 8 and 16 bytes (E = 2,
+//          3, 4) and each window j (record words j - 1, j; word -1 is zero):
+//          FS_SLOTS slots of (window shift | table byte offset << 5, field
+//          mask << E), the code groups whose field, read from bit
+//          (pos + 32 - E) % 32 of word j - 1, lands at bit E of the window; unused
+//          slots read the zero entry (the used slots come first);
+//   [3][W + 1]  the number of used slots of each window, per entry size.
+constexpr int FS_SLOTS = 8;
+constexpr int FG_BITS = 6;
+
+static_assert(sizeof(DevHead) == 216, "DevHead layout");
 
 }  // namespace sq

@@ -113,6 +113,95 @@ static ScoreSched build_score_sched(const HeadCal &hc) {
 }
 
 
+// Fused decode schedule of one head (FS layout in devtypes.h).
+struct FusedSched {
+  std::vector<uint32_t> words;  // FS layout (devtypes.h)
+  int n_groups = 0, n_ent = 0, n_qjl = 0;
+};
+
+// Empty schedule (n_groups = 0: sq_decode refuses the head) when a window
+// holds more than FS_SLOTS code groups or the QJL bits do not lie in the
+// record's last two words (m > 16).
+static FusedSched build_fused_sched(const HeadCal &hc) {
+  struct Grp { int pos, width, first, count; bool qjl; };
+  std::vector<Grp> g;
+  const int d = hc.d;
+  for (int i = 0; i < d;) {
+    if (hc.widths[i] == 0) { ++i; continue; }
+    Grp cur{hc.bit_off[i], hc.widths[i], i, 1, false};
+    int j = i + 1;
+    // extend over following coordinates (zero-width ones add no bits)
+    while (j < d && cur.width + hc.widths[j] <= FG_BITS && cur.width <= FG_BITS) {
+      cur.width += hc.widths[j];
+      ++j;
+    }
+    // trailing zero-width coordinates are not part of the group
+    while (j > i + 1 && hc.widths[j - 1] == 0) --j;
+    cur.count = j - i;
+    g.push_back(cur);
+    i = j;
+  }
+  const int n_code = (int)g.size();
+  for (int j = 0; j < hc.m; j += FG_BITS) {
+    const int n = std::min(FG_BITS, hc.m - j);
+    g.push_back(Grp{hc.code_bits + j, n, j, n, true});
+  }
+  FusedSched F;
+  const int ng = (int)g.size(), nq = ng - n_code, W = hc.W;
+  if (hc.m > 16) return F;
+  // tables placed largest first: each starts at a multiple of its size
+  std::vector<int> order(ng);
+  for (int k = 0; k < ng; ++k) order[k] = k;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return g[x].width > g[y].width; });
+  std::vector<uint32_t> e0(ng);
+  uint32_t ent = 0;
+  for (int k : order) {
+    e0[k] = ent;
+    ent += 1u << g[k].width;
+  }
+  const size_t slots_off = ((size_t)2 * ng + nq + 15) & ~(size_t)15;
+  const size_t var_words = (size_t)(W + 1) * FS_SLOTS * 2;
+  F.words.assign(slots_off + 3 * var_words + 3 * (size_t)(W + 1), 0u);
+  uint32_t *Q = F.words.data() + 2 * ng;
+  int iq = 0;
+  for (int k = 0; k < ng; ++k) {
+    const Grp &q = g[k];
+    F.words[2 * k] = (uint32_t)q.width | (q.qjl ? 16u : 0u) | (e0[k] << 8);
+    F.words[2 * k + 1] = (uint32_t)q.first | ((uint32_t)q.count << 12);
+    if (q.qjl) {
+      const int rel = q.pos - 32 * (W - 2);  // within words W-2, W-1 (word -1 reads as zero)
+      if (rel < 0 || rel + q.width > 48) return FusedSched{};
+      Q[iq++] = (uint32_t)rel | ((uint32_t)q.width << 8) | (e0[k] << 12);
+    }
+  }
+  // window slots, for table entries of 4, 8 and 16 bytes (E = 2, 3, 4): group
+  // k with field at bit pos is read from window j = (pos + 32 - E) / 32 (the
+  // 64 bits of words j - 1, j starting at bit (pos + 32 - E) % 32 of word j - 1,
+  // so that the field lands at bit E); slot (shift | table byte offset << 5,
+  // field mask << E); unused slots read the zero entry after the tables
+  for (int v = 0; v < 3; ++v) {
+    const int E = 2 + v;
+    uint32_t *S = F.words.data() + slots_off + v * var_words;
+    std::vector<int> used(W + 1, 0);
+    uint32_t *Ncnt = F.words.data() + slots_off + 3 * var_words + (size_t)v * (W + 1);
+    for (int j = 0; j <= W; ++j)
+      for (int u = 0; u < FS_SLOTS; ++u) S[((size_t)j * FS_SLOTS + u) * 2] = (ent << E) << 5;
+    for (int k = 0; k < n_code; ++k) {
+      const Grp &q = g[k];
+      const int j = (q.pos + 32 - E) / 32;
+      if (j > W || used[j] == FS_SLOTS) return FusedSched{};
+      uint32_t *sl = S + ((size_t)j * FS_SLOTS + used[j]++) * 2;
+      sl[0] = (uint32_t)((q.pos + 32 - E) & 31) | ((e0[k] << E) << 5);
+      sl[1] = ((1u << q.width) - 1u) << E;
+    }
+    for (int j = 0; j <= W; ++j) Ncnt[j] = (uint32_t)used[j];
+  }
+  F.n_groups = ng;
+  F.n_qjl = nq;
+  F.n_ent = (int)ent;
+  return F;
+}
+
 void release_tables(sq_calib *c) {
   if (c->dev_blob) {
     int cur = -1;
@@ -431,6 +520,8 @@ sq_status upload_tables(sq_calib *c, void *stream) {
   std::vector<ScoreSched> scheds(nh);
   for (int h = 0; h < nh; ++h) scheds[h] = build_score_sched(c->heads[h]);
   std::vector<HostPlan2> plans2(nh);
+  std::vector<FusedSched> fsch(nh);
+  for (int h = 0; h < nh; ++h) fsch[h] = build_fused_sched(c->heads[h]);
   for (int h = 0; h < nh; ++h) plans2[h] = build_plan2(c->heads[h]);
   // host image of the blob: [DevHead x nh] then per-head sections
   std::vector<DevHead> desc(nh);
@@ -475,6 +566,10 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.off_tree2 = off;   off = align256(off + sizeof(float) * std::max<size_t>(1, P2.tree.size()));
     D.off_csig2 = off;   off = align256(off + sizeof(float) * std::max<size_t>(1, P2.csig.size()));
     D.off_Rfrag2 = off;  off = align256(off + (P2.ok ? sizeof(uint16_t) * 3 * d * d : 1));
+    D.n_fgroups = fsch[h].n_groups;
+    D.n_fent = fsch[h].n_ent;
+    D.n_fqjl = fsch[h].n_qjl;
+    D.off_fsched = off;  off = align256(off + sizeof(uint32_t) * fsch[h].words.size());
   }
   std::vector<uint8_t> img(off, 0);
   std::memcpy(img.data(), desc.data(), sizeof(DevHead) * nh);
@@ -534,6 +629,7 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
     for (int i = 0; i < d; ++i) Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};
     std::memcpy(img.data() + D.off_sched, scheds[h].quads.data(), sizeof(uint32_t) * scheds[h].quads.size());
+    std::memcpy(img.data() + D.off_fsched, fsch[h].words.data(), sizeof(uint32_t) * fsch[h].words.size());
     std::memcpy(img.data() + D.off_plut, scheds[h].lut.data(), sizeof(uint32_t) * scheds[h].lut.size());
     if (!P.tree.empty()) std::memcpy(img.data() + D.off_tree, P.tree.data(), sizeof(float) * P.tree.size());
     if (!P.csig.empty()) std::memcpy(img.data() + D.off_csig, P.csig.data(), sizeof(float) * P.csig.size());

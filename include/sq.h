@@ -197,6 +197,12 @@ sq_status sq_compress_append(const sq_calib *c, int first_head, int n_heads,
 
 /*
  * sq_scores -- raw q.k scores read from the packed keys (no softmax scale).
+ * SpectralQuant README "Overview" (decode-time attention reads the compressed
+ * keys: the query is rotated into the calibrated basis once and scored against
+ * the codes) and "Repository Structure" (selective_qjl: the QJL correction on
+ * the signal dims); the sign-sketch inner-product estimator with factor
+ * sqrt(pi/2)/m is the QJL estimator (TurboQuant reference-implementation page,
+ * "Project Structure", the Prod quantiser's QJL stage).
  * The query of each query head is rotated once, q~ = R q; then
  *   s_t = sum_i q~_i C_i[code_ti] + sqrt(pi/2)/m * gamma_t * sum_j w_j (2 z_tj - 1),
  * w = S q~[0:d_eff].  Query head hq of batch b reads KV head
@@ -218,7 +224,11 @@ size_t sq_attend_workspace_bytes(int batch, int n_q_heads, int64_t n_tokens,
 
 /*
  * sq_attend -- o = sum_t softmax(scale * s)_t * v~_t for every (b, hq), where v~
- * is the dequantised value (R_v^T C[code]).  Split over token chunks with
+ * is the dequantised value (R_v^T C[code]).  SpectralQuant README "Overview"
+ * (values are dequantised for the attention-weighted sum; no QJL on values:
+ * TurboQuant reference-implementation page, "Key Findings" 2, MSE quantiser
+ * for values).  Softmax is max-subtracted; the sum is formed in the rotated
+ * value space and un-rotated once (R_v^T is linear).  Split over token chunks with
  * (max, sum exp, partial sum) partials in `workspace`, then an ordered
  * (deterministic) combine and one un-rotation per (b, hq).
  * scores  DEVICE float [batch][n_q_heads][n_tokens] (e.g. from sq_scores).
@@ -232,6 +242,38 @@ sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride,
                     float scale, const uint32_t *vpacked, int64_t ps_batch,
                     int64_t ps_head, int64_t n_tokens, void *workspace,
                     size_t ws_bytes, float *out, sq_stream stream);
+
+/*
+ * sq_decode -- the fused decode step: for every (b, hq),
+ *   o = sum_t softmax(scale * s)_t v~_t,  s_t the score sq_scores gives,
+ * computed in one pass over the packed keys and values with no score tensor
+ * in device memory (SpectralQuant README "Overview": decode-time attention
+ * over the compressed cache; "Headline Results": the per-step decode
+ * latency).  Each key record is read once by the lane of its token; its
+ * code fields are cut into groups of at most 6 bits (a wider field alone),
+ * and per (batch, KV head) the query group's tables of every group's
+ * contribution (sum of q~_i C_i[code] over the group's coordinates, and the
+ * QJL term sqrt(pi/2)/m sum_j w_j (2 z_j - 1) of the sign bits) are built
+ * once in LDS in fp32, so a score costs one table read per group.  Then the
+ * online softmax and the value sum of sq_attend; split over token chunks with
+ * the same (max, sum exp, partial sum) partials and ordered combine.
+ * q        DEVICE [batch][n_q_heads][head_dim], dtype qdt, contiguous.
+ * kpacked  DEVICE key slots (kps_batch, kps_head words), as from sq_compress
+ *          with kc; vpacked likewise for vc.  Head (b, h) of both handles is
+ *          first_head + b * calib_batch_stride + h.
+ * workspace DEVICE, ws_bytes >= sq_attend_workspace_bytes(batch, n_q_heads,
+ *          n_tokens, head_dim).
+ * out      DEVICE float [batch][n_q_heads][head_dim].  n_tokens == 0 writes zeros.
+ * Errors: as sq_scores and sq_attend; SQ_ERR_UNSUPPORTED when a key record
+ * exceeds 32 words or the score tables do not fit the LDS (use sq_scores +
+ * sq_attend then).
+ */
+sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first_head,
+                    int calib_batch_stride, int batch, int n_q_heads, int n_kv_heads,
+                    const void *q, sq_dtype qdt, const uint32_t *kpacked,
+                    int64_t kps_batch, int64_t kps_head, const uint32_t *vpacked,
+                    int64_t vps_batch, int64_t vps_head, int64_t n_tokens, float scale,
+                    void *workspace, size_t ws_bytes, float *out, sq_stream stream);
 
 /*
  * sq_attend_noalloc -- sq_attend for callers that cannot allocate device
@@ -265,12 +307,16 @@ sq_status sq_attend_noalloc(const sq_calib *vc, int first_head, int calib_batch_
  *   attend_waves       waves (token chunks) per workgroup
  *   attend_blocks      64-coordinate blocks each wave serves (head_dim / 64)
  *   attend_chunks      token chunks per (batch, query head)
+ *   decode_launches    launches of the fused kernel (query heads served four
+ *                      at a time), decode_waves its waves per workgroup,
+ *                      decode_lds_bytes its LDS per workgroup
  * Errors: as sq_scores / sq_attend for the head range; SQ_ERR_STATE when a
  * handle is not uploaded.
  */
 typedef struct {
   int score_passes, score_quads, score_wave_groups;
   int attend_placement, attend_waves, attend_blocks, attend_chunks;
+  int decode_launches, decode_waves, decode_lds_bytes;  /* sq_decode (both handles given) */
 } sq_decode_plan;
 sq_status sq_plan_decode(const sq_calib *kc, const sq_calib *vc, int first_head,
                          int calib_batch_stride, int batch, int n_q_heads, int n_kv_heads,
@@ -278,7 +324,9 @@ sq_status sq_plan_decode(const sq_calib *kc, const sq_calib *vc, int first_head,
 
 /*
  * sq_dequantize -- diagnostic: x~ = R^T (C[code] + pad_d(sqrt(pi/2)/m * gamma *
- * S^T (2z-1))) for every packed vector.
+ * S^T (2z-1))) for every packed vector: the reconstruction the scores see
+ * (SpectralQuant README "Headline Results": per-vector cosine similarity of
+ * the reconstruction; "Repository Structure", metrics.py).
  * out DEVICE float [batch][n_heads][n_tokens][head_dim].
  */
 sq_status sq_dequantize(const sq_calib *c, int first_head, int n_heads, int batch,

@@ -146,3 +146,43 @@ def test_fullsize_attend_outputs_are_convex_combinations(full):
         hi = np.array([c.max() if len(c) else 0.0 for c in oc.centroids])
         slack = 1e-3 * (np.abs(lo) + np.abs(hi)) + 1e-3 * oc.sigma[0]
         assert np.all(y >= lo - slack) and np.all(y <= hi + slack), f"head {h}"
+
+
+def test_fullsize_decode_on_oracle_inputs(full):
+    """sq_decode over the whole decode batch, in the launch configuration the
+    benchmark times, with one slot's key and value records replaced by the
+    oracle's; that slot's outputs against oracle.attend on oracle scores."""
+    f = full
+    torch = f["torch"]
+    b, h = 45, 6
+    T, G, d = f["T"], f["Hq"] // f["Hkv"], f["d"]
+    _case(f"full-size sq_decode slot b={b} h={h}")
+    xk = f["K"][b, h].float().cpu().numpy()
+    xv = f["V"][b, h].float().cpu().numpy()
+    rk = oracle.compress(f["kors"][h], xk)
+    rv = oracle.compress(f["vors"][h], xv)
+    krec = oracle.pack(f["kors"][h].widths, f["kors"][h].m, rk.codes, rk.z, rk.gamma)
+    vrec = oracle.pack(f["vors"][h].widths, 0, rv.codes, rv.z, rv.gamma)
+    kp = f["kp"].clone()
+    vp = f["vp"].clone()
+    kp[b, h, :krec.size] = torch.from_numpy(krec.view(np.int32)).cuda()
+    vp[b, h, :vrec.size] = torch.from_numpy(vrec.view(np.int32)).cuda()
+    out = torch.empty_like(f["out"])
+    scale = 1.0 / math.sqrt(d)
+    f["sq"].sq_decode(f["kcal"], f["vcal"], f["qd"], kp, vp, T, scale, f["ws"], out, f["Hkv"])
+    torch.cuda.synchronize()
+    o = out[b, h * G:(h + 1) * G].cpu().numpy()
+    qg = f["q"][b, h * G:(h + 1) * G]
+    s = oracle.scores_rotated(f["kors"][h], qg, rk.codes, rk.z, rk.gamma)
+    ref = oracle.attend(f["vors"][h], s, scale, rv.codes)
+    floor = np.linalg.norm(ref, axis=1, keepdims=True) / math.sqrt(d)
+    worst = H.assert_close_floor(o, ref, floor, "full-size decode")
+    print(f"  decode worst err/tol {worst:.3g}", flush=True)
+    allout = out.cpu().numpy()
+    assert np.all(np.isfinite(allout))
+    # the other slots against the split path on the same records, to the parity tolerance
+    ref_all = f["out"].cpu().numpy()
+    mask = np.ones(allout.shape[:2], bool)
+    mask[b, h * G:(h + 1) * G] = False
+    fl = np.linalg.norm(ref_all[mask], axis=1, keepdims=True) / math.sqrt(d)
+    H.assert_close_floor(allout[mask], ref_all[mask], fl, "full-size decode vs scores + attend")

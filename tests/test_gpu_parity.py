@@ -311,3 +311,46 @@ def test_attend_table_placements_on_oracle_records(torch_dev, sq, name, cfgname,
         ref = oracle.attend(vors[k], s[k * G:(k + 1) * G].astype(np.float64), scale, rv[k].codes)
         floor = np.linalg.norm(ref, axis=1, keepdims=True) / math.sqrt(cfg.head_dim)
         H.assert_close_floor(o_gpu[k * G:(k + 1) * G], ref, floor, f"attend {name} head {k}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_attend_head_dim_256_column_tables(torch_dev, sq, G):
+    """head_dim 256 values with widths of at most 6 bits take the column-table
+    attend kernel with four 64-coordinate blocks per wave (the lane's four
+    fields in one 64-bit window of record rows); compared on oracle records
+    and random scores."""
+    torch = torch_dev
+    d, T, nkv = 256, 900, 2
+    _case(f"attend d=256 column tables G={G} T={T}")
+    X = np.stack([wl.flat_data(600, d, seed=50 + k) * np.linspace(3.0, 0.5, d) for k in range(nkv)])
+    X = X.astype(np.float32)
+    vcal = sq.sq_calibrate(X, 3.0, 0, None).upload()
+    vors = [oracle.calibrate(X[k], 3.0, 0, None) for k in range(nkv)]
+    for k in range(nkv):
+        assert np.array_equal(vcal.export(k)["widths"], vors[k].widths)
+    plan = sq.sq_plan_decode(None, vcal, 1, nkv * G, nkv, T)
+    print(f"  max width {max(int(v.widths.max()) for v in vors)}; placement {plan.attend_placement}, "
+          f"waves {plan.attend_waves}, blocks {plan.attend_blocks}", flush=True)
+    assert plan.attend_placement == 0 and plan.attend_blocks == 4
+    x = np.stack([wl.flat_data(T, d, seed=70 + k) * np.linspace(3.0, 0.5, d) for k in range(nkv)])
+    x = wl.round_bf16(x)
+    vp = np.zeros((1, nkv, vcal.packed_head_words(T)), np.uint32)
+    rv = []
+    for k in range(nkv):
+        r = oracle.compress(vors[k], x[k])
+        p = oracle.pack(vors[k].widths, 0, r.codes, r.z, r.gamma)
+        vp[0, k, :len(p)] = p
+        rv.append(r)
+    s = (np.random.default_rng(19 + G).standard_normal((nkv * G, T)) * 16.0).astype(np.float32)
+    scale = 1.0 / math.sqrt(d)
+    ws = torch.zeros(sq.sq_attend_workspace_bytes(1, nkv * G, T, d) // 4 + 1, dtype=torch.float32,
+                     device="cuda")
+    out = torch.zeros((1, nkv * G, d), dtype=torch.float32, device="cuda")
+    sq.sq_attend(vcal, torch.from_numpy(s[None].copy()).cuda(), scale,
+                 torch.from_numpy(vp.view(np.int32)).cuda(), T, ws, out, nkv)
+    torch.cuda.synchronize()
+    o_gpu = out.cpu().numpy()[0]
+    for k in range(nkv):
+        ref = oracle.attend(vors[k], s[k * G:(k + 1) * G].astype(np.float64), scale, rv[k].codes)
+        floor = np.linalg.norm(ref, axis=1, keepdims=True) / math.sqrt(d)
+        H.assert_close_floor(o_gpu[k * G:(k + 1) * G], ref, floor, f"attend d=256 G={G} head {k}")
