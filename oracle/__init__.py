@@ -34,8 +34,8 @@ from .spectralquant import (  # noqa: F401
     dequantize, scores_plain, scores_rotated, softmax, attend, band_mask,
     qjl_band_mask, CompressResult,
 )
-from .record import record_words, field_offsets, pack, unpack  # noqa: F401
-from .turboquant import tq_prod_keys, tq_mse_values, tq_mse_unit  # noqa: F401
+from .record import record_words, field_offsets, norm_position, pack, unpack  # noqa: F401
+from .turboquant import tq_prod_keys, tq_mse_values, tq_mse_unit, tq_calibration  # noqa: F401
 from .metrics import cosine, rel_mse, bits_per_coord, compression_ratio  # noqa: F401
 
 # Pin map: every oracle function and the tests that hold it to something other
@@ -61,6 +61,11 @@ PARITY = {
     "pack/unpack/record_words": "pinned: hand-worked word, brute-force bit writer",
     "tq_mse_unit/tq_mse_values": "pinned: scos-lab distortion table; nearest Max level",
     "tq_prod_keys": "pinned: estimator unbiased with closed-form variance over 5000 sketches",
+    "tq_calibration (normalised pipeline)": "pinned: codes equal the nearest-level rule; reconstructions "
+                                            "equal tq_prod_keys / tq_mse_values to the half rounding "
+                                            "of the stored norms",
+    "normalised variant (calibrate/compress normalize)": "pinned: codes invariant under scaling; "
+                                                         "reconstruction scales with the vector",
     "cosine/rel_mse/bits_per_coord/compression_ratio": "pinned: README headline ratios; "
                                                        "SQ > TQ ordering on every workload",
 }

@@ -24,6 +24,12 @@ Readings taken where the pages are silent (each repeated at its function):
       estimator factor sqrt(pi/2) / m.
   R7  code_i = #{ j : threshold_ij < y_i } (a tie goes to the lower cell, NaN
       gives 0); a zero-width coordinate reconstructs to 0.
+  R8  normalised variant (README Repository Structure lists normalised and
+      unnormalised result sets; TurboQuant stores a per-vector norm): every
+      sample is divided by its norm before calibration, and at compression
+      the vector's norm nu is stored (IEEE half) and the unit vector x / nu
+      is rotated and quantised; reconstructions, scores and value sums are
+      scaled back by the stored nu.  A zero vector keeps nu = 0.
 """
 from __future__ import annotations
 
@@ -215,12 +221,20 @@ class Calibration:
     offsets: np.ndarray        # [d] bit offset of each code field
     qjl_offset: int            # bit offset of z_0
     has_gamma: bool
+    normalized: bool = False   # R8: per-vector norm stored, unit vectors quantised
+
+
+def _unit_rows(x: np.ndarray):
+    """(x / |x| row-wise, |x|); zero rows stay zero."""
+    nu = np.sqrt((x * x).sum(axis=1))
+    return x / np.where(nu > 0, nu, 1.0)[:, None], nu
 
 
 def calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
               gauss: Optional[np.ndarray], max_bits: int = 8,
-              lloyd_iters: int = 200) -> Calibration:
-    """Calibrate one head on ``samples`` [n, d].
+              lloyd_iters: int = 200, normalize: bool = False) -> Calibration:
+    """Calibrate one head on ``samples`` [n, d] (normalised variant R8: on the
+    samples divided by their norms).
 
     1. C = X^T X / n; eigh; descending; sign rule R1; R = V^T.
     2. d_eff = round(PR), kappa (conftest fixture).
@@ -230,6 +244,8 @@ def calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
     5. QJL matrix S = gauss[:m, :d_eff], m = qjl_bits * d_eff (R6).
     """
     x = np.asarray(samples, dtype=np.float64)
+    if normalize:
+        x, _ = _unit_rows(x)
     n, d = x.shape
     lam, R = eigenbasis(second_moment(x))
     sigma = np.sqrt(lam)
@@ -254,9 +270,9 @@ def calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
         S = np.asarray(gauss, dtype=np.float32)[:m, :d_eff].astype(np.float64)
     else:
         S = np.zeros((0, d_eff))
-    W = record_words(widths, m)
+    W = record_words(widths, m, normalize)
     return Calibration(d, R, lam, sigma, pr, d_eff, kappa, widths, thresholds, centroids,
-                       books, m, S, W, field_offsets(widths), int(widths.sum()), m > 0)
+                       books, m, S, W, field_offsets(widths), int(widths.sum()), m > 0, normalize)
 
 
 # --------------------------------------------------------------------------
@@ -265,13 +281,14 @@ def calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
 
 @dataclasses.dataclass
 class CompressResult:
-    y: np.ndarray        # [T, d] rotated coordinates
+    y: np.ndarray        # [T, d] rotated coordinates (of x / nu when normalised)
     codes: np.ndarray    # [T, d] int
     yhat: np.ndarray     # [T, d] centroid reconstruction (rotated space)
     z: np.ndarray        # [T, m] uint8 QJL bits
     gamma: np.ndarray    # [T] float16 residual norm
     sr: np.ndarray       # [T, m] S r (before the sign)
     rnorm: np.ndarray    # [T] ||r|| in float64
+    nu: Optional[np.ndarray] = None   # [T] float16 vector norms (normalised variant)
 
 
 def rotate(cal: Calibration, x: np.ndarray) -> np.ndarray:
@@ -296,7 +313,13 @@ def quantize(cal: Calibration, y: np.ndarray):
 
 
 def compress(cal: Calibration, x: np.ndarray) -> CompressResult:
-    """Rotate, quantise, and (keys) the selective QJL of the signal residual."""
+    """Rotate, quantise, and (keys) the selective QJL of the signal residual
+    (normalised variant: of the unit vector x / nu, nu stored as a half)."""
+    x = np.asarray(x, dtype=np.float64)
+    nu16 = None
+    if cal.normalized:
+        x, nu = _unit_rows(x)
+        nu16 = nu.astype(np.float16)
     y = rotate(cal, x)
     codes, yhat = quantize(cal, y)
     T = y.shape[0]
@@ -311,7 +334,7 @@ def compress(cal: Calibration, x: np.ndarray) -> CompressResult:
         sr = np.zeros((T, 0))
         z = np.zeros((T, 0), dtype=np.uint8)
         gamma = np.zeros(T, dtype=np.float16)
-    return CompressResult(y, codes, yhat, z, gamma, sr, rn)
+    return CompressResult(y, codes, yhat, z, gamma, sr, rn, nu16)
 
 
 def band_mask(cal: Calibration, y: np.ndarray, rel: float = 1e-4) -> np.ndarray:
@@ -358,29 +381,44 @@ def _qjl_term(cal: Calibration, z: np.ndarray, gamma: np.ndarray) -> np.ndarray:
     return (math.sqrt(math.pi / 2) / cal.m) * gamma.astype(np.float64)[:, None] * (sgn @ cal.S)
 
 
-def dequantize(cal: Calibration, codes: np.ndarray, z: np.ndarray, gamma: np.ndarray) -> np.ndarray:
-    """x~ = R^T ( yhat + pad_d( QJL correction ) )   (values: R^T yhat)."""
+def _nu_scale(cal: Calibration, nu) -> np.ndarray:
+    """Per-token factor of the normalised variant (the stored half nu), else 1."""
+    if not cal.normalized:
+        return None
+    return np.asarray(nu, dtype=np.float16).astype(np.float64)
+
+
+def dequantize(cal: Calibration, codes: np.ndarray, z: np.ndarray, gamma: np.ndarray,
+               nu=None) -> np.ndarray:
+    """x~ = R^T ( yhat + pad_d( QJL correction ) )   (values: R^T yhat),
+    times the stored norm nu in the normalised variant."""
     yh = _centroid_values(cal, codes)
     if cal.m > 0:
         yh[:, :cal.d_eff] += _qjl_term(cal, z, gamma)
+    f = _nu_scale(cal, nu)
+    if f is not None:
+        yh *= f[:, None]
     return yh @ cal.R
 
 
-def scores_plain(cal: Calibration, q: np.ndarray, codes, z, gamma) -> np.ndarray:
+def scores_plain(cal: Calibration, q: np.ndarray, codes, z, gamma, nu=None) -> np.ndarray:
     """Route (i): s = <q, x~_t> for queries q [G, d] -> [G, T]."""
-    return np.asarray(q, np.float64) @ dequantize(cal, codes, z, gamma).T
+    return np.asarray(q, np.float64) @ dequantize(cal, codes, z, gamma, nu).T
 
 
-def scores_rotated(cal: Calibration, q: np.ndarray, codes, z, gamma) -> np.ndarray:
+def scores_rotated(cal: Calibration, q: np.ndarray, codes, z, gamma, nu=None) -> np.ndarray:
     """Route (ii), the decode-time form: rotate the query once (q~ = R q), then
     s_t = sum_i q~_i C_i[code_ti] + sqrt(pi/2)/m * gamma_t * sum_j w_j (2 z_tj - 1)
-    with w = S q~[:d_eff].  [G, T]."""
+    with w = S q~[:d_eff]; times nu_t in the normalised variant.  [G, T]."""
     qt = np.asarray(q, np.float64) @ cal.R.T
     s = qt @ _centroid_values(cal, codes).T
     if cal.m > 0:
         w = qt[:, :cal.d_eff] @ cal.S.T                   # [G, m]
         sgn = 2.0 * z.astype(np.float64) - 1.0            # [T, m]
         s += (math.sqrt(math.pi / 2) / cal.m) * (w @ sgn.T) * gamma.astype(np.float64)[None, :]
+    f = _nu_scale(cal, nu)
+    if f is not None:
+        s *= f[None, :]
     return s
 
 
@@ -392,8 +430,11 @@ def softmax(s: np.ndarray, scale: float) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def attend(cal_v: Calibration, scores: np.ndarray, scale: float, codes_v) -> np.ndarray:
+def attend(cal_v: Calibration, scores: np.ndarray, scale: float, codes_v, nu_v=None) -> np.ndarray:
     """o = sum_t softmax(scale * s)_t x~v_t, computed as R_v^T sum_t p_t yhat_v,t
-    (values carry no QJL term).  scores [G, T] -> [G, d]."""
+    (values carry no QJL term; normalised variant: p_t nu_t).  scores [G, T] -> [G, d]."""
     p = softmax(scores, scale)
+    f = _nu_scale(cal_v, nu_v)
+    if f is not None:
+        p = p * f[None, :]
     return (p @ _centroid_values(cal_v, codes_v)) @ cal_v.R

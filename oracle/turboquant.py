@@ -17,7 +17,8 @@ import math
 
 import numpy as np
 
-from .spectralquant import lloyd_max_gaussian
+from .record import record_words, field_offsets
+from .spectralquant import Calibration, lloyd_max_gaussian
 
 
 def _codebook(bits: int, d: int):
@@ -54,3 +55,26 @@ def tq_prod_keys(x: np.ndarray, rot: np.ndarray, sketch: np.ndarray, bits: int) 
     sgn = np.where(rho @ sketch.T >= 0, 1.0, -1.0)
     corr = (math.sqrt(math.pi / 2) / d) * np.linalg.norm(rho, axis=1, keepdims=True) * (sgn @ sketch)
     return nu * ((wh + corr) @ rot)
+
+
+def tq_calibration(rot: np.ndarray, sketch, bits: int, keys: bool) -> Calibration:
+    """The TurboQuant-style scheme written as a calibration of the generic
+    (normalised, R8) SpectralQuant pipeline, so the same compress / dequantize
+    / scores / attend and record layout run it: rotation Pi = rot (rows), every
+    coordinate at width bits - 1 (keys: the MSE stage) or bits (values) with
+    the Gaussian Lloyd-Max codebook scaled by 1/sqrt(d), the QJL sketch over
+    all d coordinates (keys: m = d rows of ``sketch``), per-vector norm stored.
+    Coordinate scale sigma_i = 1/sqrt(d), the law of a rotated unit vector's
+    coordinate (it sets the parity band)."""
+    rot = np.asarray(rot, np.float64)
+    d = rot.shape[0]
+    b = bits - 1 if keys else bits
+    c, t = _codebook(b, d) if b > 0 else (np.zeros(1), np.zeros(0))
+    widths = np.full(d, b, dtype=np.int64)
+    m = d if keys else 0
+    S = np.asarray(sketch, np.float32).astype(np.float64)[:m, :d] if keys else np.zeros((0, d))
+    sigma = np.full(d, 1.0 / math.sqrt(d))
+    return Calibration(d, rot.copy(), sigma ** 2, sigma, float(d), d, math.inf, widths,
+                       [t.copy() for _ in range(d)], [c.copy() for _ in range(d)], {}, m, S,
+                       record_words(widths, m, True), field_offsets(widths), int(widths.sum()), m > 0,
+                       True)
