@@ -31,7 +31,7 @@ EXPORTS = ("sq_calib_default_opts", "sq_calibrate", "sq_calib_upload", "sq_calib
            "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_compress_append", "sq_scores",
            "sq_attend_workspace_bytes", "sq_attend", "sq_dequantize", "sq_unpack",
            "sq_last_error", "sq_build_digest", "sq_plan_decode",
-           "sq_attend_noalloc", "sq_decode")
+           "sq_attend_noalloc", "sq_decode", "sq_calibrate_tq")
 
 
 class StaleLibraryError(RuntimeError):
@@ -47,7 +47,7 @@ class SQError(RuntimeError):
 class CalibOpts(C.Structure):
     _fields_ = [("head_dim", C.c_int), ("avg_bits", C.c_double),
                 ("qjl_bits_per_signal_dim", C.c_int), ("max_bits", C.c_int),
-                ("lloyd_max_iters", C.c_int), ("n_threads", C.c_int)]
+                ("lloyd_max_iters", C.c_int), ("n_threads", C.c_int), ("normalize", C.c_int)]
 
 
 class HeadInfo(C.Structure):
@@ -55,7 +55,8 @@ class HeadInfo(C.Structure):
                 ("code_bits", C.c_int), ("record_words", C.c_int),
                 ("n_thresholds", C.c_int), ("n_centroids", C.c_int),
                 ("n_regions", C.c_int), ("lloyd_unconverged", C.c_int),
-                ("participation_ratio", C.c_double), ("kappa", C.c_double)]
+                ("participation_ratio", C.c_double), ("kappa", C.c_double),
+                ("normalized", C.c_int)]
 
 
 class DecodePlan(C.Structure):
@@ -102,7 +103,8 @@ def _load():
         "sq_attend_workspace_bytes": (U64, [I, I, I64, I]),
         "sq_attend": (I, [P, I, I, I, I, I, P, C.c_float, P, I64, I64, I64, P, U64, P, P]),
         "sq_dequantize": (I, [P, I, I, I, I, P, I64, I64, I64, P, P]),
-        "sq_unpack": (I, [P, I, P, I64, P, P, P]),
+        "sq_unpack": (I, [P, I, P, I64, P, P, P, P]),
+        "sq_calibrate_tq": (I, [P, P, I, C.POINTER(CalibOpts), C.POINTER(C.c_void_p)]),
         "sq_last_error": (C.c_char_p, []),
         "sq_build_digest": (C.c_char_p, []),
         "sq_plan_decode": (I, [P, P, I, I, I, I, I, I64, C.POINTER(DecodePlan)]),
@@ -205,9 +207,11 @@ def sq_calib_default_opts(head_dim: int) -> CalibOpts:
 
 def sq_calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
                  qjl_gauss: Optional[np.ndarray] = None, max_bits: int = 8,
-                 lloyd_max_iters: int = 200, n_threads: int = 0) -> Calibration:
+                 lloyd_max_iters: int = 200, n_threads: int = 0,
+                 normalize: bool = False) -> Calibration:
     """samples: host float32 [n_heads][n_samples][d]; qjl_gauss: host float32
-    [n_heads][qjl_bits*d][d] (required when qjl_bits > 0)."""
+    [n_heads][qjl_bits*d][d] (required when qjl_bits > 0); normalize: the
+    normalised variant (per-vector norm stored)."""
     x = np.ascontiguousarray(samples, dtype=np.float32)
     assert x.ndim == 3
     H, n, d = x.shape
@@ -217,12 +221,33 @@ def sq_calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
     o.max_bits = int(max_bits)
     o.lloyd_max_iters = int(lloyd_max_iters)
     o.n_threads = int(n_threads)
+    o.normalize = 1 if normalize else 0
     g = None
     if qjl_gauss is not None:
         g = np.ascontiguousarray(qjl_gauss, dtype=np.float32)
         assert g.shape == (H, max(1, qjl_bits) * d, d), g.shape
     h = C.c_void_p()
     _check(_load().sq_calibrate(_ptr(x), H, n, C.byref(o), _ptr(g), C.byref(h)))
+    return Calibration(h.value)
+
+
+def sq_calibrate_tq(rotation: np.ndarray, bits: int, keys: bool,
+                    qjl_gauss: Optional[np.ndarray] = None) -> Calibration:
+    """TurboQuant-style calibration: rotation host float32 [n_heads][d][d];
+    keys: (bits - 1)-bit codes + QJL over all dims from qjl_gauss [n_heads][d][d];
+    values: bits-bit codes."""
+    r = np.ascontiguousarray(rotation, dtype=np.float32)
+    assert r.ndim == 3 and r.shape[1] == r.shape[2]
+    H, d, _ = r.shape
+    o = sq_calib_default_opts(d)
+    o.avg_bits = float(bits)
+    o.qjl_bits_per_signal_dim = 1 if keys else 0
+    g = None
+    if keys:
+        g = np.ascontiguousarray(qjl_gauss, dtype=np.float32)
+        assert g.shape == (H, d, d), g.shape
+    h = C.c_void_p()
+    _check(_load().sq_calibrate_tq(_ptr(r), _ptr(g), H, C.byref(o), C.byref(h)))
     return Calibration(h.value)
 
 
@@ -345,8 +370,10 @@ def sq_plan_decode(kcal: Optional[Calibration], vcal: Optional[Calibration], bat
     return out
 
 
-def sq_unpack(cal: Calibration, head: int, packed_host: np.ndarray, n_tokens: int):
-    """Host decode of one head's slot -> (codes uint8 [T][d], qjl uint8 [T][m], gamma float32 [T])."""
+def sq_unpack(cal: Calibration, head: int, packed_host: np.ndarray, n_tokens: int,
+              with_norm: bool = False):
+    """Host decode of one head's slot -> (codes uint8 [T][d], qjl uint8 [T][m],
+    gamma float32 [T]) and, with with_norm, nu float32 [T]."""
     inf = cal.info(head)
     p = np.ascontiguousarray(packed_host).view(np.uint32)
     need = -(-n_tokens // 64) * 64 * inf.record_words
@@ -354,6 +381,9 @@ def sq_unpack(cal: Calibration, head: int, packed_host: np.ndarray, n_tokens: in
     codes = np.zeros((n_tokens, inf.head_dim), np.uint8)
     qjl = np.zeros((n_tokens, max(1, inf.m)), np.uint8)
     gamma = np.zeros(n_tokens, np.float32)
+    nu = np.zeros(n_tokens, np.float32)
     _check(_load().sq_unpack(cal.handle, head, _ptr(p), n_tokens, _ptr(codes), _ptr(qjl),
-                             _ptr(gamma)))
+                             _ptr(gamma), _ptr(nu)))
+    if with_norm:
+        return codes, qjl[:, :inf.m], gamma, nu
     return codes, qjl[:, :inf.m], gamma

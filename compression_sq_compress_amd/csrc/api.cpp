@@ -43,6 +43,7 @@ extern "C" sq_status sq_calib_default_opts(sq_calib_opts *o, int head_dim) {
   o->max_bits = 8;
   o->lloyd_max_iters = 200;
   o->n_threads = 0;
+  o->normalize = 0;
   clear_error();
   return SQ_OK;
 }
@@ -57,6 +58,7 @@ static sq_status check_opts(const sq_calib_opts *o) {
   if (o->qjl_bits_per_signal_dim < 0 || o->qjl_bits_per_signal_dim > 8)
     return fail(SQ_ERR_ARG, "qjl_bits_per_signal_dim must be in [0, 8]");
   if (o->lloyd_max_iters < 0) return fail(SQ_ERR_ARG, "lloyd_max_iters must be >= 0");
+  if (o->normalize != 0 && o->normalize != 1) return fail(SQ_ERR_ARG, "normalize must be 0 or 1");
   return SQ_OK;
 }
 
@@ -122,6 +124,48 @@ extern "C" sq_status sq_calibrate(const float *samples, int n_heads, int64_t n_s
   return SQ_OK;
 }
 
+extern "C" sq_status sq_calibrate_tq(const float *rotation, const float *qjl_gauss, int n_heads,
+                                     const sq_calib_opts *opts, sq_calib **out) {
+  if (!out) return fail(SQ_ERR_ARG, "sq_calibrate_tq: out is NULL");
+  *out = nullptr;
+  sq_status st = check_opts(opts);
+  if (st != SQ_OK) return st;
+  if (!rotation) return fail(SQ_ERR_ARG, "sq_calibrate_tq: rotation is NULL");
+  if (n_heads <= 0) return fail(SQ_ERR_ARG, "sq_calibrate_tq: n_heads must be > 0");
+  const bool keys = opts->qjl_bits_per_signal_dim > 0;
+  if (keys && opts->qjl_bits_per_signal_dim != 1)
+    return fail(SQ_ERR_ARG, "sq_calibrate_tq: the keys' sketch has one bit per dim (qjl_bits_per_signal_dim 1)");
+  const double b = opts->avg_bits;
+  const int lo = keys ? 2 : 1, hi = keys ? 9 : 8;
+  if (b != std::floor(b) || b < lo || b > hi)
+    return fail(SQ_ERR_ARG, "sq_calibrate_tq: avg_bits must be an integer in [1, 8] (values) or [2, 9] (keys)");
+  if (keys && !qjl_gauss) return fail(SQ_ERR_ARG, "sq_calibrate_tq: qjl_gauss is NULL for keys");
+  sq_calib *c = new (std::nothrow) sq_calib();
+  if (!c) return fail(SQ_ERR_ALLOC, "sq_calibrate_tq: out of host memory");
+  c->opts = *opts;
+  c->opts.normalize = 1;
+  const int d = opts->head_dim;
+  try {
+    c->heads.resize(n_heads);
+    for (int h = 0; h < n_heads; ++h) {
+      std::string err;
+      st = calibrate_head_tq(rotation + (size_t)h * d * d, d, c->opts,
+                             keys ? qjl_gauss + (size_t)h * d * d : nullptr, c->heads[h], err);
+      if (st != SQ_OK) {
+        delete c;
+        return fail(st, "sq_calibrate_tq: head " + std::to_string(h) + ": " + err);
+      }
+    }
+  } catch (...) {
+    delete c;
+    return fail(SQ_ERR_ALLOC, "sq_calibrate_tq: out of host memory");
+  }
+  compute_wmax(c);
+  *out = c;
+  clear_error();
+  return SQ_OK;
+}
+
 extern "C" int sq_calib_n_heads(const sq_calib *c) { return c ? (int)c->heads.size() : 0; }
 
 extern "C" sq_status sq_calib_info(const sq_calib *c, int head, sq_head_info *info) {
@@ -139,6 +183,7 @@ extern "C" sq_status sq_calib_info(const sq_calib *c, int head, sq_head_info *in
   info->lloyd_unconverged = h.unconverged;
   info->participation_ratio = h.pr;
   info->kappa = h.kappa;
+  info->normalized = h.normalized ? 1 : 0;
   clear_error();
   return SQ_OK;
 }
@@ -160,11 +205,13 @@ extern "C" sq_status sq_calib_export(const sq_calib *c, int head, double *eigenv
 }
 
 // ---------------------------------------------------------------- save / load
-// File: "SQCALIB1", u32 version, opts (fixed fields), u32 n_heads, then per
-// head: i32 d, d_eff, m; f64 pr, kappa; f64 lam[d]; f64 R[d*d]; i32 widths[d];
-// f32 thr[n_thr]; f32 cent[n_cent]; f32 S[m*d_eff].  Little-endian.
+// File: "SQCALIB1", u32 version, opts (fixed fields; version 2 adds
+// normalize), u32 n_heads, then per head: i32 d, d_eff, m; f64 pr, kappa;
+// f64 lam[d]; f64 R[d*d]; i32 widths[d]; i32 n_regions, unconverged
+// (version 2: and normalized); f32 thr[n_thr]; f32 cent[n_cent];
+// f32 S[m*d_eff].  Little-endian.  Version 1 files load as unnormalised.
 static const char kMagic[8] = {'S', 'Q', 'C', 'A', 'L', 'I', 'B', '1'};
-static const uint32_t kVersion = 1;
+static const uint32_t kVersion = 2;  // 2: normalised variant flag in the options and per head
 
 namespace {
 struct File {
@@ -183,8 +230,8 @@ extern "C" sq_status sq_calib_save(const sq_calib *c, const char *path) {
   if (!F.f) return fail(SQ_ERR_IO, std::string("sq_calib_save: cannot open ") + path);
   F.w(kMagic, 8);
   F.w(&kVersion, 4);
-  int32_t oi[5] = {c->opts.head_dim, c->opts.qjl_bits_per_signal_dim, c->opts.max_bits,
-                   c->opts.lloyd_max_iters, c->opts.n_threads};
+  int32_t oi[6] = {c->opts.head_dim, c->opts.qjl_bits_per_signal_dim, c->opts.max_bits,
+                   c->opts.lloyd_max_iters, c->opts.n_threads, c->opts.normalize};
   F.w(oi, sizeof(oi));
   F.w(&c->opts.avg_bits, 8);
   uint32_t nh = (uint32_t)c->heads.size();
@@ -197,7 +244,7 @@ extern "C" sq_status sq_calib_save(const sq_calib *c, const char *path) {
     F.w(h.lam.data(), h.lam.size() * 8);
     F.w(h.R.data(), h.R.size() * 8);
     F.w(h.widths.data(), h.widths.size() * 4);
-    int32_t extra[2] = {h.n_regions, h.unconverged};
+    int32_t extra[3] = {h.n_regions, h.unconverged, h.normalized ? 1 : 0};
     F.w(extra, sizeof(extra));
     F.w(h.thr.data(), h.thr.size() * 4);
     F.w(h.cent.data(), h.cent.size() * 4);
@@ -218,17 +265,18 @@ extern "C" sq_status sq_calib_load(const char *path, sq_calib **out) {
   uint32_t ver = 0;
   F.r(magic, 8);
   F.r(&ver, 4);
-  if (!F.ok || std::memcmp(magic, kMagic, 8) != 0 || ver != kVersion)
-    return fail(SQ_ERR_IO, "sq_calib_load: not a calibration file of this version");
+  if (!F.ok || std::memcmp(magic, kMagic, 8) != 0 || ver < 1 || ver > kVersion)
+    return fail(SQ_ERR_IO, "sq_calib_load: not a calibration file of a known version");
   sq_calib *c = new (std::nothrow) sq_calib();
   if (!c) return fail(SQ_ERR_ALLOC, "sq_calib_load: out of host memory");
-  int32_t oi[5];
-  F.r(oi, sizeof(oi));
+  int32_t oi[6] = {0, 0, 0, 0, 0, 0};
+  F.r(oi, ver >= 2 ? sizeof(oi) : 5 * sizeof(int32_t));
   c->opts.head_dim = oi[0];
   c->opts.qjl_bits_per_signal_dim = oi[1];
   c->opts.max_bits = oi[2];
   c->opts.lloyd_max_iters = oi[3];
   c->opts.n_threads = oi[4];
+  c->opts.normalize = oi[5];
   F.r(&c->opts.avg_bits, 8);
   uint32_t nh = 0;
   F.r(&nh, 4);
@@ -256,10 +304,12 @@ extern "C" sq_status sq_calib_load(const char *path, sq_calib **out) {
     F.r(h.lam.data(), h.lam.size() * 8);
     F.r(h.R.data(), h.R.size() * 8);
     F.r(h.widths.data(), h.widths.size() * 4);
-    int32_t extra[2];
-    F.r(extra, sizeof(extra));
+    int32_t extra[3] = {0, 0, 0};
+    F.r(extra, ver >= 2 ? sizeof(extra) : 2 * sizeof(int32_t));
     h.n_regions = extra[0];
     h.unconverged = extra[1];
+    if (extra[2] != 0 && extra[2] != 1) F.ok = false;
+    h.normalized = extra[2] == 1;
     for (int32_t b : h.widths)
       if (b < 0 || b > 8) F.ok = false;
     if (!F.ok) {
@@ -296,8 +346,18 @@ extern "C" int64_t sq_packed_head_words(const sq_calib *c, int64_t n_tokens) {
 }
 
 // ---------------------------------------------------------------- host unpack
+static float half_to_float(uint32_t hb) {
+  const uint32_t sgn = (hb >> 15) & 1, ex = (hb >> 10) & 31, man = hb & 1023;
+  float v;
+  if (ex == 0) v = std::ldexp((float)man, -24);
+  else if (ex == 31) v = man ? NAN : INFINITY;
+  else v = std::ldexp((float)(man | 1024), (int)ex - 25);
+  return sgn ? -v : v;
+}
+
 extern "C" sq_status sq_unpack(const sq_calib *c, int head, const uint32_t *packed,
-                               int64_t n_tokens, uint8_t *codes, uint8_t *qjl, float *gamma) {
+                               int64_t n_tokens, uint8_t *codes, uint8_t *qjl, float *gamma,
+                               float *nu) {
   if (!c || !packed || !codes) return fail(SQ_ERR_ARG, "sq_unpack: NULL argument");
   if (head < 0 || head >= (int)c->heads.size()) return fail(SQ_ERR_ARG, "sq_unpack: head out of range");
   if (n_tokens < 0) return fail(SQ_ERR_ARG, "sq_unpack: n_tokens < 0");
@@ -316,20 +376,8 @@ extern "C" sq_status sq_unpack(const sq_calib *c, int head, const uint32_t *pack
     for (int i = 0; i < h.d; ++i)
       codes[(size_t)t * h.d + i] = h.widths[i] ? (uint8_t)field(h.bit_off[i], h.widths[i]) : 0;
     for (int j = 0; j < h.m; ++j) qjl[(size_t)t * h.m + j] = (uint8_t)field(h.code_bits + j, 1);
-    if (gamma) {
-      if (h.m > 0) {
-        const uint32_t hb = rec[W - 1] >> 16;
-        // IEEE half -> float
-        const uint32_t sgn = (hb >> 15) & 1, ex = (hb >> 10) & 31, man = hb & 1023;
-        float v;
-        if (ex == 0) v = std::ldexp((float)man, -24);
-        else if (ex == 31) v = man ? NAN : INFINITY;
-        else v = std::ldexp((float)(man | 1024), (int)ex - 25);
-        gamma[t] = sgn ? -v : v;
-      } else {
-        gamma[t] = 0.0f;
-      }
-    }
+    if (gamma) gamma[t] = h.m > 0 ? half_to_float(rec[W - 1] >> 16) : 0.0f;
+    if (nu) nu[t] = h.normalized ? half_to_float(h.m > 0 ? rec[W - 1] & 0xFFFFu : rec[W - 1] >> 16) : 0.0f;
   }
   clear_error();
   return SQ_OK;

@@ -211,6 +211,8 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   const int ch = a.first_head + b * a.cbs + hkv;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d, W = hd->W;
+  const bool vnorm = hd->normalized != 0;
+  const int vm = hd->m;
   const SQ_CONST DevCoord *coords = cptr<DevCoord>(a.blob + hd->off_coord);
   uint32_t *lut = (uint32_t *)smem;
   float *stage = smem + a.lds_wave_off + wv * a.wave_floats;  // two buffers: words, then scores
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
 
   const int lsh = LM == LM_COL ? 6 : 0;  // gather index: (field << lsh) + cb
   // sq_decode: the score tables of this KV head's query group
-  int kW = 0, km = 0, knq = 0;
+  int kW = 0, km = 0, knq = 0, knorm = 0;
   const SQ_CONST uint32_t *kslots = nullptr, *kqslots = nullptr, *kscnt = nullptr;
   const uint32_t *kslot = nullptr;
   if constexpr (FUSED) {
@@ -281,6 +283,7 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
     kW = kh->W;
     km = kh->m;
     knq = kh->n_fqjl;
+    knorm = kh->normalized;
     const int ng = kh->n_fgroups;
     constexpr int E = GQ == 4 ? 4 : GQ == 2 ? 3 : 2;  // log2 of an entry's bytes
     const SQ_CONST uint32_t *fs = cptr<uint32_t>(a.kblob + kh->off_fsched);
@@ -337,11 +340,11 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
     }
   };
   // sq_decode: the key record of this lane's token, word k in kw[k + 1]
-  // (kw[0] = 0 is the word before the record); its last two words again in
-  // qlo, qhi (QJL bits and gamma); pad tokens of the last tile hold all-zero
-  // records
+  // (kw[0] = 0 is the word before the record); the words qb, qb + 1 holding
+  // the QJL bits again in qlo, qhi and the last word (gamma, the norm) in
+  // wlast; pad tokens of the last tile hold all-zero records
   uint32_t kw[FUSED ? DEC_KW + 2 : 1];
-  uint32_t qlo = 0u, qhi = 0u;
+  uint32_t qlo = 0u, qhi = 0u, wlast = 0u;
   auto load_keys = [&](int64_t t0) {
     if constexpr (FUSED) {
       const uint32_t *src = kslot + (t0 >> 6) * (int64_t)kW * 64 + lane;
@@ -349,9 +352,11 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
 #pragma unroll
       for (int k = 0; k < DEC_KW; ++k) kw[k + 1] = k < kW ? src[k * 64] : 0u;
       kw[DEC_KW + 1] = 0u;
+      if (km > 0 || knorm) wlast = src[(kW - 1) * 64];
       if (km > 0) {
-        qhi = src[(kW - 1) * 64];
-        qlo = kW >= 2 ? src[(kW - 2) * 64] : 0u;
+        const int qb = kW - 2 - knorm;
+        qhi = qb + 1 >= 0 ? src[(qb + 1) * 64] : 0u;
+        qlo = qb >= 0 ? src[qb * 64] : 0u;
       }
     }
   };
@@ -428,13 +433,22 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
 #pragma unroll
           for (int g = 0; g < GQ; ++g) q4[g] += e[g];
         }
-        gm = half_bits_to_f32(qhi >> 16);  // gamma: top half of the last word
+        gm = half_bits_to_f32(wlast >> 16);  // gamma: top half of the last word
       }
+      // normalised keys: the score is nu times the unit vector's
+      const float knu = knorm ? half_bits_to_f32(km > 0 ? (wlast & 0xFFFFu) : (wlast >> 16)) : 1.0f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) sv[g] = t < te ? a.scale * fmaf(gm, q4[g], s4[g]) : -INFINITY;
+      for (int g = 0; g < G; ++g) sv[g] = t < te ? a.scale * (knu * fmaf(gm, q4[g], s4[g])) : -INFINITY;
     } else {
 #pragma unroll
       for (int g = 0; g < G; ++g) sv[g] = t < te ? a.scale * sr[g * 64 + lane] : -INFINITY;
+    }
+    // normalised values: the token's value is nu_t times its unit-vector
+    // reconstruction, so its weight in the sum (not in the normaliser) is p nu
+    float vnu = 1.0f;
+    if (vnorm) {
+      const uint32_t wl = rec[W * ATT_RS + lane];  // staged row W = word W - 1
+      vnu = half_bits_to_f32(vm > 0 ? (wl & 0xFFFFu) : (wl >> 16));
     }
     // The reference max moves only when a tile exceeds it by more than
     // ATT_TAU: weights stay below e^ATT_TAU and the sums are rescaled rarely.
@@ -452,9 +466,10 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
       }
       const float pv = __expf(sv[g] - mrun[g]);  // 0 for tokens past the end
       lsum[g] += pv;
-      const uint32_t hp = bf16_pair_rne(pv);
+      const float pw = pv * vnu;  // the value's norm (normalised values), else 1
+      const uint32_t hp = bf16_pair_rne(pw);
       ph[g * ATT_PS + lane] = hp;
-      pl[g * ATT_PS + lane] = bf16_pair_rne(pv - __uint_as_float(hp << 16));
+      pl[g * ATT_PS + lane] = bf16_pair_rne(pw - __uint_as_float(hp << 16));
     }
 #pragma unroll
     for (int g = G; g < GP; ++g) {

@@ -143,7 +143,7 @@ void finish_layout(HeadCal &h) {
   h.code_bits = bits;
   h.n_thr = nt;
   h.n_cent = nc;
-  const int total = bits + h.m + (h.m > 0 ? 16 : 0);
+  const int total = bits + h.m + (h.m > 0 ? 16 : 0) + (h.normalized ? 16 : 0);
   h.W = std::max(1, (total + 31) / 32);
 }
 
@@ -151,6 +151,22 @@ sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &
                          const float *gauss, HeadCal &h, std::string &err) {
   h = HeadCal();
   h.d = d;
+  h.normalized = o.normalize != 0;
+  // normalised variant: every sample divided by its norm (a zero sample stays zero)
+  std::vector<double> unit;
+  if (h.normalized) {
+    unit.assign((size_t)n * d, 0.0);
+    for (int64_t t = 0; t < n; ++t) {
+      const float *xr = x + (size_t)t * d;
+      double s = 0.0;
+      for (int i = 0; i < d; ++i) s += (double)xr[i] * (double)xr[i];
+      const double nrm = std::sqrt(s);
+      for (int i = 0; i < d; ++i) unit[(size_t)t * d + i] = nrm > 0 ? (double)xr[i] / nrm : 0.0;
+    }
+  }
+  auto sample = [&](int64_t t, int i) -> double {
+    return h.normalized ? unit[(size_t)t * d + i] : (double)x[(size_t)t * d + i];
+  };
   // 1. second moment C = X^T X / n (uncentered), double
   std::vector<double> C((size_t)d * d, 0.0);
   std::vector<double> row(d);
@@ -161,7 +177,7 @@ sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &
         err = "non-finite calibration sample";
         return SQ_ERR_NUMERIC;
       }
-      row[i] = (double)xr[i];
+      row[i] = sample(t, i);
     }
     for (int i = 0; i < d; ++i) {
       const double ri = row[i];
@@ -227,9 +243,8 @@ sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &
         if (!(sigma[i] > 0)) continue;
         const double *Ri = &h.R[(size_t)i * d];
         for (int64_t t = 0; t < n; ++t) {
-          const float *xr = x + (size_t)t * d;
           double y = 0.0;
-          for (int j = 0; j < d; ++j) y += Ri[j] * (double)xr[j];
+          for (int j = 0; j < d; ++j) y += Ri[j] * sample(t, j);
           u.push_back(y / sigma[i]);
         }
       }
@@ -253,6 +268,79 @@ sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &
     }
     for (int j = 0; j < h.m; ++j)
       for (int i = 0; i < h.d_eff; ++i) h.S[(size_t)j * h.d_eff + i] = gauss[(size_t)j * d + i];
+  }
+  return SQ_OK;
+}
+
+// Lloyd-Max quantiser of the standard normal density with L levels (Max,
+// 1960): iterate the centroid condition c_j = (phi(a) - phi(b)) / (Phi(b) -
+// Phi(a)) over the cells (a, b] between midpoints from uniformly spread
+// levels until the levels stop moving; returns the levels, ascending.
+static std::vector<double> gaussian_lloyd_max(int L) {
+  std::vector<double> c(L, 0.0);
+  if (L == 1) return c;
+  for (int j = 0; j < L; ++j) c[j] = -2.0 + 4.0 * j / (L - 1);
+  auto phi = [](double t) { return std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI); };
+  auto Phi = [](double t) { return 0.5 * std::erfc(-t / std::sqrt(2.0)); };
+  for (int it = 0; it < 200000; ++it) {
+    double delta = 0.0;
+    std::vector<double> nc(L);
+    for (int j = 0; j < L; ++j) {
+      const double a = j == 0 ? -INFINITY : 0.5 * (c[j - 1] + c[j]);
+      const double b = j == L - 1 ? INFINITY : 0.5 * (c[j] + c[j + 1]);
+      const double pa = std::isinf(a) ? 0.0 : phi(a), pb = std::isinf(b) ? 0.0 : phi(b);
+      const double mass = (std::isinf(b) ? 1.0 : Phi(b)) - (std::isinf(a) ? 0.0 : Phi(a));
+      nc[j] = (pa - pb) / mass;
+      delta = std::max(delta, std::fabs(nc[j] - c[j]));
+    }
+    c = nc;
+    if (delta < 1e-15) break;
+  }
+  return c;
+}
+
+sq_status calibrate_head_tq(const float *rotation, int d, const sq_calib_opts &o, const float *gauss,
+                            HeadCal &h, std::string &err) {
+  h = HeadCal();
+  h.d = d;
+  h.normalized = true;
+  const bool keys = o.qjl_bits_per_signal_dim > 0;
+  const int bits = (int)std::lround(o.avg_bits);
+  const int b = keys ? bits - 1 : bits;
+  h.R.assign((size_t)d * d, 0.0);
+  for (size_t k = 0; k < (size_t)d * d; ++k) {
+    if (!std::isfinite(rotation[k])) {
+      err = "non-finite rotation entry";
+      return SQ_ERR_NUMERIC;
+    }
+    h.R[k] = (double)rotation[k];
+  }
+  h.lam.assign(d, 1.0 / d);  // a rotated unit vector's coordinate variance
+  h.pr = (double)d;
+  h.d_eff = d;                // the QJL sketch covers every coordinate
+  h.kappa = std::numeric_limits<double>::infinity();
+  h.widths.assign(d, b);
+  h.m = keys ? d : 0;
+  finish_layout(h);
+  h.thr.assign(h.n_thr, 0.0f);
+  h.cent.assign(h.n_cent, 0.0f);
+  if (b > 0) {
+    const int L = 1 << b;
+    const std::vector<double> c = gaussian_lloyd_max(L);
+    const double s = 1.0 / std::sqrt((double)d);
+    for (int i = 0; i < d; ++i) {
+      for (int j = 0; j < L; ++j) h.cent[h.cent_base[i] + j] = (float)(s * c[j]);
+      for (int j = 0; j + 1 < L; ++j) h.thr[h.thr_base[i] + j] = (float)(s * 0.5 * (c[j] + c[j + 1]));
+    }
+    h.n_regions = 1;
+  }
+  h.S.assign((size_t)h.m * h.d_eff, 0.0f);
+  if (h.m > 0) {
+    if (!gauss) {
+      err = "qjl_gauss is NULL but the keys' QJL sketch was requested";
+      return SQ_ERR_ARG;
+    }
+    for (size_t k = 0; k < (size_t)d * d; ++k) h.S[k] = gauss[k];
   }
   return SQ_OK;
 }

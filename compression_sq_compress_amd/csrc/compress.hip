@@ -411,6 +411,20 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
     // into the LDS word buffer.  With a small sketch (m, d_eff <= 8) wave 0
     // holds the whole signal range and adds the QJL bits and gamma itself.
     float *yrow = ytile + lane * a.ys;
+    if (hd->normalized) {
+      // normalised variant: the vector's norm nu = |y| (= |x|) goes into the
+      // record as a half and the unit vector y / nu is quantised (a zero
+      // vector stays zero; a NaN one stays NaN)
+      if (w == 0) {
+        float s2 = 0.0f;
+        for (int i = 0; i < D; ++i) s2 = fmaf(yrow[i], yrow[i], s2);
+        const float nu = __builtin_amdgcn_sqrtf(s2);
+        const float inv = nu > 0.0f ? 1.0f / nu : 0.0f;
+        for (int i = 0; i < D; ++i) yrow[i] *= inv;
+        atomicOr(bwrow + (W - 1), half_bits_rne(nu) << (m > 0 ? 0 : 16));
+      }
+      __syncthreads();
+    }
     const bool qin = m > 0 && m <= 8 && d_eff <= 8 && w == 0;
     const float *sp = smem + a.lds_sp_off;
     {
@@ -936,6 +950,7 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
   {
     // (the kernel's per-lane load offsets within a 64-token tile are 32-bit;
     // each of its d/16 waves stores at most C2_WMAX record words per tile)
+    // (normalised heads have no register plan: n_p2 = 0)
     bool use2 = d <= 128 && 64 * xs_token * esz < ((int64_t)1 << 32) && c->W_max <= C2_WMAX * (d / 16) &&
                 n_heads <= 65535 && batch <= 65535;
     int mt = 0, mc = 0, mq = 0;

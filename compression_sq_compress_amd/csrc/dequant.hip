@@ -55,6 +55,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         }
         v += hd->qjl_scale * half_bits_to_f32(word(t, W - 1) >> 16) * s;
       }
+      if (hd->normalized) {  // normalised variant: times the stored vector norm
+        const uint32_t wl = word(t, W - 1);
+        v *= half_bits_to_f32(m > 0 ? (wl & 0xFFFFu) : (wl >> 16));
+      }
     }
     yb[tt * 257 + i] = v;
   }

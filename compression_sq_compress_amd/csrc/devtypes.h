@@ -72,7 +72,9 @@ struct DevHead {
                         // (hi + lo reproduces the fp32 centroid to ~2^-17)
   int64_t off_csig;     // float [n_csig]  signal centroids * sigma_i per plan chunk
   // register-quantising compress plan (P2_* layout below); n_p2 = 0: not available
-  int32_t n_p2, n_tree2, n_csig2, pad3;
+  int32_t n_p2, n_tree2, n_csig2;
+  int32_t normalized;   // records carry the vector norm nu (half): bits [32W-32, 32W-16)
+                        // if m > 0, else [32W-16, 32W); the unit vector was quantised
   int64_t off_p2;       // uint32 [d/16][P2_WAVE]
   int64_t off_tree2;    // float [n_tree2] per-coordinate padded trees (see P2_WAVE)
   int64_t off_csig2;    // float [n_csig2] signal centroids * sigma_i, padded per coordinate
@@ -109,9 +111,9 @@ static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
 // them.  Layout (uint32), n = n_fgroups, nq = n_fqjl:
 //   [2n]   per group: width (bits 0-3) | QJL group (bit 4) | first table entry
 //          << 8; first coordinate or QJL bit (bits 0-11) | count << 12;
-//   [nq]   per QJL group: bit position relative to word W - 2 (bits 0-7) |
-//          width << 8 | first table entry << 12 (the QJL bits and gamma lie in
-//          the last two words when m <= 16);
+//   [nq]   per QJL group: bit position relative to word qb (bits 0-7) |
+//          width << 8 | first table entry << 12, qb = W - 2, or W - 3 when
+//          normalised (the QJL bits then lie in words qb, qb + 1: m <= 16);
 //   (padded to 16 words)
 //   [3][W + 1][FS_SLOTS][2]  for table entries of 4, 8 and 16 bytes (E = 2,
 //          3, 4) and each window j (record words j - 1, j; word -1 is zero):

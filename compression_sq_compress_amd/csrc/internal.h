@@ -16,6 +16,7 @@ struct HeadCal {
   int d = 0, d_eff = 0, m = 0, W = 0, code_bits = 0;
   int n_thr = 0, n_cent = 0, n_regions = 0, unconverged = 0;
   double pr = 0.0, kappa = 0.0;
+  bool normalized = false;        // records carry the vector norm; unit vectors quantised
   std::vector<double> lam;        // [d] descending
   std::vector<double> R;          // [d*d] row i = eigenvector i
   std::vector<int32_t> widths;    // [d]
@@ -51,6 +52,8 @@ void clear_error();
 sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &o,
                          const float *gauss, HeadCal &out, std::string &err);
 void finish_layout(HeadCal &h);
+sq_status calibrate_head_tq(const float *rotation, int d, const sq_calib_opts &o, const float *gauss,
+                            HeadCal &out, std::string &err);
 
 // device entry points (kernels.hip)
 sq_status upload_tables(sq_calib *c, void *stream);

@@ -396,6 +396,18 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
           }
         }
       }
+      if (hd->normalized) {  // normalised keys: s = nu * (...), each partial scaled (linear)
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          const uint32_t tl = tile_lds + (u * NS + t) * SLOTB;
+          const uint32_t wl = *(const uint32_t *)(sm + tl + (W - 1) * 256u);
+          const float nu = half_bits_to_f32(m > 0 ? (wl & 0xFFFFu) : (wl >> 16));
+#pragma unroll
+          for (int g = 0; g < GR; ++g)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[t][g][rr] *= nu;
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         float *pw = pbuf + ((((ss & 1) * NS + t) * TS + tau) * KS + kk) * GP * 64 + lane;

@@ -169,8 +169,11 @@ static FusedSched build_fused_sched(const HeadCal &hc) {
     F.words[2 * k] = (uint32_t)q.width | (q.qjl ? 16u : 0u) | (e0[k] << 8);
     F.words[2 * k + 1] = (uint32_t)q.first | ((uint32_t)q.count << 12);
     if (q.qjl) {
-      const int rel = q.pos - 32 * (W - 2);  // within words W-2, W-1 (word -1 reads as zero)
-      if (rel < 0 || rel + q.width > 48) return FusedSched{};
+      // within words qb, qb + 1, qb = W - 2 (W - 3 when the norm shares word W - 1
+      // with gamma); word -1 reads as zero
+      const int qb = W - 2 - (hc.normalized ? 1 : 0);
+      const int rel = q.pos - 32 * qb;
+      if (rel < 0 || rel + q.width > 64) return FusedSched{};
       Q[iq++] = (uint32_t)rel | ((uint32_t)q.width << 8) | (e0[k] << 12);
     }
   }
@@ -308,10 +311,12 @@ static HostPlan build_plan(const HeadCal &hc) {
   // bits (for the last wave with QJL, below the QJL bits)
   std::vector<int> dfirst(NW), dend(NW);
   for (int w = 0; w < NW; ++w) {
-    const int ecode = (w == NW - 1 && hc.m > 0) ? hc.code_bits : ebit[w];
+    // (the last words also hold the QJL bits, gamma or the vector norm)
+    const bool tail = hc.m > 0 || hc.normalized;
+    const int ecode = (w == NW - 1 && tail) ? hc.code_bits : ebit[w];
     dfirst[w] = (sbit[w] + 31) / 32;
     dend[w] = std::max(dfirst[w], ecode / 32);
-    if (w == NW - 1 && hc.m == 0) dend[w] = std::max(dfirst[w], hc.W);
+    if (w == NW - 1 && !tail) dend[w] = std::max(dfirst[w], hc.W);
   }
   // every other word is OR-assembled in LDS and stored by the highest wave
   // that touches it
@@ -509,7 +514,9 @@ static HostPlan2 build_plan2(const HeadCal &hc) {
     }
   }
   P.words = hdr;
-  P.ok = P.tree.size() < 65536 && hc.W < 256;  // 16-bit tree bases, 8-bit word indices in the kernel
+  // 16-bit tree bases, 8-bit word indices in the kernel; the normalised
+  // variant goes through compress_kernel
+  P.ok = P.tree.size() < 65536 && hc.W < 256 && !hc.normalized;
   return P;
 }
 
@@ -560,6 +567,7 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.off_csig = off;    off = align256(off + sizeof(float) * std::max<size_t>(1, P.csig.size()));
     const HostPlan2 &P2 = plans2[h];
     D.n_p2 = P2.ok ? (int)P2.words.size() : 0;
+    D.normalized = hc.normalized ? 1 : 0;
     D.n_tree2 = (int)P2.tree.size();
     D.n_csig2 = (int)P2.csig.size();
     D.off_p2 = off;      off = align256(off + sizeof(uint32_t) * std::max<size_t>(1, P2.words.size()));

@@ -38,7 +38,10 @@
  *     back to back from bit 0 (fields may straddle words);
  *   - then the m QJL bits z_0..z_{m-1};
  *   - if m > 0: gamma (residual norm) as IEEE half in bits [32W-16, 32W);
- *   - W = max(1, ceil((sum b_i + m + 16*[m>0]) / 32)); unused bits are zero;
+ *   - normalised calibrations: the vector norm nu as IEEE half in bits
+ *     [32W-32, 32W-16) if m > 0, else in bits [32W-16, 32W);
+ *   - W = max(1, ceil((sum b_i + m + 16*[m>0] + 16*[normalised]) / 32));
+ *     unused bits are zero;
  *   - word w of token t lives at 32-bit element ((t/64)*W + w)*64 + t%64 of the
  *     head's slot, so one wavefront reads word w of 64 tokens as one coalesced
  *     256-byte access.  T is padded to a multiple of 64 with all-zero records.
@@ -75,6 +78,9 @@ typedef struct {
   int max_bits;                 /* widest code field, 1..8 */
   int lloyd_max_iters;          /* cap of the per-region Lloyd-Max iteration */
   int n_threads;                /* host threads used by sq_calibrate; 0 = hardware count */
+  int normalize;                /* 1: normalised variant -- samples divided by their norms
+                                   before calibration; each record stores its vector's
+                                   norm (IEEE half) and the unit vector is quantised */
 } sq_calib_opts;
 
 typedef struct sq_calib sq_calib; /* opaque, library-owned */
@@ -91,6 +97,7 @@ typedef struct {
   int lloyd_unconverged; /* regions that hit the iteration cap */
   double participation_ratio;
   double kappa;        /* lambda[d_eff-1] / lambda[d_eff]; +inf if d_eff == d */
+  int normalized;      /* records carry the vector norm (normalised variant) */
 } sq_head_info;
 
 /* Defaults: avg_bits 3, qjl 1 (keys), max_bits 8, 200 Lloyd-Max iterations. */
@@ -123,6 +130,27 @@ sq_status sq_calib_default_opts(sq_calib_opts *opts, int head_dim);
 sq_status sq_calibrate(const float *samples, int n_heads, int64_t n_samples,
                        const sq_calib_opts *opts, const float *qjl_gauss,
                        sq_calib **out);
+
+/*
+ * sq_calibrate_tq -- the TurboQuant-style baseline (random rotation, per-vector
+ * norm, Gaussian Lloyd-Max codebook of the rotated unit vector's coordinates,
+ * QJL over all dims for keys) as a calibration handle that the same device
+ * calls run (TurboQuant reference-implementation page, "Project Structure":
+ * the MSE quantiser, and the Prod quantiser = (b-1)-bit MSE stage + 1-bit QJL
+ * of the residual; "Key Findings" 2: Prod for keys, MSE for values).  No data
+ * is needed.  Per head: R = rotation[h] (rows: y = R x, orthogonal);
+ * normalised records; every coordinate at width b - 1 (keys:
+ * opts->qjl_bits_per_signal_dim == 1, then m = d QJL rows S = qjl_gauss[h]
+ * over all d coordinates) or b (values: qjl_bits_per_signal_dim == 0), with
+ * b = opts->avg_bits (an integer 1..8 for values, 2..9 for keys, minus the
+ * QJL bit at most 8); codebook: the Lloyd-Max quantiser of N(0, 1) (Max,
+ * 1960) scaled by 1/sqrt(d), the same for every coordinate.
+ * rotation  HOST float [n_heads][head_dim][head_dim].
+ * qjl_gauss HOST float [n_heads][head_dim][head_dim] (keys), else NULL.
+ * Errors: SQ_ERR_ARG (null, bits out of range), SQ_ERR_UNSUPPORTED (head_dim).
+ */
+sq_status sq_calibrate_tq(const float *rotation, const float *qjl_gauss, int n_heads,
+                          const sq_calib_opts *opts, sq_calib **out);
 
 /* Copy the handle's tables to the current HIP device (enqueued on `stream`,
  * which is synchronised before return).  Device memory is owned by the handle.
@@ -337,10 +365,12 @@ sq_status sq_dequantize(const sq_calib *c, int first_head, int n_heads, int batc
 /*
  * sq_unpack -- HOST decode of one head's slot (for tests and tools).
  * packed HOST uint32 slot of calibration head `head`; codes uint8 [T][d],
- * qjl uint8 [T][m] (may be NULL when m == 0), gamma float [T] (may be NULL).
+ * qjl uint8 [T][m] (may be NULL when m == 0), gamma float [T] (may be NULL),
+ * nu float [T] (vector norms of a normalised calibration, else 0; may be NULL).
  */
 sq_status sq_unpack(const sq_calib *c, int head, const uint32_t *packed,
-                    int64_t n_tokens, uint8_t *codes, uint8_t *qjl, float *gamma);
+                    int64_t n_tokens, uint8_t *codes, uint8_t *qjl, float *gamma,
+                    float *nu);
 
 /* Message of the last error on the calling thread ("" if none). */
 const char *sq_last_error(void);

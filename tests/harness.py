@@ -68,7 +68,8 @@ def compare_compress(oc, gpu_slot: np.ndarray, x: np.ndarray, T: int):
     res = oracle.compress(oc, x)
     band = oracle.band_mask(oc, res.y, BAND)
     qband = oracle.qjl_band_mask(oc, res, QJL_BAND)
-    ref = oracle.pack(oc.widths, oc.m, res.codes, res.z, res.gamma)
+    norm = bool(getattr(oc, "normalized", False))
+    ref = oracle.pack(oc.widths, oc.m, res.codes, res.z, res.gamma, res.nu if norm else None)
     W = oc.W
     gw = words_of(gpu_slot, W, T).astype(np.uint64)
     rw = words_of(ref, W, T).astype(np.uint64)
@@ -76,7 +77,10 @@ def compare_compress(oc, gpu_slot: np.ndarray, x: np.ndarray, T: int):
     # pad tokens must be zero
     pad = (gpu_slot[:Tp * W].reshape(Tp // 64, W, 64).transpose(0, 2, 1).reshape(Tp, W)[T:])
     assert np.all(pad == 0), "pad tokens not zero"
-    gc, gz, gg = oracle.unpack(oc.widths, oc.m, gpu_slot, T)
+    if norm:
+        gc, gz, gg, gn = oracle.unpack(oc.widths, oc.m, gpu_slot, T, norm=True)
+    else:
+        gc, gz, gg = oracle.unpack(oc.widths, oc.m, gpu_slot, T)
     diff = gc != res.codes
     assert not np.any(diff & ~band), f"{int((diff & ~band).sum())} code mismatches outside the band"
     assert np.all(np.abs(gc - res.codes)[diff] <= 1), "in-band flip larger than one code"
@@ -98,20 +102,33 @@ def compare_compress(oc, gpu_slot: np.ndarray, x: np.ndarray, T: int):
         g_ref = res.gamma.astype(np.float64)
         ulp16 = np.exp2(np.floor(np.log2(np.maximum(g_ref, 2.0 ** -14))) - 10)
         xn = np.linalg.norm(np.asarray(x, np.float64), axis=1)
-        tol = ulp16 + math.sqrt(oc.d_eff) * (oc.head_dim + 1) * 2.0 ** -24 * xn
+        if norm:
+            xn = np.ones_like(xn)  # r lives in the unit vector's space
+        tol = ulp16 + math.sqrt(oc.d_eff) * (oc.head_dim + 2) * 2.0 ** -24 * xn
         gbad = (np.abs(gg.astype(np.float64) - g_ref) > tol) & ~sig_flip
         assert not np.any(gbad), f"{int(gbad.sum())} gamma values outside one ulp + rotation error"
         out["qjl_flips"] = int(zd.sum())
         out["gamma_ulp"] = int((gu != ru).sum())
-    # tokens with no excused difference must match bit for bit (gamma aside)
+    if norm:
+        # the norm: |y| of the fp32 rotation against |x| in float64, one half
+        # rounding each: within one half ulp plus the rotation's error
+        n_ref = res.nu.astype(np.float64)
+        ulpn = np.exp2(np.floor(np.log2(np.maximum(n_ref, 2.0 ** -14))) - 10)
+        xn = np.linalg.norm(np.asarray(x, np.float64), axis=1)
+        ntol = ulpn + (oc.head_dim + 2) * 2.0 ** -24 * xn
+        nbad = np.abs(gn.astype(np.float64) - n_ref) > ntol
+        nbad &= ~(np.isnan(n_ref) & np.isnan(gn.astype(np.float64)))
+        assert not np.any(nbad), f"{int(nbad.sum())} vector norms outside one ulp + rotation error"
+        out["nu_ulp"] = int((gn.view(np.uint16) != res.nu.view(np.uint16)).sum())
+    # tokens with no excused difference must match bit for bit (gamma and the norm aside)
     clean = ~tok_flip
+    mask = np.full(W, 0xFFFFFFFF, np.uint64)
     if oc.m > 0:
         clean &= ~(gz != res.z).any(axis=1)
-        mask = np.full(W, 0xFFFFFFFF, np.uint64)
-        mask[W - 1] = 0x0000FFFF
-        assert np.array_equal(gw[clean] & mask, rw[clean] & mask)
-    else:
-        assert np.array_equal(gw[clean], rw[clean])
+        mask[W - 1] &= 0x0000FFFF
+    if norm:
+        mask[W - 1] &= 0xFFFF0000 if oc.m > 0 else 0x0000FFFF
+    assert np.array_equal(gw[clean] & mask, rw[clean] & mask)
     return out, res
 
 

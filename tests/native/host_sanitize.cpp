@@ -64,7 +64,8 @@ static Export export_head(const sq_calib *c, int h) {
   return e;
 }
 
-static void one_case(int d, int n_heads, int64_t n, double bits, int qjl, int max_bits, const char *tmp) {
+static void one_case(int d, int n_heads, int64_t n, double bits, int qjl, int max_bits, const char *tmp,
+                     int normalize = 0) {
   std::vector<float> x((size_t)n_heads * n * d), g((size_t)n_heads * std::max(1, qjl) * d * d);
   for (int h = 0; h < n_heads; ++h)
     for (int64_t t = 0; t < n; ++t)
@@ -78,6 +79,7 @@ static void one_case(int d, int n_heads, int64_t n, double bits, int qjl, int ma
   o.max_bits = max_bits;
   o.lloyd_max_iters = 50;
   o.n_threads = 2;
+  o.normalize = normalize;
   sq_calib *c = nullptr;
   CHECK(sq_calibrate(x.data(), n_heads, n, &o, qjl ? g.data() : nullptr, &c) == SQ_OK);
   if (!c) return;
@@ -98,7 +100,8 @@ static void one_case(int d, int n_heads, int64_t n, double bits, int qjl, int ma
   std::vector<uint8_t> codes((size_t)T * d), z((size_t)T * 8 * d + 1);
   std::vector<float> gam(T);
   for (int h = 0; h < n_heads; ++h) {
-    CHECK(sq_unpack(c, h, words.data(), T, codes.data(), z.data(), gam.data()) == SQ_OK);
+    std::vector<float> nus(T);
+    CHECK(sq_unpack(c, h, words.data(), T, codes.data(), z.data(), gam.data(), nus.data()) == SQ_OK);
     sq_head_info inf{};
     sq_calib_info(c, h, &inf);
     for (int64_t t = 0; t < T; ++t)
@@ -134,6 +137,36 @@ int main(int argc, char **argv) {
   one_case(128, 2, 300, 3.0, 1, 8, tmp);
   one_case(128, 1, 200, 2.0, 1, 2, tmp);     // capped widths
   one_case(256, 1, 300, 3.0, 1, 8, tmp);
+  one_case(64, 2, 120, 3.0, 1, 8, tmp, 1);   // normalised variant
+  // TurboQuant-style calibrations: random rotation, keys and values
+  {
+    const int d = 64;
+    std::vector<float> rot((size_t)2 * d * d), g((size_t)2 * d * d);
+    for (float &v : rot) v = (float)gauss();
+    for (float &v : g) v = (float)gauss();
+    sq_calib_opts o;
+    sq_calib_default_opts(&o, d);
+    o.avg_bits = 3.0;
+    sq_calib *k = nullptr, *v = nullptr;
+    CHECK(sq_calibrate_tq(rot.data(), g.data(), 2, &o, &k) == SQ_OK);
+    o.qjl_bits_per_signal_dim = 0;
+    CHECK(sq_calibrate_tq(rot.data(), nullptr, 2, &o, &v) == SQ_OK);
+    o.avg_bits = 2.5;
+    sq_calib *bad = nullptr;
+    CHECK(sq_calibrate_tq(rot.data(), nullptr, 2, &o, &bad) == SQ_ERR_ARG && !bad);
+    if (k && v) {
+      Export ek = export_head(k, 1), ev = export_head(v, 0);
+      CHECK(ek.widths[0] == 2 && ev.widths[5] == 3);
+      CHECK(sq_calib_save(k, tmp) == SQ_OK);
+      sq_calib *k2 = nullptr;
+      CHECK(sq_calib_load(tmp, &k2) == SQ_OK);
+      sq_head_info inf{};
+      if (k2) CHECK(sq_calib_info(k2, 0, &inf) == SQ_OK && inf.normalized == 1 && inf.m == d);
+      sq_calib_destroy(k2);
+    }
+    sq_calib_destroy(k);
+    sq_calib_destroy(v);
+  }
   // error paths
   sq_calib_opts o;
   sq_calib *c = nullptr;
@@ -156,7 +189,7 @@ int main(int argc, char **argv) {
   CHECK(sq_calib_load("/nonexistent/dir/file", &c) == SQ_ERR_IO);
   CHECK(sq_calib_info(nullptr, 0, nullptr) == SQ_ERR_ARG);
   CHECK(sq_packed_head_words(nullptr, 10) == -1);
-  CHECK(sq_unpack(nullptr, 0, nullptr, 1, nullptr, nullptr, nullptr) == SQ_ERR_ARG);
+  CHECK(sq_unpack(nullptr, 0, nullptr, 1, nullptr, nullptr, nullptr, nullptr) == SQ_ERR_ARG);
   CHECK(std::strlen(sq_build_digest()) > 0);
   sq_calib_destroy(nullptr);
   std::printf("host sanitize driver: %d failures\n", g_fail);

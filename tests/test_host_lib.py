@@ -211,3 +211,44 @@ def test_stale_library_is_refused(tmp_path):
         f.write("\n// a later edit\n")
     r = subprocess.run([sys.executable, "-c", probe], capture_output=True, text=True)
     assert r.returncode != 0 and "StaleLibraryError" in r.stderr, (r.stdout, r.stderr[-2000:])
+
+
+def test_turboquant_style_calibration_matches_oracle():
+    """sq_calibrate_tq (host C++) against oracle.tq_calibration: same widths,
+    QJL rows, record length, rotation and sketch; Gaussian Lloyd-Max tables
+    (Max, 1960, over sqrt(d)) to float32 rounding."""
+    for keys, bits, d in ((True, 3, 128), (False, 3, 128), (True, 4, 32), (False, 2, 256)):
+        r = np.random.default_rng(d + bits)
+        rot = np.stack([wl.random_orthogonal(r, d) for _ in range(2)]).astype(np.float32)
+        sk = r.standard_normal((2, d, d)).astype(np.float32)
+        cal = sq.sq_calibrate_tq(rot, bits, keys, sk if keys else None)
+        for h in range(2):
+            oc = oracle.tq_calibration(rot[h].astype(np.float64), sk[h], bits, keys)
+            ex = cal.export(h)
+            inf = ex["info"]
+            assert inf.normalized == 1 and inf.m == oc.m and inf.record_words == oc.W
+            np.testing.assert_array_equal(ex["widths"], oc.widths)
+            np.testing.assert_array_equal(ex["rotation"], rot[h].astype(np.float64))
+            thr = np.concatenate([t for t in oc.thresholds if len(t)] or [np.zeros(0)])
+            cen = np.concatenate([c for c in oc.centroids if len(c)] or [np.zeros(0)])
+            np.testing.assert_allclose(ex["thresholds"], thr, rtol=1e-6, atol=1e-9)
+            np.testing.assert_allclose(ex["centroids"], cen, rtol=1e-6, atol=1e-9)
+            if keys:
+                np.testing.assert_array_equal(ex["qjl"], sk[h])
+
+
+def test_normalized_calibration_matches_oracle():
+    cfg = wl.CONFIGS["llama8b"]
+    for which in ("k", "v"):
+        X, G = _heads(cfg, which, [(0, 2), (0, 5)])
+        qb = 1 if which == "k" else 0
+        cal = sq.sq_calibrate(X, 3.0, qb, G, normalize=True)
+        for k in range(2):
+            oc = oracle.calibrate(X[k], 3.0, qb, G[k] if G is not None else None, normalize=True)
+            ex = cal.export(k)
+            inf = ex["info"]
+            assert inf.normalized == 1 and inf.d_eff == oc.d_eff and inf.record_words == oc.W
+            np.testing.assert_array_equal(ex["widths"], oc.widths)
+            np.testing.assert_allclose(ex["eigenvalues"], oc.lam, rtol=0, atol=1e-12 * oc.lam[0])
+            cen = np.concatenate([c for c in oc.centroids if len(c)])
+            np.testing.assert_allclose(ex["centroids"], cen, rtol=1e-6, atol=1e-6 * oc.sigma[0])
