@@ -57,6 +57,15 @@ def parse():
     ap.add_argument("--copy-ref-mb", type=int, default=0,
                     help="also run one fp32 copy kernel of this many MiB before the timed "
                          "region (reference for scaling HBM byte counters)")
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "tiny", "llama8b", "qwen14b", "gemma9b"],
+                    help="decode (default): the throughput benchmark; the others: one decode "
+                         "step's latency over every layer of that model shape")
+    ap.add_argument("--scheme", default="sq", choices=["sq", "tq"],
+                    help="latency workloads: SpectralQuant (sq) or the TurboQuant-style baseline (tq)")
+    ap.add_argument("--bits", type=float, default=None,
+                    help="latency workloads: code bits per coordinate (default: the workload's first budget; "
+                         "tq: an integer)")
     return ap.parse_args()
 
 
@@ -132,6 +141,113 @@ def cpu_baseline(cfg, kcal_in, vcal_in, n_seqs, n_tokens):
                         f"softmax+attend; {n_vec} vectors in {dt:.2f} s of oracle time"))
 
 
+def latency(args):
+    """One decode step of a whole model shape (every layer, batch 1): for each
+    layer and KV head, append the new token's K and V (sq_compress_append),
+    then scores + softmax + value sum over the T-token compressed cache, as
+    sq_scores + sq_attend and as the fused sq_decode.  Layers are the batch
+    dimension of one call (calibration head = layer * kv_heads + head).  The
+    cache itself is compressed once before the timed region (its time is
+    reported as prefill).  Prints one JSON line."""
+    import torch
+    import workloads as wl
+    import compression_sq_compress_amd as sq
+    cfg = wl.CONFIGS[args.workload]
+    L, Hkv, Hq, d = cfg.layers, cfg.kv_heads, cfg.q_heads, cfg.head_dim
+    T = args.tokens or cfg.tokens[-1]
+    G = Hq // Hkv
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+    heads = [(l, h) for l in range(L) for h in range(Hkv)]
+    if args.scheme == "tq":
+        bits = int(args.bits or 3)
+        rot = np.stack([wl.tq_rotation(cfg, l, h) for l, h in heads]).astype(np.float32)
+        sk = np.stack([wl.tq_qjl(cfg, l, h) for l, h in heads]).astype(np.float32)
+        kcal = sq.sq_calibrate_tq(rot, bits, True, sk).upload(sh)
+        vcal = sq.sq_calibrate_tq(rot, bits, False).upload(sh)
+        label = f"TurboQuant-style, {bits} bits ({bits - 1}-bit keys + all-dims QJL)"
+    else:
+        bits = float(args.bits or cfg.budgets[0])
+        Xk = np.stack([wl.calibration_set(cfg, l, h, "k") for l, h in heads]).astype(np.float32)
+        Gk = np.stack([wl.qjl_gaussian(cfg, l, h) for l, h in heads])
+        Xv = np.stack([wl.calibration_set(cfg, l, h, "v") for l, h in heads]).astype(np.float32)
+        kcal = sq.sq_calibrate(Xk, bits, cfg.qjl_bits, Gk).upload(sh)
+        vcal = sq.sq_calibrate(Xv, bits, 0, None).upload(sh)
+        label = f"SpectralQuant, {bits} bits/coord + QJL on the signal dims"
+    with torch.cuda.stream(stream):
+        K = wl.layers_kv_on_device(cfg, "k", range(L), T + 1)
+        V = wl.layers_kv_on_device(cfg, "v", range(L), T + 1)
+        dtq = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        q = torch.from_numpy(wl.queries(cfg, L, Hq)).to(dev).to(dtq)
+        kp = torch.zeros((L, Hkv, kcal.packed_head_words(T + 1)), dtype=torch.int32, device=dev)
+        vp = torch.zeros((L, Hkv, vcal.packed_head_words(T + 1)), dtype=torch.int32, device=dev)
+        s = torch.empty((L, Hq, T + 1), dtype=torch.float32, device=dev)
+        ws = torch.empty(sq.sq_attend_workspace_bytes(L, Hq, T + 1, d) // 4, dtype=torch.float32, device=dev)
+        out = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
+        out2 = torch.empty_like(out)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    Kc, Vc = K[:, :, :T], V[:, :, :T]
+    Kn, Vn = K[:, :, T:T + 1], V[:, :, T:T + 1]
+
+    def prefill():
+        sq.sq_compress(kcal, Kc, kp, calib_batch_stride=Hkv, stream=sh)
+        sq.sq_compress(vcal, Vc, vp, calib_batch_stride=Hkv, stream=sh)
+
+    def append():
+        sq.sq_compress_append(kcal, Kn, kp, T, calib_batch_stride=Hkv, stream=sh)
+        sq.sq_compress_append(vcal, Vn, vp, T, calib_batch_stride=Hkv, stream=sh)
+
+    def split():
+        sq.sq_scores(kcal, q, kp, T + 1, s, Hkv, calib_batch_stride=Hkv, stream=sh)
+        sq.sq_attend(vcal, s, scale, vp, T + 1, ws, out, Hkv, calib_batch_stride=Hkv, stream=sh)
+
+    fused_ok = True
+    try:
+        sq.sq_decode(kcal, vcal, q, kp, vp, T + 1, scale, ws, out2, Hkv, calib_batch_stride=Hkv, stream=sh)
+    except sq.SQError as e:
+        fused_ok = False
+        fused_msg = str(e)
+
+    def fused():
+        sq.sq_decode(kcal, vcal, q, kp, vp, T + 1, scale, ws, out2, Hkv, calib_batch_stride=Hkv, stream=sh)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    ms_prefill = timed(prefill)
+    ms_append = timed(append)
+    ms_split = timed(split)
+    ms_fused = timed(fused) if fused_ok else None
+    step_ms = ms_append + (min(ms_split, ms_fused) if fused_ok else ms_split)
+    res = {
+        "metric": "decode step latency over every layer (append 1 token + scores + softmax + value sum)",
+        "value": step_ms, "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_ms, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {L} layers x {Hkv} KV / {Hq} q heads, hd{d}, {T}-token cache, "
+                               f"batch 1; {label}", "layers": L, "tokens": T, "scheme": args.scheme,
+                   "bits": bits, "record_words_k": kcal.info(0).record_words,
+                   "record_words_v": vcal.info(0).record_words},
+        "ms": {"append_kv": ms_append, "scores_plus_attend": ms_split, "decode_fused": ms_fused,
+               "prefill_compress_kv": ms_prefill},
+        "note": ("working set below the 256 MB Infinity Cache (MALL): latency, not an HBM-bandwidth figure"
+                 + ("" if fused_ok else f"; sq_decode refused: {fused_msg}")),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -139,6 +255,9 @@ def main():
               "(the decode workload shards by KV head with no exchange; one GPU's share is "
               "what is measured).", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "decode":
+        latency(args)
+        return
     import torch
     import workloads as wl
     import compression_sq_compress_amd as sq

@@ -285,3 +285,23 @@ def decode_kv_on_device(cfg: Config, which: str, seed: int = DEFAULT_SEED, devic
             z = torch.randn((T, d), generator=g, device=device, dtype=torch.float32)
             out[b, h] = (z @ facs[h]).to(torch.bfloat16)
     return out
+
+
+def layers_kv_on_device(cfg: Config, which: str, layers, n_tokens: int, seed: int = DEFAULT_SEED,
+                        device="cuda"):
+    """K or V of several layers of one sequence, [len(layers)][kv_heads][T][d] in
+    the configuration's dtype on the GPU (layers as the batch dimension, the
+    calibration heads of layer l being l * kv_heads + h), drawn with torch's
+    seeded generator times each (layer, head)'s factor A."""
+    import torch
+    d = cfg.head_dim
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + cfg.cid * 101 + (1 if which == "k" else 2) + 7919)
+    out = torch.empty((len(layers), cfg.kv_heads, n_tokens, d), dtype=dt, device=device)
+    for i, l in enumerate(layers):
+        for h in range(cfg.kv_heads):
+            a = torch.from_numpy(head_covariance_factor(cfg, l, h, which, seed).astype(np.float32)).to(device)
+            z = torch.randn((n_tokens, d), generator=g, device=device, dtype=torch.float32)
+            out[i, h] = (z @ a).to(dt)
+    return out
