@@ -31,7 +31,7 @@ EXPORTS = ("sq_calib_default_opts", "sq_calibrate", "sq_calib_upload", "sq_calib
            "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_compress_append", "sq_scores",
            "sq_attend_workspace_bytes", "sq_attend", "sq_dequantize", "sq_unpack",
            "sq_last_error", "sq_build_digest", "sq_plan_decode",
-           "sq_attend_noalloc", "sq_decode", "sq_calibrate_tq")
+           "sq_attend_noalloc", "sq_decode", "sq_calibrate_tq", "sq_calibrate_device")
 
 
 class StaleLibraryError(RuntimeError):
@@ -47,7 +47,8 @@ class SQError(RuntimeError):
 class CalibOpts(C.Structure):
     _fields_ = [("head_dim", C.c_int), ("avg_bits", C.c_double),
                 ("qjl_bits_per_signal_dim", C.c_int), ("max_bits", C.c_int),
-                ("lloyd_max_iters", C.c_int), ("n_threads", C.c_int), ("normalize", C.c_int)]
+                ("lloyd_max_iters", C.c_int), ("n_threads", C.c_int), ("normalize", C.c_int),
+                ("deff_cumvar", C.c_double)]
 
 
 class HeadInfo(C.Structure):
@@ -105,6 +106,7 @@ def _load():
         "sq_dequantize": (I, [P, I, I, I, I, P, I64, I64, I64, P, P]),
         "sq_unpack": (I, [P, I, P, I64, P, P, P, P]),
         "sq_calibrate_tq": (I, [P, P, I, C.POINTER(CalibOpts), C.POINTER(C.c_void_p)]),
+        "sq_calibrate_device": (I, [P, I, I64, C.POINTER(CalibOpts), P, P, C.POINTER(C.c_void_p)]),
         "sq_last_error": (C.c_char_p, []),
         "sq_build_digest": (C.c_char_p, []),
         "sq_plan_decode": (I, [P, P, I, I, I, I, I, I64, C.POINTER(DecodePlan)]),
@@ -205,16 +207,8 @@ def sq_calib_default_opts(head_dim: int) -> CalibOpts:
     return o
 
 
-def sq_calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
-                 qjl_gauss: Optional[np.ndarray] = None, max_bits: int = 8,
-                 lloyd_max_iters: int = 200, n_threads: int = 0,
-                 normalize: bool = False) -> Calibration:
-    """samples: host float32 [n_heads][n_samples][d]; qjl_gauss: host float32
-    [n_heads][qjl_bits*d][d] (required when qjl_bits > 0); normalize: the
-    normalised variant (per-vector norm stored)."""
-    x = np.ascontiguousarray(samples, dtype=np.float32)
-    assert x.ndim == 3
-    H, n, d = x.shape
+def _calib_opts(d, avg_bits, qjl_bits, max_bits, lloyd_max_iters, n_threads, normalize,
+                deff_cumvar) -> CalibOpts:
     o = sq_calib_default_opts(d)
     o.avg_bits = float(avg_bits)
     o.qjl_bits_per_signal_dim = int(qjl_bits)
@@ -222,12 +216,53 @@ def sq_calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
     o.lloyd_max_iters = int(lloyd_max_iters)
     o.n_threads = int(n_threads)
     o.normalize = 1 if normalize else 0
-    g = None
-    if qjl_gauss is not None:
-        g = np.ascontiguousarray(qjl_gauss, dtype=np.float32)
-        assert g.shape == (H, max(1, qjl_bits) * d, d), g.shape
+    o.deff_cumvar = float(deff_cumvar)
+    return o
+
+
+def _gauss(qjl_gauss, H, qjl_bits, d):
+    if qjl_gauss is None:
+        return None
+    g = np.ascontiguousarray(qjl_gauss, dtype=np.float32)
+    assert g.shape == (H, max(1, qjl_bits) * d, d), g.shape
+    return g
+
+
+def sq_calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
+                 qjl_gauss: Optional[np.ndarray] = None, max_bits: int = 8,
+                 lloyd_max_iters: int = 200, n_threads: int = 0,
+                 normalize: bool = False, deff_cumvar: float = 0.0) -> Calibration:
+    """samples: host float32 [n_heads][n_samples][d]; qjl_gauss: host float32
+    [n_heads][qjl_bits*d][d] (required when qjl_bits > 0); normalize: the
+    normalised variant (per-vector norm stored); deff_cumvar: 0 for d_eff by
+    the rounded participation ratio, else the cumulative-variance fraction."""
+    x = np.ascontiguousarray(samples, dtype=np.float32)
+    assert x.ndim == 3
+    H, n, d = x.shape
+    o = _calib_opts(d, avg_bits, qjl_bits, max_bits, lloyd_max_iters, n_threads, normalize, deff_cumvar)
+    g = _gauss(qjl_gauss, H, qjl_bits, d)
     h = C.c_void_p()
     _check(_load().sq_calibrate(_ptr(x), H, n, C.byref(o), _ptr(g), C.byref(h)))
+    return Calibration(h.value)
+
+
+def sq_calibrate_device(samples, avg_bits: float, qjl_bits: int,
+                        qjl_gauss: Optional[np.ndarray] = None, max_bits: int = 8,
+                        lloyd_max_iters: int = 200, n_threads: int = 0,
+                        normalize: bool = False, deff_cumvar: float = 0.0,
+                        stream=None) -> Calibration:
+    """As sq_calibrate with samples a contiguous device float32 tensor
+    [n_heads][n_samples][d] (covariance, eigendecomposition and rotation on
+    the GPU); qjl_gauss stays a host array."""
+    assert samples.is_cuda and samples.dim() == 3 and samples.is_contiguous()
+    import torch
+    assert samples.dtype == torch.float32
+    H, n, d = samples.shape
+    o = _calib_opts(d, avg_bits, qjl_bits, max_bits, lloyd_max_iters, n_threads, normalize, deff_cumvar)
+    g = _gauss(qjl_gauss, H, qjl_bits, d)
+    h = C.c_void_p()
+    _check(_load().sq_calibrate_device(_ptr(samples), H, n, C.byref(o), _ptr(g), _stream(stream),
+                                       C.byref(h)))
     return Calibration(h.value)
 
 

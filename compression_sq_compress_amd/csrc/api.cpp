@@ -44,11 +44,12 @@ extern "C" sq_status sq_calib_default_opts(sq_calib_opts *o, int head_dim) {
   o->lloyd_max_iters = 200;
   o->n_threads = 0;
   o->normalize = 0;
+  o->deff_cumvar = 0.0;
   clear_error();
   return SQ_OK;
 }
 
-static sq_status check_opts(const sq_calib_opts *o) {
+sq_status sq::check_calib_opts(const sq_calib_opts *o) {
   if (!o) return fail(SQ_ERR_ARG, "opts is NULL");
   if (!supported_dim(o->head_dim))
     return fail(SQ_ERR_UNSUPPORTED, "head_dim must be 32, 64, 128 or 256");
@@ -59,6 +60,8 @@ static sq_status check_opts(const sq_calib_opts *o) {
     return fail(SQ_ERR_ARG, "qjl_bits_per_signal_dim must be in [0, 8]");
   if (o->lloyd_max_iters < 0) return fail(SQ_ERR_ARG, "lloyd_max_iters must be >= 0");
   if (o->normalize != 0 && o->normalize != 1) return fail(SQ_ERR_ARG, "normalize must be 0 or 1");
+  if (!(o->deff_cumvar >= 0.0 && o->deff_cumvar <= 1.0))
+    return fail(SQ_ERR_ARG, "deff_cumvar must be 0 (participation ratio) or in (0, 1]");
   return SQ_OK;
 }
 
@@ -72,7 +75,7 @@ extern "C" sq_status sq_calibrate(const float *samples, int n_heads, int64_t n_s
                                   sq_calib **out) {
   if (!out) return fail(SQ_ERR_ARG, "sq_calibrate: out is NULL");
   *out = nullptr;
-  sq_status st = check_opts(opts);
+  sq_status st = check_calib_opts(opts);
   if (st != SQ_OK) return st;
   if (!samples) return fail(SQ_ERR_ARG, "sq_calibrate: samples is NULL");
   if (n_heads <= 0) return fail(SQ_ERR_ARG, "sq_calibrate: n_heads must be > 0");
@@ -128,7 +131,7 @@ extern "C" sq_status sq_calibrate_tq(const float *rotation, const float *qjl_gau
                                      const sq_calib_opts *opts, sq_calib **out) {
   if (!out) return fail(SQ_ERR_ARG, "sq_calibrate_tq: out is NULL");
   *out = nullptr;
-  sq_status st = check_opts(opts);
+  sq_status st = check_calib_opts(opts);
   if (st != SQ_OK) return st;
   if (!rotation) return fail(SQ_ERR_ARG, "sq_calibrate_tq: rotation is NULL");
   if (n_heads <= 0) return fail(SQ_ERR_ARG, "sq_calibrate_tq: n_heads must be > 0");
@@ -206,12 +209,12 @@ extern "C" sq_status sq_calib_export(const sq_calib *c, int head, double *eigenv
 
 // ---------------------------------------------------------------- save / load
 // File: "SQCALIB1", u32 version, opts (fixed fields; version 2 adds
-// normalize), u32 n_heads, then per head: i32 d, d_eff, m; f64 pr, kappa;
+// normalize, version 3 the f64 deff_cumvar after avg_bits), u32 n_heads, then per head: i32 d, d_eff, m; f64 pr, kappa;
 // f64 lam[d]; f64 R[d*d]; i32 widths[d]; i32 n_regions, unconverged
 // (version 2: and normalized); f32 thr[n_thr]; f32 cent[n_cent];
 // f32 S[m*d_eff].  Little-endian.  Version 1 files load as unnormalised.
 static const char kMagic[8] = {'S', 'Q', 'C', 'A', 'L', 'I', 'B', '1'};
-static const uint32_t kVersion = 2;  // 2: normalised variant flag in the options and per head
+static const uint32_t kVersion = 3;  // 2: normalised variant flag; 3: d_eff rule in the options
 
 namespace {
 struct File {
@@ -234,6 +237,7 @@ extern "C" sq_status sq_calib_save(const sq_calib *c, const char *path) {
                    c->opts.lloyd_max_iters, c->opts.n_threads, c->opts.normalize};
   F.w(oi, sizeof(oi));
   F.w(&c->opts.avg_bits, 8);
+  F.w(&c->opts.deff_cumvar, 8);
   uint32_t nh = (uint32_t)c->heads.size();
   F.w(&nh, 4);
   for (const HeadCal &h : c->heads) {
@@ -278,9 +282,11 @@ extern "C" sq_status sq_calib_load(const char *path, sq_calib **out) {
   c->opts.n_threads = oi[4];
   c->opts.normalize = oi[5];
   F.r(&c->opts.avg_bits, 8);
+  c->opts.deff_cumvar = 0.0;
+  if (ver >= 3) F.r(&c->opts.deff_cumvar, 8);
   uint32_t nh = 0;
   F.r(&nh, 4);
-  if (!F.ok || check_opts(&c->opts) != SQ_OK || nh == 0 || nh > (1u << 24)) {
+  if (!F.ok || check_calib_opts(&c->opts) != SQ_OK || nh == 0 || nh > (1u << 24)) {
     delete c;
     return fail(SQ_ERR_IO, "sq_calib_load: malformed header");
   }

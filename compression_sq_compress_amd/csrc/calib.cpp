@@ -193,31 +193,74 @@ sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &
   // 2. eigendecomposition, descending, clamped, sign rule
   std::vector<double> V;
   jacobi_eigen(C, V, d);
+  std::vector<double> lam, R;
+  order_eigenpairs(C, V, d, lam, R);
+  // rotated samples y_t = R x_t (x_t divided by its norm in the normalised variant)
+  std::vector<double> Y((size_t)n * d);
+  for (int64_t t = 0; t < n; ++t)
+    for (int i = 0; i < d; ++i) {
+      const double *Ri = &R[(size_t)i * d];
+      double y = 0.0;
+      for (int j = 0; j < d; ++j) y += Ri[j] * sample(t, j);
+      Y[(size_t)t * d + i] = y;
+    }
+  return finish_head_from_eigen(lam, R, Y.data(), n, d, o, gauss, h, err);
+}
+
+void order_eigenpairs(const std::vector<double> &a, const std::vector<double> &V, int d, std::vector<double> &lam,
+                      std::vector<double> &R) {
   std::vector<int> order(d);
   std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-    return C[(size_t)a * d + a] > C[(size_t)b * d + b];
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    return a[(size_t)x * d + x] > a[(size_t)y * d + y];
   });
-  h.lam.resize(d);
-  h.R.assign((size_t)d * d, 0.0);
+  lam.resize(d);
+  R.assign((size_t)d * d, 0.0);
   for (int k = 0; k < d; ++k) {
     const int src = order[k];
-    h.lam[k] = std::max(0.0, C[(size_t)src * d + src]);
+    lam[k] = std::max(0.0, a[(size_t)src * d + src]);
     int jmax = 0;
     double vmax = -1.0;
     for (int j = 0; j < d; ++j) {
-      const double a = std::fabs(V[(size_t)j * d + src]);
-      if (a > vmax) { vmax = a; jmax = j; }
+      const double v = std::fabs(V[(size_t)j * d + src]);
+      if (v > vmax) { vmax = v; jmax = j; }
     }
     const double sgn = V[(size_t)jmax * d + src] < 0 ? -1.0 : 1.0;
-    for (int j = 0; j < d; ++j) h.R[(size_t)k * d + j] = sgn * V[(size_t)j * d + src];
+    for (int j = 0; j < d; ++j) R[(size_t)k * d + j] = sgn * V[(size_t)j * d + src];
   }
-  // 3. participation ratio, d_eff, kappa
+}
+
+int deff_from_spectrum(const std::vector<double> &lam, double cumvar) {
+  const int d = (int)lam.size();
+  double s1 = 0.0, s2 = 0.0;
+  for (double l : lam) { s1 += l; s2 += l * l; }
+  if (cumvar > 0) {
+    // smallest k whose leading k eigenvalues hold at least the fraction cumvar of the total
+    double acc = 0.0;
+    for (int k = 1; k <= d; ++k) {
+      acc += lam[k - 1];
+      if (acc >= cumvar * s1) return k;
+    }
+    return d;
+  }
+  const double pr = s2 > 0 ? s1 * s1 / s2 : 0.0;
+  const long r = (long)std::nearbyint(pr);  // default rounding mode: half to even
+  return (int)std::min<long>(std::max<long>(r, 1), d);
+}
+
+sq_status finish_head_from_eigen(const std::vector<double> &lam, const std::vector<double> &R, const double *Y,
+                                 int64_t n, int d, const sq_calib_opts &o, const float *gauss, HeadCal &h,
+                                 std::string &err) {
+  h = HeadCal();
+  h.d = d;
+  h.normalized = o.normalize != 0;
+  h.lam = lam;
+  h.R = R;
+  // 3. participation ratio, d_eff (rounded PR, or the cumulative-variance rule), kappa
   double s1 = 0.0, s2 = 0.0;
   for (double l : h.lam) { s1 += l; s2 += l * l; }
   h.pr = s2 > 0 ? s1 * s1 / s2 : 0.0;
-  long r = (long)std::nearbyint(h.pr);  // default rounding mode: half to even
-  h.d_eff = (int)std::min<long>(std::max<long>(r, 1), d);
+  h.d_eff = deff_from_spectrum(h.lam, o.deff_cumvar);
   h.kappa = (h.d_eff >= d || h.lam[h.d_eff] <= 0) ? std::numeric_limits<double>::infinity()
                                                   : h.lam[h.d_eff - 1] / h.lam[h.d_eff];
   // 4. widths
@@ -241,12 +284,7 @@ sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &
       u.reserve((size_t)n * coords.size());
       for (int i : coords) {
         if (!(sigma[i] > 0)) continue;
-        const double *Ri = &h.R[(size_t)i * d];
-        for (int64_t t = 0; t < n; ++t) {
-          double y = 0.0;
-          for (int j = 0; j < d; ++j) y += Ri[j] * sample(t, j);
-          u.push_back(y / sigma[i]);
-        }
+        for (int64_t t = 0; t < n; ++t) u.push_back(Y[(size_t)t * d + i] / sigma[i]);
       }
       std::sort(u.begin(), u.end());
       const int L = 1 << b;

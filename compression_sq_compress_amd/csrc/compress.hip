@@ -1,6 +1,9 @@
 // sq_compress and sq_compress_append: rotation, quantisation, selective QJL
 // and packing of K/V vectors (gfx950).
 
+#include <cstdlib>
+#include <cstring>
+
 #include "devcommon.h"
 
 namespace sq {
@@ -520,6 +523,11 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
 //             the words with QJL bits or gamma: every wave first adds its
 //             share of the QJL rows (and one wave gamma) from the residual
 //             tile, and those words are stored after the next barrier.
+// With GRID the quantise step reads instead one grid cell per value (code =
+// cells' count left of it + one compare with the cell's threshold), the MFMA
+// rows are the coordinates in natural order (R fragments of compress_kernel),
+// and a lane's four codes (coordinates 16 w + 4 s .. + 3, adjacent fields) are
+// combined in registers and OR-ed into the record tile as one 64-bit window.
 // x tiles are double-buffered and fetched two tiles ahead; the record tile
 // is triple-buffered, the residual tile double-buffered, so the barrier of
 // tile t also separates tile t+1's writes from the reads of tiles t-1, t-2.
@@ -545,7 +553,10 @@ constexpr int C2_WMAX = 6;  // record words stored per wave and tile (word k goe
 
 // RS: record tile row stride in words (odd, above the record length: the
 // last column is a pad), a constant so that token-block offsets are immediates
-template <int D, bool F32, int RS>
+// GRID: quantise with the grid tables (one cell read per value, codes of a
+// lane's four registers combined before one pair of record-tile ORs; MFMA
+// rows in natural coordinate order) instead of the padded trees.
+template <int D, bool F32, int RS, bool GRID>
 __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   extern __shared__ float smem[];
   constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
@@ -562,10 +573,17 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   float *csig = smem + a.lds_csig_off;
   float *Sl = smem + a.lds_s_off;  // [m][C2_SP]
   {
-    const float *g = (const float *)(a.blob + hd->off_tree2);
-    for (int k = threadIdx.x; k < hd->n_tree2; k += NT) trees[k] = g[k];
-    const float *gc = (const float *)(a.blob + hd->off_csig2);
-    for (int k = threadIdx.x; k < hd->n_csig2; k += NT) csig[k] = gc[k];
+    if constexpr (GRID) {
+      const uint32_t *g = (const uint32_t *)(a.blob + hd->off_gcells);
+      for (int k = threadIdx.x; k < 2 * hd->n_gcells; k += NT) ((uint32_t *)trees)[k] = g[k];
+      const float *gc = (const float *)(a.blob + hd->off_gcsig);
+      for (int k = threadIdx.x; k < hd->n_gcsig; k += NT) csig[k] = gc[k];
+    } else {
+      const float *g = (const float *)(a.blob + hd->off_tree2);
+      for (int k = threadIdx.x; k < hd->n_tree2; k += NT) trees[k] = g[k];
+      const float *gc = (const float *)(a.blob + hd->off_csig2);
+      for (int k = threadIdx.x; k < hd->n_csig2; k += NT) csig[k] = gc[k];
+    }
     const float *gs = (const float *)(a.blob + hd->off_S);
     for (int k = threadIdx.x; k < m * C2_SP; k += NT)
       Sl[k] = (k % C2_SP) < d_eff ? gs[(k / C2_SP) * d_eff + k % C2_SP] : 0.0f;
@@ -576,7 +594,28 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   // per lane and register: tree base | (record word | bit shift << 8 |
   // straddles << 13) << 16; coordinate | signal-centroid base << 8 (0xFFFFFF: none)
   uint32_t tw[4], cc[4];
-  {
+  // grid quantiser, per lane and register (coordinate 16 w + 4 s + r): u = y a + b,
+  // its region's cells (LDS byte address) and last cell, signal-centroid base,
+  // field shift; the lane's run of four fields: record word | bit shift << 8
+  float ga[4], gb[4], gcmf[4];
+  uint32_t gtab[4], gfs[4], gpos = 0;  // gfs: field shift | signal-centroid base << 8 (0xFFFFFF: none)
+  if constexpr (GRID) {
+    const uint32_t cells0 = (uint32_t)(uintptr_t)trees;
+    const uint4 *GC = (const uint4 *)(a.blob + hd->off_gcoord);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 16 * w + 4 * s4 + r;
+      const uint4 v0 = GC[2 * c], v1 = GC[2 * c + 1];
+      ga[r] = __uint_as_float(v0.x);
+      gb[r] = __uint_as_float(v0.y);
+      gtab[r] = cells0 + v0.z;
+      gcmf[r] = (float)v0.w;
+      gfs[r] = v1.y | ((v1.x == 0xFFFFFFFFu ? 0xFFFFFFu : v1.x) << 8);
+      if (r == 0) gpos = v1.z;
+      dep[r] = 0;
+      tw[r] = cc[r] = 0u;
+    }
+  } else {
     const uint32_t *Hv = (const uint32_t *)(a.blob + hd->off_p2) + w * P2_WAVE;  // per-lane reads
     const DevCoord *cd = (const DevCoord *)(a.blob + hd->off_coord);
 #pragma unroll
@@ -599,7 +638,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   }
   // QJL rows of this wave (all 64 tokens): [jb, je)
   const int jb = (w * m) / NW, je = ((w + 1) * m) / NW;
-  const uint4 *Rf = (const uint4 *)(a.blob + hd->off_Rfrag2);
+  const uint4 *Rf = (const uint4 *)(a.blob + (GRID ? hd->off_Rfrag : hd->off_Rfrag2));
   uint4 rf[3][KB];
 #pragma unroll
   for (int sp = 0; sp < 3; ++sp)
@@ -709,10 +748,45 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     // registers by decreasing depth, so the registers still descending at a
     // level are a prefix.  (The descriptors are decoded per tile: hoisting the
     // decoded fields out of the loop would not fit the register budget.)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(tw[r]), "+v"(cc[r]));
     uint32_t *rec = rec0 + rb * 64 * rs;
     float *rtile = smem + a.lds_res_off + par * 64 * C2_RS;
+    if constexpr (GRID) {
+      // one cell read per value; the lane's four codes (adjacent fields) are
+      // combined, then OR-ed into the record tile as one 64-bit window
+      typedef const __attribute__((address_space(3))) uint64_t lds_u64;
+      uint32_t F[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t code[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // a NaN u converts to cell 0 and fails the compare: code 0
+          // (v_med3_f32 returns 0 for a NaN first operand; +-inf clamp to the ends)
+          const float u = fmaf(acc[j][r], ga[r], gb[r]);
+          const int cell = (int)__builtin_amdgcn_fmed3f(u, 0.0f, gcmf[r]);
+          const uint64_t e = *(lds_u64 *)(uintptr_t)(gtab[r] + (uint32_t)cell * 8u);
+          code[j] = (uint32_t)(e >> 32) + (u > __uint_as_float((uint32_t)e) ? 1u : 0u);
+          F[j] |= code[j] << (gfs[r] & 31u);
+        }
+        const uint32_t gcb = gfs[r] >> 8;
+        if (m > 0 && gcb != 0xFFFFFFu) {
+          const int crd = 16 * w + 4 * s4 + r;  // < d_eff <= 16
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            rtile[((lane & 15) + 16 * j) * C2_RS + crd] = acc[j][r] - csig[gcb + code[j]];
+        }
+      }
+      uint32_t *rw = rec + (lane & 15) * rs + (gpos & 0xFFu);
+      const uint32_t sh = gpos >> 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t v = (uint64_t)F[j] << sh;
+        atomicOr(rw + 16 * j * rs, (uint32_t)v);
+        atomicOr(rw + 16 * j * rs + 1, (uint32_t)(v >> 32));
+      }
+    } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(tw[r]), "+v"(cc[r]));
     uint32_t k[4][4];
     const float *tr[4];
 #pragma unroll
@@ -781,6 +855,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
             rtile[((lane & 15) + 16 * j) * C2_RS + crd] = acc[j][r] - csig[cb + k[r][j] - (1u << dep[r])];
         }
       }
+    }
     }
     // ---- the next tile's x has landed (this wave's loads; the barrier covers
     // every wave's); then the tile after it goes into the buffer just read
@@ -886,15 +961,21 @@ static void launch_compress(dim3 grid, size_t lds, hipStream_t s, const Compress
   hipLaunchKernelGGL((compress_kernel<D, F32, TG>), grid, dim3(4 * D), lds, s, a);
 }
 
-template <int D, bool F32>
-static void launch_compress2(int rsc, dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
+template <int D, bool F32, bool GRID>
+static void launch_compress2_g(int rsc, dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
   // record strides this head size can need (at most C2_WMAX words per wave)
   if (rsc == 17) {
-    hipLaunchKernelGGL((compress2_kernel<D, F32, 17>), grid, dim3(4 * D), lds, s, a);
+    hipLaunchKernelGGL((compress2_kernel<D, F32, 17, GRID>), grid, dim3(4 * D), lds, s, a);
   } else if constexpr (D >= 64) {
-    if (rsc == 33) hipLaunchKernelGGL((compress2_kernel<D, F32, 33>), grid, dim3(4 * D), lds, s, a);
-    else if constexpr (D == 128) hipLaunchKernelGGL((compress2_kernel<D, F32, 49>), grid, dim3(4 * D), lds, s, a);
+    if (rsc == 33) hipLaunchKernelGGL((compress2_kernel<D, F32, 33, GRID>), grid, dim3(4 * D), lds, s, a);
+    else if constexpr (D == 128) hipLaunchKernelGGL((compress2_kernel<D, F32, 49, GRID>), grid, dim3(4 * D), lds, s, a);
   }
+}
+
+template <int D, bool F32>
+static void launch_compress2(bool gridq, int rsc, dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
+  if (gridq) launch_compress2_g<D, F32, true>(rsc, grid, lds, s, a);
+  else launch_compress2_g<D, F32, false>(rsc, grid, lds, s, a);
 }
 
 template <int D>
@@ -953,16 +1034,29 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
     // (normalised heads have no register plan: n_p2 = 0)
     bool use2 = d <= 128 && 64 * xs_token * esz < ((int64_t)1 << 32) && c->W_max <= C2_WMAX * (d / 16) &&
                 n_heads <= 65535 && batch <= 65535;
-    int mt = 0, mc = 0, mq = 0;
+    // quantiser: the grid tables when every head has them, else the padded
+    // trees (the environment variable SQ_QUANTISER = "tree" forces the trees)
+    const char *qenv = std::getenv("SQ_QUANTISER");
+    bool gridq = use2 && !(qenv && std::strcmp(qenv, "tree") == 0);
+    bool treeq = use2;
+    int mt = 0, mc = 0, mq = 0, mg = 0, mgc = 0;
     for (int bb = 0; bb < std::max(1, batch) && use2; ++bb) {
       for (int h = 0; h < n_heads; ++h) {
         const DevHead &hd = c->host_desc[first_head + bb * calib_batch_stride + h];
-        if (hd.n_p2 == 0) use2 = false;
+        if (hd.n_p2 == 0) treeq = false;
+        if (hd.n_gcells == 0) gridq = false;
         mt = std::max(mt, hd.n_tree2);
         mc = std::max(mc, hd.n_csig2);
         mq = std::max(mq, hd.m);
+        mg = std::max(mg, 2 * hd.n_gcells);
+        mgc = std::max(mgc, hd.n_gcsig);
       }
       if (calib_batch_stride == 0) break;
+    }
+    use2 = gridq || treeq;
+    if (gridq) {
+      mt = mg;
+      mc = mgc;
     }
     if (use2) {
       Compress2Args b2{};
@@ -998,9 +1092,9 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
         dim3 grid((unsigned)((b2.n_tiles + b2.tiles_per_wg - 1) / b2.tiles_per_wg), n_heads, batch);
         hipStream_t s = (hipStream_t)stream;
         switch (d) {
-          case 32: f32 ? launch_compress2<32, true>(rsc, grid, lds2, s, b2) : launch_compress2<32, false>(rsc, grid, lds2, s, b2); break;
-          case 64: f32 ? launch_compress2<64, true>(rsc, grid, lds2, s, b2) : launch_compress2<64, false>(rsc, grid, lds2, s, b2); break;
-          default: f32 ? launch_compress2<128, true>(rsc, grid, lds2, s, b2) : launch_compress2<128, false>(rsc, grid, lds2, s, b2); break;
+          case 32: f32 ? launch_compress2<32, true>(gridq, rsc, grid, lds2, s, b2) : launch_compress2<32, false>(gridq, rsc, grid, lds2, s, b2); break;
+          case 64: f32 ? launch_compress2<64, true>(gridq, rsc, grid, lds2, s, b2) : launch_compress2<64, false>(gridq, rsc, grid, lds2, s, b2); break;
+          default: f32 ? launch_compress2<128, true>(gridq, rsc, grid, lds2, s, b2) : launch_compress2<128, false>(gridq, rsc, grid, lds2, s, b2); break;
         }
         return launched(fn);
       }

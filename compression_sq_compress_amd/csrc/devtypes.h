@@ -80,7 +80,33 @@ struct DevHead {
   int64_t off_csig2;    // float [n_csig2] signal centroids * sigma_i, padded per coordinate
   int64_t off_Rfrag2;   // bf16 [3][d/16][d/32][64][8] like off_Rfrag, rows permuted (see P2_WAVE)
   int64_t off_fsched;   // uint32 fused decode schedule (FS_* layout below)
+  // grid quantiser of the register compress plan (GRID_* layout below);
+  // n_gcells = 0: not available for this head
+  int32_t n_gcells, n_gcsig;
+  int64_t off_gcoord;   // uint32 [d][GRID_COORD_WORDS]
+  int64_t off_gcells;   // uint32 [n_gcells][2]
+  int64_t off_gcsig;    // float [n_gcsig] signal centroids * sigma_i, per coordinate
 };
+
+// Grid quantiser.  A coordinate's thresholds are sigma_i times the thresholds
+// t_0 < .. < t_{n-1} of its region (regime, width); each region gets a
+// uniform grid of cells of width h < min(t_{j+1} - t_j) starting at o, so a
+// cell holds at most one threshold, and o, h are chosen so that every
+// threshold sits at least 1/512 of a cell away from the cell edges.  With
+// u = (y / sigma_i - o) / h = y * a_i + b_i and cell = clamp(trunc(u), 0,
+// C - 1), the code is code_lo(cell) + [u > t_cell(cell)], where code_lo
+// counts the thresholds left of the cell and t_cell is the cell's threshold
+// in cell units (+inf when it has none).  A rounding of u that moves a value
+// across a cell edge cannot change the code: no threshold lies that close to
+// an edge.  Cell 0 of the table is (+inf, 0), used by zero-width coordinates
+// (a_i = b_i = 0).  Per coordinate c (natural order; MFMA row 4s + r of wave
+// w is coordinate 16w + 4s + r): [0] a_i (fp32 bits), [1] b_i, [2] byte offset
+// of its region's cells, [3] C - 1, [4] signal-centroid base (floats) or
+// 0xFFFFFFFF, [5] bit offset of its field within the fields of coordinates
+// 4k .. 4k + 3 (k = c / 4), [6] that run's record word | bit shift << 8.
+// Cells: (t_cell as fp32 bits, code_lo).
+constexpr int GRID_COORD_WORDS = 8;
+constexpr int GRID_MAX_CELLS = 6144;
 
 // Register-quantising compress plan.  Coordinates are taken in groups of 4
 // (equal widths where possible, spread over different record words; depth =
@@ -125,6 +151,6 @@ static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
 constexpr int FS_SLOTS = 8;
 constexpr int FG_BITS = 6;
 
-static_assert(sizeof(DevHead) == 216, "DevHead layout");
+static_assert(sizeof(DevHead) == 248, "DevHead layout");
 
 }  // namespace sq

@@ -52,6 +52,18 @@ void clear_error();
 sq_status calibrate_head(const float *x, int64_t n, int d, const sq_calib_opts &o,
                          const float *gauss, HeadCal &out, std::string &err);
 void finish_layout(HeadCal &h);
+// eigenpairs of a Jacobi result (diag(a), columns of V) in descending order,
+// clamped at zero, each vector signed so its largest-magnitude entry is positive
+void order_eigenpairs(const std::vector<double> &a, const std::vector<double> &V, int d,
+                      std::vector<double> &lam, std::vector<double> &R);
+// d_eff: rounded participation ratio (cumvar == 0) or the cumulative-variance rule
+int deff_from_spectrum(const std::vector<double> &lam, double cumvar);
+// steps 3-6 of a calibration from the ordered eigenpairs and the rotated
+// samples Y [n][d] (of the unit samples in the normalised variant)
+sq_status finish_head_from_eigen(const std::vector<double> &lam, const std::vector<double> &R, const double *Y,
+                                 int64_t n, int d, const sq_calib_opts &o, const float *gauss, HeadCal &h,
+                                 std::string &err);
+sq_status check_calib_opts(const sq_calib_opts *o);
 sq_status calibrate_head_tq(const float *rotation, int d, const sq_calib_opts &o, const float *gauss,
                             HeadCal &out, std::string &err);
 

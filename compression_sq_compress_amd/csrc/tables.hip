@@ -520,6 +520,117 @@ static HostPlan2 build_plan2(const HeadCal &hc) {
   return P;
 }
 
+// Grid quantiser tables (GRID_* layout).  Only for heads the register plan
+// serves (d <= 128, not normalised); fails (ok = false) when a region has a
+// zero or repeated threshold gap, a coordinate of nonzero width has zero
+// variance, or the cells of all regions exceed GRID_MAX_CELLS.
+static uint32_t fbits(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  return u;
+}
+
+struct GridPlan {
+  std::vector<uint32_t> coord;  // [d][GRID_COORD_WORDS]
+  std::vector<uint32_t> cells;  // [n][2]
+  std::vector<float> csig;
+  bool ok = false;
+};
+
+static GridPlan build_grid(const HeadCal &hc) {
+  GridPlan G;
+  const int d = hc.d;
+  if (d != 32 && d != 64 && d != 128) return G;
+  if (hc.normalized || (hc.m > 0 && (hc.d_eff > 16 || hc.m > 32))) return G;
+  const float inf = std::numeric_limits<float>::infinity();
+  G.cells = {fbits(inf), 0u};  // cell 0: zero-width coordinates
+  G.coord.assign((size_t)d * GRID_COORD_WORDS, 0u);
+  constexpr double MARGIN = 1.0 / 512;
+  // region (regime, width) -> (first cell, C, o, h)
+  struct Reg { int first = -1, C = 0; double o = 0, h = 0; };
+  Reg regs[2][9];
+  for (int c = 0; c < d; ++c) {
+    const int b = hc.widths[c];
+    uint32_t *gc = G.coord.data() + (size_t)c * GRID_COORD_WORDS;
+    gc[4] = 0xFFFFFFFFu;
+    const int c0 = c & ~3;
+    gc[5] = (uint32_t)(hc.bit_off[c] - hc.bit_off[c0]);
+    gc[6] = (uint32_t)(hc.bit_off[c0] >> 5) | ((uint32_t)(hc.bit_off[c0] & 31) << 8);
+    if (b == 0) continue;  // a = b = 0, cells at 0, C - 1 = 0
+    const double sig = std::sqrt(hc.lam[c]);
+    if (!(sig > 0)) return G;
+    Reg &R = regs[c < hc.d_eff ? 0 : 1][b];
+    const int n = (1 << b) - 1;
+    if (R.first < 0) {
+      std::vector<double> t(n);
+      for (int j = 0; j < n; ++j) t[j] = (double)hc.thr[hc.thr_base[c] + j] / sig;
+      double gmin = std::numeric_limits<double>::infinity();
+      for (int j = 0; j + 1 < n; ++j) gmin = std::min(gmin, t[j + 1] - t[j]);
+      if (n > 1 && !(gmin > 0)) return G;
+      bool found = false;
+      if (n == 1) {  // one cell around the only threshold
+        R.h = 1.0;
+        R.o = t[0] - 0.5;
+        R.C = 1;
+        found = true;
+      }
+      for (int fi = 0; fi < 10 && !found; ++fi) {
+        const double h = gmin * (0.95 - 0.05 * fi);
+        for (int k = 1; k < 512 && !found; ++k) {
+          const double o = t[0] - h * (k / 512.0);
+          bool good = true;
+          for (int j = 0; j < n && good; ++j) {
+            const double p = (t[j] - o) / h, fr = p - std::floor(p);
+            good = fr >= MARGIN && fr <= 1 - MARGIN;
+          }
+          if (good) {
+            R.h = h;
+            R.o = o;
+            R.C = (int)std::floor((t[n - 1] - o) / h) + 1;
+            found = true;
+          }
+        }
+      }
+      if (!found || R.C > GRID_MAX_CELLS) return G;
+      R.first = (int)(G.cells.size() / 2);
+      std::vector<uint32_t> cell((size_t)R.C * 2);
+      for (int k = 0; k < R.C; ++k) {
+        cell[2 * k] = fbits(inf);
+        cell[2 * k + 1] = 0u;
+      }
+      for (int j = 0; j < n; ++j) {
+        const double p = (t[j] - R.o) / R.h;
+        const int k = (int)std::floor(p);
+        cell[2 * k] = fbits((float)p);
+      }
+      // code_lo(k) = thresholds in cells before k
+      uint32_t cnt = 0;
+      for (int k = 0; k < R.C; ++k) {
+        cell[2 * k + 1] = cnt;
+        if (cell[2 * k] != fbits(inf)) ++cnt;
+      }
+      G.cells.insert(G.cells.end(), cell.begin(), cell.end());
+      if (G.cells.size() / 2 > (size_t)GRID_MAX_CELLS) return G;
+    }
+    gc[0] = fbits((float)(1.0 / (sig * R.h)));
+    gc[1] = fbits((float)(-R.o / R.h));
+    gc[2] = (uint32_t)R.first * 8u;
+    gc[3] = (uint32_t)(R.C - 1);
+    if (hc.m > 0 && c < hc.d_eff) {
+      gc[4] = (uint32_t)G.csig.size();
+      for (int k = 0; k <= n; ++k) G.csig.push_back(hc.cent[hc.cent_base[c] + k]);
+    }
+  }
+  if (hc.m > 0)  // signal coordinates of zero width still need a centroid (0)
+    for (int c = 0; c < hc.d_eff; ++c)
+      if (hc.widths[c] == 0) {
+        G.coord[(size_t)c * GRID_COORD_WORDS + 4] = (uint32_t)G.csig.size();
+        G.csig.push_back(0.0f);
+      }
+  G.ok = true;
+  return G;
+}
+
 sq_status upload_tables(sq_calib *c, void *stream) {
   const int nh = (int)c->heads.size();
   std::vector<HostPlan> plans(nh);
@@ -530,6 +641,8 @@ sq_status upload_tables(sq_calib *c, void *stream) {
   std::vector<FusedSched> fsch(nh);
   for (int h = 0; h < nh; ++h) fsch[h] = build_fused_sched(c->heads[h]);
   for (int h = 0; h < nh; ++h) plans2[h] = build_plan2(c->heads[h]);
+  std::vector<GridPlan> grids(nh);
+  for (int h = 0; h < nh; ++h) grids[h] = build_grid(c->heads[h]);
   // host image of the blob: [DevHead x nh] then per-head sections
   std::vector<DevHead> desc(nh);
   size_t off = align256(sizeof(DevHead) * nh);
@@ -578,6 +691,12 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.n_fent = fsch[h].n_ent;
     D.n_fqjl = fsch[h].n_qjl;
     D.off_fsched = off;  off = align256(off + sizeof(uint32_t) * fsch[h].words.size());
+    const GridPlan &Gp = grids[h];
+    D.n_gcells = Gp.ok ? (int)(Gp.cells.size() / 2) : 0;
+    D.n_gcsig = Gp.ok ? (int)Gp.csig.size() : 0;
+    D.off_gcoord = off;  off = align256(off + sizeof(uint32_t) * std::max<size_t>(1, Gp.coord.size()));
+    D.off_gcells = off;  off = align256(off + sizeof(uint32_t) * std::max<size_t>(1, Gp.cells.size()));
+    D.off_gcsig = off;   off = align256(off + sizeof(float) * std::max<size_t>(1, Gp.csig.size()));
   }
   std::vector<uint8_t> img(off, 0);
   std::memcpy(img.data(), desc.data(), sizeof(DevHead) * nh);
@@ -633,6 +752,12 @@ sq_status upload_tables(sq_calib *c, void *stream) {
                             F1 + ((((size_t)sp * MB2 + mb1) * KB2 + kb) * 64 + l1) * 8, 16);
               }
       }
+    }
+    if (grids[h].ok) {
+      const GridPlan &Gp = grids[h];
+      std::memcpy(img.data() + D.off_gcoord, Gp.coord.data(), sizeof(uint32_t) * Gp.coord.size());
+      std::memcpy(img.data() + D.off_gcells, Gp.cells.data(), sizeof(uint32_t) * Gp.cells.size());
+      if (!Gp.csig.empty()) std::memcpy(img.data() + D.off_gcsig, Gp.csig.data(), sizeof(float) * Gp.csig.size());
     }
     DevCoord *Cd = (DevCoord *)(img.data() + D.off_coord);
     for (int i = 0; i < d; ++i) Cd[i] = DevCoord{hc.bit_off[i], hc.widths[i], hc.thr_base[i], hc.cent_base[i]};

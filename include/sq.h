@@ -81,6 +81,11 @@ typedef struct {
   int normalize;                /* 1: normalised variant -- samples divided by their norms
                                    before calibration; each record stores its vector's
                                    norm (IEEE half) and the unit vector is quantised */
+  double deff_cumvar;           /* d_eff rule.  0: rounded participation ratio (default).
+                                   In (0, 1]: the smallest k whose k leading eigenvalues
+                                   hold at least this fraction of their sum (the README's
+                                   "participation ratio vs cumvar" sweep; its threshold is
+                                   not given there, so the caller chooses it) */
 } sq_calib_opts;
 
 typedef struct sq_calib sq_calib; /* opaque, library-owned */
@@ -100,7 +105,8 @@ typedef struct {
   int normalized;      /* records carry the vector norm (normalised variant) */
 } sq_head_info;
 
-/* Defaults: avg_bits 3, qjl 1 (keys), max_bits 8, 200 Lloyd-Max iterations. */
+/* Defaults: avg_bits 3, qjl 1 (keys), max_bits 8, 200 Lloyd-Max iterations,
+ * unnormalised, d_eff by the rounded participation ratio. */
 sq_status sq_calib_default_opts(sq_calib_opts *opts, int head_dim);
 
 /*
@@ -112,7 +118,9 @@ sq_status sq_calib_default_opts(sq_calib_opts *opts, int head_dim);
  *   1. C = X^T X / n; Jacobi eigendecomposition; eigenvalues descending
  *      (clamped at 0); each eigenvector signed so its largest-magnitude entry
  *      is positive; R = rows of eigenvectors.
- *   2. d_eff = round-half-even(PR), PR = (sum l)^2 / sum l^2; kappa.
+ *   2. d_eff = round-half-even(PR), PR = (sum l)^2 / sum l^2 (or, with
+ *      opts->deff_cumvar > 0, the smallest k with l_0 + .. + l_{k-1} >=
+ *      deff_cumvar * sum l); kappa = l[d_eff-1] / l[d_eff].
  *   3. widths: greedy reverse water-filling of round(avg_bits*d) bits, one bit
  *      at a time to argmax l_i * 4^-b_i (ties to the lower index), b_i <= max_bits.
  *   4. regions (signal = i < d_eff | noise, width); per region a Lloyd-Max
@@ -130,6 +138,32 @@ sq_status sq_calib_default_opts(sq_calib_opts *opts, int head_dim);
 sq_status sq_calibrate(const float *samples, int n_heads, int64_t n_samples,
                        const sq_calib_opts *opts, const float *qjl_gauss,
                        sq_calib **out);
+
+/*
+ * sq_calibrate_device -- the same calibration with its dense steps on the
+ * GPU (README "Overview": a one-time calibration pass; "Repository
+ * Structure": calibration by PCA, d_eff, kappa).  On `stream`, in fp64: the
+ * per-sample norms (normalised variant), C = X^T X / n, a parallel cyclic
+ * Jacobi eigendecomposition of every head (one workgroup per head; rotations
+ * of the same 2 x 2 Schur form as sq_calibrate's solver, applied to the d/2
+ * disjoint pairs of a round-robin step at once), and the rotated samples
+ * Y = X R^T.  The host then applies the eigen-order and sign rule, d_eff,
+ * widths, the per-region Lloyd-Max fits and the QJL rows exactly as
+ * sq_calibrate does, on opts->n_threads threads.  Results equal
+ * sq_calibrate's up to rounding order: eigenvalues and the eigenvectors of
+ * well-separated eigenvalues to ~1e-12 relative, codebooks to ~1e-6.
+ * samples   DEVICE float [n_heads][n_samples][head_dim] (read only).
+ * qjl_gauss HOST float, as for sq_calibrate.
+ * Allocates device scratch of 24 d^2 n_heads bytes (+ 8 n_samples n_heads
+ * when normalising) and at most 512 MiB of rotated samples per chunk of
+ * heads (also on the host); returns after the stream work is complete.
+ * Errors: as sq_calibrate; SQ_ERR_UNSUPPORTED for more than 65535 heads or
+ * more than 2^30 samples, or when one head's rotated samples exceed 512 MiB;
+ * SQ_ERR_HIP on a failed launch or copy.
+ */
+sq_status sq_calibrate_device(const float *samples, int n_heads, int64_t n_samples,
+                              const sq_calib_opts *opts, const float *qjl_gauss,
+                              sq_stream stream, sq_calib **out);
 
 /*
  * sq_calibrate_tq -- the TurboQuant-style baseline (random rotation, per-vector
@@ -190,6 +224,11 @@ int64_t sq_packed_head_words(const sq_calib *c, int64_t n_tokens);
  *         ps_head >= sq_packed_head_words(c, n_tokens).  Every word of the
  *         ceil(T/64)*64-token range is written (pad tokens as zeros).
  * n_tokens == 0 or batch == 0 is a no-op.
+ * Quantiser: code = #{thresholds < y} by a uniform-grid table per region
+ * (one cell read and one compare per value) when the calibration's grid
+ * tables exist (head_dim <= 128, unnormalised, at most 6144 cells per head),
+ * else by a descent of padded threshold trees; both give the same codes.
+ * The environment variable SQ_QUANTISER=tree forces the trees (a test hook).
  */
 sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
                       int calib_batch_stride, const void *x, sq_dtype dt,

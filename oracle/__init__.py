@@ -32,7 +32,8 @@ from .spectralquant import (  # noqa: F401
     effective_dim, spectral_gap, water_fill, regions, lloyd_max_samples,
     lloyd_max_gaussian, gaussian_distortion, rotate, quantize, compress,
     dequantize, scores_plain, scores_rotated, softmax, attend, band_mask,
-    qjl_band_mask, CompressResult,
+    qjl_band_mask, CompressResult, effective_dim_cumvar, coefficient_of_variation,
+    calibration_stability,
 )
 from .record import record_words, field_offsets, norm_position, pack, unpack  # noqa: F401
 from .turboquant import tq_prod_keys, tq_mse_values, tq_mse_unit, tq_calibration  # noqa: F401
@@ -47,6 +48,10 @@ PARITY = {
     "participation_ratio/effective_dim": "pinned: identity, isotropic rank-k, Wishart mean, "
                                          "half-to-even rounding, PR <= rank",
     "spectral_gap": "pinned: test_spectral_gap",
+    "effective_dim_cumvar": "pinned: flat spectrum ceil(f d), geometric closed form, exact "
+                            "boundary ties, fraction 1 gives the rank (test_oracle_calib_variants.py)",
+    "coefficient_of_variation/calibration_stability": "pinned: two planted spectra of known PR give "
+                                                      "|a-b|/(a+b); identical and rescaled splits give 0",
     "water_fill": "pinned: brute-force optimum, monotone widths, real-valued water level, caps, ties",
     "regions": "pinned: hand-worked map; uniform vs Gaussian laws at equal width give the "
                "closed-form Lloyd-Max levels of each law (test_oracle_regions_bands_tq.py)",

@@ -30,6 +30,15 @@ Readings taken where the pages are silent (each repeated at its function):
       the vector's norm nu is stored (IEEE half) and the unit vector x / nu
       is rotated and quantised; reconstructions, scores and value sums are
       scaled back by the stored nu.  A zero vector keeps nu = 0.
+  R9  d_eff by cumulative variance (README Repository Structure: the deff
+      sweep compares the participation ratio with a cumulative-variance
+      rule, threshold not given): the smallest k whose k leading eigenvalues
+      sum to at least a caller-given fraction of the total.
+  R10 calibration stability (README paper-section table: a calibration
+      coefficient of variation, no definition given): the population
+      coefficient of variation (std / mean, numpy's default ddof = 0) of the
+      participation ratio and of d_eff across calibrations of one head on
+      disjoint, equally sized sample sets.
 """
 from __future__ import annotations
 
@@ -81,6 +90,48 @@ def effective_dim(lam: np.ndarray) -> int:
     even), clamped to [1, d]."""
     d = len(lam)
     return int(min(max(int(round(participation_ratio(lam))), 1), d))
+
+
+def effective_dim_cumvar(lam: np.ndarray, fraction: float) -> int:
+    """d_eff by cumulative variance (reading R9): the smallest k in [1, d]
+    with lambda_0 + ... + lambda_{k-1} >= fraction * (lambda_0 + ... +
+    lambda_{d-1}), partial sums taken left to right; fraction in (0, 1]."""
+    if not 0.0 < fraction <= 1.0:
+        raise ValueError("fraction must be in (0, 1]")
+    lam = np.asarray(lam, dtype=np.float64)
+    csum = np.cumsum(lam)                  # sequential partial sums
+    total = csum[-1]
+    for k in range(1, len(lam) + 1):
+        if csum[k - 1] >= fraction * total:
+            return k
+    return len(lam)
+
+
+def coefficient_of_variation(values) -> float:
+    """Population std / mean (reading R10)."""
+    v = np.asarray(values, dtype=np.float64)
+    return float(v.std() / v.mean())
+
+
+def calibration_stability(samples: np.ndarray, n_splits: int, deff_cumvar: float = 0.0,
+                          normalize: bool = False) -> dict:
+    """Reading R10: split the calibration samples [n, d] into n_splits
+    contiguous, disjoint, equal parts (a remainder is dropped), take each
+    part's spectrum (second moment, eigenvalues) and report the participation
+    ratio and d_eff of every part with their coefficients of variation."""
+    x = np.asarray(samples, dtype=np.float64)
+    if normalize:
+        x, _ = _unit_rows(x)
+    per = x.shape[0] // n_splits
+    if per < 2:
+        raise ValueError("each split needs at least 2 samples")
+    prs, deffs = [], []
+    for k in range(n_splits):
+        lam, _ = eigenbasis(second_moment(x[k * per:(k + 1) * per]))
+        prs.append(participation_ratio(lam))
+        deffs.append(effective_dim_cumvar(lam, deff_cumvar) if deff_cumvar > 0 else effective_dim(lam))
+    return dict(pr=np.array(prs), d_eff=np.array(deffs), pr_cv=coefficient_of_variation(prs),
+                deff_cv=coefficient_of_variation(deffs), samples_per_split=per)
 
 
 def spectral_gap(lam: np.ndarray, d_eff: int) -> float:
@@ -232,12 +283,14 @@ def _unit_rows(x: np.ndarray):
 
 def calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
               gauss: Optional[np.ndarray], max_bits: int = 8,
-              lloyd_iters: int = 200, normalize: bool = False) -> Calibration:
+              lloyd_iters: int = 200, normalize: bool = False,
+              deff_cumvar: float = 0.0) -> Calibration:
     """Calibrate one head on ``samples`` [n, d] (normalised variant R8: on the
     samples divided by their norms).
 
     1. C = X^T X / n; eigh; descending; sign rule R1; R = V^T.
-    2. d_eff = round(PR), kappa (conftest fixture).
+    2. d_eff = round(PR) (conftest fixture), or by cumulative variance when
+       deff_cumvar > 0 (R9); kappa.
     3. widths by greedy water-filling of round(avg_bits * d) bits (R2).
     4. per region (R3) Lloyd-Max on pooled u = (R x)_i / sigma_i (R4);
        tables scaled back by sigma_i (R5).
@@ -250,7 +303,7 @@ def calibrate(samples: np.ndarray, avg_bits: float, qjl_bits: int,
     lam, R = eigenbasis(second_moment(x))
     sigma = np.sqrt(lam)
     pr = participation_ratio(lam)
-    d_eff = effective_dim(lam)
+    d_eff = effective_dim_cumvar(lam, deff_cumvar) if deff_cumvar > 0 else effective_dim(lam)
     kappa = spectral_gap(lam, d_eff)
     widths = water_fill(lam, int(round(avg_bits * d)), max_bits)
     y = x @ R.T                                           # rotated samples

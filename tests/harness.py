@@ -148,3 +148,30 @@ def score_floor(oc, q: np.ndarray, xt: np.ndarray) -> np.ndarray:
     qn = np.linalg.norm(q, axis=1)
     xn = np.linalg.norm(xt, axis=1)
     return qn[:, None] * xn[None, :] / math.sqrt(oc.head_dim)
+
+
+def assert_calibration_matches(ex: dict, oc, pr_rtol=1e-10):
+    """A libsq calibration export of one head against the oracle's calibration
+    of the same samples: integer layout exact; eigenvalues to 1e-12 of the
+    largest; eigenvectors of well-separated eigenvalues to 1e-9 (same sign
+    rule); codebooks to 1e-6; the QJL rows are the same float32 draws."""
+    inf = ex["info"]
+    assert inf.d_eff == oc.d_eff and inf.m == oc.m and inf.record_words == oc.W
+    assert inf.code_bits == int(oc.widths.sum())
+    np.testing.assert_array_equal(ex["widths"], oc.widths)
+    assert abs(inf.participation_ratio - oc.pr) <= pr_rtol * oc.pr
+    if math.isinf(oc.kappa):
+        assert math.isinf(inf.kappa)
+    else:
+        assert abs(inf.kappa - oc.kappa) <= 1e-8 * oc.kappa
+    np.testing.assert_allclose(ex["eigenvalues"], oc.lam, rtol=0, atol=1e-12 * oc.lam[0])
+    gaps = np.abs(np.diff(oc.lam))
+    sep = np.minimum(np.r_[np.inf, gaps], np.r_[gaps, np.inf])
+    good = sep > 1e-3 * oc.lam[0]
+    np.testing.assert_allclose(ex["rotation"][good], oc.R[good], atol=1e-9)
+    thr = np.concatenate([t for t in oc.thresholds if len(t)] or [np.zeros(0)])
+    cen = np.concatenate([c for c in oc.centroids if len(c)] or [np.zeros(0)])
+    np.testing.assert_allclose(ex["thresholds"], thr, rtol=1e-6, atol=1e-6 * oc.sigma[0])
+    np.testing.assert_allclose(ex["centroids"], cen, rtol=1e-6, atol=1e-6 * oc.sigma[0])
+    if oc.m:
+        np.testing.assert_array_equal(ex["qjl"], oc.S.astype(np.float32))

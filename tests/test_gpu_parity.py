@@ -66,10 +66,13 @@ CASES = [
 
 @pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("which", ["k", "v"])
-def test_compress_matches_oracle(torch_dev, sq, name, cfgname, heads, T, budget, which):
+@pytest.mark.parametrize("quantiser", ["grid", "tree"])
+def test_compress_matches_oracle(torch_dev, sq, name, cfgname, heads, T, budget, which, quantiser,
+                                 monkeypatch):
     torch = torch_dev
     cfg = wl.CONFIGS[cfgname]
-    _case(f"compress {name} {which} T={T} budget={budget}")
+    monkeypatch.setenv("SQ_QUANTISER", quantiser)
+    _case(f"compress {name} {which} T={T} budget={budget} quantiser={quantiser}")
     cal, ors = H.calibrate_both(sq, cfg, heads, which, budget, n_tokens=T)
     cal.upload()
     x = H.data_block(cfg, heads, which, T)                 # [H][T][d]

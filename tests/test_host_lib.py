@@ -252,3 +252,32 @@ def test_normalized_calibration_matches_oracle():
             np.testing.assert_allclose(ex["eigenvalues"], oc.lam, rtol=0, atol=1e-12 * oc.lam[0])
             cen = np.concatenate([c for c in oc.centroids if len(c)])
             np.testing.assert_allclose(ex["centroids"], cen, rtol=1e-6, atol=1e-6 * oc.sigma[0])
+
+
+@pytest.mark.parametrize("which,frac", [("k", 0.9), ("k", 0.5), ("v", 0.95)])
+def test_cumvar_calibration_matches_oracle(which, frac):
+    from harness import assert_calibration_matches
+    cfg = wl.CONFIGS["llama8b"]
+    X, G = _heads(cfg, which, [(0, 0), (0, 3)])
+    qb = 1 if which == "k" else 0
+    cal = sq.sq_calibrate(X, 3.0, qb, G, deff_cumvar=frac)
+    for k in range(2):
+        oc = oracle.calibrate(X[k], 3.0, qb, G[k] if G is not None else None, deff_cumvar=frac)
+        assert_calibration_matches(cal.export(k), oc)
+
+
+def test_cumvar_option_is_checked_and_saved(tmp_path):
+    cfg = wl.CONFIGS["tiny"]
+    X, G = _heads(cfg, "k", [(0, 0)])
+    for bad in (-0.1, 1.5, float("nan")):
+        with pytest.raises(sq.SQError) as e:
+            sq.sq_calibrate(X, 3.0, 1, G, deff_cumvar=bad)
+        assert e.value.status == 1
+    o = sq.sq_calib_default_opts(64)
+    assert o.deff_cumvar == 0.0
+    cal = sq.sq_calibrate(X, 3.0, 1, G, deff_cumvar=0.99)
+    p = str(tmp_path / "cv.sqcal")
+    cal.save(p)
+    cal2 = sq.Calibration.load(p)
+    assert cal2.info(0).d_eff == cal.info(0).d_eff
+    np.testing.assert_array_equal(cal2.export(0)["qjl"], cal.export(0)["qjl"])
