@@ -31,7 +31,8 @@ EXPORTS = ("sq_calib_default_opts", "sq_calibrate", "sq_calib_upload", "sq_calib
            "sq_calib_destroy", "sq_packed_head_words", "sq_compress", "sq_compress_append", "sq_scores",
            "sq_attend_workspace_bytes", "sq_attend", "sq_dequantize", "sq_unpack",
            "sq_last_error", "sq_build_digest", "sq_plan_decode",
-           "sq_attend_noalloc", "sq_decode", "sq_calibrate_tq", "sq_calibrate_device")
+           "sq_attend_noalloc", "sq_decode", "sq_calibrate_tq", "sq_calibrate_device",
+           "sq_paged_block_words", "sq_compress_append_paged", "sq_decode_paged")
 
 
 class StaleLibraryError(RuntimeError):
@@ -58,6 +59,12 @@ class HeadInfo(C.Structure):
                 ("n_regions", C.c_int), ("lloyd_unconverged", C.c_int),
                 ("participation_ratio", C.c_double), ("kappa", C.c_double),
                 ("normalized", C.c_int)]
+
+
+class Paged(C.Structure):
+    """sq_paged: block table (device int32 [batch][table_stride]), tiles per block, pool blocks."""
+    _fields_ = [("block_table", C.c_void_p), ("table_stride", C.c_int64), ("block_tiles", C.c_int32),
+                ("n_blocks", C.c_int32)]
 
 
 class DecodePlan(C.Structure):
@@ -107,6 +114,9 @@ def _load():
         "sq_unpack": (I, [P, I, P, I64, P, P, P, P]),
         "sq_calibrate_tq": (I, [P, P, I, C.POINTER(CalibOpts), C.POINTER(C.c_void_p)]),
         "sq_calibrate_device": (I, [P, I, I64, C.POINTER(CalibOpts), P, P, C.POINTER(C.c_void_p)]),
+        "sq_paged_block_words": (I64, [P, I]),
+        "sq_compress_append_paged": (I, [P, I, I, I, I, P, I, I64, I64, I64, I64, P, C.POINTER(Paged), I64, P]),
+        "sq_decode_paged": (I, [P, P, I, I, I, I, I, P, I, P, P, C.POINTER(Paged), I64, C.c_float, P, U64, P, P]),
         "sq_last_error": (C.c_char_p, []),
         "sq_build_digest": (C.c_char_p, []),
         "sq_plan_decode": (I, [P, P, I, I, I, I, I, I64, C.POINTER(DecodePlan)]),
@@ -369,6 +379,44 @@ def sq_decode(kcal: Calibration, vcal: Calibration, q, kpacked, vpacked, n_token
                              _ptr(q), _dtype_code(q), _ptr(kpacked), kpacked.stride(0), kpacked.stride(1),
                              _ptr(vpacked), vpacked.stride(0), vpacked.stride(1), n_tokens, float(scale),
                              _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
+
+
+def paged(block_table, block_tiles: int, n_blocks: int) -> Paged:
+    """Describe a paged cache: block_table device int32 [batch][table_stride]."""
+    import torch
+    assert block_table.is_cuda and block_table.dtype == torch.int32 and block_table.dim() == 2
+    assert block_table.stride(1) == 1
+    return Paged(block_table.data_ptr(), block_table.stride(0), int(block_tiles), int(n_blocks))
+
+
+def sq_paged_block_words(cal: Calibration, block_tiles: int) -> int:
+    return int(_load().sq_paged_block_words(cal.handle, int(block_tiles)))
+
+
+def sq_compress_append_paged(cal: Calibration, x, pool, pg: Paged, token0: int, first_head: int = 0,
+                             calib_batch_stride: int = 0, stream=None):
+    """sq_compress_append into a paged pool (device int32/uint32, flat):
+    x device [batch][n_heads][T][d]; pg from paged()."""
+    assert x.dim() == 4 and x.stride(3) == 1 and x.is_cuda
+    B, H, T, d = x.shape
+    assert pool.is_cuda and pool.element_size() == 4
+    _check(_load().sq_compress_append_paged(cal.handle, first_head, H, B, calib_batch_stride, _ptr(x),
+                                            _dtype_code(x), T, x.stride(0), x.stride(1), x.stride(2),
+                                            _ptr(pool), C.byref(pg), int(token0), _stream(stream)))
+
+
+def sq_decode_paged(kcal: Calibration, vcal: Calibration, q, kpool, vpool, pg: Paged, n_tokens: int,
+                    scale: float, workspace, out, n_kv_heads: int, first_head: int = 0,
+                    calib_batch_stride: int = 0, stream=None):
+    """sq_decode over paged key / value pools sharing the block table of pg."""
+    import torch
+    assert q.is_contiguous() and q.dim() == 3
+    B, Hq, d = q.shape
+    assert out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, d)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().sq_decode_paged(kcal.handle, vcal.handle, first_head, calib_batch_stride, B, Hq, n_kv_heads,
+                                   _ptr(q), _dtype_code(q), _ptr(kpool), _ptr(vpool), C.byref(pg), n_tokens,
+                                   float(scale), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
 
 
 def sq_attend_noalloc(cal: Calibration, scores, scale: float, vpacked, n_tokens: int, out,

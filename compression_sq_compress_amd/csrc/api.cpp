@@ -346,6 +346,11 @@ extern "C" void sq_calib_destroy(sq_calib *c) {
   delete c;
 }
 
+extern "C" int64_t sq_paged_block_words(const sq_calib *c, int block_tiles) {
+  if (!c || block_tiles < 1) return -1;
+  return (int64_t)block_tiles * 64 * c->W_max;
+}
+
 extern "C" int64_t sq_packed_head_words(const sq_calib *c, int64_t n_tokens) {
   if (!c || n_tokens < 0) return -1;
   return ((n_tokens + 63) / 64) * 64 * (int64_t)c->W_max;

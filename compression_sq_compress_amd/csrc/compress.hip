@@ -53,6 +53,7 @@ struct CompressArgs {
   int lds_b_off;        // floats: shared record-word buffer
   int ys;               // y tile row stride (floats, d + 3)
   int bws;              // word buffer row stride (words, odd)
+  PageArgs pg;          // paged destination (pg.table == nullptr: contiguous slots)
 };
 
 __device__ __forceinline__ void split3(const float *v, uint4 &p0, uint4 &p1, uint4 &p2) {
@@ -321,14 +322,12 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
   // the shared words it owns) and zeroes the shared ones for the next tile.
   for (int k = threadIdx.x; k < 64 * a.bws; k += NT) bwords[k] = 0u;
   uint32_t *const bwrow = bwords + lane * a.bws;
-  uint32_t *pdst = nullptr;  // destination of the previous tile's records
-  bool pvalid = false, pin = false;
+  uint32_t *pdst = nullptr;  // this lane's destination of the previous tile's records
+  bool pvalid = false, pin = false, have_prev = false;
   // Source token i lands in slot token token0 + i: lane l of a source tile
   // writes destination lane (token0 + l) % 64 of its tile or of the next.
   // Lanes past the last token zero their words up to the end of the last
   // destination tile and write nothing beyond it.
-  const int ol = (int)(a.token0 & 63) + lane;
-  const int64_t lofs = (int64_t)(ol >> 6) * W * 64 + (ol & 63);
   const int64_t send = ((a.token0 + T + 63) & ~(int64_t)63) - a.token0;
   auto store_prev = [&]() {
     for (int k = dfirst; k < dend; ++k)
@@ -354,7 +353,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
         *(uint4 *)(xt + (c / CPR) * XS * ESZ + (c % CPR) * 16) = xr[q];
       }
     }
-    if (pdst) store_prev();
+    if (have_prev) store_prev();
     __syncthreads();
     if (item + (int)gridDim.x < a.items) load_x(item + gridDim.x);
     // ---- rotate this wave's 16 coordinates for the 64 tokens (4 blocks of 16)
@@ -492,14 +491,19 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
       }
       bwrow[k] = word;
     }
-    pdst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + ((a.token0 >> 6) + tile) * W * 64 + lofs;
     pvalid = t0 + lane < T;
     pin = t0 + lane < send;
+    // destination of this lane's token (contiguous slot or its block; nullptr: dropped)
+    pdst = pin ? page_token(a.pg, a.pg.table ? a.packed : a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h,
+                            b, h, a.token0 + t0 + lane, W)
+               : nullptr;
+    pin = pin && pdst != nullptr;
+    have_prev = true;
     // The x tile was last read by the MFMAs, which every wave finished before
     // the barrier above; the y tile and the word buffer are rewritten only
     // after the barrier that follows the next x store.
   }
-  if (pdst) store_prev();
+  if (have_prev) store_prev();
 }
 
 
@@ -545,6 +549,7 @@ struct Compress2Args {
   int n_tiles, tiles_per_wg;  // workgroup (x, head, batch entry) takes tiles [x * tiles_per_wg, ...)
   int lds_tree_off, lds_csig_off, lds_s_off, lds_x_off, lds_rec_off, lds_res_off;  // floats
   int x_buf_floats;
+  PageArgs pg;                // paged destination (pg.table == nullptr: contiguous slots)
 };
 
 constexpr int C2_RS = 20;   // residual tile row stride (floats; 16-byte rows, conflict-free)
@@ -691,10 +696,14 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   // writes destination lane (token0 + l) % 64 of its tile or of the next;
   // lanes past the last token zero their words up to the end of the last
   // destination tile and write nothing beyond it
-  uint32_t *obase = a.packed + (int64_t)bz * a.ps_b + (int64_t)h * a.ps_h + (a.token0 >> 6) * W * 64;
-  const int ol = (int)(a.token0 & 63) + lane;
-  const uint32_t lofs = (uint32_t)((ol >> 6) * W * 64 + (ol & 63));
+  uint32_t *oslot = a.pg.table ? a.packed : a.packed + (int64_t)bz * a.ps_b + (int64_t)h * a.ps_h;
   const int64_t send = ((a.token0 + a.n_tokens + 63) & ~(int64_t)63) - a.token0;
+  // word 0 of this lane's destination token for source tile tl (contiguous
+  // slot or its block), nullptr when the lane writes nothing
+  auto dst_of = [&](int tl) __attribute__((always_inline)) -> uint32_t * {
+    const int64_t st = (int64_t)tl * 64 + lane;
+    return st < send ? page_token(a.pg, oslot, bz, h, a.token0 + st, W) : nullptr;
+  };
   // record words of this wave: w + NW i for i < nmine
   const int nmine = W > w ? (W - 1 - w) / NW + 1 : 0;
   int par = 0, rb = 0;
@@ -868,11 +877,11 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
       const bool has_prev = t != tb;
       const int prb = rb == 0 ? 2 : rb - 1;
       const uint32_t lrow = (uint32_t)lane * (uint32_t)rs;
-      uint32_t *ocur = obase + (int64_t)t * W * 64;
-      uint32_t *oprv = obase + (int64_t)(t - 1) * W * 64;
+      uint32_t *ocur = dst_of(t);
+      uint32_t *oprv = has_prev ? dst_of(t - 1) : nullptr;
       const bool valid = (int64_t)t * 64 + lane < a.n_tokens;
       const bool pvalid = (int64_t)(t - 1) * 64 + lane < a.n_tokens;
-      const bool in = (int64_t)t * 64 + lane < send, pin = (int64_t)(t - 1) * 64 + lane < send;
+      const bool in = ocur != nullptr, pin = oprv != nullptr;
       // words w + NW i, two at a time: this tile's (no QJL bits) or the
       // previous tile's; a slot past this wave's words reads and clears the
       // pad column rs - 1
@@ -894,7 +903,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
           const bool q = qmask >> i & 1u;
           if (i < nmine && (!q || has_prev) && (q ? pin : in)) {
             uint32_t *o = q ? oprv : ocur;
-            o[(uint32_t)(w + NW * i) * 64u + lofs] = (q ? pvalid : valid) ? v[u] : 0u;
+            o[(uint32_t)(w + NW * i) * 64u] = (q ? pvalid : valid) ? v[u] : 0u;
           }
         }
       }
@@ -943,9 +952,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   if (m > 0) {
     __syncthreads();
     uint32_t *rlast = rec0 + ((te - 1 - tb) % 3) * 64 * rs + lane * rs;
-    uint32_t *dst = obase + (int64_t)(te - 1) * W * 64 + lofs;
+    uint32_t *dst = dst_of(te - 1);
     const bool valid = (int64_t)(te - 1) * 64 + lane < a.n_tokens;
-    const bool in = (int64_t)(te - 1) * 64 + lane < send;
+    const bool in = dst != nullptr;
 #pragma unroll
     for (int i = 0; i < C2_WMAX; ++i)
       if ((qmask >> i & 1u) && i < nmine && in) dst[(int64_t)(w + NW * i) * 64] = valid ? rlast[w + NW * i] : 0u;
@@ -990,7 +999,8 @@ static void launch_compress_d(bool f32, bool tg, dim3 grid, size_t lds, hipStrea
 static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head, int n_heads, int batch,
                                int calib_batch_stride, const void *x, sq_dtype dt, int64_t n_tokens,
                                int64_t xs_batch, int64_t xs_head, int64_t xs_token, uint32_t *packed,
-                               int64_t ps_batch, int64_t ps_head, int64_t token0, sq_stream stream) {
+                               int64_t ps_batch, int64_t ps_head, int64_t token0, sq_stream stream,
+                               const sq_paged *paged = nullptr) {
   const std::string f(fn);
   sq_status st = check_handle(c, fn);
   if (st != SQ_OK) return st;
@@ -1003,8 +1013,13 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
   if (!x || !packed) return fail(SQ_ERR_ARG, f + ": NULL pointer");
   if (n_tokens > ((int64_t)1 << 36) || token0 > ((int64_t)1 << 36))
     return fail(SQ_ERR_UNSUPPORTED, f + ": too many tokens");
-  st = check_slots(c, token0 + n_tokens, n_heads, batch, ps_batch, ps_head, fn);
-  if (st != SQ_OK) return st;
+  PageArgs pga{};
+  if (paged) {
+    if ((st = check_paged(c, paged, token0 + n_tokens, n_heads, fn, pga)) != SQ_OK) return st;
+  } else {
+    st = check_slots(c, token0 + n_tokens, n_heads, batch, ps_batch, ps_head, fn);
+    if (st != SQ_OK) return st;
+  }
   const int esz = dt == SQ_F32 ? 4 : 2;
   if (((uintptr_t)x % 16) || (xs_token * esz) % 16 || (xs_head * esz) % 16 || (xs_batch * esz) % 16)
     return fail(SQ_ERR_ARG, f + ": x and its strides must be 16-byte aligned");
@@ -1076,6 +1091,7 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
         b2.blob = (const uint8_t *)c->dev_blob;
         b2.x = x;
         b2.packed = packed;
+        b2.pg = pga;
         b2.xs_b = xs_batch; b2.xs_h = xs_head; b2.xs_t = xs_token;
         b2.ps_b = ps_batch; b2.ps_h = ps_head;
         b2.n_tokens = n_tokens;
@@ -1126,6 +1142,7 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
   a.blob = (const uint8_t *)c->dev_blob;
   a.x = x;
   a.packed = packed;
+  a.pg = pga;
   a.xs_b = xs_batch; a.xs_h = xs_head; a.xs_t = xs_token;
   a.ps_b = ps_batch; a.ps_h = ps_head;
   a.n_tokens = n_tokens;
@@ -1159,6 +1176,16 @@ extern "C" sq_status sq_compress(const sq_calib *c, int first_head, int n_heads,
                                  int64_t ps_head, sq_stream stream) {
   return compress_impl("sq_compress", c, first_head, n_heads, batch, calib_batch_stride, x, dt, n_tokens,
                        xs_batch, xs_head, xs_token, packed, ps_batch, ps_head, 0, stream);
+}
+
+extern "C" sq_status sq_compress_append_paged(const sq_calib *c, int first_head, int n_heads, int batch,
+                                              int calib_batch_stride, const void *x, sq_dtype dt,
+                                              int64_t n_tokens, int64_t xs_batch, int64_t xs_head,
+                                              int64_t xs_token, uint32_t *pool, const sq_paged *pg,
+                                              int64_t token0, sq_stream stream) {
+  if (!pg) return fail(SQ_ERR_ARG, "sq_compress_append_paged: pg is NULL");
+  return compress_impl("sq_compress_append_paged", c, first_head, n_heads, batch, calib_batch_stride, x, dt,
+                       n_tokens, xs_batch, xs_head, xs_token, pool, 0, 0, token0, stream, pg);
 }
 
 extern "C" sq_status sq_compress_append(const sq_calib *c, int first_head, int n_heads, int batch,

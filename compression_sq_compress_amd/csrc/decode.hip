@@ -160,12 +160,12 @@ sq_status plan_decode(const sq_calib *kc, const sq_calib *vc, int first_head, in
 
 }  // namespace sq
 
-extern "C" sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first_head, int calib_batch_stride,
-                               int batch, int n_q_heads, int n_kv_heads, const void *q, sq_dtype qdt,
-                               const uint32_t *kpacked, int64_t kps_batch, int64_t kps_head,
-                               const uint32_t *vpacked, int64_t vps_batch, int64_t vps_head, int64_t n_tokens,
-                               float scale, void *workspace, size_t ws_bytes, float *out, sq_stream stream) {
-  const char *fn = "sq_decode";
+static sq_status decode_impl(const char *fn, const sq_calib *kc, const sq_calib *vc, int first_head,
+                             int calib_batch_stride, int batch, int n_q_heads, int n_kv_heads, const void *q,
+                             sq_dtype qdt, const uint32_t *kpacked, int64_t kps_batch, int64_t kps_head,
+                             const uint32_t *vpacked, int64_t vps_batch, int64_t vps_head, int64_t n_tokens,
+                             float scale, void *workspace, size_t ws_bytes, float *out, sq_stream stream,
+                             const sq_paged *paged) {
   sq_status st = check_handle(kc, fn);
   if (st != SQ_OK) return st;
   st = check_handle(vc, fn);
@@ -196,8 +196,14 @@ extern "C" sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first
     return launched(fn);
   }
   if (!q || !kpacked || !vpacked || !workspace) return fail(SQ_ERR_ARG, "sq_decode: NULL pointer");
-  if ((st = check_slots(kc, n_tokens, n_kv_heads, batch, kps_batch, kps_head, fn)) != SQ_OK) return st;
-  if ((st = check_slots(vc, n_tokens, n_kv_heads, batch, vps_batch, vps_head, fn)) != SQ_OK) return st;
+  PageArgs kpg{}, vpg{};
+  if (paged) {
+    if ((st = check_paged(kc, paged, n_tokens, n_kv_heads, fn, kpg)) != SQ_OK) return st;
+    if ((st = check_paged(vc, paged, n_tokens, n_kv_heads, fn, vpg)) != SQ_OK) return st;
+  } else {
+    if ((st = check_slots(kc, n_tokens, n_kv_heads, batch, kps_batch, kps_head, fn)) != SQ_OK) return st;
+    if ((st = check_slots(vc, n_tokens, n_kv_heads, batch, vps_batch, vps_head, fn)) != SQ_OK) return st;
+  }
   if (n_tokens > ((int64_t)1 << 36)) return fail(SQ_ERR_UNSUPPORTED, "sq_decode: too many tokens");
   if (ws_bytes < sq_attend_workspace_bytes(batch, n_q_heads, n_tokens, d))
     return fail(SQ_ERR_ARG, "sq_decode: workspace too small (sq_attend_workspace_bytes)");
@@ -216,6 +222,8 @@ extern "C" sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first
   a.scale = scale;
   a.ws = (float *)workspace;
   a.out = out;
+  a.kpg = kpg;
+  a.vpg = vpg;
   for (int g0 = 0; g0 < G; g0 += P.gsub) {
     a.g0 = g0;
     const int gn = std::min(P.gsub, G - g0);
@@ -225,4 +233,24 @@ extern "C" sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first
   }
   launch_attend_combine(a, batch, d, s);
   return launched(fn);
+}
+
+extern "C" sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first_head, int calib_batch_stride,
+                               int batch, int n_q_heads, int n_kv_heads, const void *q, sq_dtype qdt,
+                               const uint32_t *kpacked, int64_t kps_batch, int64_t kps_head,
+                               const uint32_t *vpacked, int64_t vps_batch, int64_t vps_head, int64_t n_tokens,
+                               float scale, void *workspace, size_t ws_bytes, float *out, sq_stream stream) {
+  return decode_impl("sq_decode", kc, vc, first_head, calib_batch_stride, batch, n_q_heads, n_kv_heads, q, qdt,
+                     kpacked, kps_batch, kps_head, vpacked, vps_batch, vps_head, n_tokens, scale, workspace,
+                     ws_bytes, out, stream, nullptr);
+}
+
+extern "C" sq_status sq_decode_paged(const sq_calib *kc, const sq_calib *vc, int first_head,
+                                     int calib_batch_stride, int batch, int n_q_heads, int n_kv_heads,
+                                     const void *q, sq_dtype qdt, const uint32_t *kpool, const uint32_t *vpool,
+                                     const sq_paged *pg, int64_t n_tokens, float scale, void *workspace,
+                                     size_t ws_bytes, float *out, sq_stream stream) {
+  if (!pg) return fail(SQ_ERR_ARG, "sq_decode_paged: pg is NULL");
+  return decode_impl("sq_decode_paged", kc, vc, first_head, calib_batch_stride, batch, n_q_heads, n_kv_heads, q,
+                     qdt, kpool, 0, 0, vpool, 0, 0, n_tokens, scale, workspace, ws_bytes, out, stream, pg);
 }

@@ -194,6 +194,59 @@ static inline sq_status check_slots(const sq_calib *c, int64_t n_tokens, int n_h
   return SQ_OK;
 }
 
+// Paged packed cache.  Tile `tile` (64 tokens) of (batch row b, head h of
+// the call) lives in physical block table[b * tstride + tile / bt], at word
+// (block * nh + h) * block_words + (tile % bt) * W * 64 of the pool; a block
+// holds bt tiles of each of the call's nh heads.  table == nullptr: the
+// contiguous slots of the unpaged calls.
+struct PageArgs {
+  const int32_t *table;
+  int64_t tstride, block_words;
+  int32_t bt, nh, n_blocks, pad;
+};
+
+// Word 0 of a tile for reads (wave-uniform): contiguous slot + tile * W * 64,
+// or the tile in its block; a block id outside [0, n_blocks) is clamped, so a
+// bad table entry can never address memory outside the pool.
+__device__ __forceinline__ const uint32_t *page_tile(const PageArgs &pg, const uint32_t *slot_or_pool, int b,
+                                                     int h, int64_t tile, int W) {
+  if (!pg.table) return slot_or_pool + tile * W * 64;
+  int64_t blk = pg.table[(int64_t)b * pg.tstride + tile / pg.bt];
+  blk = blk < 0 ? 0 : blk >= pg.n_blocks ? pg.n_blocks - 1 : blk;
+  return slot_or_pool + (blk * pg.nh + h) * pg.block_words + (tile % pg.bt) * W * 64;
+}
+
+// Word 0 of destination token dtok for writes (per lane); nullptr for a
+// block id outside [0, n_blocks) (the words are dropped).
+__device__ __forceinline__ uint32_t *page_token(const PageArgs &pg, uint32_t *slot_or_pool, int b, int h,
+                                                int64_t dtok, int W) {
+  const int64_t tile = dtok >> 6;
+  if (!pg.table) return slot_or_pool + tile * W * 64 + (dtok & 63);
+  const int64_t blk = pg.table[(int64_t)b * pg.tstride + tile / pg.bt];
+  if (blk < 0 || blk >= pg.n_blocks) return nullptr;
+  return slot_or_pool + (blk * pg.nh + h) * pg.block_words + (tile % pg.bt) * W * 64 + (dtok & 63);
+}
+
+// Host checks of a paged cache description for a call that touches tokens
+// [0, n_tokens) of each batch row; fills the kernels' PageArgs.
+static inline sq_status check_paged(const sq_calib *c, const sq_paged *pg, int64_t n_tokens, int n_heads,
+                                    const char *fn, PageArgs &out) {
+  const std::string f(fn);
+  if (!pg || !pg->block_table) return fail(SQ_ERR_ARG, f + ": paged cache without a block table");
+  if (pg->block_tiles < 1 || pg->n_blocks < 1) return fail(SQ_ERR_ARG, f + ": block_tiles and n_blocks must be >= 1");
+  const int64_t tiles = (n_tokens + 63) / 64;
+  const int64_t blocks = (tiles + pg->block_tiles - 1) / pg->block_tiles;
+  if (pg->table_stride < blocks) return fail(SQ_ERR_ARG, f + ": table_stride below the logical blocks of the call");
+  out = PageArgs{};
+  out.table = pg->block_table;
+  out.tstride = pg->table_stride;
+  out.block_words = (int64_t)pg->block_tiles * 64 * c->W_max;
+  out.bt = pg->block_tiles;
+  out.nh = n_heads;
+  out.n_blocks = pg->n_blocks;
+  return SQ_OK;
+}
+
 static inline sq_status launched(const char *fn) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(fn, e);

@@ -237,6 +237,29 @@ sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
                       int64_t ps_head, sq_stream stream);
 
 /*
+ * Paged packed cache (the decode-time cache layout of serving engines: the
+ * sequences of a batch share a pool of fixed-size blocks handed out as they
+ * grow).  A block holds block_tiles 64-token tiles of every head of a call;
+ * logical block j of batch row b (its tiles j*block_tiles ..) is physical
+ * block block_table[b * table_stride + j] of the pool, whose head h (0 <= h <
+ * n_heads of the call) takes the words [(block * n_heads + h) * block_words,
+ * + block_words) with block_words = sq_paged_block_words(c, block_tiles);
+ * tile i of a block starts i * 64 * W words in, in the word-interleaved
+ * record layout of the contiguous slots.  Block ids are the caller's; an id
+ * outside [0, n_blocks) is never dereferenced (its writes are dropped, its
+ * reads take the first or last block instead).
+ */
+typedef struct {
+  const int32_t *block_table;  /* DEVICE int32 [batch][table_stride] */
+  int64_t table_stride;        /* >= the logical blocks a call touches */
+  int32_t block_tiles;         /* 64-token tiles per block, >= 1 */
+  int32_t n_blocks;            /* physical blocks in the pool, >= 1 */
+} sq_paged;
+
+/* Words per (block, head) of a pool for this handle: block_tiles * 64 * W_max. */
+int64_t sq_paged_block_words(const sq_calib *c, int block_tiles);
+
+/*
  * sq_compress_append -- sq_compress of n_tokens new vectors into token slots
  * token0 .. token0 + n_tokens - 1 of an existing packed cache: the decode-time
  * producer of the compressed cache (SpectralQuant README "Overview": the
@@ -261,6 +284,23 @@ sq_status sq_compress_append(const sq_calib *c, int first_head, int n_heads,
                              uint32_t *packed, int64_t ps_batch,
                              int64_t ps_head, int64_t token0,
                              sq_stream stream);
+
+/*
+ * sq_compress_append_paged -- sq_compress_append into a paged cache (layout
+ * above): the words of tokens token0 .. token0 + n_tokens - 1 of batch row b,
+ * head h go to their tiles' blocks, with the same zero fill to the end of
+ * the last tile.  The record words equal those of sq_compress_append.
+ * pool    DEVICE uint32, n_blocks * n_heads * sq_paged_block_words(c, block_tiles) words.
+ * pg      HOST pointer to the block table description (the table is DEVICE).
+ * Errors: as sq_compress_append; SQ_ERR_ARG for a NULL pg, table or pool,
+ * block_tiles or n_blocks < 1, or table_stride below the logical blocks of
+ * token0 + n_tokens tokens.
+ */
+sq_status sq_compress_append_paged(const sq_calib *c, int first_head, int n_heads,
+                                   int batch, int calib_batch_stride, const void *x,
+                                   sq_dtype dt, int64_t n_tokens, int64_t xs_batch,
+                                   int64_t xs_head, int64_t xs_token, uint32_t *pool,
+                                   const sq_paged *pg, int64_t token0, sq_stream stream);
 
 /*
  * sq_scores -- raw q.k scores read from the packed keys (no softmax scale).
@@ -341,6 +381,21 @@ sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first_head,
                     int64_t kps_batch, int64_t kps_head, const uint32_t *vpacked,
                     int64_t vps_batch, int64_t vps_head, int64_t n_tokens, float scale,
                     void *workspace, size_t ws_bytes, float *out, sq_stream stream);
+
+/*
+ * sq_decode_paged -- sq_decode over paged key and value caches that share
+ * one block table (layout above; kpool's block_words from kc, vpool's from
+ * vc).  The result equals sq_decode's over the same records in contiguous
+ * slots, bit for bit.
+ * Errors: as sq_decode; SQ_ERR_ARG for a NULL pg, table or pool, block_tiles
+ * or n_blocks < 1, or table_stride below the logical blocks of n_tokens.
+ */
+sq_status sq_decode_paged(const sq_calib *kc, const sq_calib *vc, int first_head,
+                          int calib_batch_stride, int batch, int n_q_heads, int n_kv_heads,
+                          const void *q, sq_dtype qdt, const uint32_t *kpool,
+                          const uint32_t *vpool, const sq_paged *pg, int64_t n_tokens,
+                          float scale, void *workspace, size_t ws_bytes, float *out,
+                          sq_stream stream);
 
 /*
  * sq_attend_noalloc -- sq_attend for callers that cannot allocate device
