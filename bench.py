@@ -356,6 +356,50 @@ def main():
     torch.cuda.synchronize()
     append_us = float(np.mean([e[0].elapsed_time(e[1]) for e in aev])) * 1e3
 
+    # the same decode over a paged cache (blocks of 4 tiles handed out in a
+    # seeded random order), outside the timed steps; must equal sq_decode bit for bit
+    bt = 4
+    nlb = ((T + 63) // 64 + bt - 1) // bt
+    n_blocks = B * nlb
+    perm = np.random.default_rng(7).permutation(n_blocks).astype(np.int32).reshape(B, nlb)
+    table = torch.from_numpy(perm).to(dev)
+    pg = sq.paged(table, bt, n_blocks)
+    with torch.cuda.stream(stream):
+        kpool = torch.empty((n_blocks * Hkv * sq.sq_paged_block_words(kcal, bt),), dtype=torch.int32, device=dev)
+        vpool = torch.empty((n_blocks * Hkv * sq.sq_paged_block_words(vcal, bt),), dtype=torch.int32, device=dev)
+    sq.sq_compress_append_paged(kcal, K, kpool, pg, 0, stream=sh)
+    sq.sq_compress_append_paged(vcal, V, vpool, pg, 0, stream=sh)
+    out3 = torch.empty_like(out)
+    for _ in range(args.warmup):
+        sq.sq_decode_paged(kcal, vcal, q, kpool, vpool, pg, T, scale, ws, out3, Hkv, stream=sh)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        pev[k][0].record(stream)
+        sq.sq_decode_paged(kcal, vcal, q, kpool, vpool, pg, T, scale, ws, out3, Hkv, stream=sh)
+        pev[k][1].record(stream)
+    torch.cuda.synchronize()
+    ms_pdec = float(np.median([e[0].elapsed_time(e[1]) for e in pev]))
+    paged_equal = bool(torch.equal(out3.view(torch.int32), out2.view(torch.int32)))
+    del kpool, vpool
+
+    # one-time calibration: host (C++, all host threads) against the device
+    # path, for this workload's 8 key heads and for 48 layers' worth of heads
+    def _wall(fn):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        r = fn()
+        torch.cuda.synchronize()
+        return r, (time.perf_counter() - t) * 1e3
+    _, cal_host_ms = _wall(lambda: sq.sq_calibrate(Xk, 3.0, 1, Gk))
+    Xk_d = torch.from_numpy(Xk).to(dev)
+    sq.sq_calibrate_device(Xk_d, 3.0, 1, Gk)  # warm-up (module load)
+    _, cal_dev_ms = _wall(lambda: sq.sq_calibrate_device(Xk_d, 3.0, 1, Gk))
+    Xk48 = Xk_d.repeat(48, 1, 1).contiguous()
+    Gk48 = np.concatenate([Gk] * 48)
+    _, cal_dev48_ms = _wall(lambda: sq.sq_calibrate_device(Xk48, 3.0, 1, Gk48))
+    _, cal_host48_ms = _wall(lambda: sq.sq_calibrate(Xk48.cpu().numpy(), 3.0, 1, Gk48))
+    del Xk48
+
     n_vec = B * Hkv * T
     # algorithmic bytes: compress reads d bf16 and writes one record per vector
     bytes_ck = n_vec * (2 * d + 4 * Wk)
@@ -406,6 +450,14 @@ def main():
                          "max_rel_diff_vs_split": dec_err},
         "append_decode": {"what": f"1 new token per (sequence, KV head), K and V: {2 * B * Hkv} vectors "
                                   f"into slots at token {T - 1}", "us": append_us},
+        "decode_paged": {"what": f"sq_decode_paged: the fused decode over paged K/V pools (blocks of "
+                                 f"{bt * 64} tokens, random block order)", "ms": ms_pdec,
+                         "GBps": gbps(bytes_dec, ms_pdec), "equal_to_contiguous": paged_equal},
+        "calibration": {"what": "one-time key calibration, 512 samples per head, hd128 (host: C++ on "
+                                f"{os.cpu_count()} threads; device: covariance, Jacobi and rotation on the GPU, "
+                                "Lloyd-Max on the host)",
+                        "heads_8": {"host_ms": cal_host_ms, "device_ms": cal_dev_ms},
+                        "heads_384": {"host_ms": cal_host48_ms, "device_ms": cal_dev48_ms}},
         "roofline": {"bound": "hbm", "kernel": "compress2_kernel<128,bf16> (register quantiser; per launch, K and V averaged)",
                      "achieved": comp_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": comp_gbps / HBM_PEAK_GBPS, "traffic": traffic,

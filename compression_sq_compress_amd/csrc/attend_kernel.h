@@ -198,8 +198,11 @@ __device__ __forceinline__ void build_score_tables(const AttendArgs &a, int b, i
 // FUSED (sq_decode): the scores of each tile are computed here from the
 // packed keys (lane = token, the key record in registers) instead of being
 // read from device memory; G <= 4 query heads per launch.
-template <int G, int LM, int NP, int WPB, int NBUF = 2, bool FUSED = false>
+// FM: 0 sq_attend (scores from device memory), 1 sq_decode (scores built from
+// the key records), 2 sq_decode over paged key and value pools
+template <int G, int LM, int NP, int WPB, int NBUF = 2, int FM = 0>
 __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) {
+  constexpr bool FUSED = FM != 0, PAGED = FM == 2;
   extern __shared__ float smem[];
   constexpr int GR = (G + 3) / 4, GP = 4 * GR;
   constexpr int GQ = G == 3 ? 4 : G;  // floats per score-table entry
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
     const SQ_CONST uint32_t *sbase = fs + ((2 * ng + knq + 15) & ~15);
     kslots = sbase + (size_t)(E - 2) * (kW + 1) * FS_SLOTS * 2;
     kscnt = sbase + (size_t)3 * (kW + 1) * FS_SLOTS * 2 + (size_t)(E - 2) * (kW + 1);
-    kslot = a.kpg.table ? a.kpacked : a.kpacked + (int64_t)b * a.kps_b + (int64_t)hkv * a.kps_h;
+    kslot = PAGED ? a.kpacked : a.kpacked + (int64_t)b * a.kps_b + (int64_t)hkv * a.kps_h;
   }
   __syncthreads();
   if (chunk >= a.n_chunks) return;  // no barrier follows
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   const int64_t tb = (int64_t)chunk * a.chunk_tokens;
   const int64_t te = min(a.n_tokens, tb + a.chunk_tokens);
   const float *srow = FUSED ? nullptr : a.scores + ((int64_t)b * a.n_q_heads + (int64_t)hkv * a.G_full + a.g0) * a.n_tokens;
-  const uint32_t *slot = a.vpg.table ? a.vpacked : a.vpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
+  const uint32_t *slot = PAGED ? a.vpacked : a.vpacked + (int64_t)b * a.ps_b + (int64_t)hkv * a.ps_h;
   float mrun[G], lsum[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   // the SIMD cover the wait.
   auto stage_tile = [&](int64_t t0, int buf) {
     uint32_t *rw = (uint32_t *)(stage + buf * a.buf_floats) + ATT_RS;  // row 1 = word 0
-    const uint32_t *src = page_tile(a.vpg, slot, b, hkv, t0 >> 6, W) + lane;
+    const uint32_t *src = (PAGED ? page_tile(a.vpg, slot, b, hkv, t0 >> 6, W) : slot + (t0 >> 6) * W * 64) + lane;
     for (int w = 0; w <= W; ++w)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + min(w, W - 1) * 64),
                                        (__attribute__((address_space(3))) void *)(rw + w * ATT_RS), 4, 0, 0);
@@ -348,7 +351,8 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
   uint32_t qlo = 0u, qhi = 0u, wlast = 0u;
   auto load_keys = [&](int64_t t0) {
     if constexpr (FUSED) {
-      const uint32_t *src = page_tile(a.kpg, kslot, b, hkv, t0 >> 6, kW) + lane;
+      const uint32_t *src =
+          (PAGED ? page_tile(a.kpg, kslot, b, hkv, t0 >> 6, kW) : kslot + (t0 >> 6) * (int64_t)kW * 64) + lane;
       kw[0] = 0u;
 #pragma unroll
       for (int k = 0; k < DEC_KW; ++k) kw[k + 1] = k < kW ? src[k * 64] : 0u;

@@ -6,66 +6,31 @@
 
 using namespace sq;
 
+namespace sq {
+// defined, per instance, in the decode_g*.hip units
+template <int G, int FM>
+bool dispatch_g(bool run, int lm, int np, int wpb, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a);
+}  // namespace sq
+
 namespace {
 
-// Waves per workgroup the fused kernel is built for, by table placement:
-// column tables share LDS among 8, 12 or 16 single-buffered waves, packed and
-// device-memory tables among 4 or 8.
-template <int G, int LM, int NP, int WPB>
-void launch_one(dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  hipLaunchKernelGGL((attend_partial_kernel<G, LM, NP, WPB, 1, true>), grid, dim3(64 * WPB), lds, s, a);
-}
-
-template <int G, int LM, int NP, int WPB>
-bool fits() {  // no static LDS (tables at address 0) and no scratch
-  static const bool ok = [] {
-    hipFuncAttributes fa{};
-    return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&attend_partial_kernel<G, LM, NP, WPB, 1, true>)) ==
-               hipSuccess && fa.sharedSizeBytes == 0 && fa.localSizeBytes == 0;
-  }();
-  return ok;
-}
-
-template <int G, int LM, int NP>
-bool dispatch_np(bool run, int wpb, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  if constexpr (LM == LM_COL) {
-    switch (wpb) {
-      case 16: if (run) launch_one<G, LM, NP, 16>(grid, lds, s, a); return fits<G, LM, NP, 16>();
-      case 12: if (run) launch_one<G, LM, NP, 12>(grid, lds, s, a); return fits<G, LM, NP, 12>();
-      case 8: if (run) launch_one<G, LM, NP, 8>(grid, lds, s, a); return fits<G, LM, NP, 8>();
-      default: return false;
-    }
-  } else {
-    switch (wpb) {
-      case 8: if (run) launch_one<G, LM, NP, 8>(grid, lds, s, a); return fits<G, LM, NP, 8>();
-      case 4: if (run) launch_one<G, LM, NP, 4>(grid, lds, s, a); return fits<G, LM, NP, 4>();
-      default: return false;
-    }
-  }
-}
-
-template <int G>
-bool dispatch_g(bool run, int lm, int np, int wpb, dim3 grid, size_t lds, hipStream_t s, const AttendArgs &a) {
-  auto by_np = [&](auto lmc) {
-    constexpr int LM = decltype(lmc)::value;
-    if (np == 1) return dispatch_np<G, LM, 1>(run, wpb, grid, lds, s, a);
-    if (np == 2) return dispatch_np<G, LM, 2>(run, wpb, grid, lds, s, a);
-    return dispatch_np<G, LM, 4>(run, wpb, grid, lds, s, a);
-  };
-  if (lm == LM_COL) return by_np(std::integral_constant<int, LM_COL>());
-  if (lm == LM_PACK) return by_np(std::integral_constant<int, LM_PACK>());
-  return by_np(std::integral_constant<int, LM_GLB>());
-}
-
-// run == false: only report whether that kernel exists without scratch
-bool dispatch(bool run, int gsub, int lm, int np, int wpb, dim3 grid, size_t lds, hipStream_t s,
-              const AttendArgs &a) {
+template <int FM>
+bool dispatch_fm(bool run, int gsub, int lm, int np, int wpb, dim3 grid, size_t lds, hipStream_t s,
+                 const AttendArgs &a) {
   switch (gsub) {
-    case 1: return dispatch_g<1>(run, lm, np, wpb, grid, lds, s, a);
-    case 2: return dispatch_g<2>(run, lm, np, wpb, grid, lds, s, a);
-    case 3: return dispatch_g<3>(run, lm, np, wpb, grid, lds, s, a);
-    default: return dispatch_g<4>(run, lm, np, wpb, grid, lds, s, a);
+    case 1: return dispatch_g<1, FM>(run, lm, np, wpb, grid, lds, s, a);
+    case 2: return dispatch_g<2, FM>(run, lm, np, wpb, grid, lds, s, a);
+    case 3: return dispatch_g<3, FM>(run, lm, np, wpb, grid, lds, s, a);
+    default: return dispatch_g<4, FM>(run, lm, np, wpb, grid, lds, s, a);
   }
+}
+
+// run == false: only report whether that kernel exists without scratch;
+// paged: the instance reading paged key and value pools
+bool dispatch(bool run, int gsub, int lm, int np, int wpb, dim3 grid, size_t lds, hipStream_t s,
+              const AttendArgs &a, bool paged = false) {
+  return paged ? dispatch_fm<2>(run, gsub, lm, np, wpb, grid, lds, s, a)
+               : dispatch_fm<1>(run, gsub, lm, np, wpb, grid, lds, s, a);
 }
 
 }  // namespace
@@ -210,6 +175,10 @@ static sq_status decode_impl(const char *fn, const sq_calib *kc, const sq_calib 
   DecodePlan P;
   if ((st = plan_decode(kc, vc, first_head, calib_batch_stride, batch, n_q_heads, n_kv_heads, n_tokens, P)) != SQ_OK)
     return st;
+  if (paged)
+    for (int g0 = 0; g0 < G; g0 += P.gsub)
+      if (!dispatch(false, std::min(P.gsub, G - g0), P.lm, P.np, P.wpb, dim3(), 0, nullptr, P.a, true))
+        return fail(SQ_ERR_UNSUPPORTED, std::string(fn) + ": no paged kernel instance without scratch for this shape");
   AttendArgs a = P.a;
   a.vpacked = vpacked;
   a.ps_b = vps_batch;
@@ -228,7 +197,7 @@ static sq_status decode_impl(const char *fn, const sq_calib *kc, const sq_calib 
     a.g0 = g0;
     const int gn = std::min(P.gsub, G - g0);
     // a remainder smaller than the launch size takes its own instance
-    dispatch(true, gn, P.lm, P.np, P.wpb, P.grid, P.lds, s, a);
+    dispatch(true, gn, P.lm, P.np, P.wpb, P.grid, P.lds, s, a, paged != nullptr);
     if ((st = launched(fn)) != SQ_OK) return st;
   }
   launch_attend_combine(a, batch, d, s);

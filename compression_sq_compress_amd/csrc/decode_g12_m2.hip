@@ -1,0 +1,7 @@
+// Fused decode kernel instances: 1 and 2 query heads per launch, paged key and value records.
+#include "decode_dispatch.h"
+
+namespace sq {
+template bool dispatch_g<1, 2>(bool, int, int, int, dim3, size_t, hipStream_t, const AttendArgs &);
+template bool dispatch_g<2, 2>(bool, int, int, int, dim3, size_t, hipStream_t, const AttendArgs &);
+}  // namespace sq

@@ -211,9 +211,11 @@ struct PageArgs {
 __device__ __forceinline__ const uint32_t *page_tile(const PageArgs &pg, const uint32_t *slot_or_pool, int b,
                                                      int h, int64_t tile, int W) {
   if (!pg.table) return slot_or_pool + tile * W * 64;
-  int64_t blk = pg.table[(int64_t)b * pg.tstride + tile / pg.bt];
+  // (tiles of one row stay below 2^31: the host limits tokens to 2^36)
+  const uint32_t t32 = (uint32_t)tile, lb = t32 / (uint32_t)pg.bt, tb = t32 - lb * (uint32_t)pg.bt;
+  int64_t blk = pg.table[(int64_t)b * pg.tstride + lb];
   blk = blk < 0 ? 0 : blk >= pg.n_blocks ? pg.n_blocks - 1 : blk;
-  return slot_or_pool + (blk * pg.nh + h) * pg.block_words + (tile % pg.bt) * W * 64;
+  return slot_or_pool + (blk * pg.nh + h) * pg.block_words + (int64_t)tb * W * 64;
 }
 
 // Word 0 of destination token dtok for writes (per lane); nullptr for a
@@ -222,9 +224,10 @@ __device__ __forceinline__ uint32_t *page_token(const PageArgs &pg, uint32_t *sl
                                                 int64_t dtok, int W) {
   const int64_t tile = dtok >> 6;
   if (!pg.table) return slot_or_pool + tile * W * 64 + (dtok & 63);
-  const int64_t blk = pg.table[(int64_t)b * pg.tstride + tile / pg.bt];
+  const uint32_t t32 = (uint32_t)tile, lb = t32 / (uint32_t)pg.bt, tb = t32 - lb * (uint32_t)pg.bt;
+  const int64_t blk = pg.table[(int64_t)b * pg.tstride + lb];
   if (blk < 0 || blk >= pg.n_blocks) return nullptr;
-  return slot_or_pool + (blk * pg.nh + h) * pg.block_words + (tile % pg.bt) * W * 64 + (dtok & 63);
+  return slot_or_pool + (blk * pg.nh + h) * pg.block_words + (int64_t)tb * W * 64 + (dtok & 63);
 }
 
 // Host checks of a paged cache description for a call that touches tokens
