@@ -69,10 +69,19 @@ __global__ __launch_bounds__(256) void covariance_kernel(const float *x, int64_t
 // Stops after a sweep that starts with no off-diagonal entry left, or after
 // JACOBI_MAX_SWEEPS.  status[h] = 1 when the matrix is not finite (a non-
 // finite sample), else 0.
+// LDSA: A is worked on in LDS (d <= 128: 128 KB of fp64) and written back at
+// the end; V stays in device memory.
+template <bool LDSA>
 __global__ __launch_bounds__(256) void jacobi_kernel(double *A, double *V, int d, int *status) {
+  extern __shared__ double a_lds[];
   const int h = blockIdx.x;
-  double *a = A + (size_t)h * d * d;
+  double *a_g = A + (size_t)h * d * d;
+  double *a = LDSA ? a_lds : a_g;
   double *v = V + (size_t)h * d * d;
+  if constexpr (LDSA) {
+    for (int k = threadIdx.x; k < d * d; k += 256) a_lds[k] = a_g[k];
+    __syncthreads();
+  }
   __shared__ double cs[128], sn[128];
   __shared__ int pp[128], qq[128];
   __shared__ double red[256];
@@ -127,9 +136,10 @@ __global__ __launch_bounds__(256) void jacobi_kernel(double *A, double *V, int d
         sn[k] = s;
       }
       __syncthreads();
-      // A <- A J and V <- V J (columns p, q of every pair)
+      // A <- A J and V <- V J (columns p, q of every pair); neighbouring
+      // threads take different pairs of one row (distinct LDS banks)
       for (int k = tid; k < half * d; k += 256) {
-        const int pr = k / d, r = k - pr * d;
+        const int r = k / half, pr = k - r * half;
         const double s = sn[pr];
         if (s == 0.0) continue;
         const int p = pp[pr], q = qq[pr];
@@ -161,6 +171,10 @@ __global__ __launch_bounds__(256) void jacobi_kernel(double *A, double *V, int d
       }
       __syncthreads();
     }
+  }
+  if constexpr (LDSA) {
+    __syncthreads();
+    for (int k = threadIdx.x; k < d * d; k += 256) a_g[k] = a_lds[k];
   }
 }
 
@@ -236,7 +250,10 @@ extern "C" sq_status sq_calibrate_device(const float *samples, int n_heads, int6
                        samples, n_samples, d, N);
   hipLaunchKernelGGL(covariance_kernel, dim3(d / 16, d / 16, n_heads), dim3(256), 0, s, samples, n_samples, d, norm,
                      (const double *)N, C);
-  hipLaunchKernelGGL(jacobi_kernel, dim3(n_heads), dim3(256), 0, s, C, V, d, S);
+  if (d <= 128)
+    hipLaunchKernelGGL(jacobi_kernel<true>, dim3(n_heads), dim3(256), sizeof(double) * dd, s, C, V, d, S);
+  else
+    hipLaunchKernelGGL(jacobi_kernel<false>, dim3(n_heads), dim3(256), 0, s, C, V, d, S);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(fn, e);
   std::vector<double> hC(dd * n_heads), hV(dd * n_heads);
   std::vector<int> hS(n_heads);
