@@ -444,32 +444,51 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
       }
     }
     __syncthreads();
-    // ---- larger sketches: the last wave adds the QJL bits and gamma to the
-    // words it owns, from the residuals, which replaced y of the signal
-    // coordinates in the tile
+    // ---- larger sketches: every wave takes m / NW of the QJL rows (16 at a
+    // time, the lane's residuals read 16 at a time) and ORs their bits into
+    // the word buffer; the last wave adds gamma.  A barrier then separates
+    // these ORs from the stores of the words at the top of the next tile.
     const bool qslow = m > 0 && !(m <= 8 && d_eff <= 8);
-    for (int k = own_f; k < own_e && qslow && w == NW - 1; ++k) {
-      if (k >= dfirst && k < dend) continue;
-      uint32_t word = bwrow[k];
-      {
-        const int lo_bit = 32 * k, hi_bit = lo_bit + 32;
-        const int jb = max(0, lo_bit - code_bits), je = min(m, hi_bit - code_bits);
-        for (int j = jb; j < je; ++j) {
-          float dot = 0.0f;
-          if (a.lds_s_off >= 0) {
-            for (int i = 0; i < d_eff; ++i) dot = fmaf(S_lds[j * d_eff + i], yrow[i], dot);
-          } else {
-            for (int i = 0; i < d_eff; ++i) dot = fmaf(S_glb[j * d_eff + i], yrow[i], dot);
+    if (qslow) {
+      const int jb = (w * m) / NW, je = ((w + 1) * m) / NW;
+      const float *Sb = a.lds_s_off >= 0 ? S_lds : (const float *)S_glb;
+      for (int j0 = jb; j0 < je; j0 += 16) {
+        const int nj = min(16, je - j0);
+        float dot[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) dot[jj] = 0.0f;
+        for (int i0 = 0; i0 < d_eff; i0 += 16) {
+          const int ni = min(16, d_eff - i0);
+          float yv[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) yv[u] = u < ni ? yrow[i0 + u] : 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            if (jj < nj) {
+              const float *srow = Sb + (size_t)(j0 + jj) * d_eff + i0;
+              float acc = dot[jj];
+#pragma unroll
+              for (int u = 0; u < 16; ++u)
+                if (u < ni) acc = fmaf(srow[u], yv[u], acc);
+              dot[jj] = acc;
+            }
           }
-          word |= (dot >= 0.0f ? 1u : 0u) << (code_bits + j - lo_bit);
         }
-        if (k == W - 1) {
-          float g2 = 0.0f;
-          for (int i = 0; i < d_eff; ++i) g2 = fmaf(yrow[i], yrow[i], g2);
-          word |= half_bits_rne(sqrtf(g2)) << 16;
-        }
+        uint32_t zb = 0u;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+          if (jj < nj) zb |= (dot[jj] >= 0.0f ? 1u : 0u) << jj;
+        const int pbit = code_bits + j0;
+        const uint64_t v = (uint64_t)zb << (pbit & 31);
+        atomicOr(bwrow + (pbit >> 5), (uint32_t)v);
+        if ((uint32_t)(v >> 32)) atomicOr(bwrow + (pbit >> 5) + 1, (uint32_t)(v >> 32));
       }
-      bwrow[k] = word;
+      if (w == NW - 1) {
+        float g2 = 0.0f;
+        for (int i = 0; i < d_eff; ++i) g2 = fmaf(yrow[i], yrow[i], g2);
+        atomicOr(bwrow + W - 1, half_bits_rne(sqrtf(g2)) << 16);
+      }
+      __syncthreads();
     }
     pvalid = t0 + lane < T;
     pin = t0 + lane < send;
@@ -565,7 +584,7 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
   {
     // (the kernel's per-lane load offsets within a 64-token tile are 32-bit;
     // each of its d/16 waves stores at most C2_WMAX record words per tile)
-    // (normalised heads have no register plan: n_p2 = 0)
+    // (normalised heads have no tree plan, n_p2 = 0: they take the grid tables)
     bool use2 = d <= 128 && 64 * xs_token * esz < ((int64_t)1 << 32) && c->W_max <= C2_WMAX * (d / 16) &&
                 n_heads <= 65535 && batch <= 65535;
     // quantiser: the grid tables when every head has them, else the padded
@@ -573,10 +592,12 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
     const char *qenv = std::getenv("SQ_QUANTISER");
     bool gridq = use2 && !(qenv && std::strcmp(qenv, "tree") == 0);
     bool treeq = use2;
-    int mt = 0, mc = 0, mq = 0, mg = 0, mgc = 0;
+    int mt = 0, mc = 0, mq = 0, mg = 0, mgc = 0, n_norm = 0, n_seen = 0;
     for (int bb = 0; bb < std::max(1, batch) && use2; ++bb) {
       for (int h = 0; h < n_heads; ++h) {
         const DevHead &hd = c->host_desc[first_head + bb * calib_batch_stride + h];
+        n_norm += hd.normalized ? 1 : 0;
+        n_seen += 1;
         if (hd.n_p2 == 0) treeq = false;
         if (hd.n_gcells == 0) gridq = false;
         mt = std::max(mt, hd.n_tree2);
@@ -587,6 +608,11 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
       }
       if (calib_batch_stride == 0) break;
     }
+    // normalised heads: the grid kernel's NORM instances (bf16 input,
+    // contiguous slots, every head of the call normalised)
+    const bool norm = n_norm > 0;
+    if (norm && (n_norm != n_seen || dt != SQ_BF16 || paged)) gridq = false;
+    if (norm) treeq = false;
     use2 = gridq || treeq;
     if (gridq) {
       mt = mg;
@@ -604,7 +630,8 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
       // record tile stride: odd, above W_max (pad column)
       const int rsc = c->W_max < 17 ? 17 : c->W_max < 33 ? 33 : 49;
       b2.lds_res_off = (b2.lds_rec_off + 3 * 64 * rsc + 3) & ~3;
-      const size_t lds2 = (size_t)(b2.lds_res_off + 2 * 64 * C2_RS) * 4;
+      b2.lds_nrm_off = b2.lds_res_off + 2 * 64 * C2_RS;
+      const size_t lds2 = (size_t)(b2.lds_nrm_off + (norm ? 64 * 8 : 0)) * 4;
       if (lds2 <= (size_t)device_lds_limit()) {
         b2.heads = c->dev_heads;
         b2.blob = (const uint8_t *)c->dev_blob;
@@ -626,7 +653,8 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
         b2.tiles_per_wg = (int)((b2.n_tiles + chunks - 1) / chunks);
         dim3 grid((unsigned)((b2.n_tiles + b2.tiles_per_wg - 1) / b2.tiles_per_wg), n_heads, batch);
         hipStream_t s = (hipStream_t)stream;
-        if (b2.pg.table) launch_compress2_pg<true>(d, f32, gridq, rsc, grid, lds2, s, b2);
+        if (norm) launch_compress2_norm(d, rsc, grid, lds2, s, b2);
+        else if (b2.pg.table) launch_compress2_pg<true>(d, f32, gridq, rsc, grid, lds2, s, b2);
         else launch_compress2_pg<false>(d, f32, gridq, rsc, grid, lds2, s, b2);
         return launched(fn);
       }
@@ -636,10 +664,13 @@ static sq_status compress_impl(const char *fn, const sq_calib *c, int first_head
   a.ys = d + 3;  // odd, and conflict-free for the MFMA-layout stores
   a.bws = (c->W_max % 2 == 0) ? c->W_max + 1 : c->W_max;
   const int xs_floats = dt == SQ_F32 ? 64 * (d + 4) : 64 * (d + 8) / 2;
-  const bool s_in_lds = max_s <= 4096;  // a large sketch is read from the L1/L2 instead
-  const int s_floats = s_in_lds ? ((max_s + 3) & ~3) : 0;
-  const int rest = ((max_csig + 3) & ~3) + max_plan + s_floats + 64 + xs_floats + 64 * a.ys + 64 * a.bws;
   const size_t limit = (size_t)device_lds_limit();
+  // the sketch goes to LDS when the workgroup still fits (else it is read
+  // through the L1/L2)
+  const int rest_no_s = ((max_csig + 3) & ~3) + max_plan + 64 + xs_floats + 64 * a.ys + 64 * a.bws;
+  const bool s_in_lds = (size_t)(rest_no_s + ((max_s + 3) & ~3)) * 4 <= limit;
+  const int s_floats = s_in_lds ? ((max_s + 3) & ~3) : 0;
+  const int rest = rest_no_s + s_floats;
   const size_t lds_in = (size_t)(((max_tree + 3) & ~3) + rest) * 4, lds_out = (size_t)rest * 4;
   // trees stay in LDS unless moving them out is what lets two workgroups share a CU
   const bool tg = lds_in > limit || (lds_in > limit / 2 && lds_out <= limit / 2);

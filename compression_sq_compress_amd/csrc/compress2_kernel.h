@@ -47,6 +47,7 @@ struct Compress2Args {
   int first_head, cbs;
   int n_tiles, tiles_per_wg;  // workgroup (x, head, batch entry) takes tiles [x * tiles_per_wg, ...)
   int lds_tree_off, lds_csig_off, lds_s_off, lds_x_off, lds_rec_off, lds_res_off;  // floats
+  int lds_nrm_off;            // floats: per-wave partial norms [64 tokens][8 waves] (normalised heads)
   int x_buf_floats;
   PageArgs pg;                // paged destination (pg.table == nullptr: contiguous slots)
 };
@@ -60,8 +61,14 @@ constexpr int C2_WMAX = 6;  // record words stored per wave and tile (word k goe
 // GRID: quantise with the grid tables (one cell read per value, codes of a
 // lane's four registers combined before one pair of record-tile ORs; MFMA
 // rows in natural coordinate order) instead of the padded trees.
-template <int D, bool F32, int RS, bool GRID, bool PG>
+// NORM (grid quantiser only): normalised heads -- each token's norm nu = |y|
+// (= |x|, R orthogonal) from the accumulators, summed over the waves in a
+// fixed order through LDS (one extra barrier per tile); the unit vector
+// y / nu is quantised and its residual sketched, and nu goes into the record
+// as an IEEE half.
+template <int D, bool F32, int RS, bool GRID, bool PG, bool NORM = false>
 __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
+  static_assert(!NORM || GRID, "normalised heads use the grid quantiser");
   extern __shared__ float smem[];
   constexpr int NW = D / 16, KB = D / 32, MB = D / 16, NT = 64 * NW;
   const int lane = threadIdx.x & 63;
@@ -265,6 +272,38 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     // decoded fields out of the loop would not fit the register budget.)
     uint32_t *rec = rec0 + rb * 64 * rs;
     float *rtile = smem + a.lds_res_off + par * 64 * C2_RS;
+    // normalised heads: 1 / nu of tokens 16 j + lane % 16 (0 for a zero vector)
+    float inv_nu[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (NORM) {
+      float *nrm = smem + a.lds_nrm_off;  // [token][wave]
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = acc[j][0] * acc[j][0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r) p[j] = fmaf(acc[j][r], acc[j][r], p[j]);
+        p[j] += __shfl_xor(p[j], 16);  // rows of the four lane groups
+        p[j] += __shfl_xor(p[j], 32);
+      }
+      if (s4 == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nrm[(16 * j + (lane & 15)) * 8 + w] = p[j];
+      }
+      __syncthreads();
+      auto norm_of = [&](int tok) __attribute__((always_inline)) {
+        const float4 u0 = *(const float4 *)(nrm + tok * 8), u1 = *(const float4 *)(nrm + tok * 8 + 4);
+        float t = u0.x;  // fixed order over the waves: every wave gets the same nu
+        t += u0.y; t += u0.z; t += u0.w; t += u1.x; t += u1.y; t += u1.z; t += u1.w;
+        return __builtin_amdgcn_sqrtf(t);
+      };
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float nu = norm_of(16 * j + (lane & 15));
+        inv_nu[j] = nu > 0.0f ? 1.0f / nu : 0.0f;
+      }
+      if (w == NW - 1)  // nu of token = lane into word W - 1 (low half after QJL bits, else high)
+        atomicOr(rec + lane * rs + W - 1, half_bits_rne(norm_of(lane)) << (m > 0 ? 0 : 16));
+    }
     if constexpr (GRID) {
       // one cell read per value; the lane's four codes (adjacent fields) are
       // combined, then OR-ed into the record tile as one 64-bit window
@@ -277,7 +316,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
         for (int j = 0; j < 4; ++j) {
           // a NaN u converts to cell 0 and fails the compare: code 0
           // (v_med3_f32 returns 0 for a NaN first operand; +-inf clamp to the ends)
-          const float u = fmaf(acc[j][r], ga[r], gb[r]);
+          const float u = fmaf(NORM ? acc[j][r] * inv_nu[j] : acc[j][r], ga[r], gb[r]);
           const int cell = (int)__builtin_amdgcn_fmed3f(u, 0.0f, gcmf[r]);
           const uint64_t e = *(lds_u64 *)(uintptr_t)(gtab[r] + (uint32_t)cell * 8u);
           code[j] = (uint32_t)(e >> 32) + (u > __uint_as_float((uint32_t)e) ? 1u : 0u);
@@ -288,7 +327,8 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
           const int crd = 16 * w + 4 * s4 + r;  // < d_eff <= 16
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            rtile[((lane & 15) + 16 * j) * C2_RS + crd] = acc[j][r] - csig[gcb + code[j]];
+            rtile[((lane & 15) + 16 * j) * C2_RS + crd] =
+                (NORM ? acc[j][r] * inv_nu[j] : acc[j][r]) - csig[gcb + code[j]];
         }
       }
       uint32_t *rw = rec + (lane & 15) * rs + (gpos & 0xFFu);
@@ -467,16 +507,19 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   }
 }
 
-template <int D, bool F32, bool GRID, bool PG>
+template <int D, bool F32, bool GRID, bool PG, bool NORM = false>
 void launch_compress2_g(int rsc, dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a) {
   // record strides this head size can need (at most C2_WMAX words per wave)
   if (rsc == 17) {
-    hipLaunchKernelGGL((compress2_kernel<D, F32, 17, GRID, PG>), grid, dim3(4 * D), lds, s, a);
+    hipLaunchKernelGGL((compress2_kernel<D, F32, 17, GRID, PG, NORM>), grid, dim3(4 * D), lds, s, a);
   } else if constexpr (D >= 64) {
-    if (rsc == 33) hipLaunchKernelGGL((compress2_kernel<D, F32, 33, GRID, PG>), grid, dim3(4 * D), lds, s, a);
-    else if constexpr (D == 128) hipLaunchKernelGGL((compress2_kernel<D, F32, 49, GRID, PG>), grid, dim3(4 * D), lds, s, a);
+    if (rsc == 33) hipLaunchKernelGGL((compress2_kernel<D, F32, 33, GRID, PG, NORM>), grid, dim3(4 * D), lds, s, a);
+    else if constexpr (D == 128) hipLaunchKernelGGL((compress2_kernel<D, F32, 49, GRID, PG, NORM>), grid, dim3(4 * D), lds, s, a);
   }
 }
+
+// normalised heads: bf16 input, contiguous slots, grid quantiser
+void launch_compress2_norm(int d, int rsc, dim3 grid, size_t lds, hipStream_t s, const Compress2Args &a);
 
 // every instance of one destination kind (PG), by head size, input dtype and quantiser
 template <bool PG>

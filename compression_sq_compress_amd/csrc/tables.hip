@@ -521,7 +521,7 @@ static HostPlan2 build_plan2(const HeadCal &hc) {
 }
 
 // Grid quantiser tables (GRID_* layout).  Only for heads the register plan
-// serves (d <= 128, not normalised); fails (ok = false) when a region has a
+// serves (d <= 128, at most 16 signal dims and 32 QJL rows); fails (ok = false) when a region has a
 // zero or repeated threshold gap, a coordinate of nonzero width has zero
 // variance, or the cells of all regions exceed GRID_MAX_CELLS.
 static uint32_t fbits(float v) {
@@ -541,7 +541,7 @@ static GridPlan build_grid(const HeadCal &hc) {
   GridPlan G;
   const int d = hc.d;
   if (d != 32 && d != 64 && d != 128) return G;
-  if (hc.normalized || (hc.m > 0 && (hc.d_eff > 16 || hc.m > 32))) return G;
+  if (hc.m > 0 && (hc.d_eff > 16 || hc.m > 32)) return G;
   const float inf = std::numeric_limits<float>::infinity();
   G.cells = {fbits(inf), 0u};  // cell 0: zero-width coordinates
   G.coord.assign((size_t)d * GRID_COORD_WORDS, 0u);

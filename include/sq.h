@@ -226,8 +226,10 @@ int64_t sq_packed_head_words(const sq_calib *c, int64_t n_tokens);
  * n_tokens == 0 or batch == 0 is a no-op.
  * Quantiser: code = #{thresholds < y} by a uniform-grid table per region
  * (one cell read and one compare per value) when the calibration's grid
- * tables exist (head_dim <= 128, unnormalised, at most 6144 cells per head),
- * else by a descent of padded threshold trees; both give the same codes.
+ * tables exist (head_dim <= 128, at most 16 signal dims and 32 QJL rows, at
+ * most 6144 cells per head), else by a descent of padded threshold trees;
+ * both give the same codes.  Normalised calibrations take the grid path for
+ * bf16 input into contiguous slots, the general kernel otherwise.
  * The environment variable SQ_QUANTISER=tree forces the trees (a test hook).
  */
 sq_status sq_compress(const sq_calib *c, int first_head, int n_heads, int batch,
