@@ -494,7 +494,8 @@ __global__ __launch_bounds__(D * 4, 4) void compress_kernel(CompressArgs a) {
     pin = t0 + lane < send;
     // destination of this lane's token (contiguous slot or its block; nullptr: dropped)
     if constexpr (PG) {
-      pdst = pin ? page_token(a.pg, a.packed, b, h, a.token0 + t0 + lane, W) : nullptr;
+      uint32_t *p = page_token_tile(a.pg, a.packed, b, h, a.token0, tile, lane, (a.token0 + T - 1) >> 6, W);
+      pdst = pin ? p : nullptr;
     } else {
       const int ol = (int)(a.token0 & 63) + lane;
       pdst = a.packed + (int64_t)b * a.ps_b + (int64_t)h * a.ps_h + ((a.token0 >> 6) + tile) * W * 64 +

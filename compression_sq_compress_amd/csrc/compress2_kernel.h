@@ -168,16 +168,25 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   const uint32_t lds_x = (uint32_t)(uintptr_t)(smem + a.lds_x_off);
   const uint32_t row_bytes = (uint32_t)a.xs_t * ESZ;  // 64 rows fit 32 bits (host check)
   const char *xbase = (const char *)a.x + ((int64_t)bz * a.xs_b + (int64_t)h * a.xs_h) * ESZ;
+  // (the x-fetch offsets are formed at each use from an opaque copy of the
+  // lane index: hoisted out of the tile loop they are spilled, and the
+  // reloads cost more than forming them again -- measured)
+  auto lane_now = [&]() __attribute__((always_inline)) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
   auto dma_x = [&](int tl, int buf) __attribute__((always_inline)) {
     // rows past the end re-read the last token (a whole tile past it, which
     // only zero-fills destination words, reads nothing else)
     const int64_t t0 = min<int64_t>((int64_t)tl * 64, a.n_tokens - 1);
     const char *src = xbase + t0 * a.xs_t * ESZ;
     const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);
+    const int ln = lane_now();
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int q = w * NB + i;
-      const int byte = q * 1024 + lane * 16, row = byte / RB, slot = (byte % RB) / 16;
+      const int byte = q * 1024 + ln * 16, row = byte / RB, slot = (byte % RB) / 16;
       const int c = slot ^ ((row / RPB) & (CPR - 1));
       lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)c * 16u,
                 lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
@@ -206,16 +215,21 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   const int64_t send = ((a.token0 + a.n_tokens + 63) & ~(int64_t)63) - a.token0;
   // source token i lands in slot token token0 + i: lane l of a source tile
   // writes destination lane (token0 + l) % 64 of its tile or of the next
-  const int ol = (int)(a.token0 & 63) + lane;
-  const uint32_t lofs = (uint32_t)((ol >> 6) * W * 64 + (ol & 63));
   // word 0 of this lane's destination token for source tile tl (contiguous
   // slot: a uniform tile offset plus the lane's; paged: through the block
   // table), nullptr when the lane writes nothing
   auto dst_of = [&](int tl) __attribute__((always_inline)) -> uint32_t * {
-    const int64_t st = (int64_t)tl * 64 + lane;
-    if (st >= send) return nullptr;
-    if constexpr (!PG) return oslot + ((a.token0 >> 6) + tl) * (int64_t)W * 64 + lofs;
-    else return page_token(a.pg, oslot, bz, h, a.token0 + st, W);
+    const int ln = lane;
+    const int64_t st = (int64_t)tl * 64 + ln;
+    if constexpr (!PG) {
+      const int ol = (int)(a.token0 & 63) + ln;
+      const uint32_t lofs = (uint32_t)((ol >> 6) * W * 64 + (ol & 63));
+      return st >= send ? nullptr : oslot + ((a.token0 >> 6) + tl) * (int64_t)W * 64 + lofs;
+    } else {
+      // (the block lookups are wave-uniform: taken before the lane test)
+      uint32_t *p = page_token_tile(a.pg, oslot, bz, h, a.token0, tl, ln, (a.token0 + a.n_tokens - 1) >> 6, W);
+      return st >= send ? nullptr : p;
+    }
   };
   // record words of this wave: w + NW i for i < nmine
   const int nmine = W > w ? (W - 1 - w) / NW + 1 : 0;
@@ -291,9 +305,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
       }
       __syncthreads();
       auto norm_of = [&](int tok) __attribute__((always_inline)) {
-        const float4 u0 = *(const float4 *)(nrm + tok * 8), u1 = *(const float4 *)(nrm + tok * 8 + 4);
-        float t = u0.x;  // fixed order over the waves: every wave gets the same nu
-        t += u0.y; t += u0.z; t += u0.w; t += u1.x; t += u1.y; t += u1.z; t += u1.w;
+        float t = nrm[tok * 8];  // the NW waves' partials in a fixed order: every wave gets the same nu
+#pragma unroll
+        for (int i = 1; i < NW; ++i) t += nrm[tok * 8 + i];
         return __builtin_amdgcn_sqrtf(t);
       };
 #pragma unroll

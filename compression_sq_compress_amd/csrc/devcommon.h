@@ -230,6 +230,29 @@ __device__ __forceinline__ uint32_t *page_token(const PageArgs &pg, uint32_t *sl
   return slot_or_pool + (blk * pg.nh + h) * pg.block_words + (int64_t)tb * W * 64 + (dtok & 63);
 }
 
+// Word 0 of destination token token0 + 64 tile + lane for writes from one
+// source tile (wave-uniform tile; token0 may be unaligned, so the wave's
+// lanes fall into destination tiles d0 = token0 / 64 + tile and d0 + 1):
+// the two blocks are looked up once per wave through the scalar cache, the
+// second only when some lane lands in it (last_dtile: the call's last
+// destination tile).  nullptr for a block id outside [0, n_blocks).
+__device__ __forceinline__ uint32_t *page_token_tile(const PageArgs &pg, uint32_t *pool, int b, int h,
+                                                     int64_t token0, int64_t tile, int lane, int64_t last_dtile,
+                                                     int W) {
+  const SQ_CONST int32_t *row = (const SQ_CONST int32_t *)(pg.table + (int64_t)b * pg.tstride);
+  const uint32_t d0 = (uint32_t)((token0 >> 6) + tile);  // tiles of one row stay below 2^31
+  const uint32_t lb0 = d0 / (uint32_t)pg.bt, tb0 = d0 - lb0 * (uint32_t)pg.bt;
+  const uint32_t d1 = d0 + 1u, lb1 = tb0 + 1u == (uint32_t)pg.bt ? lb0 + 1u : lb0;
+  const uint32_t tb1 = tb0 + 1u == (uint32_t)pg.bt ? 0u : tb0 + 1u;
+  const int32_t blk0 = row[lb0];
+  const int32_t blk1 = (int64_t)d1 <= last_dtile ? row[lb1] : -1;
+  const bool hi = (int)(token0 & 63) + lane >= 64;
+  const int32_t blk = hi ? blk1 : blk0;
+  if (blk < 0 || blk >= pg.n_blocks) return nullptr;
+  const uint32_t tb = hi ? tb1 : tb0;
+  return pool + ((int64_t)blk * pg.nh + h) * pg.block_words + (int64_t)tb * W * 64 + ((token0 + lane) & 63);
+}
+
 // Host checks of a paged cache description for a call that touches tokens
 // [0, n_tokens) of each batch row; fills the kernels' PageArgs.
 static inline sq_status check_paged(const sq_calib *c, const sq_paged *pg, int64_t n_tokens, int n_heads,

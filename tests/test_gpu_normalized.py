@@ -98,6 +98,34 @@ def test_normalized_compress_matches_oracle(torch_dev, sq, scheme, cfgname, head
         assert tot["flips"] <= max(3, tot["band"] // 5)
 
 
+def test_normalized_compress_bf16_head_dim_32(torch_dev, sq):
+    """Normalised SpectralQuant heads of head_dim 32 with bf16 input: the grid
+    kernel's normalised instance with two waves, whose per-token norm sums
+    the partials of those two waves only.  The input is rounded to bf16 first
+    and the oracle quantises the same rounded vectors; 300 tokens leave a
+    ragged last tile."""
+    torch = torch_dev
+    cfg = wl.CONFIGS["tiny"]
+    heads = [(0, 0), (1, 2), (2, 3)]
+    T = 300
+    _case(f"compress norm tiny bf16 T={T}")
+    kcal, vcal, kors, vors = _norm_handles(sq, cfg, heads, 3.0)
+    for which, cal, ors in (("k", kcal, kors), ("v", vcal, vors)):
+        xd = torch.from_numpy(H.data_block(cfg, heads, which, T)[None]).cuda().to(torch.bfloat16)
+        x = xd.float().cpu().numpy()[0].astype(np.float64)
+        packed = torch.full((1, len(heads), cal.packed_head_words(T)), -1, dtype=torch.int32, device="cuda")
+        sq.sq_compress(cal, xd, packed)
+        torch.cuda.synchronize()
+        pk = packed.cpu().numpy().view(np.uint32)[0]
+        tot = dict(band=0, flips=0, nu_ulp=0)
+        for k in range(len(heads)):
+            st, _ = H.compare_compress(ors[k], pk[k], x[k], T)
+            for key in tot:
+                tot[key] += st.get(key, 0)
+        print(f"  {which}: in-band={tot['band']} flips={tot['flips']} nu-ulp={tot['nu_ulp']}", flush=True)
+        assert tot["flips"] <= max(3, tot["band"] // 5)
+
+
 @pytest.mark.parametrize("scheme,cfgname,heads,T,b", CASES, ids=IDS)
 def test_normalized_read_side_on_oracle_records(torch_dev, sq, scheme, cfgname, heads, T, b):
     """sq_scores, sq_attend, sq_dequantize (and sq_decode where it applies: QJL
