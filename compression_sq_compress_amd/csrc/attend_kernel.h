@@ -406,38 +406,22 @@ __global__ __launch_bounds__(64 * WPB) void attend_partial_kernel(AttendArgs a) 
 #pragma unroll
       for (int j = 0; j <= DEC_KW; ++j) {
         if (j <= kW) {
-          // the window's slot words, all loaded before the first table read
-          // (a scalar load waited for between two table reads would also
-          // wait for every table read in flight)
+          // every slot of the window: its slot words in one scalar load before
+          // the first table read (a scalar load waited for between two table
+          // reads would also wait for every table read in flight); unused
+          // slots read the zero entry
           const SQ_CONST uint32_t *sl = kslots + j * FS_SLOTS * 2;
-          uint32_t dsc[2 * FS_SLOTS];
-#pragma unroll
-          for (int i = 0; i < 2 * FS_SLOTS; ++i) dsc[i] = sl[i];
-          // the first half of the slots always (an unused slot reads the zero
-          // entry), the second half when the window uses it
-          const bool more = kscnt[j] > (uint32_t)(FS_SLOTS / 2);
           float e[FS_SLOTS][GQ];
-          auto slot = [&](int u) __attribute__((always_inline)) {
-            const uint32_t d0 = dsc[2 * u], d1 = dsc[2 * u + 1];
+#pragma unroll
+          for (int u = 0; u < FS_SLOTS; ++u) {
+            const uint32_t d0 = sl[2 * u], d1 = sl[2 * u + 1];
             const uint32_t win = __builtin_amdgcn_alignbit(kw[j + 1], kw[j], d0);  // (shift = d0 mod 32)
             entry((win & d1) | ((d0 >> 5) + (uint32_t)a.lds_ktab), e[u]);
-          };
-#pragma unroll
-          for (int u = 0; u < FS_SLOTS / 2; ++u) slot(u);
-          if (more) {
-#pragma unroll
-            for (int u = FS_SLOTS / 2; u < FS_SLOTS; ++u) slot(u);
           }
 #pragma unroll
-          for (int u = 0; u < FS_SLOTS / 2; ++u)
+          for (int u = 0; u < FS_SLOTS; ++u)
 #pragma unroll
             for (int g = 0; g < GQ; ++g) s4[g] += e[u][g];
-          if (more) {
-#pragma unroll
-            for (int u = FS_SLOTS / 2; u < FS_SLOTS; ++u)
-#pragma unroll
-              for (int g = 0; g < GQ; ++g) s4[g] += e[u][g];
-          }
         }
       }
       float gm = 0.0f;
