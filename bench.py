@@ -42,6 +42,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_kernel_decode_traffic.md")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "decode_kernels_shader_counters.md")
+CLOCK_GHZ = 2.4                 # MI355X peak engine clock, published
+N_SIMDS = 256 * 4               # 256 CUs x 4 SIMDs
 
 
 def parse():
@@ -87,6 +90,29 @@ def measured_traffic(kernel: str = "compress"):
     if not m_src or not m_b or m_src.group(1) != kernel_source_digest():
         return None
     return float(m_b.group(1))
+
+
+def measured_counters_per_tile(column: int = 0):
+    """Per-tile shader counters of one kernel column (0: the compress kernel)
+    from the committed counter summary, or None when it is missing or was
+    taken on other kernel sources."""
+    try:
+        txt = open(COUNTER_FILE).read()
+    except OSError:
+        return None
+    m_src = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]{16})", txt)
+    if not m_src or m_src.group(1) != kernel_source_digest():
+        return None
+    out = {}
+    for line in txt.splitlines():
+        m = re.match(r"\|\s*(SQ_[A-Z_]+)\s*\|(.*)\|\s*$", line)
+        if m:
+            cells = [c.strip() for c in m.group(2).split("|")]
+            try:
+                out[m.group(1)] = float(cells[column])
+            except (IndexError, ValueError):
+                pass
+    return out or None
 
 
 def cpu_model() -> str:
@@ -437,6 +463,16 @@ def main():
         "compress_GBps": gbps(bytes_ck + bytes_cv, comp_ms),
         "compress_mfma_frac_alg": flops_comp / (comp_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         "compress_mfma_frac_issued": 3 * flops_comp / (comp_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        # the third roofline of the compress kernel, VALU issue: its non-MFMA
+        # VALU instructions per 64-token tile (committed counter summary, same
+        # sources) x 4 cycles per wave64 instruction, over the SIMD cycles of
+        # a launch at the peak clock; null when the summary is stale
+        "compress_valu_frac": (None if not (cc := measured_counters_per_tile(0)) else
+                               (cc["SQ_INSTS_VALU"] - cc["SQ_INSTS_MFMA"]) * 4 * (n_vec / 64) /
+                               (N_SIMDS * comp_launch_ms * 1e-3 * CLOCK_GHZ * 1e9)),
+        "compress_mfma_busy_frac": (None if not cc else
+                                    cc["SQ_VALU_MFMA_BUSY_CYCLES"] * (n_vec / 64) /
+                                    (N_SIMDS * comp_launch_ms * 1e-3 * CLOCK_GHZ * 1e9)),
         "score_GBps": gbps(bytes_sc, ms_sc),
         "score_hbm_frac": gbps(bytes_sc, ms_sc) / HBM_PEAK_GBPS,
         "score_packedK_GBps": gbps(n_vec * 4 * Wk, ms_sc),
