@@ -23,6 +23,15 @@ BAND = 1e-4
 QJL_BAND = 1e-3
 RTOL = 1e-3
 
+# A head_dim-64 shape, not one of the pages' five workloads: only here do the
+# kernels' 64-wide instances run (the register compress kernel at d = 64, one
+# 64-coordinate attend block, the fused decode with NP = 1).  The spectra are
+# the Llama-shaped families evaluated at d = 64; 2 layers x 4 KV heads, 16
+# query heads (groups of 4), bf16 data, 512-token calibration sets.
+HD64 = wl.Config("hd64", 5, 64, 2, 4, 16, (700,), 1, "bf16", 512, (3.0,), 1,
+                 "keys128", "values128", 170.0, 3.0)
+wl.CONFIGS.setdefault("hd64", HD64)
+
 
 def calib_inputs(cfg, heads, which, seed=wl.DEFAULT_SEED, n_tokens=None):
     """heads: list of (layer, kv_head).  Returns (samples [H][n][d], gauss or None)."""

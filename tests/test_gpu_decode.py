@@ -44,6 +44,7 @@ CASES = [
     ("qwen14b-2.5b", "qwen14b", [(l, h) for l in (0, 47) for h in range(8)], 512, 2.5),
     ("qwen14b-3.5b", "qwen14b", [(l, h) for l in (1,) for h in range(8)], 1024, 3.5),
     ("gemma9b", "gemma9b", [(l, h) for l in (0,) for h in range(4)], 700, 3.0),
+    ("hd64", "hd64", [(l, h) for l in range(2) for h in range(4)], 700, 3.0),
 ]
 
 

@@ -61,6 +61,7 @@ CASES = [
     ("qwen14b-2.5b", "qwen14b", [(l, h) for l in (0, 47) for h in range(8)], 512, 2.5),
     ("qwen14b-3.5b", "qwen14b", [(l, h) for l in (1,) for h in range(8)], 1024, 3.5),
     ("gemma9b", "gemma9b", [(l, h) for l in (0,) for h in range(4)], 700, 3.0),
+    ("hd64", "hd64", [(l, h) for l in range(2) for h in range(4)], 700, 3.0),
 ]
 
 
@@ -115,6 +116,8 @@ def test_scores_attend_dequant_on_oracle_records(torch_dev, sq, name, cfgname, h
           f"{plan.attend_waves}, blocks {plan.attend_blocks}, chunks {plan.attend_chunks}", flush=True)
     if cfg.head_dim == 256:
         assert plan.score_passes >= 2 and plan.attend_blocks == 4
+    if cfg.head_dim == 64:
+        assert plan.attend_blocks == 1
     xk = H.data_block(cfg, heads, "k", T)
     xv = H.data_block(cfg, heads, "v", T)
     slot_k = kcal.packed_head_words(T)
