@@ -67,6 +67,7 @@ CASES = [
     ("tq", "tiny", [(0, 0), (2, 3)], 256, 3),
     ("norm", "llama8b", [(0, h) for h in range(4)], 700, 3.0),
     ("norm", "gemma9b", [(0, 2), (0, 5)], 400, 3.0),
+    ("norm", "hd64", [(0, 1), (1, 2)], 300, 3.0),
 ]
 IDS = [f"{c[0]}-{c[1]}" for c in CASES]
 

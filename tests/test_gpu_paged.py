@@ -56,6 +56,7 @@ PIECES = [700, 1, 1, 37, 1, 160, 100]   # 1000 tokens in unaligned pieces
     ("llama8b", 3.0, 4, "tree"),
     ("qwen14b", 2.5, 3, "grid"),
     ("gemma9b", 3.0, 2, "grid"),
+    ("hd64", 3.0, 2, "grid"),
 ])
 def test_paged_append_and_decode_match_contiguous(torch_dev, sq, cfgname, budget, bt, quantiser, monkeypatch):
     torch = torch_dev
