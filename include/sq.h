@@ -373,9 +373,11 @@ sq_status sq_attend(const sq_calib *vc, int first_head, int calib_batch_stride,
  * workspace DEVICE, ws_bytes >= sq_attend_workspace_bytes(batch, n_q_heads,
  *          n_tokens, head_dim).
  * out      DEVICE float [batch][n_q_heads][head_dim].  n_tokens == 0 writes zeros.
- * Errors: as sq_scores and sq_attend; SQ_ERR_UNSUPPORTED when a key record
- * exceeds 32 words or the score tables do not fit the LDS (use sq_scores +
- * sq_attend then).
+ * Errors: as sq_scores and sq_attend; SQ_ERR_UNSUPPORTED (nothing enqueued;
+ * use sq_scores + sq_attend then) when a key record exceeds 32 words, a key
+ * head has more than 16 QJL bits (e.g. the TurboQuant-style keys, m = d) or a
+ * record word in which more than 8 code groups start, the query group is
+ * larger than 8, or the score tables and staging do not fit the LDS.
  */
 sq_status sq_decode(const sq_calib *kc, const sq_calib *vc, int first_head,
                     int calib_batch_stride, int batch, int n_q_heads, int n_kv_heads,
