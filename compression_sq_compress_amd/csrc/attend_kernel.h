@@ -26,11 +26,17 @@ namespace sq {
 // (batch, query head) combines the chunks in order (no atomics,
 // deterministic) and un-rotates once: o = R_v^T o_rot / L.
 
-// Tokens per chunk: 2048 when that still gives about two waves per CU or
-// more (fewer partials to combine and table loads), else 1024.  A function of
-// (batch, query heads, tokens) only, so the workspace size follows it.
+// Tokens per chunk: the largest of 2048, 1024, ..., 128 that still gives
+// batch x query heads x chunks >= 4096 partials (about two waves per CU or
+// more; longer chunks mean fewer partials to combine and fewer table loads),
+// else 64 (one tile: short caches are spread over as many waves as they
+// have tiles).  A function of (batch, query heads, tokens) only, so the
+// workspace size follows it.
 static inline int64_t attend_chunk_tokens(int batch, int n_q_heads, int64_t n_tokens) {
-  return (int64_t)batch * n_q_heads * (n_tokens / 2048) >= 4096 ? 2048 : 1024;
+  const int64_t bh = (int64_t)batch * n_q_heads;
+  for (int64_t ct = 2048; ct >= 128; ct /= 2)
+    if (bh * ((n_tokens + ct - 1) / ct) >= 4096) return ct;
+  return 64;
 }
 static constexpr int ATT_RS = 68;  // staged record row stride (words): 16-byte aligned, bank-spread
 static constexpr int ATT_PS = 68;  // weight row stride (words): rows of different heads in different banks

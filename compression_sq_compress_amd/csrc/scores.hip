@@ -82,6 +82,7 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
   const int ch = a.first_head + b * a.cbs + hkv;
   const SQ_CONST DevHead *hd = cptr<DevHead>(a.heads) + ch;
   const int d = hd->d, d_eff = hd->d_eff, m = hd->m, W = hd->W, code_bits = hd->code_bits;
+  const bool knorm = hd->normalized != 0;  // (read once: the loop's barriers keep loads in place)
   const int KS = a.ks, TS = a.ts, G = a.G;
   const int qp0 = a.pass * KS * SC_QMAX;
   const int nq_pass = min(hd->n_quads - qp0, KS * SC_QMAX);
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
           }
         }
       }
-      if (hd->normalized) {  // normalised keys: s = nu * (...), each partial scaled (linear)
+      if (knorm) {  // normalised keys: s = nu * (...), each partial scaled (linear)
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
           const uint32_t tl = tile_lds + (u * NS + t) * SLOTB;

@@ -183,10 +183,12 @@ def test_error_paths():
 
 
 def test_workspace_size_formula():
-    # [batch][q head][chunk][d + 2] fp32; chunks of 2048 tokens when batch * q heads *
-    # (tokens / 2048) >= 4096, else 1024
-    assert sq.sq_attend_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * 16 * 130 * 4
-    assert sq.sq_attend_workspace_bytes(1, 32, 32768, 128) == 32 * 32 * 130 * 4
+    # [batch][q head][chunk][d + 2] fp32; chunks of the largest of 2048, 1024,
+    # ..., 128 tokens with batch * q heads * chunks >= 4096, else 64
+    assert sq.sq_attend_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * 16 * 130 * 4  # 2048
+    assert sq.sq_attend_workspace_bytes(1, 32, 32768, 128) == 32 * 128 * 130 * 4       # 256
+    assert sq.sq_attend_workspace_bytes(48, 40, 512, 128) == 48 * 40 * 4 * 130 * 4     # 128
+    assert sq.sq_attend_workspace_bytes(1, 32, 2048, 128) == 32 * 32 * 130 * 4         # 64
     assert sq.sq_attend_workspace_bytes(1, 4, 1, 32) == 4 * 1 * 34 * 4
     assert sq.sq_attend_workspace_bytes(1, 4, 0, 32) == 0
 
