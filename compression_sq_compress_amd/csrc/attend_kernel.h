@@ -167,28 +167,56 @@ __device__ __forceinline__ void build_score_tables(const AttendArgs &a, int b, i
     const bool qj = (fw >> 4) & 1u;
     const uint32_t e0 = fw >> 8;
     const int first = (int)(bw & 4095u), cnt = (int)((bw >> 12) & 255u);
-    for (int k = lane; k < (GQ << width); k += 64) {
-      const int v = k / GQ, g = k - v * GQ;
-      float e = 0.0f;
-      if (g < G) {
-        if (qj) {
+    if (qj) {
+      for (int k = lane; k < (GQ << width); k += 64) {
+        const int v = k / GQ, g = k - v * GQ;
+        float e = 0.0f;
+        if (g < G)
           for (int c = 0; c < cnt; ++c) {
             const float w = wq[g * km + first + c];
             e += ((v >> c) & 1) ? w : -w;
           }
-        } else {
-          int sh = 0;
-          for (int c = 0; c < cnt; ++c) {
-            const DevCoord cd = load_coord(kc + first + c);
-            if (cd.width) {
-              const int code = (v >> sh) & ((1 << cd.width) - 1);
-              e = fmaf(qt[g * d + first + c], kcent[cd.cent_base + code], e);
-              sh += cd.width;
-            }
+        tab[(size_t)(e0 + v) * GQ + g] = e;
+      }
+      continue;
+    }
+    // code group: a lane per entry v and every head at once; the centroids of
+    // the group's first CMAX coordinates are loaded together (one load each
+    // for all heads), then each head's sum runs over the coordinates in order
+    constexpr int CMAX = 8;
+    for (int v = lane; v < (1 << width); v += 64) {
+      float cv[CMAX];
+      int sh = 0;
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c) {
+        cv[c] = 0.0f;
+        if (c < cnt) {
+          const DevCoord cd = load_coord(kc + first + c);
+          if (cd.width) {
+            cv[c] = kcent[cd.cent_base + ((v >> sh) & ((1 << cd.width) - 1))];
+            sh += cd.width;
           }
         }
       }
-      tab[(size_t)(e0 + v) * GQ + g] = e;
+      float e[GQ];
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) e[g] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CMAX; ++c)
+        if (c < cnt && kc[first + c].width)
+#pragma unroll
+          for (int g = 0; g < G; ++g) e[g] = fmaf(qt[g * d + first + c], cv[c], e[g]);
+      for (int c = CMAX; c < cnt; ++c) {  // (longer groups: zero-width coordinates among the fields)
+        const DevCoord cd = load_coord(kc + first + c);
+        if (cd.width) {
+          const float x = kcent[cd.cent_base + ((v >> sh) & ((1 << cd.width) - 1))];
+          sh += cd.width;
+#pragma unroll
+          for (int g = 0; g < G; ++g) e[g] = fmaf(qt[g * d + first + c], x, e[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) tab[(size_t)(e0 + v) * GQ + g] = e[g];
     }
   }
   if (threadIdx.x < GQ) tab[(size_t)kh->n_fent * GQ + threadIdx.x] = 0.0f;  // the zero entry of unused slots
