@@ -386,7 +386,11 @@ def paged(block_table, block_tiles: int, n_blocks: int) -> Paged:
     import torch
     assert block_table.is_cuda and block_table.dtype == torch.int32 and block_table.dim() == 2
     assert block_table.stride(1) == 1
-    return Paged(block_table.data_ptr(), block_table.stride(0), int(block_tiles), int(n_blocks))
+    pg = Paged(block_table.data_ptr(), block_table.stride(0), int(block_tiles), int(n_blocks))
+    # the description holds the table's address only: keep the tensor alive
+    # with it, or the caching allocator may hand that memory to another tensor
+    pg._table = block_table
+    return pg
 
 
 def sq_paged_block_words(cal: Calibration, block_tiles: int) -> int:

@@ -132,6 +132,66 @@ def test_paged_append_and_decode_match_contiguous(torch_dev, sq, cfgname, budget
     np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("cfgname,scheme", [("llama8b", "norm"), ("hd64", "norm"), ("llama8b", "tq")])
+def test_paged_normalized_append_matches_oracle(torch_dev, sq, cfgname, scheme):
+    """Normalised records (the normalised SpectralQuant variant, and the
+    TurboQuant-style keys and values) appended in unaligned pieces to a paged
+    pool go through the general compress kernel's paged instances; the
+    gathered records are compared with the oracle's under the acceptance
+    rules (vector norms included)."""
+    import oracle
+    torch = torch_dev
+    cfg = wl.CONFIGS[cfgname]
+    B, Hkv, bt = 2, 2, 3
+    heads = [(0, h) for h in range(Hkv)]
+    T = sum(PIECES)
+    d = cfg.head_dim
+    _case(f"paged normalised {scheme} {cfgname} bt={bt} T={T}")
+    if scheme == "norm":
+        Xk, Gk = H.calib_inputs(cfg, heads, "k")
+        Xv, _ = H.calib_inputs(cfg, heads, "v")
+        kcal = sq.sq_calibrate(Xk, 3.0, 1, Gk, normalize=True).upload()
+        vcal = sq.sq_calibrate(Xv, 3.0, 0, None, normalize=True).upload()
+        kors = [oracle.calibrate(Xk[k], 3.0, 1, Gk[k], normalize=True) for k in range(Hkv)]
+        vors = [oracle.calibrate(Xv[k], 3.0, 0, None, normalize=True) for k in range(Hkv)]
+    else:
+        rot = np.stack([wl.tq_rotation(cfg, l, h) for l, h in heads]).astype(np.float32)
+        sk = np.stack([wl.tq_qjl(cfg, l, h) for l, h in heads]).astype(np.float32)
+        kcal = sq.sq_calibrate_tq(rot, 3, True, sk).upload()
+        vcal = sq.sq_calibrate_tq(rot, 3, False).upload()
+        kors = [oracle.tq_calibration(rot[k].astype(np.float64), sk[k], 3, True) for k in range(Hkv)]
+        vors = [oracle.tq_calibration(rot[k].astype(np.float64), None, 3, False) for k in range(Hkv)]
+    n_tiles = (T + 63) // 64
+    nlb = (n_tiles + bt - 1) // bt
+    n_blocks = B * nlb + 3
+    table = np.random.default_rng(5).permutation(n_blocks)[:B * nlb].reshape(B, nlb).astype(np.int32)
+    table_d = torch.from_numpy(table).cuda()
+    pg = sq.paged(table_d, bt, n_blocks)
+    for which, cal, ors in (("k", kcal, kors), ("v", vcal, vors)):
+        x = np.stack([np.stack([wl.kv_block(cfg, 0, h, which, T, "data", batch_index=b) for h in range(Hkv)])
+                      for b in range(B)])
+        X = torch.from_numpy(x.astype(np.float32)).cuda().to(torch.bfloat16)
+        xr = X.float().cpu().numpy().astype(np.float64)  # the bf16 values both sides quantise
+        bw = sq.sq_paged_block_words(cal, bt)
+        pool = torch.full((n_blocks * Hkv * bw,), -1, dtype=torch.int32, device="cuda")
+        t0 = 0
+        for n in PIECES:
+            sq.sq_compress_append_paged(cal, X[:, :, t0:t0 + n, :], pool, pg, t0)
+            t0 += n
+        torch.cuda.synchronize()
+        p = pool.cpu().numpy().view(np.uint32)
+        tot = dict(band=0, flips=0)
+        for h in range(Hkv):
+            Wh = cal.info(h).record_words
+            g = _gather(p, table, B, Hkv, n_tiles, bt, bw, Wh, n_tiles * Wh * 64)
+            for b in range(B):
+                st, _ = H.compare_compress(ors[h], g[b, h], xr[b, h], T)
+                for key in tot:
+                    tot[key] += st[key]
+        print(f"  {which}: in-band={tot['band']} flips={tot['flips']}", flush=True)
+        assert tot["flips"] <= max(3, tot["band"] // 5)
+
+
 def test_paged_argument_errors_and_bad_block_ids(torch_dev, sq):
     torch = torch_dev
     cfg = wl.CONFIGS["llama8b"]
