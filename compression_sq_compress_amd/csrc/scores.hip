@@ -34,6 +34,14 @@ constexpr int SC_LOADERS = 3;  // waves issuing the record loads
 constexpr int SC_BLOCK = 64 * (SC_WAVES + SC_LOADERS);
 // quads held in registers per consumer wave (4 or 8 query heads per MFMA row set)
 __host__ __device__ constexpr int sc_qmax(int gr) { return gr == 1 ? 9 : 5; }
+// QJL term by table lookup for sketches of at most SC_QTAB_MAX_M rows: the
+// sign bits split into a chunk of the first min(m, 8) bits and one of the
+// rest, and each chunk gets a table over its bit patterns holding, per query
+// row, sum_j w_j (2 z_j - 1) over the chunk's rows.  Entries of both chunks:
+constexpr int SC_QTAB_MAX_M = 16;
+__host__ __device__ constexpr int sc_qtab_entries(int m) {
+  return m <= 0 || m > SC_QTAB_MAX_M ? 0 : (1 << (m < 8 ? m : 8)) + (m > 8 ? (1 << (m - 8)) : 0);
+}
 
 struct ScoresArgs {
   const DevHead *heads;
@@ -50,7 +58,7 @@ struct ScoresArgs {
   int ks, ts;             // wave groups over quads, tile streams (ks * ts = SC_WAVES)
   int pass;               // quads [pass * ks * sc_qmax(GR), ...) of every head
   int dma16;              // records 16-byte aligned: 1 KB direct-to-LDS loads
-  int lds_lut, lds_qt, lds_wq, lds_slot, lds_pbuf;  // byte offsets
+  int lds_lut, lds_qt, lds_wq, lds_qtab, lds_slot, lds_pbuf;  // byte offsets
 };
 
 // How sq_scores launches for a given call (see plan_scores).
@@ -175,6 +183,28 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
     }
   }
   __syncthreads();  // wq complete
+  // QJL tables [entry][GP] (chunk 0's 2^min(m,8) entries, then chunk 1's)
+  const bool qtab = m > 0 && m <= SC_QTAB_MAX_M;
+  const int qn0 = 1 << min(m, 8);
+  const float *qtb = (const float *)(sm + a.lds_qtab);
+  if (qtab) {
+    if (consumer) {
+      float *qo = (float *)(sm + a.lds_qtab);
+      const int ne = sc_qtab_entries(m);
+      for (int k = ct; k < ne * GP; k += 64 * SC_WAVES) {
+        const int e = k / GP, g = k - e * GP;
+        const bool c1 = e >= qn0;
+        const int z = c1 ? e - qn0 : e, j0 = c1 ? 8 : 0, nb = c1 ? m - 8 : min(m, 8);
+        float acc = 0.0f;
+        for (int j = 0; j < nb; ++j) {
+          const float wv = wq[(j0 + j) * GP + g];
+          acc += ((z >> j) & 1) ? wv : -wv;
+        }
+        qo[k] = acc;
+      }
+    }
+    __syncthreads();
+  }
   float *pbuf = (float *)(sm + a.lds_pbuf);
 
   if (loader) {
@@ -196,14 +226,12 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
   const int nqb = nq_pass / KS, nqr = nq_pass - nqb * KS;
   const int nq = nqb + (kk < nqr ? 1 : 0);
   const int q0 = qp0 + kk * nqb + min(kk, nqr);
-  // QJL term: wave kk adds it for the query heads (rows) r = kk, kk + KS, ..
-  // to its own partial sum, so that every row gets it exactly once
+  // QJL term: the wave that sums the partials of query head (row) r =
+  // kk + j KS adds it for that row, so that every row gets it exactly once:
+  // from the tables (qv, carried to the reduction one super-step later), or
+  // for longer sketches bit by bit into the wave's own partial sum
   const bool qjl = m > 0 && a.pass == 0 && kk < min(G, GP);
-  const bool qjl_fast = qjl && KS >= GP && m <= 8;  // one row per wave, weights in scalars
-  uint32_t qw[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    qw[j] = qjl_fast && j < m ? __float_as_uint(wq[j * GP + kk]) : 0u;  // (vector registers)
+  const bool qjl_tab = qjl && qtab;
   const SQ_CONST uint32_t *sch = cptr<uint32_t>(a.blob + hd->off_sched);
   // Every wave runs SC_QMAX quads; those past its share are empty (mask 0,
   // A operands 0) so that the quads form one straight-line block.  Table
@@ -231,7 +259,7 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
       const int pos = (int)(pw & 0xFFFFu) - 3, wd = (int)(pw >> 16);
       hsh[2 * qi + hh] = to_vgpr((uint32_t)(pos - 32 * j) & 63u);
       hmk[2 * qi + hh] = to_vgpr(real ? ((1u << wd) - 1u) << 3 : 0u);
-      hlut[2 * qi + hh] = (LG ? 0u : (uint32_t)a.lds_lut) + e[2 + hh] * 8u;
+      hlut[2 * qi + hh] = to_vgpr((LG ? 0u : (uint32_t)a.lds_lut) + e[2 + hh] * 8u);
     }
     wad[qi] = tile_lds + (uint32_t)j * 256u;
     const uint32_t s01 = e[4], s23 = e[5];
@@ -255,6 +283,12 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
   const uint2 *glut = (const uint2 *)(a.blob + hd->off_plut);
   const int zsh = code_bits & 31;
 
+  // QJL terms of the rows this wave sums, per tile of the super-step
+  float qv[NS][GP];
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int j = 0; j < GP; ++j) qv[t][j] = 0.0f;
   // sum the wave group's partials of super-step sp (fixed order) and store
   auto reduce_k = [&](int sp, auto ksc) __attribute__((always_inline)) {
     constexpr int K = decltype(ksc)::value;
@@ -274,6 +308,7 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
         float v = pv[0];
 #pragma unroll
         for (int k2 = 1; k2 < K; ++k2) v += pv[k2];
+        if (qjl_tab) v += qv[t][row0 / K];
         if (row < G && tok < a.n_tokens) {
           float *o = a.scores + ((int64_t)b * a.n_q_heads + (int64_t)hkv * G + row) * a.n_tokens + tok;
           if (a.pass) __hip_atomic_fetch_add(o, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // one add per pass
@@ -357,43 +392,50 @@ __global__ __launch_bounds__(SC_BLOCK) void scores_kernel(ScoresArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the stages in this order
       }
-      if (qjl) {  // + gamma * sum_j w_j (2 z_j - 1), w already scaled by sqrt(pi/2)/m
+      if (qjl_tab) {  // gamma * sum_j w_j (2 z_j - 1) per row (w scaled by sqrt(pi/2)/m), times nu if normalised
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          const uint32_t tl = tile_lds + (u * NS + t) * SLOTB;
+          const uint32_t wl = *(const uint32_t *)(sm + tl + (W - 1) * 256u);
+          float gm = half_bits_to_f32(wl >> 16);
+          if (knorm) gm *= half_bits_to_f32(wl & 0xFFFFu);
+          const uint32_t ad = tl + (code_bits >> 5) * 256u;
+          const uint32_t z = __builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
+                                                       *(const uint32_t *)(sm + ad), zsh);
+          const float *t0 = qtb + (z & (uint32_t)(qn0 - 1)) * GP;
+          const float *t1 = qtb + (qn0 + ((z >> 8) & ((1u << max(m - 8, 0)) - 1u))) * GP;  // used when m > 8 (qn0 = 256)
+#pragma unroll
+          for (int j = 0; j < GP; ++j) {
+            const int row = kk + j * KS;
+            if (row < min(G, GP)) {
+              float v = t0[row];
+              if (m > 8) v += t1[row];
+              qv[t][j] = gm * v;
+            }
+          }
+        }
+      } else if (qjl) {  // longer sketches: + gamma * sum_j w_j (2 z_j - 1) into this wave's partial
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
           const uint32_t tl = tile_lds + (u * NS + t) * SLOTB;
           const float gm = half_bits_to_f32(*(const uint32_t *)(sm + tl + (W - 1) * 256u) >> 16);
-          if (qjl_fast) {
-            const uint32_t ad = tl + (code_bits >> 5) * 256u;
-            const uint32_t nz = ~__builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
-                                                          *(const uint32_t *)(sm + ad), zsh);
+          for (int row = kk; row < min(G, GP); row += KS) {
             float qa = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)  // +w_j where z_j = 1, -w_j where z_j = 0 (w_j = 0 past m)
-              qa += __uint_as_float(qw[j] ^ ((nz << (31 - j)) & 0x80000000u));
+            for (int j0 = 0; j0 < m; j0 += 32) {
+              const uint32_t ad = tl + ((code_bits + j0) >> 5) * 256u;
+              const uint32_t z = __builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
+                                                           *(const uint32_t *)(sm + ad), zsh);
+              const int jn = min(32, m - j0);
+              for (int j = 0; j < jn; ++j) {
+                const float wv = wq[(j0 + j) * GP + row];
+                qa += ((z >> j) & 1u) ? wv : -wv;
+              }
+            }
 #pragma unroll
             for (int g = 0; g < GR; ++g)
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr)
-                if (4 * g + rr == kk) acc[t][g][rr] = fmaf(gm, qa, acc[t][g][rr]);
-          } else {
-            for (int row = kk; row < min(G, GP); row += KS) {
-              float qa = 0.0f;
-              for (int j0 = 0; j0 < m; j0 += 32) {
-                const uint32_t ad = tl + ((code_bits + j0) >> 5) * 256u;
-                const uint32_t z = __builtin_amdgcn_alignbit(*(const uint32_t *)(sm + ad + 256),
-                                                             *(const uint32_t *)(sm + ad), zsh);
-                const int jn = min(32, m - j0);
-                for (int j = 0; j < jn; ++j) {
-                  const float wv = wq[(j0 + j) * GP + row];
-                  qa += ((z >> j) & 1u) ? wv : -wv;
-                }
-              }
-#pragma unroll
-              for (int g = 0; g < GR; ++g)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                  if (4 * g + rr == row) acc[t][g][rr] = fmaf(gm, qa, acc[t][g][rr]);
-            }
+                if (4 * g + rr == row) acc[t][g][rr] = fmaf(gm, qa, acc[t][g][rr]);
           }
         }
       }
@@ -459,7 +501,7 @@ sq_status plan_scores(const sq_calib *kc, int first_head, int calib_batch_stride
                       int n_kv_heads, int64_t n_tokens, ScorePlan &P) {
   const int G = n_q_heads / n_kv_heads;
   const int d = kc->heads[first_head].d;
-  int max_q = 1, max_plut = 1, max_m = 0, max_W = 1;
+  int max_q = 1, max_plut = 1, max_m = 0, max_W = 1, max_qe = 0;
   for (int bb = 0; bb < std::max(1, batch); ++bb) {
     for (int h = 0; h < n_kv_heads; ++h) {
       const DevHead &D = kc->host_desc[first_head + bb * calib_batch_stride + h];
@@ -467,6 +509,7 @@ sq_status plan_scores(const sq_calib *kc, int first_head, int calib_batch_stride
       max_q = std::max(max_q, D.n_quads);
       max_plut = std::max(max_plut, D.n_plut);
       max_m = std::max(max_m, D.m);
+      max_qe = std::max(max_qe, sc_qtab_entries(D.m));
       max_W = std::max(max_W, D.W);
     }
     if (calib_batch_stride == 0) break;
@@ -492,6 +535,7 @@ sq_status plan_scores(const sq_calib *kc, int first_head, int calib_batch_stride
     a.lds_qt = (int)off;   off += (size_t)G * d * 4;
     off = (off + 15) & ~(size_t)15;
     a.lds_wq = (int)off;   off += (size_t)std::max(1, max_m) * GP * 4;
+    a.lds_qtab = (int)off; off += (size_t)max_qe * GP * 4;
     off = (off + 1023) & ~(size_t)1023;
     a.lds_slot = (int)off; off += (size_t)R * P.slotb;
     a.lds_pbuf = (int)off; off += (size_t)2 * (P.slotb == 8192 ? 2 : 1) * SC_WAVES * GP * 64 * 4;  // parity x slots per barrier
