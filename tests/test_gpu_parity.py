@@ -176,6 +176,55 @@ def test_scores_attend_dequant_on_oracle_records(torch_dev, sq, name, cfgname, h
         H.assert_close_floor(o_gpu[k * G:(k + 1) * G], ref, floor, f"attend head {k}")
 
 
+@pytest.mark.parametrize("qjl_bits", [2, 4, 6])
+def test_scores_qjl_sketch_lengths(torch_dev, sq, qjl_bits):
+    """Scores and compress with longer QJL sketches on the Llama-shaped keys
+    (d_eff 3): m = 6 and 12 take the scores kernel's sign-pattern tables (one
+    chunk, then two chunks of 8 and 4 bits), m = 18 its per-row loop; records
+    compressed on the GPU are checked against the oracle's, scores on oracle
+    records against the oracle."""
+    torch = torch_dev
+    cfg = wl.CONFIGS["llama8b"]
+    heads, T, G = [(0, 0), (0, 5)], 700, cfg.q_heads // cfg.kv_heads
+    _case(f"qjl sketch: qjl_bits={qjl_bits} T={T}")
+    X = np.stack([wl.calibration_set(cfg, l, h, "k") for l, h in heads]).astype(np.float32)
+    Gs = np.stack([wl.qjl_gaussian(cfg, l, h, "k", qjl_bits=qjl_bits) for l, h in heads])
+    kcal = sq.sq_calibrate(X, 3.0, qjl_bits, Gs)
+    ors = [oracle.calibrate(X[k], 3.0, qjl_bits, Gs[k]) for k in range(len(heads))]
+    for k, oc in enumerate(ors):
+        assert kcal.info(k).m == oc.m == qjl_bits * oc.d_eff
+    print(f"  m = {[oc.m for oc in ors]}", flush=True)
+    kcal.upload()
+    xk = H.data_block(cfg, heads, "k", T)
+    packed = _compress_gpu(torch, sq, kcal, xk[None], torch.bfloat16, T)[0]
+    for k in range(len(heads)):
+        H.compare_compress(ors[k], packed[k], xk[k], T)
+    nkv = len(heads)
+    kp = np.zeros((1, nkv, kcal.packed_head_words(T)), np.uint32)
+    rk = []
+    for k in range(nkv):
+        r = oracle.compress(ors[k], xk[k])
+        p = oracle.pack(ors[k].widths, ors[k].m, r.codes, r.z, r.gamma)
+        kp[0, k, :len(p)] = p
+        rk.append(r)
+    q = wl.queries(cfg, 1, nkv * G)
+    qd = _to_dev(torch, q, torch.bfloat16)
+    kpd = torch.from_numpy(kp.view(np.int32)).cuda()
+    scores = torch.zeros((1, nkv * G, T), dtype=torch.float32, device="cuda")
+    sq.sq_scores(kcal, qd, kpd, T, scores, nkv)
+    torch.cuda.synchronize()
+    s_gpu = scores.cpu().numpy()[0]
+    worst = 0.0
+    for k in range(nkv):
+        oc, r = ors[k], rk[k]
+        xt = oracle.dequantize(oc, r.codes, r.z, r.gamma)
+        qg = q[0, k * G:(k + 1) * G].astype(np.float64)
+        ref = oracle.scores_rotated(oc, qg, r.codes, r.z, r.gamma)
+        worst = max(worst, H.assert_close_floor(s_gpu[k * G:(k + 1) * G], ref,
+                                                H.score_floor(oc, qg, xt), f"scores head {k}"))
+    print(f"  scores worst err/tol = {worst:.3g}", flush=True)
+
+
 @pytest.mark.parametrize("name,cfgname,heads,T,budget", CASES, ids=[c[0] for c in CASES])
 def test_end_to_end(torch_dev, sq, name, cfgname, heads, T, budget):
     """GPU compress -> GPU scores -> GPU attend against the all-oracle pipeline;
