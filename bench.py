@@ -457,7 +457,9 @@ def main():
         "config": {"workload": f"decode: {B} seqs x {T} tokens, {Hq} q / {Hkv} KV heads, hd{d}, "
                                f"bf16 K/V, 3 bits/coord, 1 QJL bit per key signal dim",
                    "batch": B, "tokens": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
-                   "avg_bits": 3.0, "record_words_k": Wk, "record_words_v": Wv},
+                   "avg_bits": 3.0, "record_words_k": Wk, "record_words_v": Wv,
+                   "step": "sq_compress of every K and V vector of the cache (the metric's compress leg, "
+                           "not a serving step), then sq_scores and sq_attend over it"},
         "kernels_ms": {"compress_k": ms_ck, "compress_v": ms_cv, "scores": ms_sc, "attend": ms_at},
         "compress_vectors_per_s": 2 * n_vec / (comp_ms * 1e-3),
         "compress_GBps": gbps(bytes_ck + bytes_cv, comp_ms),
