@@ -44,7 +44,8 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_kernel_decode_traffic.md")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "decode_kernels_shader_counters.md")
 CLOCK_GHZ = 2.4                 # MI355X peak engine clock, published
-N_SIMDS = 256 * 4               # 256 CUs x 4 SIMDs
+N_CUS = 256
+N_SIMDS = N_CUS * 4             # 256 CUs x 4 SIMDs
 
 
 def parse():
@@ -504,7 +505,12 @@ def main():
                             "achieved": gbps(bytes_sc, ms_sc), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": gbps(bytes_sc, ms_sc) / HBM_PEAK_GBPS,
                             "traffic": measured_traffic("scores"), "alg_bytes_per_launch": bytes_sc,
-                            "launch_ms": ms_sc},
+                            "launch_ms": ms_sc,
+                            # its LDS roofline: LDS-busy cycles per 64-token tile (committed counter
+                            # summary, same sources) over the CU cycles of the launch at 2.4 GHz
+                            "lds_busy_frac": (None if not (cs := measured_counters_per_tile(1)) else
+                                              cs["SQ_LDS_IDX_ACTIVE"] * (n_vec / 64) /
+                                              (N_CUS * ms_sc * 1e-3 * CLOCK_GHZ * 1e9))},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, (Xk, Gk), Xv, args.cpu_sample_seqs, T)
