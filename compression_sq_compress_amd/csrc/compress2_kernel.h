@@ -108,7 +108,11 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   // grid quantiser, per lane and register (coordinate 16 w + 4 s + r): u = y a + b,
   // its region's cells (LDS byte address) and last cell, signal-centroid base,
   // field shift; the lane's run of four fields: record word | bit shift << 8
-  float ga[4], gb[4], gcmf[4];
+  // (UQ: R rows pre-scaled by a_i, the MFMAs start at b_i and give u; ga then
+  // holds 1 / a_i for the signal residuals, 1 for a zero-width row)
+  constexpr bool UQ = GRID && !NORM;
+  float ga[4], gcmf[4];
+  f32x4 gbv = f32x4{0.f, 0.f, 0.f, 0.f};
   uint32_t gtab[4], gfs[4], gpos = 0;  // gfs: field shift | signal-centroid base << 8 (0xFFFFFF: none)
   if constexpr (GRID) {
     const uint32_t cells0 = (uint32_t)(uintptr_t)trees;
@@ -117,8 +121,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * w + 4 * s4 + r;
       const uint4 v0 = GC[2 * c], v1 = GC[2 * c + 1];
-      ga[r] = __uint_as_float(v0.x);
-      gb[r] = __uint_as_float(v0.y);
+      const float av = __uint_as_float(v0.x);
+      ga[r] = !UQ ? av : av != 0.0f ? 1.0f / av : 1.0f;
+      gbv[r] = __uint_as_float(v0.y);
       gtab[r] = cells0 + v0.z;
       gcmf[r] = (float)v0.w;
       gfs[r] = v1.y | ((v1.x == 0xFFFFFFFFu ? 0xFFFFFFu : v1.x) << 8);
@@ -149,7 +154,10 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   }
   // QJL rows of this wave (all 64 tokens): [jb, je)
   const int jb = (w * m) / NW, je = ((w + 1) * m) / NW;
-  const uint4 *Rf = (const uint4 *)(a.blob + (GRID ? hd->off_Rfrag : hd->off_Rfrag2));
+  // Grid quantiser, plain heads: R with row i scaled by a_i and the
+  // accumulators started at b_i, so the MFMAs give u = a_i y_i + b_i directly
+  // (signal residuals take y = (u - b_i) / a_i).
+  const uint4 *Rf = (const uint4 *)(a.blob + (GRID ? (UQ ? hd->off_Rfrag_u : hd->off_Rfrag) : hd->off_Rfrag2));
   uint4 rf[3][KB];
 #pragma unroll
   for (int sp = 0; sp < 3; ++sp)
@@ -237,8 +245,9 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
   for (int t = tb; t < te; ++t, par ^= 1, rb = rb == 2 ? 0 : rb + 1) {
     // ---- rotate: 16 rows x 64 tokens (4 blocks of 16)
     f32x4 acc[4];
+    const f32x4 acc0 = UQ ? gbv : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[j] = acc0;
     const char *xt = (const char *)(smem + a.lds_x_off + par * a.x_buf_floats) + xrow;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
         for (int j = 0; j < 4; ++j) {
           // a NaN u converts to cell 0 and fails the compare: code 0
           // (v_med3_f32 returns 0 for a NaN first operand; +-inf clamp to the ends)
-          const float u = fmaf(NORM ? acc[j][r] * inv_nu[j] : acc[j][r], ga[r], gb[r]);
+          const float u = UQ ? acc[j][r] : fmaf(acc[j][r] * inv_nu[j], ga[r], gbv[r]);
           const int cell = (int)__builtin_amdgcn_fmed3f(u, 0.0f, gcmf[r]);
           const uint64_t e = *(lds_u64 *)(uintptr_t)(gtab[r] + (uint32_t)cell * 8u);
           code[j] = (uint32_t)(e >> 32) + (u > __uint_as_float((uint32_t)e) ? 1u : 0u);
@@ -339,10 +348,11 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
         const uint32_t gcb = gfs[r] >> 8;
         if (m > 0 && gcb != 0xFFFFFFu) {
           const int crd = 16 * w + 4 * s4 + r;  // < d_eff <= 16
+          // y = (u - b) / a (ga holds 1 / a here; 1 and b = 0 for zero-width rows)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             rtile[((lane & 15) + 16 * j) * C2_RS + crd] =
-                (NORM ? acc[j][r] * inv_nu[j] : acc[j][r]) - csig[gcb + code[j]];
+                (UQ ? (acc[j][r] - gbv[r]) * ga[r] : acc[j][r] * inv_nu[j]) - csig[gcb + code[j]];
         }
       }
       uint32_t *rw = rec + (lane & 15) * rs + (gpos & 0xFFu);

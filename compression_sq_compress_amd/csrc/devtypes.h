@@ -86,6 +86,9 @@ struct DevHead {
   int64_t off_gcoord;   // uint32 [d][GRID_COORD_WORDS]
   int64_t off_gcells;   // uint32 [n_gcells][2]
   int64_t off_gcsig;    // float [n_gcsig] signal centroids * sigma_i, per coordinate
+  int64_t off_Rfrag_u;  // bf16 [3][d/16][d/32][64][8] like off_Rfrag with row i scaled by the
+                        // grid quantiser's a_i (its MFMA gives u = a_i y_i + b_i when the
+                        // accumulator starts at b_i); grid heads only
 };
 
 // Grid quantiser.  A coordinate's thresholds are sigma_i times the thresholds
@@ -151,6 +154,6 @@ static_assert(sizeof(DevCoord) == 16, "DevCoord layout");
 constexpr int FS_SLOTS = 8;
 constexpr int FG_BITS = 6;
 
-static_assert(sizeof(DevHead) == 248, "DevHead layout");
+static_assert(sizeof(DevHead) == 256, "DevHead layout");
 
 }  // namespace sq

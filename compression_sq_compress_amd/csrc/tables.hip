@@ -697,6 +697,7 @@ sq_status upload_tables(sq_calib *c, void *stream) {
     D.off_gcoord = off;  off = align256(off + sizeof(uint32_t) * std::max<size_t>(1, Gp.coord.size()));
     D.off_gcells = off;  off = align256(off + sizeof(uint32_t) * std::max<size_t>(1, Gp.cells.size()));
     D.off_gcsig = off;   off = align256(off + sizeof(float) * std::max<size_t>(1, Gp.csig.size()));
+    D.off_Rfrag_u = off; off = align256(off + (Gp.ok ? sizeof(uint16_t) * 3 * d * d : 1));
   }
   std::vector<uint8_t> img(off, 0);
   std::memcpy(img.data(), desc.data(), sizeof(DevHead) * nh);
@@ -712,26 +713,40 @@ sq_status upload_tables(sq_calib *c, void *stream) {
       for (int j = 0; j < d; ++j) RT[(size_t)j * d + i] = (float)hc.R[(size_t)i * d + j];
     // bf16 x3 split of R (hi + mid + lo reproduces R to ~2^-24 relative), laid
     // out as MFMA 16x16x32 A operands: fragment (s, mb, kb), lane l, element e
-    // holds R_s[mb*16 + l%16][kb*32 + 8*(l/16) + e].
-    uint16_t *F = (uint16_t *)(img.data() + D.off_Rfrag);
+    // holds R_s[mb*16 + l%16][kb*32 + 8*(l/16) + e]; row_scale multiplies row i
+    // (in double, before the split) by row_scale[i]
     const int MB = d / 16, KB = d / 32;
-    for (int mb = 0; mb < MB; ++mb)
-      for (int kb = 0; kb < KB; ++kb)
-        for (int l = 0; l < 64; ++l)
-          for (int e = 0; e < 8; ++e) {
-            const int row = mb * 16 + (l & 15), col = kb * 32 + 8 * (l >> 4) + e;
-            double v = hc.R[(size_t)row * d + col];
-            uint16_t parts[3];
-            for (int s = 0; s < 3; ++s) {
-              parts[s] = f32_to_bf16_rne((float)v);
-              float back;
-              uint32_t u = (uint32_t)parts[s] << 16;
-              std::memcpy(&back, &u, 4);
-              v -= (double)back;
+    auto fragments = [&](uint16_t *F, const std::vector<double> *row_scale) {
+      for (int mb = 0; mb < MB; ++mb)
+        for (int kb = 0; kb < KB; ++kb)
+          for (int l = 0; l < 64; ++l)
+            for (int e = 0; e < 8; ++e) {
+              const int row = mb * 16 + (l & 15), col = kb * 32 + 8 * (l >> 4) + e;
+              double v = hc.R[(size_t)row * d + col] * (row_scale ? (*row_scale)[row] : 1.0);
+              uint16_t parts[3];
+              for (int s = 0; s < 3; ++s) {
+                parts[s] = f32_to_bf16_rne((float)v);
+                float back;
+                uint32_t u = (uint32_t)parts[s] << 16;
+                std::memcpy(&back, &u, 4);
+                v -= (double)back;
+              }
+              for (int s = 0; s < 3; ++s)
+                F[((((size_t)s * MB + mb) * KB + kb) * 64 + l) * 8 + e] = parts[s];
             }
-            for (int s = 0; s < 3; ++s)
-              F[((((size_t)s * MB + mb) * KB + kb) * 64 + l) * 8 + e] = parts[s];
-          }
+    };
+    fragments((uint16_t *)(img.data() + D.off_Rfrag), nullptr);
+    if (grids[h].ok) {
+      // rows scaled by the grid's a_i (the float the kernel would multiply
+      // by); a zero-width signal row keeps scale 1 (its u is y, its code 0)
+      std::vector<double> a_row(d);
+      for (int i = 0; i < d; ++i) {
+        float av;
+        std::memcpy(&av, &grids[h].coord[(size_t)i * GRID_COORD_WORDS + 0], 4);
+        a_row[i] = (hc.widths[i] == 0 && hc.m > 0 && i < hc.d_eff) ? 1.0 : (double)av;
+      }
+      fragments((uint16_t *)(img.data() + D.off_Rfrag_u), &a_row);
+    }
     {
       const HostPlan2 &P2 = plans2[h];
       if (P2.ok) {
