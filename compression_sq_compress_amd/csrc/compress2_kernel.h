@@ -28,7 +28,9 @@ namespace sq {
 //             tile, and those words are stored after the next barrier.
 // With GRID the quantise step reads instead one grid cell per value (code =
 // cells' count left of it + one compare with the cell's threshold), the MFMA
-// rows are the coordinates in natural order (R fragments of compress_kernel),
+// rows are the coordinates in natural order (R fragments of compress_kernel;
+// for plain heads pre-scaled by the grid's a_i, the accumulators starting at
+// b_i, so that the MFMAs return the grid coordinate u = a_i y_i + b_i),
 // and a lane's four codes (coordinates 16 w + 4 s .. + 3, adjacent fields) are
 // combined in registers and OR-ed into the record tile as one 64-bit window.
 // x tiles are double-buffered and fetched two tiles ahead; the record tile

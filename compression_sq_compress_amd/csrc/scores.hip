@@ -27,7 +27,10 @@ namespace sq {
 // with direct-to-LDS loads issued by the loader waves, DS super-steps of NS
 // slots ahead; one workgroup barrier per super-step.  The partial sums of a
 // wave group meet in LDS and are added in a fixed order (deterministic) one
-// super-step later, the last wave of each group adding the QJL term.
+// super-step later by the wave that owns the query head's row, which adds
+// the QJL term too (gamma times one or two reads of per-query tables over the
+// sign-bit patterns, built in the prologue; sketches longer than 16 rows are
+// summed bit by bit into a wave's partial instead).
 
 constexpr int SC_WAVES = 8;    // consumer waves per workgroup
 constexpr int SC_LOADERS = 3;  // waves issuing the record loads
