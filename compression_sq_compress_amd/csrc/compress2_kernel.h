@@ -191,15 +191,16 @@ __global__ __launch_bounds__(D * 4, 4) void compress2_kernel(Compress2Args a) {
     // only zero-fills destination words, reads nothing else)
     const int64_t t0 = min<int64_t>((int64_t)tl * 64, a.n_tokens - 1);
     const char *src = xbase + t0 * a.xs_t * ESZ;
-    const int last = (int)min<int64_t>(63, a.n_tokens - 1 - t0);
-    const int ln = lane_now();
+    const uint32_t last = (uint32_t)min<int64_t>(63, a.n_tokens - 1 - t0);
+    const uint32_t ln = (uint32_t)lane_now();
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int q = w * NB + i;
-      const int byte = q * 1024 + ln * 16, row = byte / RB, slot = (byte % RB) / 16;
-      const int c = slot ^ ((row / RPB) & (CPR - 1));
-      lds_dma16(src, (uint32_t)min(row, last) * row_bytes + (uint32_t)c * 16u,
-                lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + (uint32_t)q * 1024u);
+      // unsigned, so that the divisions by the power-of-two row size are shifts
+      const uint32_t q = (uint32_t)(w * NB + i);
+      const uint32_t byte = q * 1024u + ln * 16u, row = byte / RB, slot = (byte % RB) / 16u;
+      const uint32_t c = slot ^ ((row / RPB) & (CPR - 1));
+      lds_dma16(src, min(row, last) * row_bytes + c * 16u,
+                lds_x + (uint32_t)buf * (uint32_t)a.x_buf_floats * 4u + q * 1024u);
     }
   };
   for (int k = threadIdx.x; k < 3 * 64 * rs; k += NT) smem[a.lds_rec_off + k] = 0.0f;
