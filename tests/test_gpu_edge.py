@@ -186,6 +186,23 @@ def test_batch_with_shared_and_per_batch_calibration(torch_dev, sq):
             H.compare_compress(lors[8 * b + h], lpn[b, h], xl[b, h], T)
 
 
+@pytest.mark.parametrize("budget", [0.125, 0.25])
+def test_zero_width_signal_coordinates(torch_dev, sq, budget):
+    """Budgets below one bit per coordinate on the tiny workload (d_eff 9)
+    leave signal coordinates of width zero: they carry no code but enter the
+    QJL residual with their full value, a case the grid quantiser's
+    pre-scaled rotation rows handle apart (scale 1, code 0)."""
+    cfg = wl.CONFIGS["tiny"]
+    heads = [(0, 0), (1, 2)]
+    _case(f"zero-width signal coordinates: tiny, budget {budget}")
+    X, G = H.calib_inputs(cfg, heads, "k")
+    cal = sq.sq_calibrate(X, budget, cfg.qjl_bits, G)
+    inf = cal.info(0)
+    w = cal.export(0)["widths"]
+    assert (w[:inf.d_eff] == 0).any() and inf.m > 0, (w[:inf.d_eff], inf.m)
+    _e2e(torch_dev, sq, cfg, heads, 200, budget, torch_dev.float32)
+
+
 @pytest.mark.parametrize("budget", [0.5, 1.0, 6.0, 8.0])
 def test_extreme_budgets(torch_dev, sq, budget):
     """Low budgets leave many zero-width coordinates; 8 bits/coord gives every
